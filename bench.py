@@ -1,0 +1,186 @@
+"""Benchmark of the dMel front end on one MI355X.
+
+One step = one pass of the whole hot path over one batch: framing + FFT +
+log-mel + quantizer (dmel_levels), the RMSNorm scales (dmel_rms_scale) and the
+bag-of-bins embedding with RMSNorm and bf16 output (dmel_embed) - the three
+launches dmel_forward enqueues - for 64 clips of 20 minutes of speech-like
+16 kHz audio (1,536,000 tokens of width 6144).  Inputs are generated on the
+device before the timed region.
+
+Prints one JSON line (see the fields below).  ``--gpus N`` with N > 1 exits:
+this front end runs on one GPU here.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from encoder_free_audio_amd import dmel as dm  # noqa: E402
+from encoder_free_audio_amd import synth  # noqa: E402
+
+ADDS_PER_TOKEN = 79 * 6144                 # sequential fp32 adds of the bag-of-bins sum
+HBM_BYTES_PER_TOKEN = 2 * 800 * 2 + 6144 * 2  # 3,200 B audio read + 12,288 B bf16 token write
+PEAK_ADD_TFLOPS = 256 * 64 * 2.4e9 / 1e12   # v_add_f32: 256 CUs x 64 lanes x 2.4 GHz = 39.32 T adds/s
+PEAK_HBM_GBPS = 8000.0
+METRIC = "audio tokens/sec (dMel frames→6144-d embeds) + achieved HBM GB/s vs peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--clips", type=int, default=64)
+    ap.add_argument("--minutes", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-frames", type=int, default=1200, help="oracle sample: frames per worker")
+    return ap.parse_args()
+
+
+def cpu_baseline(audio_dev, clip_len, table_bits, n_clips, frames_per_worker):
+    """Time the CPU oracle on a bounded sample of the same workload: the first
+    frames of several clips (causal framing makes them the clip's first frames)."""
+    import multiprocessing as mp
+
+    from oracle import dmel_oracle  # noqa: F401  (imported here: test infrastructure)
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    workers = max(1, min(cores, 16, n_clips))
+    n = frames_per_worker * 800
+    segs = [audio_dev[c * clip_len: c * clip_len + n].cpu().numpy() for c in range(workers)]
+    tb = table_bits.cpu().numpy().view(np.uint16)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        t0 = time.perf_counter()
+        res = pool.starmap(_oracle_job, [(s, tb) for s in segs])
+        dt = time.perf_counter() - t0
+    tokens = sum(res)
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"first {frames_per_worker} frames of each of {workers} clips ({tokens} tokens, "
+                      f"RMSNorm on, bf16 out), one oracle process per core, {dt:.1f} s wall"}
+
+
+def _oracle_job(seg, tb):
+    from threadpoolctl import threadpool_limits
+
+    from oracle import dmel_oracle as o
+    with threadpool_limits(1):
+        _, _, out, _ = o.forward(seg, tb, rms_weight=np.ones(tb.shape[1], dtype=np.float32))
+    return int(out.shape[0])
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs the dMel front end on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards by clips with no collective, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda"
+    n_clips = args.clips
+    clip_len = int(round(args.minutes * 60 * 16000))
+    T_clip = dm.dmel_num_frames(clip_len)
+    n_tok = n_clips * T_clip
+    d = 6144
+    print(f"[bench] generating {n_clips} x {args.minutes:g} min speech-like audio on the GPU", file=sys.stderr,
+          flush=True)
+    t0 = time.time()
+    audio = synth.speech_clips(seed=2, lengths=[clip_len] * n_clips, device=dev)
+    table = synth.table_bf16(seed=1234).to(dev)
+    rms_w = torch.ones(d, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    ctx = dm.dmel_create(0)
+    so, fo, T = dm.clip_offsets([clip_len] * n_clips, dev)
+    assert T == n_tok
+    out = torch.empty((n_tok, d), dtype=torch.int16, device=dev)
+    gram = torch.empty((1280, 1280), dtype=torch.float32, device=dev)
+    levels = torch.empty((n_tok, 80), dtype=torch.uint8, device=dev)
+    scale = torch.empty(n_tok, dtype=torch.float32, device=dev)
+    dm.dmel_rms_gram(table, d, gram)   # once per table (weight preparation), outside the step
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dm.dmel_levels(ctx, audio, audio.numel(), so, fo, n_clips, n_tok, None, levels, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        dm.dmel_rms_scale(levels, n_tok, gram, d, 1e-6, scale, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        dm.dmel_embed(levels, n_tok, table, d, rms_w, scale, out, dm.DMEL_BF16, d, None, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in events])  # ms
+    k_front, k_scale, k_embed = per.mean(axis=0)
+    ms_step = wall * 1e3 / args.steps
+    tok_s = n_tok / (ms_step * 1e-3)
+    embed_adds = ADDS_PER_TOKEN * n_tok
+    achieved = embed_adds / (k_embed * 1e-3) / 1e12
+    hbm = HBM_BYTES_PER_TOKEN * n_tok / (ms_step * 1e-3) / 1e9
+    print(f"[bench] per step: levels {k_front:.3f} ms, rms_scale {k_scale:.3f} ms, embed {k_embed:.3f} ms; "
+          f"wall {ms_step:.3f} ms", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        try:
+            cpu = cpu_baseline(audio, clip_len, table, n_clips, args.cpu_frames)
+        except Exception as e:  # report, never hide the GPU line
+            cpu = {"value": None, "unit": "tokens/s", "cores": 0, "kind": "oracle", "sample": f"failed: {e}"}
+    dm.dmel_destroy(ctx)
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"dMel forward: {n_clips} clips x {args.minutes:g} min of 16 kHz speech-like audio "
+                               f"({n_tok} tokens), table 1280x6144 bf16, fp32 sum, RMSNorm on, bf16 out",
+                   "global_batch": n_clips, "seq_len": T_clip, "parallelism": "single GPU"},
+        "hbm_achieved_GBps": hbm,
+        "hbm_frac": hbm / PEAK_HBM_GBPS,
+        "kernel_ms": {"frontend_levels": k_front, "rms_scale": k_scale, "embed": k_embed},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_ADD_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_ADD_TFLOPS, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

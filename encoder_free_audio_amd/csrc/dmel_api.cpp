@@ -1,0 +1,333 @@
+// C ABI of libdmel: argument validation (host only, before any HIP call),
+// context management and kernel launches.  See include/dmel.h.
+#include "dmel.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "internal.h"
+
+struct dmel_ctx {
+  int device = -1;
+  void* dev_mem = nullptr;  // one allocation holding every constant table
+  dmel::FrontTables tabs{};
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DMEL_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Validation of the audio arguments shared by dmel_frames/levels/forward.
+int check_audio(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total, const int64_t* sample_off,
+                const int64_t* frame_off, int32_t n_clips, int64_t n_frames_total, const void* out,
+                const char* out_name) {
+  if (n_samples_total < 0) return fail(DMEL_EINVAL, "n_samples_total is negative (%lld)", (long long)n_samples_total);
+  if (n_clips < 0) return fail(DMEL_EINVAL, "n_clips is negative (%d)", n_clips);
+  if (n_frames_total < 0) return fail(DMEL_EINVAL, "n_frames_total is negative (%lld)", (long long)n_frames_total);
+  if (n_frames_total > n_samples_total / dmel::kHop)
+    return fail(DMEL_ESHAPE, "n_frames_total %lld exceeds n_samples_total / 800 = %lld", (long long)n_frames_total,
+                (long long)(n_samples_total / dmel::kHop));
+  if (n_frames_total > 0 && n_clips == 0) return fail(DMEL_ESHAPE, "frames requested but n_clips is 0");
+  if (n_frames_total > 0) {
+    if (audio == nullptr) return fail(DMEL_EINVAL, "audio is NULL");
+    if (sample_off == nullptr || frame_off == nullptr) return fail(DMEL_EINVAL, "sample_off / frame_off is NULL");
+    if (out == nullptr) return fail(DMEL_EINVAL, "%s is NULL", out_name);
+    if (!aligned(audio, 4)) return fail(DMEL_EALIGN, "audio is not 4-byte aligned");
+    if (!aligned(sample_off, 8) || !aligned(frame_off, 8)) return fail(DMEL_EALIGN, "offset arrays are not 8-byte aligned");
+  }
+  if (ctx == nullptr) return fail(DMEL_EINVAL, "ctx is NULL");
+  if (ctx->dev_mem == nullptr) return fail(DMEL_ESTATE, "ctx has no device tables");
+  return DMEL_OK;
+}
+
+int check_table(const uint16_t* table, int32_t d_model) {
+  if (d_model < 16 || d_model > 65536 || d_model % 16 != 0)
+    return fail(DMEL_ESHAPE, "d_model must be a multiple of 16 in [16, 65536] (got %d)", d_model);
+  if (table == nullptr) return fail(DMEL_EINVAL, "table is NULL");
+  if (!aligned(table, 16)) return fail(DMEL_EALIGN, "table is not 16-byte aligned");
+  return DMEL_OK;
+}
+
+int check_out(void* out, int32_t out_dtype, int64_t out_row_stride, int32_t width, const int64_t* out_rows) {
+  if (out_dtype != DMEL_BF16 && out_dtype != DMEL_F32) return fail(DMEL_EDTYPE, "unsupported out_dtype %d", out_dtype);
+  if (out == nullptr) return fail(DMEL_EINVAL, "out is NULL");
+  const int64_t esize = out_dtype == DMEL_BF16 ? 2 : 4;
+  if (out_row_stride < width) return fail(DMEL_ESHAPE, "out_row_stride %lld < d_model %d", (long long)out_row_stride, width);
+  if (!aligned(out, 16)) return fail(DMEL_EALIGN, "out is not 16-byte aligned");
+  if ((out_row_stride * esize) % 16 != 0) return fail(DMEL_EALIGN, "out_row_stride * element size is not a multiple of 16 bytes");
+  if (out_rows != nullptr && !aligned(out_rows, 8)) return fail(DMEL_EALIGN, "out_rows is not 8-byte aligned");
+  return DMEL_OK;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+int dmel_get_params(dmel_params* out) {
+  if (out == nullptr) return fail(DMEL_EINVAL, "out is NULL");
+  out->sample_rate = dmel::kSampleRate;
+  out->hop = dmel::kHop;
+  out->window = dmel::kWindow;
+  out->n_fft = dmel::kNfft;
+  out->n_bins = dmel::kBins;
+  out->n_mels = dmel::kMels;
+  out->n_levels = dmel::kLevels;
+  out->n_rows = dmel::kRows;
+  out->clamp_min = dmel::kClampMin;
+  out->clamp_max = dmel::kClampMax;
+  out->log_floor = dmel::kLogFloor;
+  out->f_min_hz = 0.0f;
+  out->f_max_hz = dmel::kSampleRate / 2.0f;
+  return DMEL_OK;
+}
+
+int64_t dmel_num_frames(int64_t n_samples) { return n_samples < 0 ? -1 : n_samples / dmel::kHop; }
+
+const char* dmel_last_error(void) { return g_last_error.c_str(); }
+
+int dmel_create(dmel_ctx** out, int device) {
+  if (out == nullptr) return fail(DMEL_EINVAL, "out is NULL");
+  *out = nullptr;
+  int n_dev = 0;
+  hipError_t e = hipGetDeviceCount(&n_dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+  if (device < 0 || device >= n_dev) return fail(DMEL_EINVAL, "device %d out of range (%d devices)", device, n_dev);
+  int prev = 0;
+  e = hipGetDevice(&prev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipSetDevice(device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+
+  dmel::HostTables* h = new (std::nothrow) dmel::HostTables;
+  dmel_ctx* ctx = new (std::nothrow) dmel_ctx;
+  if (h == nullptr || ctx == nullptr) {
+    delete h;
+    delete ctx;
+    (void)hipSetDevice(prev);
+    return fail(DMEL_ENOMEM, "host allocation failed");
+  }
+  dmel::build_host_tables(h);
+  // layout: window | tw800 | tw1600 | mel_lo | mel_cnt | mel_off | mel_w
+  size_t off_window = 0;
+  size_t off_tw800 = round_up(off_window + sizeof(h->window), 256);
+  size_t off_tw1600 = round_up(off_tw800 + sizeof(h->tw800), 256);
+  size_t off_lo = round_up(off_tw1600 + sizeof(h->tw1600), 256);
+  size_t off_cnt = round_up(off_lo + sizeof(h->mel_lo), 256);
+  size_t off_off = round_up(off_cnt + sizeof(h->mel_cnt), 256);
+  size_t off_w = round_up(off_off + sizeof(h->mel_off), 256);
+  size_t total = round_up(off_w + sizeof(float) * h->mel_nnz, 256);
+  char* staging = new (std::nothrow) char[total];
+  if (staging == nullptr) {
+    delete h;
+    delete ctx;
+    (void)hipSetDevice(prev);
+    return fail(DMEL_ENOMEM, "host allocation failed");
+  }
+  std::memset(staging, 0, total);
+  std::memcpy(staging + off_window, h->window, sizeof(h->window));
+  std::memcpy(staging + off_tw800, h->tw800, sizeof(h->tw800));
+  std::memcpy(staging + off_tw1600, h->tw1600, sizeof(h->tw1600));
+  std::memcpy(staging + off_lo, h->mel_lo, sizeof(h->mel_lo));
+  std::memcpy(staging + off_cnt, h->mel_cnt, sizeof(h->mel_cnt));
+  std::memcpy(staging + off_off, h->mel_off, sizeof(h->mel_off));
+  std::memcpy(staging + off_w, h->mel_w, sizeof(float) * h->mel_nnz);
+  int rc = DMEL_OK;
+  char* dev = nullptr;
+  e = hipMalloc(reinterpret_cast<void**>(&dev), total);
+  if (e != hipSuccess) {
+    rc = fail(DMEL_ENOMEM, "hipMalloc of %zu bytes failed: %s", total, hipGetErrorString(e));
+  } else {
+    e = hipMemcpy(dev, staging, total, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      rc = hip_fail(e, "hipMemcpy of constant tables");
+      (void)hipFree(dev);
+      dev = nullptr;
+    }
+  }
+  if (rc == DMEL_OK) {
+    ctx->device = device;
+    ctx->dev_mem = dev;
+    ctx->tabs.window = reinterpret_cast<const float*>(dev + off_window);
+    ctx->tabs.tw800 = reinterpret_cast<const float2*>(dev + off_tw800);
+    ctx->tabs.tw1600 = reinterpret_cast<const float2*>(dev + off_tw1600);
+    ctx->tabs.mel_lo = reinterpret_cast<const int*>(dev + off_lo);
+    ctx->tabs.mel_cnt = reinterpret_cast<const int*>(dev + off_cnt);
+    ctx->tabs.mel_off = reinterpret_cast<const int*>(dev + off_off);
+    ctx->tabs.mel_w = reinterpret_cast<const float*>(dev + off_w);
+    ctx->tabs.mel_nnz = h->mel_nnz;
+    *out = ctx;
+  } else {
+    delete ctx;
+  }
+  delete[] staging;
+  delete h;
+  (void)hipSetDevice(prev);
+  return rc;
+}
+
+int dmel_destroy(dmel_ctx* ctx) {
+  if (ctx == nullptr) return DMEL_OK;
+  int rc = DMEL_OK;
+  if (ctx->dev_mem != nullptr) {
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(ctx->device);
+    hipError_t e = hipFree(ctx->dev_mem);
+    if (e != hipSuccess) rc = hip_fail(e, "hipFree");
+    (void)hipSetDevice(prev);
+  }
+  ctx->dev_mem = nullptr;
+  delete ctx;
+  return rc;
+}
+
+int dmel_frames(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total, const int64_t* sample_off,
+                const int64_t* frame_off, int32_t n_clips, int64_t n_frames_total, const float* carry,
+                float* logmel, void* stream) {
+  int rc = check_audio(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, logmel, "logmel");
+  if (rc != DMEL_OK) return rc;
+  if (carry != nullptr && !aligned(carry, 4)) return fail(DMEL_EALIGN, "carry is not 4-byte aligned");
+  if (n_frames_total == 0) return DMEL_OK;
+  hipError_t e = dmel::launch_frontend(ctx->tabs, audio, n_samples_total, sample_off, frame_off, n_clips,
+                                       n_frames_total, carry, logmel, nullptr, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "frontend launch");
+}
+
+int dmel_levels(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total, const int64_t* sample_off,
+                const int64_t* frame_off, int32_t n_clips, int64_t n_frames_total, const float* carry,
+                uint8_t* levels, void* stream) {
+  int rc = check_audio(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, levels, "levels");
+  if (rc != DMEL_OK) return rc;
+  if (carry != nullptr && !aligned(carry, 4)) return fail(DMEL_EALIGN, "carry is not 4-byte aligned");
+  if (n_frames_total == 0) return DMEL_OK;
+  hipError_t e = dmel::launch_frontend(ctx->tabs, audio, n_samples_total, sample_off, frame_off, n_clips,
+                                       n_frames_total, carry, nullptr, levels, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "frontend launch");
+}
+
+int dmel_rms_gram(const uint16_t* table, int32_t d_model, float* gram, void* stream) {
+  int rc = check_table(table, d_model);
+  if (rc != DMEL_OK) return rc;
+  if (gram == nullptr) return fail(DMEL_EINVAL, "gram is NULL");
+  if (!aligned(gram, 4)) return fail(DMEL_EALIGN, "gram is not 4-byte aligned");
+  hipError_t e = dmel::launch_gram(table, d_model, gram, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "gram launch");
+}
+
+int dmel_rms_scale(const uint8_t* levels, int64_t n_tokens, const float* gram, int32_t d_model, float eps,
+                   float* scale, void* stream) {
+  if (n_tokens < 0) return fail(DMEL_EINVAL, "n_tokens is negative");
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(DMEL_EINVAL, "eps must be finite and >= 0");
+  if (d_model <= 0) return fail(DMEL_ESHAPE, "d_model must be positive");
+  if (n_tokens == 0) return DMEL_OK;
+  if (levels == nullptr || gram == nullptr || scale == nullptr) return fail(DMEL_EINVAL, "NULL pointer argument");
+  if (!aligned(levels, 16)) return fail(DMEL_EALIGN, "levels is not 16-byte aligned");
+  if (!aligned(gram, 4) || !aligned(scale, 4)) return fail(DMEL_EALIGN, "gram / scale not 4-byte aligned");
+  hipError_t e = dmel::launch_rms_scale(levels, n_tokens, gram, d_model, eps, scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "rms_scale launch");
+}
+
+int dmel_embed(const uint8_t* levels, int64_t n_tokens, const uint16_t* table, int32_t d_model,
+               const float* rms_weight, const float* rms_scale, void* out, int32_t out_dtype,
+               int64_t out_row_stride, const int64_t* out_rows, void* stream) {
+  if (n_tokens < 0) return fail(DMEL_EINVAL, "n_tokens is negative");
+  int rc = check_table(table, d_model);
+  if (rc != DMEL_OK) return rc;
+  rc = check_out(out, out_dtype, out_row_stride, d_model, out_rows);
+  if (rc != DMEL_OK) return rc;
+  if (rms_weight != nullptr && rms_scale == nullptr) return fail(DMEL_EINVAL, "rms_weight given without rms_scale");
+  if (rms_weight != nullptr && (!aligned(rms_weight, 4) || !aligned(rms_scale, 4)))
+    return fail(DMEL_EALIGN, "rms_weight / rms_scale not 4-byte aligned");
+  if (n_tokens == 0) return DMEL_OK;
+  if (levels == nullptr) return fail(DMEL_EINVAL, "levels is NULL");
+  if (!aligned(levels, 16)) return fail(DMEL_EALIGN, "levels is not 16-byte aligned");
+  hipError_t e = dmel::launch_embed(levels, n_tokens, table, d_model, rms_weight, rms_scale, out,
+                                    out_dtype == DMEL_F32, out_row_stride, out_rows, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "embed launch");
+}
+
+size_t dmel_forward_workspace_bytes(int64_t n_frames_total) {
+  if (n_frames_total < 0) return 0;
+  const size_t n = static_cast<size_t>(n_frames_total);
+  return round_up(n * dmel::kMels, 256) + round_up(n * sizeof(float), 256);
+}
+
+int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total, const int64_t* sample_off,
+                 const int64_t* frame_off, int32_t n_clips, int64_t n_frames_total, const float* carry,
+                 const uint16_t* table, int32_t d_model, const float* rms_weight, const float* gram, float eps,
+                 void* out, int32_t out_dtype, int64_t out_row_stride, const int64_t* out_rows, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  int rc = check_audio(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, out, "out");
+  if (rc != DMEL_OK) return rc;
+  if (carry != nullptr && !aligned(carry, 4)) return fail(DMEL_EALIGN, "carry is not 4-byte aligned");
+  rc = check_table(table, d_model);
+  if (rc != DMEL_OK) return rc;
+  rc = check_out(out, out_dtype, out_row_stride, d_model, out_rows);
+  if (rc != DMEL_OK) return rc;
+  if (rms_weight != nullptr) {
+    if (gram == nullptr) return fail(DMEL_EINVAL, "rms_weight given without gram");
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(DMEL_EINVAL, "eps must be finite and >= 0");
+    if (!aligned(rms_weight, 4) || !aligned(gram, 4)) return fail(DMEL_EALIGN, "rms_weight / gram not 4-byte aligned");
+  }
+  const size_t need = dmel_forward_workspace_bytes(n_frames_total);
+  if (workspace_bytes < need)
+    return fail(DMEL_ENOMEM, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  if (n_frames_total == 0) return DMEL_OK;
+  if (workspace == nullptr) return fail(DMEL_EINVAL, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(DMEL_EALIGN, "workspace is not 256-byte aligned");
+  auto* levels = static_cast<uint8_t*>(workspace);
+  auto* scale = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         round_up(static_cast<size_t>(n_frames_total) * dmel::kMels, 256));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dmel::launch_frontend(ctx->tabs, audio, n_samples_total, sample_off, frame_off, n_clips,
+                                       n_frames_total, carry, nullptr, levels, s);
+  if (e != hipSuccess) return hip_fail(e, "frontend launch");
+  if (rms_weight != nullptr) {
+    e = dmel::launch_rms_scale(levels, n_frames_total, gram, d_model, eps, scale, s);
+    if (e != hipSuccess) return hip_fail(e, "rms_scale launch");
+  }
+  e = dmel::launch_embed(levels, n_frames_total, table, d_model, rms_weight, rms_weight ? scale : nullptr, out,
+                         out_dtype == DMEL_F32, out_row_stride, out_rows, s);
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "embed launch");
+}
+
+int dmel_gather_rows(const uint16_t* table, int64_t n_table_rows, int32_t d_model, const int32_t* ids, int64_t n,
+                     uint16_t* out, int64_t out_row_stride, const int64_t* out_rows, void* stream) {
+  if (n < 0 || n_table_rows < 0) return fail(DMEL_EINVAL, "negative count");
+  if (d_model <= 0 || d_model % 8 != 0) return fail(DMEL_ESHAPE, "d_model must be a positive multiple of 8");
+  int rc = check_out(out, DMEL_BF16, out_row_stride, d_model, out_rows);
+  if (rc != DMEL_OK) return rc;
+  if (n == 0) return DMEL_OK;
+  if (table == nullptr || ids == nullptr) return fail(DMEL_EINVAL, "table / ids is NULL");
+  if (!aligned(table, 16)) return fail(DMEL_EALIGN, "table is not 16-byte aligned");
+  if (!aligned(ids, 4)) return fail(DMEL_EALIGN, "ids is not 4-byte aligned");
+  hipError_t e = dmel::launch_gather_rows(table, n_table_rows, d_model, ids, n, out, out_row_stride, out_rows,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "gather_rows launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,321 @@
+// Front end: framing + Hann window + 1600-point real FFT + power + sparse mel
+// projection + log + clamp + 16-level quantizer, fused in one kernel.
+//
+// "Inside Inkling: Audio Design", Part 1: 16 kHz mono audio becomes an
+// 80-channel log-mel spectrogram (hop 800, window 1600) whose 80 values per
+// frame are quantized to 16 levels; "Why this is a reasonable bet" gives the
+// clamp range [-7, 2].  Open steps are read as: causal framing (frame t of a
+// clip covers samples [800 t - 800, 800 t + 800), the clip's carry or zeros
+// before sample 0), periodic Hann window, 1600-point FFT with 801 bins, power
+// spectrum, 80 HTK triangles over 0..8000 Hz, ln(max(M, 1e-10)), and
+// level = min(15, floor((clamp(l, -7, 2) + 7) * 16 / 9)) decided exactly.
+//
+// Work decomposition (one workgroup = 256 threads = 8 frames, fp32, LDS):
+//  1. load the 1600 windowed samples of each frame as 800 complex values
+//     z[m] = x[2m] + i x[2m+1];
+//  2. 800-point complex FFT, 800 = 32 x 25:
+//     pass A - one thread per (frame, n1 < 32): a 25-point DFT (5 x 5) over
+//              z[n1 + 32 n2] in registers, then the twiddle W800^(n1 k2);
+//     pass B - one thread per (frame, k2 < 25): a 32-point DFT (8 x 4) over
+//              n1 in registers, giving Z[k2 + 25 k1];
+//     the exchange between the passes goes through LDS rows padded to 33
+//     complex values so that neither pass has bank conflicts;
+//  3. split Z into the 801-bin spectrum of the real frame and take |X|^2;
+//  4. each (frame, filter) sums its contiguous band of weighted bins, then log,
+//     clamp and quantize.
+#include "internal.h"
+
+namespace dmel {
+namespace {
+
+constexpr int kFramesPerBlock = 8;
+constexpr int kThreads = 256;
+constexpr int kSlots = 825;  // complex slots per frame in LDS: 25 rows x 33
+
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+  return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+// multiply by -i
+__device__ __forceinline__ float2 mul_mi(float2 a) { return make_float2(a.y, -a.x); }
+
+// In-place 5-point forward DFT, X_k = sum_n x_n exp(-2 pi i n k / 5).
+__device__ __forceinline__ void dft5(float2& x0, float2& x1, float2& x2, float2& x3, float2& x4) {
+  const float c1 = 0.30901699437494745f;   // cos(2 pi / 5)
+  const float c2 = -0.8090169943749473f;   // cos(4 pi / 5)
+  const float s1 = 0.9510565162951535f;    // sin(2 pi / 5)
+  const float s2 = 0.5877852522924732f;    // sin(4 pi / 5)
+  const float2 t1 = cadd(x1, x4), t2 = cadd(x2, x3);
+  const float2 t3 = csub(x1, x4), t4 = csub(x2, x3);
+  const float2 a1 = make_float2(x0.x + c1 * t1.x + c2 * t2.x, x0.y + c1 * t1.y + c2 * t2.y);
+  const float2 a2 = make_float2(x0.x + c2 * t1.x + c1 * t2.x, x0.y + c2 * t1.y + c1 * t2.y);
+  const float2 b1 = make_float2(s1 * t3.x + s2 * t4.x, s1 * t3.y + s2 * t4.y);
+  const float2 b2 = make_float2(s2 * t3.x - s1 * t4.x, s2 * t3.y - s1 * t4.y);
+  x0 = cadd(x0, cadd(t1, t2));
+  // X1 = a1 - i b1, X4 = a1 + i b1, X2 = a2 - i b2, X3 = a2 + i b2
+  x1 = make_float2(a1.x + b1.y, a1.y - b1.x);
+  x4 = make_float2(a1.x - b1.y, a1.y + b1.x);
+  x2 = make_float2(a2.x + b2.y, a2.y - b2.x);
+  x3 = make_float2(a2.x - b2.y, a2.y + b2.x);
+}
+
+// In-place 4-point forward DFT.
+__device__ __forceinline__ void dft4(float2& a0, float2& a1, float2& a2, float2& a3) {
+  const float2 t0 = cadd(a0, a2), t1 = csub(a0, a2);
+  const float2 t2 = cadd(a1, a3), t3 = csub(a1, a3);
+  a0 = cadd(t0, t2);
+  a2 = csub(t0, t2);
+  a1 = cadd(t1, mul_mi(t3));
+  a3 = csub(t1, mul_mi(t3));
+}
+
+// 8-point forward DFT of v[0..7] (in place), radix 2 over two 4-point DFTs.
+__device__ __forceinline__ void dft8(float2 (&v)[8]) {
+  const float h = 0.70710678118654752f;
+  float2 e0 = v[0], e1 = v[2], e2 = v[4], e3 = v[6];
+  float2 o0 = v[1], o1 = v[3], o2 = v[5], o3 = v[7];
+  dft4(e0, e1, e2, e3);
+  dft4(o0, o1, o2, o3);
+  // W8^1 = h (1 - i), W8^2 = -i, W8^3 = h (-1 - i)
+  const float2 w1o = make_float2(h * (o1.x + o1.y), h * (o1.y - o1.x));
+  const float2 w2o = mul_mi(o2);
+  const float2 w3o = make_float2(h * (o3.y - o3.x), -h * (o3.x + o3.y));
+  v[0] = cadd(e0, o0);
+  v[4] = csub(e0, o0);
+  v[1] = cadd(e1, w1o);
+  v[5] = csub(e1, w1o);
+  v[2] = cadd(e2, w2o);
+  v[6] = csub(e2, w2o);
+  v[3] = cadd(e3, w3o);
+  v[7] = csub(e3, w3o);
+}
+
+// Clip of global frame g: the largest c with frame_off[c] <= g.
+__device__ __forceinline__ int clip_of(const int64_t* frame_off, int n_clips, int64_t g) {
+  int lo = 0, hi = n_clips;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (frame_off[mid] <= g) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Exact level of a log-mel value: the number of edges -7 + 9k/16 (k = 1..15)
+// that the clamped value reaches, i.e. floor((c + 7) * 16 / 9) without rounding.
+__device__ __forceinline__ int quantize(float l) {
+  const float c = fminf(fmaxf(l, kClampMin), kClampMax);
+  int q = static_cast<int>((c - kClampMin) * (16.0f / 9.0f));
+  q = q > 15 ? 15 : q;
+  // the estimate is within one of the exact level; the edges are exact in fp32
+  if (q > 0 && c < kClampMin + 0.5625f * static_cast<float>(q)) --q;
+  if (q < 15 && c >= kClampMin + 0.5625f * static_cast<float>(q + 1)) ++q;
+  return q;
+}
+
+__global__ void __launch_bounds__(kThreads)
+frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_samples_total,
+                const int64_t* __restrict__ sample_off, const int64_t* __restrict__ frame_off,
+                int n_clips, int64_t n_frames, const float* __restrict__ carry,
+                float* __restrict__ logmel, uint8_t* __restrict__ levels) {
+  __shared__ float2 zbuf[kFramesPerBlock * kSlots];
+  __shared__ float2 tw[kHalf];
+  __shared__ int64_t s_base[kFramesPerBlock];
+  __shared__ int s_clip[kFramesPerBlock];
+  __shared__ int s_first[kFramesPerBlock];
+  __shared__ int s_valid[kFramesPerBlock];
+
+  const int tid = threadIdx.x;
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kFramesPerBlock;
+
+  for (int i = tid; i < kHalf; i += kThreads) tw[i] = tabs.tw800[i];
+  if (tid < kFramesPerBlock) {
+    const int64_t g = g0 + tid;
+    const int valid = g < n_frames;
+    int c = 0;
+    int64_t base = 0;
+    int first = 0;
+    if (valid) {
+      c = clip_of(frame_off, n_clips, g);
+      const int64_t t = g - frame_off[c];
+      base = sample_off[c] + kHop * t - kHop;
+      first = (t == 0);
+    }
+    s_valid[tid] = valid;
+    s_clip[tid] = c;
+    s_base[tid] = base;
+    s_first[tid] = first;
+  }
+  __syncthreads();
+
+  // ---- 1. windowed samples, stored as z[m] = (x[2m], x[2m+1]) -----------
+  {
+    float* zf = reinterpret_cast<float*>(zbuf);
+    for (int it = tid; it < kFramesPerBlock * kWindow; it += kThreads) {
+      const int f = it / kWindow;
+      const int n = it - f * kWindow;
+      float v = 0.0f;
+      if (s_valid[f]) {
+        if (s_first[f] && n < kHop) {
+          if (carry != nullptr) v = carry[static_cast<int64_t>(s_clip[f]) * kHop + n];
+        } else {
+          const int64_t s = s_base[f] + n;
+          if (s >= 0 && s < n_samples_total) v = audio[s];
+        }
+      }
+      zf[2 * f * kSlots + n] = v * tabs.window[n];
+    }
+  }
+  __syncthreads();
+
+  const int f = tid >> 5;      // frame within the block
+  const int lane = tid & 31;   // n1 in pass A, k2 in pass B
+  float2* zf = zbuf + f * kSlots;
+
+  // ---- 2a. 25-point DFTs over n2 for each n1, then twiddle ---------------
+  {
+    float2 x[25];
+#pragma unroll
+    for (int n2 = 0; n2 < 25; ++n2) x[n2] = zf[lane + 32 * n2];
+    // n2 = 5 a + b: 5-point DFTs over a for each b
+#pragma unroll
+    for (int b = 0; b < 5; ++b) dft5(x[b], x[5 + b], x[10 + b], x[15 + b], x[20 + b]);
+    // twiddle W25^(b c) for slot 5 c + b  (W25^m = W800^(32 m))
+#pragma unroll
+    for (int c = 1; c < 5; ++c) {
+#pragma unroll
+      for (int b = 1; b < 5; ++b) x[5 * c + b] = cmul(x[5 * c + b], tw[32 * b * c]);
+    }
+    // 5-point DFTs over b for each c: output index c + 5 d
+    float2 y[25];
+#pragma unroll
+    for (int c = 0; c < 5; ++c) {
+      float2 u0 = x[5 * c], u1 = x[5 * c + 1], u2 = x[5 * c + 2], u3 = x[5 * c + 3], u4 = x[5 * c + 4];
+      dft5(u0, u1, u2, u3, u4);
+      y[c] = u0;
+      y[c + 5] = u1;
+      y[c + 10] = u2;
+      y[c + 15] = u3;
+      y[c + 20] = u4;
+    }
+#pragma unroll
+    for (int k2 = 1; k2 < 25; ++k2) y[k2] = cmul(y[k2], tw[lane * k2]);
+    __syncthreads();
+#pragma unroll
+    for (int k2 = 0; k2 < 25; ++k2) zf[lane + 33 * k2] = y[k2];
+  }
+  __syncthreads();
+
+  // ---- 2b. 32-point DFTs over n1 for each k2 ---------------------------
+  {
+    float2 a[32];
+    const bool active = lane < 25;
+    const int k2 = active ? lane : 0;
+#pragma unroll
+    for (int n1 = 0; n1 < 32; ++n1) a[n1] = zf[n1 + 33 * k2];
+    // n1 = 4 p + q: 8-point DFTs over p for each q, output r
+    float2 v[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) v[q][p] = a[4 * p + q];
+      dft8(v[q]);
+    }
+    // twiddle W32^(q r) = W800^(25 q r)
+#pragma unroll
+    for (int q = 1; q < 4; ++q) {
+#pragma unroll
+      for (int r = 1; r < 8; ++r) v[q][r] = cmul(v[q][r], tw[25 * q * r]);
+    }
+    // 4-point DFTs over q for each r: output k1 = r + 8 s
+#pragma unroll
+    for (int r = 0; r < 8; ++r) dft4(v[0][r], v[1][r], v[2][r], v[3][r]);
+    __syncthreads();
+    if (active) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) zf[k2 + 25 * (r + 8 * s)] = v[s][r];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. real-spectrum split and power ---------------------------------
+  // E[k] = (Z[k] + conj Z[800-k]) / 2, O[k] = (Z[k] - conj Z[800-k]) / 2i,
+  // X[k] = E + W1600^k O and X[800-k] = conj(E - W1600^k O), k = 0..400.
+  constexpr int kPairs = kHalf / 2 + 1;  // 401
+  constexpr int kItems = kFramesPerBlock * kPairs;
+  constexpr int kPer = (kItems + kThreads - 1) / kThreads;
+  float p_lo[kPer], p_hi[kPer];
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) {
+    const int it = tid + kThreads * m;
+    p_lo[m] = 0.0f;
+    p_hi[m] = 0.0f;
+    if (it < kItems) {
+      const int ff = it / kPairs;
+      const int k = it - ff * kPairs;
+      const float2 zk = zbuf[ff * kSlots + k];
+      const float2 zm = zbuf[ff * kSlots + (k == 0 ? 0 : kHalf - k)];
+      const float2 e = make_float2(0.5f * (zk.x + zm.x), 0.5f * (zk.y - zm.y));
+      const float2 o = make_float2(0.5f * (zk.y + zm.y), -0.5f * (zk.x - zm.x));
+      const float2 wo = cmul(tabs.tw1600[k], o);
+      const float2 x1 = cadd(e, wo), x2 = csub(e, wo);
+      p_lo[m] = x1.x * x1.x + x1.y * x1.y;
+      p_hi[m] = x2.x * x2.x + x2.y * x2.y;
+    }
+  }
+  __syncthreads();
+  {
+    float* pf = reinterpret_cast<float*>(zbuf);
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int it = tid + kThreads * m;
+      if (it < kItems) {
+        const int ff = it / kPairs;
+        const int k = it - ff * kPairs;
+        pf[2 * ff * kSlots + k] = p_lo[m];
+        pf[2 * ff * kSlots + kHalf - k] = p_hi[m];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. mel bands, log, clamp, quantize ---------------------------------
+  {
+    const float* pf = reinterpret_cast<const float*>(zbuf);
+    for (int it = tid; it < kFramesPerBlock * kMels; it += kThreads) {
+      const int ff = it / kMels;
+      const int j = it - ff * kMels;
+      const int64_t g = g0 + ff;
+      if (g >= n_frames) continue;
+      const int lo = tabs.mel_lo[j];
+      const int cnt = tabs.mel_cnt[j];
+      const float* w = tabs.mel_w + tabs.mel_off[j];
+      const float* pw = pf + 2 * ff * kSlots + lo;
+      float m = 0.0f;
+      for (int i = 0; i < cnt; ++i) m = fmaf(w[i], pw[i], m);
+      const float l = logf(fmaxf(m, kLogFloor));
+      if (logmel != nullptr) logmel[g * kMels + j] = l;
+      if (levels != nullptr) levels[g * kMels + j] = static_cast<uint8_t>(quantize(l));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_frontend(const FrontTables& tabs, const float* audio, int64_t n_samples_total,
+                           const int64_t* sample_off, const int64_t* frame_off, int n_clips,
+                           int64_t n_frames, const float* carry, float* logmel, uint8_t* levels,
+                           hipStream_t stream) {
+  if (n_frames <= 0) return hipSuccess;
+  const int64_t blocks = (n_frames + kFramesPerBlock - 1) / kFramesPerBlock;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(frontend_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                     tabs, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames, carry,
+                     logmel, levels);
+  return hipGetLastError();
+}
+
+}  // namespace dmel

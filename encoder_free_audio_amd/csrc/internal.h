@@ -1,0 +1,70 @@
+// Internal declarations shared by the host API and the HIP kernels of libdmel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace dmel {
+
+// Front-end constants ("Inside Inkling: Audio Design", Part 1 and "Why this is
+// a reasonable bet": 16 kHz, hop 800, window 1600, 80 mel bins, 16 levels).
+constexpr int kSampleRate = 16000;
+constexpr int kHop = 800;
+constexpr int kWindow = 1600;
+constexpr int kNfft = 1600;
+constexpr int kBins = 801;    // one-sided bins of the 1600-point FFT
+constexpr int kHalf = 800;    // the real FFT runs as an 800-point complex FFT
+constexpr int kMels = 80;
+constexpr int kLevels = 16;
+constexpr int kRows = kMels * kLevels;  // 1280
+constexpr float kClampMin = -7.0f;
+constexpr float kClampMax = 2.0f;
+constexpr float kLogFloor = 1e-10f;
+
+// Device-resident constant tables of a context.
+struct FrontTables {
+  const float* window;   // [1600] periodic Hann
+  const float2* tw800;   // [800] exp(-2 pi i m / 800)
+  const float2* tw1600;  // [401] exp(-2 pi i k / 1600)
+  const int* mel_lo;     // [80] first bin with a nonzero weight
+  const int* mel_cnt;    // [80] number of nonzero weights
+  const int* mel_off;    // [80] offset of the filter's weights in mel_w
+  const float* mel_w;    // [mel_nnz] weights, bin order
+  int mel_nnz;
+};
+
+// Host-built tables, in the layout FrontTables points to (see tables.cpp).
+struct HostTables {
+  float window[kWindow];
+  float tw800[2 * kHalf];
+  float tw1600[2 * (kHalf / 2 + 1)];
+  int mel_lo[kMels];
+  int mel_cnt[kMels];
+  int mel_off[kMels];
+  float mel_w[kBins * 2];
+  int mel_nnz;
+};
+void build_host_tables(HostTables* t);
+
+// Kernel launchers (all enqueue on `stream` and return the launch status).
+hipError_t launch_frontend(const FrontTables& tabs, const float* audio, int64_t n_samples_total,
+                           const int64_t* sample_off, const int64_t* frame_off, int n_clips,
+                           int64_t n_frames, const float* carry, float* logmel, uint8_t* levels,
+                           hipStream_t stream);
+
+hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, const uint16_t* table, int d_model,
+                        const float* rms_weight, const float* rms_scale, void* out, bool out_f32,
+                        int64_t out_row_stride, const int64_t* out_rows, hipStream_t stream);
+
+hipError_t launch_gram(const uint16_t* table, int d_model, float* gram, hipStream_t stream);
+
+hipError_t launch_rms_scale(const uint8_t* levels, int64_t n_tokens, const float* gram, int d_model,
+                            float eps, float* scale, hipStream_t stream);
+
+hipError_t launch_gather_rows(const uint16_t* table, int64_t n_table_rows, int d_model,
+                              const int32_t* ids, int64_t n, uint16_t* out, int64_t out_row_stride,
+                              const int64_t* out_rows, hipStream_t stream);
+
+}  // namespace dmel

@@ -1,0 +1,66 @@
+// Host construction of the front end's constant tables, in fp64, stored fp32.
+//
+// Readings of the open steps ("Inside Inkling: Audio Design", Part 1 names an
+// 80-channel log-mel over a 1600-sample window; the page gives no window shape,
+// FFT size or mel formula):
+//  * periodic Hann window w[n] = 0.5 - 0.5 cos(2 pi n / 1600);
+//  * 1600-point FFT computed as an 800-point complex FFT of the even/odd
+//    sample pairs, so the twiddles needed are exp(-2 pi i m / 800) and, for the
+//    final real-spectrum split, exp(-2 pi i k / 1600);
+//  * 80 triangular filters on the HTK mel scale m(f) = 2595 log10(1 + f / 700),
+//    82 edges equally spaced in mel from 0 Hz to 8000 Hz (outer edges set to
+//    exactly 0 and 8000 Hz), unit peak, evaluated at bin frequencies 10 k Hz.
+#include <cmath>
+
+#include "internal.h"
+
+namespace dmel {
+
+namespace {
+double hz_to_mel(double f) { return 2595.0 * std::log10(1.0 + f / 700.0); }
+double mel_to_hz(double m) { return 700.0 * (std::pow(10.0, m / 2595.0) - 1.0); }
+}  // namespace
+
+void build_host_tables(HostTables* t) {
+  const double two_pi = 2.0 * M_PI;
+  for (int n = 0; n < kWindow; ++n) {
+    t->window[n] = static_cast<float>(0.5 - 0.5 * std::cos(two_pi * n / kWindow));
+  }
+  for (int m = 0; m < kHalf; ++m) {
+    t->tw800[2 * m] = static_cast<float>(std::cos(two_pi * m / kHalf));
+    t->tw800[2 * m + 1] = static_cast<float>(-std::sin(two_pi * m / kHalf));
+  }
+  for (int k = 0; k <= kHalf / 2; ++k) {
+    t->tw1600[2 * k] = static_cast<float>(std::cos(two_pi * k / kNfft));
+    t->tw1600[2 * k + 1] = static_cast<float>(-std::sin(two_pi * k / kNfft));
+  }
+  // mel filter edges
+  double edges[kMels + 2];
+  const double mel_hi = hz_to_mel(kSampleRate / 2.0);
+  for (int i = 0; i < kMels + 2; ++i) edges[i] = mel_to_hz(mel_hi * i / (kMels + 1));
+  edges[0] = 0.0;
+  edges[kMels + 1] = kSampleRate / 2.0;
+  int nnz = 0;
+  for (int j = 0; j < kMels; ++j) {
+    const double lo = edges[j], mid = edges[j + 1], hi = edges[j + 2];
+    int first = -1, count = 0;
+    for (int k = 0; k < kBins; ++k) {
+      const double f = static_cast<double>(k) * kSampleRate / kNfft;
+      const double up = (f - lo) / (mid - lo);
+      const double down = (hi - f) / (hi - mid);
+      const double w = std::fmax(0.0, std::fmin(up, down));
+      if (w > 0.0) {
+        if (first < 0) first = k;
+        t->mel_w[nnz + count] = static_cast<float>(w);
+        ++count;
+      }
+    }
+    t->mel_lo[j] = first < 0 ? 0 : first;
+    t->mel_cnt[j] = count;
+    t->mel_off[j] = nnz;
+    nnz += count;
+  }
+  t->mel_nnz = nnz;
+}
+
+}  // namespace dmel

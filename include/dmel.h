@@ -1,0 +1,202 @@
+/*
+ * dmel.h - C ABI of libdmel, the gfx950 (MI355X) implementation of the dMel
+ * audio front end: 16 kHz mono audio -> 80-bin log-mel -> 16 levels per bin ->
+ * one d_model-wide token per frame (the sum of 80 rows of a 1280-row table).
+ *
+ * The method is described in "Inside Inkling: Audio Design", Part 1 -
+ * Modeling (pipeline, nn.Embedding(80 x 16 = 1280 -> 6144), optional RMSNorm)
+ * and its subsection "Why this is a reasonable bet" (hop 800, window 1600,
+ * 20 frames per second, n_mel_bins 80, mel_vocab_size 16, clamp [-7, 2], each
+ * bin owning a block of 16 rows).  Steps the page leaves open are fixed as:
+ * periodic Hann window, 1600-point FFT (801 bins), power spectrum, 80 HTK
+ * triangles over 0..8000 Hz (unit peak, edges equally spaced in mel),
+ * ln(max(M, 1e-10)), level = min(15, floor((clamp(x, -7, 2) + 7) * 16 / 9))
+ * evaluated exactly, causal framing (frame t of a clip covers samples
+ * [800 t - 800, 800 t + 800), with the clip's 800-sample carry or zeros before
+ * sample 0, so a clip of N samples gives floor(N / 800) frames), table row
+ * 16 * bin + level, sum in fp32 in bin order 0..79, and
+ * RMSNorm y = s * w / sqrt(mean(s^2) + eps).
+ *
+ * Conventions shared by every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller, unless a
+ *    comment says otherwise.  The library allocates nothing after
+ *    dmel_create and never synchronises inside a call: every compute call
+ *    validates its arguments on the host, enqueues work on `stream`
+ *    (a hipStream_t; NULL = the legacy default stream) and returns.
+ *  - Argument validation is host code that runs before any HIP call.  On an
+ *    error the call returns a negative dmel_status, enqueues nothing, and
+ *    dmel_last_error() describes the failure (thread-local).  A failed launch
+ *    returns DMEL_EHIP with the HIP error string.
+ *  - Ragged clips: clip c is audio[sample_off[c] .. sample_off[c+1]) and its
+ *    frames are token rows frame_off[c] .. frame_off[c+1), where
+ *    frame_off[0] = 0 and frame_off[c+1] - frame_off[c] =
+ *    (sample_off[c+1] - sample_off[c]) / 800.  Both arrays are device int64
+ *    [n_clips + 1] and must be non-decreasing.  Offsets that break these rules
+ *    give unspecified values but never an out-of-bounds access: every sample
+ *    read is bounds-checked against n_samples_total.
+ *  - bf16 values travel as their uint16 bit patterns.  bf16 outputs are
+ *    rounded to nearest-even.
+ */
+#ifndef DMEL_H
+#define DMEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dmel_status {
+  DMEL_OK = 0,
+  DMEL_EINVAL = -1,  /* null pointer, negative count, bad enum value */
+  DMEL_ESHAPE = -2,  /* inconsistent sizes (d_model, strides, frame counts) */
+  DMEL_EDTYPE = -3,  /* unsupported output dtype */
+  DMEL_EALIGN = -4,  /* pointer or stride not aligned as required */
+  DMEL_EHIP = -5,    /* a HIP runtime call or kernel launch failed */
+  DMEL_ENOMEM = -6,  /* device allocation failed (dmel_create only) or workspace too small */
+  DMEL_ESTATE = -7   /* context not usable (wrong device, destroyed) */
+} dmel_status;
+
+typedef enum dmel_dtype { DMEL_BF16 = 0, DMEL_F32 = 1 } dmel_dtype;
+
+/* Fixed constants of the front end (read-only). */
+typedef struct dmel_params {
+  int32_t sample_rate;  /* 16000 */
+  int32_t hop;          /* 800 */
+  int32_t window;       /* 1600 */
+  int32_t n_fft;        /* 1600 */
+  int32_t n_bins;       /* 801 */
+  int32_t n_mels;       /* 80 */
+  int32_t n_levels;     /* 16 */
+  int32_t n_rows;       /* 1280 = n_mels * n_levels */
+  float clamp_min;      /* -7.0 */
+  float clamp_max;      /* 2.0 */
+  float log_floor;      /* 1e-10 */
+  float f_min_hz;       /* 0 */
+  float f_max_hz;       /* 8000 */
+} dmel_params;
+
+/* Opaque per-device context: holds the window, FFT twiddles and the sparse
+ * mel filterbank, uploaded once to the device it was created on. */
+typedef struct dmel_ctx dmel_ctx;
+
+/* Fills *out with the constants above.  DMEL_EINVAL if out is NULL. */
+int dmel_get_params(dmel_params* out);
+
+/* Frames produced by a clip of n_samples samples: floor(n_samples / 800)
+ * (the "audio_tokens" count a server reports for that clip; "Inside Inkling:
+ * Audio Design", Part 3, "Where audio touches the serving path").
+ * Returns -1 for a negative count. */
+int64_t dmel_num_frames(int64_t n_samples);
+
+/* Thread-local description of the last failure in this thread ("" if none). */
+const char* dmel_last_error(void);
+
+/* Creates a context on HIP device `device`: allocates and uploads the constant
+ * tables (about 30 KB), synchronously.  The only call that allocates device
+ * memory.  The caller's current device is left unchanged.
+ * Errors: DMEL_EINVAL (out NULL, bad device), DMEL_ENOMEM, DMEL_EHIP. */
+int dmel_create(dmel_ctx** out, int device);
+
+/* Frees a context (NULL is a no-op).  Work already enqueued with it must have
+ * completed. */
+int dmel_destroy(dmel_ctx* ctx);
+
+/* Log-mel of every frame ("an 80-channel log-mel spectrogram", Part 1).
+ *  audio      fp32 [n_samples_total], 4-byte aligned
+ *  carry      fp32 [n_clips, 800] or NULL: the samples that precede each clip
+ *             (the previous hop of a stream); NULL means zeros
+ *  logmel     fp32 [n_frames_total, 80] out, row-major
+ * Frames are independent; the result depends only on each frame's 1600
+ * samples.  Arithmetic is fp32.
+ * Errors: DMEL_EINVAL, DMEL_ESHAPE (n_frames_total > n_samples_total / 800),
+ * DMEL_EALIGN, DMEL_EHIP. */
+int dmel_frames(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total,
+                const int64_t* sample_off, const int64_t* frame_off, int32_t n_clips,
+                int64_t n_frames_total, const float* carry, float* logmel, void* stream);
+
+/* Levels of every frame ("each of the 80 mel energies in a frame is quantized
+ * to one of 16 levels", Part 1; clamp range [-7, 2], "Why this is a reasonable
+ * bet").  Same audio arguments as dmel_frames.
+ *  levels     uint8 [n_frames_total, 80] out, values 0..15.
+ * The level is decided exactly from the fp32 log-mel value that dmel_frames
+ * returns for the same input. */
+int dmel_levels(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total,
+                const int64_t* sample_off, const int64_t* frame_off, int32_t n_clips,
+                int64_t n_frames_total, const float* carry, uint8_t* levels, void* stream);
+
+/* Gram matrix of the table, G[r][r'] = sum_c E[r][c] * E[r'][c], accumulated
+ * in fp64 and stored as fp32, for the RMSNorm of dmel_embed / dmel_forward.
+ *  table      bf16 [1280, d_model], 16-byte aligned, row-major
+ *  gram       fp32 [1280, 1280] out (both triangles are written)
+ * Recompute whenever the table's contents change.  d_model % 16 == 0. */
+int dmel_rms_gram(const uint16_t* table, int32_t d_model, float* gram, void* stream);
+
+/* Per-token RMSNorm scale r_t = 1 / sqrt(|s_t|^2 / d_model + eps), where
+ * |s_t|^2 = sum_{j,j'} G[16 j + L_tj][16 j' + L_tj'] is the squared norm of
+ * the exact sum of the token's 80 rows (the "optional RMSNorm" of Part 1).
+ * It differs from the norm of the fp32-rounded sum by about 1e-7 relative.
+ *  levels     uint8 [n_tokens, 80], 16-byte aligned; values > 15 read as 15
+ *  gram       fp32 [1280, 1280] from dmel_rms_gram
+ *  scale      fp32 [n_tokens] out
+ * Errors: DMEL_EINVAL (eps < 0 or not finite), DMEL_EALIGN, DMEL_ESHAPE. */
+int dmel_rms_scale(const uint8_t* levels, int64_t n_tokens, const float* gram, int32_t d_model,
+                   float eps, float* scale, void* stream);
+
+/* Bag-of-bins embedding ("A frame's 80 rows are summed into one 6144-dimensional
+ * vector, with an optional RMSNorm", Part 1; "each mel bin owns its own block of
+ * 16 rows", "Why this is a reasonable bet").
+ *  levels     uint8 [n_tokens, 80], 16-byte aligned; values > 15 read as 15, so
+ *             no table read is out of bounds
+ *  table      bf16 [1280, d_model], 16-byte aligned; row 16 * bin + level
+ *  d_model    multiple of 16, 16 <= d_model <= 65536
+ *  rms_weight fp32 [d_model] or NULL (NULL: no RMSNorm)
+ *  rms_scale  fp32 [n_tokens] from dmel_rms_scale; required iff rms_weight
+ *  out        out_dtype (DMEL_BF16 / DMEL_F32) rows of d_model values; token i
+ *             goes to row out_rows ? out_rows[i] : i, i.e. at
+ *             out + row * out_row_stride elements; 16-byte aligned, and
+ *             out_row_stride * element size must be a multiple of 16 bytes
+ *  out_rows   int64 [n_tokens] or NULL; rows must be distinct and in range
+ * Token value: s = E[r_0], then s = fl32(s + E[r_j]) for j = 1..79, exactly
+ * (bit-identical to that sequential fp32 sum); with RMSNorm, y = s * r * w in
+ * fp32. */
+int dmel_embed(const uint8_t* levels, int64_t n_tokens, const uint16_t* table, int32_t d_model,
+               const float* rms_weight, const float* rms_scale, void* out, int32_t out_dtype,
+               int64_t out_row_stride, const int64_t* out_rows, void* stream);
+
+/* Bytes of device workspace dmel_forward needs for n_frames_total frames
+ * (levels plus per-token scales, each 256-byte aligned).  0 for a negative count. */
+size_t dmel_forward_workspace_bytes(int64_t n_frames_total);
+
+/* End to end: audio -> levels -> tokens, i.e. dmel_levels, then (when
+ * rms_weight is non-NULL) dmel_rms_scale with `gram`, then dmel_embed, on one
+ * stream.  Audio arguments as dmel_frames, table/output arguments as
+ * dmel_embed.  `workspace` is device memory of at least
+ * dmel_forward_workspace_bytes(n_frames_total) bytes, 256-byte aligned; it
+ * holds intermediates only and may be reused once the call's work is done.
+ * gram is required iff rms_weight is non-NULL. */
+int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total,
+                 const int64_t* sample_off, const int64_t* frame_off, int32_t n_clips,
+                 int64_t n_frames_total, const float* carry, const uint16_t* table,
+                 int32_t d_model, const float* rms_weight, const float* gram, float eps,
+                 void* out, int32_t out_dtype, int64_t out_row_stride, const int64_t* out_rows,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Row copy for the text positions of an interleaved sequence (one audio item
+ * expands into its frame positions among text tokens; "Inside Inkling: Audio
+ * Design", Part 3, "Where audio touches the serving path").
+ *  table      bf16 [n_table_rows, d_model], 16-byte aligned
+ *  ids        int32 [n]; an id outside [0, n_table_rows) writes a zero row
+ *  out        bf16; row i goes to out + (out_rows ? out_rows[i] : i) * out_row_stride,
+ *             16-byte aligned rows as in dmel_embed
+ * d_model % 8 == 0. */
+int dmel_gather_rows(const uint16_t* table, int64_t n_table_rows, int32_t d_model,
+                     const int32_t* ids, int64_t n, uint16_t* out, int64_t out_row_stride,
+                     const int64_t* out_rows, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMEL_H */

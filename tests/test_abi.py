@@ -1,0 +1,209 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, reports the method's constants, and rejects bad arguments in host
+code before any HIP call (no GPU needed for any of these)."""
+
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+from oracle import dmel_oracle as o
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def dm():
+    from encoder_free_audio_amd import dmel
+    dmel.lib()
+    return dmel
+
+
+def _header_symbols():
+    with open(os.path.join(ROOT, "include", "dmel.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dmel_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_header_symbol(dm):
+    syms = _header_symbols()
+    assert len(syms) >= 13
+    assert sorted(dm.EXPORTS) == syms
+    out = subprocess.run(["nm", "-D", "--defined-only", dm.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (dmel_\w+)", out))
+    missing = [s for s in syms if s not in exported]
+    assert not missing, missing
+
+
+def test_params_match_the_method(dm):
+    p = dm.dmel_get_params()
+    assert p["sample_rate"] == o.SAMPLE_RATE and p["hop"] == o.HOP and p["window"] == o.WINDOW
+    assert p["n_fft"] == o.N_FFT and p["n_bins"] == o.N_BINS
+    assert p["n_mels"] == o.N_MELS and p["n_levels"] == o.N_LEVELS and p["n_rows"] == o.N_ROWS
+    assert p["clamp_min"] == o.CLAMP_MIN and p["clamp_max"] == o.CLAMP_MAX
+    assert abs(p["log_floor"] - o.LOG_FLOOR) < 1e-17
+    assert p["f_min_hz"] == o.F_MIN and p["f_max_hz"] == o.F_MAX
+
+
+def test_num_frames(dm):
+    for n in (0, 1, 799, 800, 801, 1599, 1600, 16000, 19_200_000, 2 ** 40 + 5):
+        assert dm.dmel_num_frames(n) == o.num_frames(n)
+    assert dm.dmel_num_frames(-1) == -1
+
+
+def test_workspace_bytes(dm):
+    assert dm.dmel_forward_workspace_bytes(0) == 0
+    assert dm.dmel_forward_workspace_bytes(-5) == 0
+    n = 1000
+    b = dm.dmel_forward_workspace_bytes(n)
+    assert b >= n * 80 + n * 4 and b % 256 == 0
+
+
+FAKE = 1 << 20  # an aligned, never-dereferenced address: validation fails first
+
+
+def _code(exc):
+    return exc.value.code
+
+
+def test_validation_frames(dm):
+    E = dm.DmelError
+    # negative counts
+    with pytest.raises(E) as e:
+        dm.dmel_frames(None, FAKE, -1, FAKE, FAKE, 1, 0, None, FAKE)
+    assert _code(e) == -1
+    with pytest.raises(E) as e:
+        dm.dmel_frames(None, FAKE, 1600, FAKE, FAKE, -1, 0, None, FAKE)
+    assert _code(e) == -1
+    # more frames than the audio can hold
+    with pytest.raises(E) as e:
+        dm.dmel_frames(None, FAKE, 1600, FAKE, FAKE, 1, 3, None, FAKE)
+    assert _code(e) == -2
+    # frames without clips
+    with pytest.raises(E) as e:
+        dm.dmel_frames(None, FAKE, 1600, FAKE, FAKE, 0, 1, None, FAKE)
+    assert _code(e) == -2
+    # null output / audio
+    with pytest.raises(E) as e:
+        dm.dmel_frames(None, FAKE, 1600, FAKE, FAKE, 1, 2, None, None)
+    assert _code(e) == -1
+    with pytest.raises(E) as e:
+        dm.dmel_levels(None, None, 1600, FAKE, FAKE, 1, 2, None, FAKE)
+    assert _code(e) == -1
+    # misaligned audio / offsets
+    with pytest.raises(E) as e:
+        dm.dmel_frames(None, FAKE + 2, 1600, FAKE, FAKE, 1, 2, None, FAKE)
+    assert _code(e) == -4
+    with pytest.raises(E) as e:
+        dm.dmel_frames(None, FAKE, 1600, FAKE + 4, FAKE, 1, 2, None, FAKE)
+    assert _code(e) == -4
+    # everything else valid: a NULL context is reported last
+    with pytest.raises(E) as e:
+        dm.dmel_frames(None, FAKE, 1600, FAKE, FAKE, 1, 2, None, FAKE)
+    assert _code(e) == -1 and "ctx" in str(e.value)
+    assert "ctx" in dm.dmel_last_error()
+
+
+def test_validation_embed(dm):
+    E = dm.DmelError
+    ok = dict(levels=FAKE, n_tokens=10, table=FAKE, d_model=6144, rms_weight=None, rms_scale=None, out=FAKE,
+              out_dtype=0, out_row_stride=6144)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        dm.dmel_embed(a["levels"], a["n_tokens"], a["table"], a["d_model"], a["rms_weight"], a["rms_scale"],
+                      a["out"], a["out_dtype"], a["out_row_stride"])
+
+    cases = [
+        (dict(n_tokens=-1), -1),
+        (dict(d_model=100), -2),
+        (dict(d_model=0), -2),
+        (dict(d_model=65536 + 16), -2),
+        (dict(table=None), -1),
+        (dict(table=FAKE + 8), -4),
+        (dict(out_dtype=7), -3),
+        (dict(out=None), -1),
+        (dict(out=FAKE + 4), -4),
+        (dict(out_row_stride=100), -2),
+        (dict(out_row_stride=6148), -4),   # 12296 bytes: not a multiple of 16
+        (dict(rms_weight=FAKE), -1),       # weight without scale
+        (dict(levels=None), -1),
+        (dict(levels=FAKE + 1), -4),
+    ]
+    for kw, code in cases:
+        with pytest.raises(E) as e:
+            call(**kw)
+        assert _code(e) == code, (kw, str(e.value))
+
+
+def test_validation_other_entry_points(dm):
+    E = dm.DmelError
+    with pytest.raises(E) as e:
+        dm.dmel_rms_gram(None, 6144, FAKE)
+    assert _code(e) == -1
+    with pytest.raises(E) as e:
+        dm.dmel_rms_gram(FAKE, 6008, FAKE)
+    assert _code(e) == -2
+    with pytest.raises(E) as e:
+        dm.dmel_rms_scale(FAKE, 5, FAKE, 6144, -1.0, FAKE)
+    assert _code(e) == -1
+    with pytest.raises(E) as e:
+        dm.dmel_rms_scale(FAKE, 5, FAKE, 6144, float("nan"), FAKE)
+    assert _code(e) == -1
+    with pytest.raises(E) as e:
+        dm.dmel_rms_scale(FAKE + 3, 5, FAKE, 6144, 1e-6, FAKE)
+    assert _code(e) == -4
+    with pytest.raises(E) as e:
+        dm.dmel_gather_rows(FAKE, 10, 12, FAKE, 5, FAKE, 16)
+    assert _code(e) == -2
+    with pytest.raises(E) as e:
+        dm.dmel_gather_rows(FAKE, 10, 16, None, 5, FAKE, 16)
+    assert _code(e) == -1
+    # forward: workspace too small, gram missing, bad dtype
+    args = [None, FAKE, 1600, FAKE, FAKE, 1, 2, None, FAKE, 6144, None, None, 1e-6, FAKE, 0, 6144, None]
+    with pytest.raises(E) as e:
+        dm.dmel_forward(*args, FAKE, 10)
+    assert _code(e) in (-1, -6)
+    a = list(args)
+    a[0] = None
+    with pytest.raises(E) as e:
+        dm.dmel_forward(*a, FAKE, dm.dmel_forward_workspace_bytes(2))
+    assert _code(e) == -1 and "ctx" in str(e.value)
+    with pytest.raises(E) as e:
+        dm.dmel_create(-1)
+    assert _code(e) in (-1, -5)
+
+
+def test_zero_work_is_a_noop(dm):
+    # T = 0 (short audio) and n_tokens = 0 need no pointers and no GPU
+    dm.dmel_embed(None, 0, FAKE, 6144, None, None, FAKE, 0, 6144)
+    dm.dmel_rms_scale(None, 0, None, 6144, 1e-6, None)
+    dm.dmel_gather_rows(None, 0, 16, None, 0, FAKE, 16)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    code = (
+        "import encoder_free_audio_amd.dmel as d\n"
+        "d.LIB_PATH = '/nonexistent/libdmel.so'\n"
+        "try:\n"
+        "    d.dmel_num_frames(16000)\n"
+        "except RuntimeError as e:\n"
+        "    print('RAISED', e)\n"
+    )
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert "RAISED" in out.stdout, out.stdout + out.stderr
+
+
+def test_product_path_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "encoder_free_audio_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".cpp", ".hip", ".h")):
+                with open(os.path.join(dirpath, fn)) as f:
+                    text = f.read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), fn
+                assert "dmel_oracle" not in text, fn

@@ -1,0 +1,282 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on the same seeded inputs (sizes the oracle finishes in seconds; several
+workgroup tiles and ragged tails)."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dmel_oracle as o
+from encoder_free_audio_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+P = None  # tests/_parity.py, imported lazily (it needs torch.cuda)
+
+
+@pytest.fixture(scope="module")
+def env():
+    global P
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests import _parity
+    from encoder_free_audio_amd import dmel as dm
+    P = _parity
+    ctx = dm.dmel_create(0)
+    yield dm, ctx
+    torch.cuda.synchronize()
+    dm.dmel_destroy(ctx)
+
+
+@pytest.fixture(scope="module")
+def table():
+    return synth.table_bf16(1234)
+
+
+def _tbits(t):
+    return t.numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+def test_c1_tones_end_to_end(env, table):
+    dm, ctx = env
+    x = synth.tones_clip(seed=0)
+    print("case: 1 s of three tones, seed 0", flush=True)
+    lm, lv = P.gpu_frames(ctx, P.to_dev(x), [x.size])
+    ora_lm = o.log_mel(x)
+    ora_lv = o.quantize(ora_lm)
+    assert lm.shape == (20, 80)
+    P.check_logmel(lm, ora_lm)
+    band, forgiven, frames = P.check_levels(lv, ora_lm, ora_lv, gpu_lm=lm)
+    print(f"edge band {band}, forgiven {forgiven} in {frames} frames")
+    # the first 0.25 s is exact silence: frames 0..4 are all level 0
+    assert np.all(lv[:5] == 0) and np.max(np.abs(lm[:5] - np.log(1e-10))) < 1e-5
+    tb = _tbits(table)
+    for dt in ("bf16", "f32"):
+        got = P.gpu_embed(ora_lv, table, 6144, out_dtype=dt)
+        want, _ = o.embed(ora_lv, tb, out_dtype=dt)
+        assert np.array_equal(got.view(np.uint32) if dt == "f32" else got,
+                              want.view(np.uint32) if dt == "f32" else want)
+    # end to end through dmel_forward
+    so, fo, T = P.offsets([x.size])
+    out = torch.empty((T, 6144), dtype=torch.int16, device="cuda")
+    ws = torch.empty(dm.dmel_forward_workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    dm.dmel_forward(ctx, P.to_dev(x), x.size, so, fo, 1, T, None, table.cuda(), 6144, None, None, 1e-6,
+                    out, dm.DMEL_BF16, 6144, None, ws, ws.numel())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    want, _ = o.embed(ora_lv, tb)
+    same = np.all(lv == ora_lv, axis=1)
+    assert same.sum() >= T - frames
+    assert np.array_equal(got[same], want[same])
+
+
+def test_c2_bursts_rmsnorm(env, table):
+    dm, ctx = env
+    x = synth.bursts_clips(seed=1, n_clips=8, n_samples=480000).numpy()
+    print("case: 8 x 30 s pink noise + bursts, seed 1", flush=True)
+    flat = x.reshape(-1)
+    lm, lv = P.gpu_frames(ctx, P.to_dev(flat), [480000] * 8)
+    assert lm.shape == (4800, 80)
+    ora_lm = np.concatenate([o.log_mel(x[c]) for c in range(8)])
+    ora_lv = o.quantize(ora_lm)
+    err, _ = P.check_logmel(lm, ora_lm)
+    band, forgiven, frames = P.check_levels(lv, ora_lm, ora_lv, gpu_lm=lm)
+    print(f"log-mel max err {err:.2e}; edge band {band} ({band / lv.size:.4%}), forgiven {forgiven} in {frames} frames")
+    # at least 10% of the samples are silent: whole silent frames give level 0
+    assert (lv == 0).all(axis=1).sum() > 0
+    # RMSNorm (w = 1, eps 1e-6) on clips 0 and 7, fed the oracle's levels
+    tb = _tbits(table)
+    sel = np.r_[0:600, 4200:4800]
+    w = np.ones(6144, dtype=np.float32)
+    got32 = P.gpu_embed(ora_lv[sel], table, 6144, out_dtype="f32", rms_weight=w)
+    _, exact = o.embed(ora_lv[sel], tb, rms_weight=w)
+    rel = P.check_rms_f32(got32, exact)
+    got16 = P.gpu_embed(ora_lv[sel], table, 6144, out_dtype="bf16", rms_weight=w)
+    nd = P.check_rms_bf16(got16, exact)
+    print(f"RMSNorm max rel err {rel:.2e}; bf16 midpoint differences {nd}")
+
+
+def test_embed_tiles_and_ragged_tail(env):
+    dm, ctx = env
+    rng = np.random.default_rng(21)
+    for n, d in ((2 * 1024 + 37, 256), (1, 16), (300, 6144), (1024, 48)):
+        print(f"case: random levels n={n} d_model={d}", flush=True)
+        t = synth.table_bf16(seed=100 + d, d_model=d)
+        lv = rng.integers(0, 16, size=(n, 80)).astype(np.uint8)
+        tb = _tbits(t)
+        got = P.gpu_embed(lv, t, d, out_dtype="f32")
+        want, _ = o.embed(lv, tb, out_dtype="f32")
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+        got = P.gpu_embed(lv, t, d, out_dtype="bf16")
+        want, _ = o.embed(lv, tb)
+        assert np.array_equal(got, want)
+
+
+def test_embed_fixed_order_golden(env, golden_dir):
+    dm, ctx = env
+    with open(os.path.join(golden_dir, "fixed_order.json")) as f:
+        c = json.load(f)
+    d = 16
+    table = np.full((1280, d), np.float32(c["poison"]), dtype=np.float32)
+    L = np.array([(7 * j + 3) % 16 for j in range(80)])
+    r = 16 * np.arange(80) + L
+    col = np.zeros((80, 5), dtype=np.float64)
+    col[:, 0] = 2.0 ** -24
+    col[0, 0] = 1.0
+    col[0, 1], col[1, 1], col[2, 1] = 2.0 ** 24, 1.0, -(2.0 ** 24)
+    col[0, 2], col[1, 2] = 1.0, 1.5 * 2.0 ** -24
+    col[:, 3] = np.arange(80)
+    col[:, 4] = -0.0
+    table[r, :5] = col.astype(np.float32)
+    bits = o.f32_to_bf16(table)
+    t = torch.from_numpy(bits.view(np.int16).copy())
+    got = P.gpu_embed(L[None, :].astype(np.uint8), t, d, out_dtype="f32")[0]
+    want = np.array([int(x["expect_f32_hex"], 16) for x in c["columns"]], dtype=np.uint32)
+    assert np.array_equal(got[:5].view(np.uint32), want)
+    got16 = P.gpu_embed(L[None, :].astype(np.uint8), t, d, out_dtype="bf16")[0]
+    want16 = np.array([int(x["expect_bf16_hex"], 16) for x in c["columns"]], dtype=np.uint16)
+    assert np.array_equal(got16[:5], want16)
+
+
+def test_integer_table_and_level_clamp(env):
+    dm, ctx = env
+    t = synth.integer_table(seed=5, d_model=64)
+    tab = o.bf16_to_f32(_tbits(t)).astype(np.int64)
+    rng = np.random.default_rng(6)
+    lv = rng.integers(0, 256, size=(50, 80)).astype(np.uint8)   # values > 15 read as 15
+    got = P.gpu_embed(lv, t, 64, out_dtype="f32")
+    lvc = np.minimum(lv, 15).astype(np.int64)
+    rows = 16 * np.arange(80)[None, :] + lvc
+    want = tab[rows].sum(axis=1)
+    assert np.array_equal(got.astype(np.int64), want)
+
+
+def test_ragged_clips_with_carry(env, table):
+    dm, ctx = env
+    rng = np.random.default_rng(31)
+    lengths = [0, 799, 800, 1601, 16123, 2400, 0, 8000]
+    clips = [(rng.standard_normal(n) * 0.1).astype(np.float32) for n in lengths]
+    flat = np.concatenate(clips) if sum(lengths) else np.zeros(0, np.float32)
+    carry = (rng.standard_normal((len(lengths), 800)) * 0.1).astype(np.float32)
+    for use_carry in (False, True):
+        print(f"case: ragged clips {lengths} carry={use_carry}", flush=True)
+        lm, lv = P.gpu_frames(ctx, P.to_dev(flat), lengths, carry=P.to_dev(carry) if use_carry else None)
+        ora_lm = np.concatenate([o.log_mel(clips[c], carry[c] if use_carry else None) for c in range(len(lengths))])
+        assert lm.shape == ora_lm.shape == (sum(n // 800 for n in lengths), 80)
+        P.check_logmel(lm, ora_lm)
+        P.check_levels(lv, ora_lm, o.quantize(ora_lm), gpu_lm=lm)
+
+
+def test_streaming_equals_batch(env, table):
+    dm, ctx = env
+    S, K = 37, 12
+    x = synth.bursts_clips(seed=3, n_clips=S, n_samples=800 * K).cuda()
+    so, fo, T = P.offsets([800 * K] * S)
+    batch_lv = torch.empty((T, 80), dtype=torch.uint8, device="cuda")
+    dm.dmel_levels(ctx, x.reshape(-1), x.numel(), so, fo, S, T, None, batch_lv)
+    tab = table.cuda()
+    batch_out = torch.empty((T, 6144), dtype=torch.int16, device="cuda")
+    dm.dmel_embed(batch_lv, T, tab, 6144, None, None, batch_out, dm.DMEL_BF16, 6144)
+    sso, sfo, _ = P.offsets([800] * S)
+    ws = torch.empty(dm.dmel_forward_workspace_bytes(S), dtype=torch.uint8, device="cuda")
+    carry = torch.zeros((S, 800), dtype=torch.float32, device="cuda")
+    step_out = torch.empty((S, 6144), dtype=torch.int16, device="cuda")
+    batch_out_v = batch_out.view(S, K, 6144)
+    for k in range(K):
+        hop = x[:, 800 * k: 800 * (k + 1)].contiguous()
+        dm.dmel_forward(ctx, hop.reshape(-1), hop.numel(), sso, sfo, S, S, carry, tab, 6144, None, None, 1e-6,
+                        step_out, dm.DMEL_BF16, 6144, None, ws, ws.numel())
+        torch.cuda.synchronize()
+        assert torch.equal(step_out, batch_out_v[:, k]), f"step {k}"
+        carry = hop
+    # and the stream frames agree with the oracle
+    xs = x.cpu().numpy()
+    lv_all = batch_lv.cpu().numpy().reshape(S, K, 80)
+    for s in (0, S - 1):
+        ora_lm = o.log_mel(xs[s])
+        P.check_levels(lv_all[s], ora_lm, o.quantize(ora_lm))
+
+
+def test_determinism_and_out_rows(env, table):
+    dm, ctx = env
+    rng = np.random.default_rng(41)
+    n, d = 700, 6144
+    lv = P.to_dev(rng.integers(0, 16, size=(n, 80)).astype(np.uint8))
+    tab = table.cuda()
+    a = torch.empty((n, d), dtype=torch.int16, device="cuda")
+    b = torch.empty((n, d), dtype=torch.int16, device="cuda")
+    dm.dmel_embed(lv, n, tab, d, None, None, a, dm.DMEL_BF16, d)
+    dm.dmel_embed(lv, n, tab, d, None, None, b, dm.DMEL_BF16, d)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    # scatter into a wider, larger buffer through out_rows
+    stride = d + 64
+    rows = torch.from_numpy(rng.permutation(2 * n)[:n].astype(np.int64)).cuda()
+    big = torch.full((2 * n, stride), 0x7777, dtype=torch.int16, device="cuda")
+    dm.dmel_embed(lv, n, tab, d, None, None, big, dm.DMEL_BF16, stride, rows)
+    torch.cuda.synchronize()
+    assert torch.equal(big[rows, :d], a)
+    untouched = torch.ones(2 * n, dtype=torch.bool, device="cuda")
+    untouched[rows] = False
+    assert bool((big[untouched] == 0x7777).all()) and bool((big[:, d:] == 0x7777).all())
+
+
+def test_gather_rows(env):
+    dm, ctx = env
+    rng = np.random.default_rng(51)
+    V, d, n = 1000, 128, 333
+    text = synth.table_bf16(seed=9, rows=V, d_model=d).cuda()
+    ids = rng.integers(-5, V + 5, size=n).astype(np.int32)
+    rows = rng.permutation(n + 10)[:n].astype(np.int64)
+    out = torch.full((n + 10, d), 0x1234, dtype=torch.int16, device="cuda")
+    dm.dmel_gather_rows(text, V, d, P.to_dev(ids), n, out, d, P.to_dev(rows))
+    torch.cuda.synchronize()
+    o_np = out.cpu().numpy()
+    t_np = text.cpu().numpy()
+    for i in range(n):
+        want = t_np[ids[i]] if 0 <= ids[i] < V else np.zeros(d, np.int16)
+        assert np.array_equal(o_np[rows[i]], want)
+
+
+def test_gram_and_rms_scale(env, table):
+    dm, ctx = env
+    tab = table.cuda()
+    gram = torch.empty((1280, 1280), dtype=torch.float32, device="cuda")
+    dm.dmel_rms_gram(tab, 6144, gram)
+    torch.cuda.synchronize()
+    E = o.bf16_to_f32(_tbits(table)).astype(np.float64)
+    G = E @ E.T
+    g = gram.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(g - G) / (np.abs(G) + 1e-3)) < 1e-6
+    rng = np.random.default_rng(61)
+    n = 1500
+    lv = rng.integers(0, 16, size=(n, 80)).astype(np.uint8)
+    scale = torch.empty(n, dtype=torch.float32, device="cuda")
+    dm.dmel_rms_scale(P.to_dev(lv), n, gram, 6144, 1e-6, scale)
+    torch.cuda.synchronize()
+    s = o.embed_sum(lv, _tbits(table)).astype(np.float64)
+    want = 1.0 / np.sqrt(np.mean(s * s, axis=1) + 1e-6)
+    rel = np.abs(scale.cpu().numpy() - want) / want
+    assert rel.max() < 1e-6, rel.max()
+
+
+def test_silence_and_empty(env, table):
+    dm, ctx = env
+    x = np.zeros(800 * 9 + 17, np.float32)
+    lm, lv = P.gpu_frames(ctx, P.to_dev(x), [x.size])
+    assert np.all(lv == 0)
+    got = P.gpu_embed(lv, table, 6144, out_dtype="f32")
+    want = o.embed_sum(np.zeros((1, 80), np.uint8), _tbits(table))[0]
+    assert np.array_equal(got, np.broadcast_to(want, got.shape))
+    # no frames: a valid no-op
+    so, fo, T = P.offsets([799])
+    assert T == 0
+    out = torch.full((1, 6144), 5, dtype=torch.int16, device="cuda")
+    dm.dmel_forward(ctx, P.to_dev(np.zeros(799, np.float32)), 799, so, fo, 1, 0, None, table.cuda(), 6144,
+                    None, None, 1e-6, out, dm.DMEL_BF16, 6144, None, None, 0)
+    torch.cuda.synchronize()
+    assert bool((out == 5).all())
