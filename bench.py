@@ -29,7 +29,7 @@ from encoder_free_audio_amd import dmel as dm  # noqa: E402
 from encoder_free_audio_amd import synth  # noqa: E402
 
 ADDS_PER_TOKEN = 79 * 6144                 # sequential fp32 adds of the bag-of-bins sum
-HBM_BYTES_PER_TOKEN = 2 * 800 * 2 + 6144 * 2  # 3,200 B audio read + 12,288 B bf16 token write
+HBM_BYTES_PER_TOKEN = 800 * 4 + 6144 * 2    # 3,200 B audio read (800 new samples) + 12,288 B bf16 token write
 PEAK_ADD_TFLOPS = 256 * 64 * 2.4e9 / 1e12   # v_add_f32: 256 CUs x 64 lanes x 2.4 GHz = 39.32 T adds/s
 PEAK_HBM_GBPS = 8000.0
 METRIC = "audio tokens/sec (dMel frames→6144-d embeds) + achieved HBM GB/s vs peak"

@@ -131,15 +131,14 @@ int dmel_create(dmel_ctx** out, int device) {
     return fail(DMEL_ENOMEM, "host allocation failed");
   }
   dmel::build_host_tables(h);
-  // layout: window | tw800 | tw1600 | mel_lo | mel_cnt | mel_off | mel_w
+  // layout: window | tw800 | tw1600 | seg_start | w_rise | w_fall
   size_t off_window = 0;
   size_t off_tw800 = round_up(off_window + sizeof(h->window), 256);
   size_t off_tw1600 = round_up(off_tw800 + sizeof(h->tw800), 256);
-  size_t off_lo = round_up(off_tw1600 + sizeof(h->tw1600), 256);
-  size_t off_cnt = round_up(off_lo + sizeof(h->mel_lo), 256);
-  size_t off_off = round_up(off_cnt + sizeof(h->mel_cnt), 256);
-  size_t off_w = round_up(off_off + sizeof(h->mel_off), 256);
-  size_t total = round_up(off_w + sizeof(float) * h->mel_nnz, 256);
+  size_t off_seg = round_up(off_tw1600 + sizeof(h->tw1600), 256);
+  size_t off_rise = round_up(off_seg + sizeof(h->seg_start), 256);
+  size_t off_fall = round_up(off_rise + sizeof(h->w_rise), 256);
+  size_t total = round_up(off_fall + sizeof(h->w_fall), 256);
   char* staging = new (std::nothrow) char[total];
   if (staging == nullptr) {
     delete h;
@@ -151,10 +150,9 @@ int dmel_create(dmel_ctx** out, int device) {
   std::memcpy(staging + off_window, h->window, sizeof(h->window));
   std::memcpy(staging + off_tw800, h->tw800, sizeof(h->tw800));
   std::memcpy(staging + off_tw1600, h->tw1600, sizeof(h->tw1600));
-  std::memcpy(staging + off_lo, h->mel_lo, sizeof(h->mel_lo));
-  std::memcpy(staging + off_cnt, h->mel_cnt, sizeof(h->mel_cnt));
-  std::memcpy(staging + off_off, h->mel_off, sizeof(h->mel_off));
-  std::memcpy(staging + off_w, h->mel_w, sizeof(float) * h->mel_nnz);
+  std::memcpy(staging + off_seg, h->seg_start, sizeof(h->seg_start));
+  std::memcpy(staging + off_rise, h->w_rise, sizeof(h->w_rise));
+  std::memcpy(staging + off_fall, h->w_fall, sizeof(h->w_fall));
   int rc = DMEL_OK;
   char* dev = nullptr;
   e = hipMalloc(reinterpret_cast<void**>(&dev), total);
@@ -174,11 +172,9 @@ int dmel_create(dmel_ctx** out, int device) {
     ctx->tabs.window = reinterpret_cast<const float*>(dev + off_window);
     ctx->tabs.tw800 = reinterpret_cast<const float2*>(dev + off_tw800);
     ctx->tabs.tw1600 = reinterpret_cast<const float2*>(dev + off_tw1600);
-    ctx->tabs.mel_lo = reinterpret_cast<const int*>(dev + off_lo);
-    ctx->tabs.mel_cnt = reinterpret_cast<const int*>(dev + off_cnt);
-    ctx->tabs.mel_off = reinterpret_cast<const int*>(dev + off_off);
-    ctx->tabs.mel_w = reinterpret_cast<const float*>(dev + off_w);
-    ctx->tabs.mel_nnz = h->mel_nnz;
+    ctx->tabs.seg_start = reinterpret_cast<const int*>(dev + off_seg);
+    ctx->tabs.w_rise = reinterpret_cast<const float*>(dev + off_rise);
+    ctx->tabs.w_fall = reinterpret_cast<const float*>(dev + off_fall);
     *out = ctx;
   } else {
     delete ctx;

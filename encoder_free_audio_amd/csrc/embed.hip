@@ -52,6 +52,87 @@ __device__ __forceinline__ const float4* row_ptr(const float* tab, const uint32_
   return reinterpret_cast<const float4*>(tab + (kLevels * j + L) * kPitch);
 }
 
+// Adds bins J0..J1-1 of this lane's token into acc (bin 0 initialises it).
+// Software pipeline: the four 16-byte reads of bin j + 1 are issued, then an
+// empty asm that "modifies" the accumulators and clobbers memory pins them
+// ahead of the adds of bin j, so a wave always has the next bin's reads in
+// flight while it adds the current one, and no more than that (hoisting all
+// the reads would exhaust the registers).
+template <int J0, int J1>
+__device__ __forceinline__ void add_bins(float (&acc)[kStrip], const float* tab, const uint32_t (&lv)[20]) {
+  float4 cur[4];
+  {
+    const float4* r = row_ptr(tab, lv, J0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cur[q] = r[q];
+  }
+#pragma unroll
+  for (int j = J0; j < J1; ++j) {
+    float4 nxt[4];
+    if (j + 1 < J1) {
+      const float4* r = row_ptr(tab, lv, j + 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) nxt[q] = r[q];
+    }
+    asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
+                 "+v"(acc[6]), "+v"(acc[7]), "+v"(acc[8]), "+v"(acc[9]), "+v"(acc[10]), "+v"(acc[11]),
+                 "+v"(acc[12]), "+v"(acc[13]), "+v"(acc[14]), "+v"(acc[15])::"memory");
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (j == 0) {
+        // the sum starts from the first row itself (not from +0)
+        acc[4 * q + 0] = cur[q].x;
+        acc[4 * q + 1] = cur[q].y;
+        acc[4 * q + 2] = cur[q].z;
+        acc[4 * q + 3] = cur[q].w;
+      } else {
+        acc[4 * q + 0] += cur[q].x;
+        acc[4 * q + 1] += cur[q].y;
+        acc[4 * q + 2] += cur[q].z;
+        acc[4 * q + 3] += cur[q].w;
+      }
+    }
+    if (j + 1 < J1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+    }
+  }
+}
+
+constexpr int kHalfRows = kRows / 2;                   // bins 0..39 | bins 40..79
+constexpr int kStageItems = kHalfRows * 2;             // 16-byte chunks per half strip (1280)
+constexpr int kStagePer = (kStageItems + kEmbThreads - 1) / kEmbThreads;  // 2
+
+// Global -> registers: this thread's chunks of half `half` of the strip at col0.
+__device__ __forceinline__ void stage_load(uint4 (&st)[kStagePer], const uint16_t* table, int d_model, int col0,
+                                           int half, int tid) {
+#pragma unroll
+  for (int k = 0; k < kStagePer; ++k) {
+    const int i = tid + k * kEmbThreads;
+    if (i < kStageItems) {
+      const int row = half * kHalfRows + (i >> 1);
+      st[k] = *reinterpret_cast<const uint4*>(table + static_cast<int64_t>(row) * d_model + col0 + 8 * (i & 1));
+    }
+  }
+}
+
+// Registers -> LDS as fp32 (80-byte rows).
+__device__ __forceinline__ void stage_store(float* tab, const uint4 (&st)[kStagePer], int half, int tid) {
+#pragma unroll
+  for (int k = 0; k < kStagePer; ++k) {
+    const int i = tid + k * kEmbThreads;
+    if (i < kStageItems) {
+      const int row = half * kHalfRows + (i >> 1);
+      const uint4 v = st[k];
+      float4* d = reinterpret_cast<float4*>(tab + row * kPitch + 8 * (i & 1));
+      d[0] = make_float4(bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
+                         bf16_to_f32(v.y >> 16));
+      d[1] = make_float4(bf16_to_f32(v.z & 0xFFFFu), bf16_to_f32(v.z >> 16), bf16_to_f32(v.w & 0xFFFFu),
+                         bf16_to_f32(v.w >> 16));
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kEmbThreads)
 embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_t* __restrict__ table,
              int d_model, const float* __restrict__ rms_weight, const float* __restrict__ rms_scale,
@@ -65,6 +146,11 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_
   const int64_t tb = blockIdx.x / static_cast<unsigned>(n_groups);
   const int64_t t = tb * kEmbThreads + tid;
   const bool active = t < n_tokens;
+  const int s_first = grp * kStripsPerGroup;
+  const int s_end = min(n_strips, s_first + kStripsPerGroup);
+
+  uint4 st[kStagePer];
+  stage_load(st, table, d_model, s_first * kStrip, 0, tid);
 
   uint32_t lv[20];
   if (active) {
@@ -87,73 +173,29 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_
     if (rms_weight != nullptr) scale = rms_scale[t];
     if (out_rows != nullptr) orow = out_rows[t];
   }
+  stage_store(tab, st, 0, tid);
+  __syncthreads();
 
-  for (int s = 0; s < kStripsPerGroup; ++s) {
-    const int strip = grp * kStripsPerGroup + s;
-    if (strip >= n_strips) break;
+  // Per strip: bins 0..39 come from the first half of the LDS slice and bins
+  // 40..79 from the second.  The global reads of the half needed next are
+  // issued before the adds of the current half, so the table staging overlaps
+  // the arithmetic; each half is written once its previous contents are dead.
+  for (int strip = s_first; strip < s_end; ++strip) {
     const int col0 = strip * kStrip;
     // make the levels look modified here so that the 80 row offsets are not
     // hoisted out of the strip loop (keeping them live would spill)
 #pragma unroll
     for (int i = 0; i < 20; ++i) asm volatile("" : "+v"(lv[i]));
-    __syncthreads();
-    // stage the 1280 x 16 slice as fp32, 80-byte rows
-    for (int i = tid; i < kRows * 2; i += kEmbThreads) {
-      const int row = i >> 1;
-      const int h = i & 1;
-      const uint4 v = *reinterpret_cast<const uint4*>(table + static_cast<int64_t>(row) * d_model + col0 + 8 * h);
-      float4* d = reinterpret_cast<float4*>(tab + row * kPitch + 8 * h);
-      d[0] = make_float4(bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
-                         bf16_to_f32(v.y >> 16));
-      d[1] = make_float4(bf16_to_f32(v.z & 0xFFFFu), bf16_to_f32(v.z >> 16), bf16_to_f32(v.w & 0xFFFFu),
-                         bf16_to_f32(v.w >> 16));
-    }
-    __syncthreads();
-
-    // Software pipeline over the 80 bins: the four 16-byte reads of bin j + 1
-    // are issued, then an empty asm that "modifies" the accumulators and
-    // clobbers memory pins them ahead of the adds of bin j, so a wave always
-    // has the next bin's reads in flight while it adds the current one.
+    stage_load(st, table, d_model, col0, 1, tid);
     float acc[kStrip];
 #pragma unroll
     for (int c = 0; c < kStrip; ++c) acc[c] = 0.0f;
-    float4 cur[4];
-    {
-      const float4* r = row_ptr(tab, lv, 0);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) cur[q] = r[q];
-    }
-#pragma unroll
-    for (int j = 0; j < kMels; ++j) {
-      float4 nxt[4];
-      if (j + 1 < kMels) {
-        const float4* r = row_ptr(tab, lv, j + 1);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) nxt[q] = r[q];
-      }
-      asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
-                   "+v"(acc[6]), "+v"(acc[7]), "+v"(acc[8]), "+v"(acc[9]), "+v"(acc[10]), "+v"(acc[11]),
-                   "+v"(acc[12]), "+v"(acc[13]), "+v"(acc[14]), "+v"(acc[15])::"memory");
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (j == 0) {
-          // the sum starts from the first row itself (not from +0)
-          acc[4 * q + 0] = cur[q].x;
-          acc[4 * q + 1] = cur[q].y;
-          acc[4 * q + 2] = cur[q].z;
-          acc[4 * q + 3] = cur[q].w;
-        } else {
-          acc[4 * q + 0] += cur[q].x;
-          acc[4 * q + 1] += cur[q].y;
-          acc[4 * q + 2] += cur[q].z;
-          acc[4 * q + 3] += cur[q].w;
-        }
-      }
-      if (j + 1 < kMels) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
-      }
-    }
+    add_bins<0, kMels / 2>(acc, tab, lv);
+    stage_store(tab, st, 1, tid);
+    __syncthreads();
+    const bool more = strip + 1 < s_end;
+    if (more) stage_load(st, table, d_model, col0 + kStrip, 0, tid);
+    add_bins<kMels / 2, kMels>(acc, tab, lv);
 
     if (active) {
       if (rms_weight != nullptr) {
@@ -175,6 +217,9 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_
         o[1] = make_uint4(w[4], w[5], w[6], w[7]);
       }
     }
+    // the first half was last read before the barrier above
+    if (more) stage_store(tab, st, 0, tid);
+    __syncthreads();
   }
 }
 
@@ -222,58 +267,108 @@ gram_kernel(const uint16_t* __restrict__ table, int d_model, float* __restrict__
 
 // ---------------------------------------------------------------------------
 // RMSNorm scale from the Gram matrix: |s|^2 = sum_j G[r_j][r_j]
-// + 2 sum_{j < j'} G[r_j][r_j'].  For each bin j the rows 16j..16j+15 of the
-// upper triangle (columns 16j..1279) are staged in LDS; every thread adds the
-// terms of its tokens.  Partial sums per bin are fp32, the total fp64.
+// + 2 sum_{j < j'} G[r_j][r_j'].  A workgroup owns 512 tokens (one per
+// thread).  For each bin j the 16 rows 16j..16j+15 of the upper triangle
+// (columns 16j..1279) are staged in LDS; the thread then adds the diagonal
+// term and the 79 - j terms of its token.  The token's 80 levels live in
+// registers as a byte string that is shifted by one byte per bin, so that the
+// level of bin j + q is always byte q: every index in the unrolled inner loop
+// is static, and the 79 - j lookups of a bin are independent loads.  Partial
+// sums per bin are fp32, the total fp64.
 // ---------------------------------------------------------------------------
-constexpr int kScaleThreads = 256;
-constexpr int kScaleTokPerThread = 2;
-constexpr int kScaleTokens = kScaleThreads * kScaleTokPerThread;
-constexpr int kLvPitch = 21;  // dwords per staged level row: an odd pitch spreads lanes over all banks
+constexpr int kScaleThreads = 1024;
+constexpr int kScaleTok = 2;                            // tokens per thread
+constexpr int kScaleBlock = kScaleThreads * kScaleTok;  // tokens per workgroup
+constexpr int kGPitch = kRows + 17;  // staged row pitch (floats): spreads the 16 rows over the banks
+
+// Off-diagonal terms q = 1..qlim of one staged row block (q = bin offset from
+// the block's bin).  QMAX bounds qlim for the range of bins the caller is in,
+// so the loop is fully unrolled with static register indices; terms past
+// qlim are read (inside the staged row pitch) but replaced by 0 in a select.
+template <int QMAX>
+__device__ __forceinline__ void row_terms(float (&off)[kScaleTok], const float* const (&row)[kScaleTok],
+                                          const uint32_t (&rot)[kScaleTok][20], int qlim) {
+#pragma unroll
+  for (int q = 1; q <= QMAX; ++q) {
+    const bool use = q <= qlim;
+#pragma unroll
+    for (int k = 0; k < kScaleTok; ++k) {
+      const float v = row[k][kLevels * q + ((rot[k][q >> 2] >> (8 * (q & 3))) & 0xFFu)];
+      off[k] += use ? v : 0.0f;
+    }
+  }
+}
 
 __global__ void __launch_bounds__(kScaleThreads)
 rms_scale_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const float* __restrict__ gram,
                  int d_model, float eps, float* __restrict__ scale) {
-  __shared__ float g_s[16 * kRows];                         // 80 KB
-  __shared__ uint32_t lv_s[kScaleTokens * kLvPitch];        // 42 KB, 84-byte rows
+  __shared__ float g_s[16 * kGPitch];  // 83 KB
   const int tid = threadIdx.x;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kScaleTokens;
-  // stage this block's levels (clamped to 15)
-  for (int i = tid; i < kScaleTokens * (kMels / 16); i += kScaleThreads) {
-    const int tok = i / (kMels / 16), q = i - tok * (kMels / 16);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (t0 + tok < n_tokens) v = reinterpret_cast<const uint4*>(levels + (t0 + tok) * kMels)[q];
-    uint32_t* d = lv_s + tok * kLvPitch + 4 * q;
-    d[0] = clamp_levels(v.x);
-    d[1] = clamp_levels(v.y);
-    d[2] = clamp_levels(v.z);
-    d[3] = clamp_levels(v.w);
-  }
-  double total[kScaleTokPerThread];
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kScaleBlock + tid;
+  uint32_t rot[kScaleTok][20];
+  double total[kScaleTok];
 #pragma unroll
-  for (int k = 0; k < kScaleTokPerThread; ++k) total[k] = 0.0;
-
+  for (int k = 0; k < kScaleTok; ++k) {
+    const int64_t t = t0 + static_cast<int64_t>(k) * kScaleThreads;
+    total[k] = 0.0;
+    if (t < n_tokens) {
+      const uint4* p = reinterpret_cast<const uint4*>(levels + t * kMels);
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const uint4 q = p[i];
+        rot[k][4 * i + 0] = clamp_levels(q.x);
+        rot[k][4 * i + 1] = clamp_levels(q.y);
+        rot[k][4 * i + 2] = clamp_levels(q.z);
+        rot[k][4 * i + 3] = clamp_levels(q.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 20; ++i) rot[k][i] = 0;
+    }
+  }
   for (int j = 0; j < kMels; ++j) {
-    const int row_len = kRows - kLevels * j;
+    const int c0 = kLevels * j;
+    const int width = kRows - c0;
     __syncthreads();
-    for (int i = tid; i < 16 * row_len; i += kScaleThreads) {
-      const int r = i / row_len, c = i - r * row_len;
-      g_s[i] = gram[static_cast<int64_t>(kLevels * j + r) * kRows + kLevels * j + c];
+    for (int i = tid; i < 16 * width; i += kScaleThreads) {
+      const int r = i / width;
+      const int c = i - r * width;
+      g_s[r * kGPitch + c] = gram[static_cast<int64_t>(c0 + r) * kRows + c0 + c];
     }
     __syncthreads();
+    // rot byte q = level of bin j + q; staged column of bin j + q, level L: 16 q + L
+    const float* row[kScaleTok];
+    float off[kScaleTok];
 #pragma unroll
-    for (int k = 0; k < kScaleTokPerThread; ++k) {
-      const uint8_t* L = reinterpret_cast<const uint8_t*>(lv_s + (tid + kScaleThreads * k) * kLvPitch);
-      const float* grow = g_s + L[j] * row_len;
-      float diag = grow[L[j]];
-      float off = 0.0f;
-      for (int jp = j + 1; jp < kMels; ++jp) off += grow[kLevels * (jp - j) + L[jp]];
-      total[k] += static_cast<double>(diag) + 2.0 * static_cast<double>(off);
+    for (int k = 0; k < kScaleTok; ++k) {
+      const uint32_t lj = rot[k][0] & 0xFFu;
+      row[k] = g_s + lj * kGPitch;
+      off[k] = 0.0f;
+      total[k] += static_cast<double>(row[k][lj]);  // diagonal term
+    }
+    const int qlim = kMels - 1 - j;
+    switch (j / 10) {
+      case 0: row_terms<79>(off, row, rot, qlim); break;
+      case 1: row_terms<69>(off, row, rot, qlim); break;
+      case 2: row_terms<59>(off, row, rot, qlim); break;
+      case 3: row_terms<49>(off, row, rot, qlim); break;
+      case 4: row_terms<39>(off, row, rot, qlim); break;
+      case 5: row_terms<29>(off, row, rot, qlim); break;
+      case 6: row_terms<19>(off, row, rot, qlim); break;
+      default: row_terms<9>(off, row, rot, qlim); break;
+    }
+#pragma unroll
+    for (int k = 0; k < kScaleTok; ++k) {
+      total[k] += 2.0 * static_cast<double>(off[k]);
+      // shift the byte string down by one byte
+#pragma unroll
+      for (int i = 0; i < 19; ++i) rot[k][i] = __builtin_amdgcn_alignbyte(rot[k][i + 1], rot[k][i], 1);
+      rot[k][19] >>= 8;
     }
   }
 #pragma unroll
-  for (int k = 0; k < kScaleTokPerThread; ++k) {
-    const int64_t t = t0 + tid + kScaleThreads * k;
+  for (int k = 0; k < kScaleTok; ++k) {
+    const int64_t t = t0 + static_cast<int64_t>(k) * kScaleThreads;
     if (t < n_tokens) {
       const double ms = total[k] / static_cast<double>(d_model);
       scale[t] = static_cast<float>(1.0 / sqrt(ms + static_cast<double>(eps)));
@@ -329,7 +424,7 @@ hipError_t launch_gram(const uint16_t* table, int d_model, float* gram, hipStrea
 hipError_t launch_rms_scale(const uint8_t* levels, int64_t n_tokens, const float* gram, int d_model,
                             float eps, float* scale, hipStream_t stream) {
   if (n_tokens <= 0) return hipSuccess;
-  const int64_t blocks = (n_tokens + kScaleTokens - 1) / kScaleTokens;
+  const int64_t blocks = (n_tokens + kScaleBlock - 1) / kScaleBlock;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rms_scale_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScaleThreads), 0, stream,
                      levels, n_tokens, gram, d_model, eps, scale);

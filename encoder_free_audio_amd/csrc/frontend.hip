@@ -11,18 +11,21 @@
 // level = min(15, floor((clamp(l, -7, 2) + 7) * 16 / 9)) decided exactly.
 //
 // Work decomposition (one workgroup = 256 threads = 8 frames, fp32, LDS):
-//  1. load the 1600 windowed samples of each frame as 800 complex values
-//     z[m] = x[2m] + i x[2m+1];
+//  1. the 1600 windowed samples of a frame are read as 800 complex values
+//     z[m] = x[2m] + i x[2m+1] straight into the registers of pass A;
 //  2. 800-point complex FFT, 800 = 32 x 25:
 //     pass A - one thread per (frame, n1 < 32): a 25-point DFT (5 x 5) over
-//              z[n1 + 32 n2] in registers, then the twiddle W800^(n1 k2);
+//              z[n1 + 32 n2] (coalesced 8-byte reads across n1) in registers,
+//              then the twiddle W800^(n1 k2);
 //     pass B - one thread per (frame, k2 < 25): a 32-point DFT (8 x 4) over
 //              n1 in registers, giving Z[k2 + 25 k1];
 //     the exchange between the passes goes through LDS rows padded to 33
 //     complex values so that neither pass has bank conflicts;
 //  3. split Z into the 801-bin spectrum of the real frame and take |X|^2;
-//  4. each (frame, filter) sums its contiguous band of weighted bins, then log,
-//     clamp and quantize.
+//  4. mel: each bin lies between two triangle edges and feeds exactly two
+//     filters (the rising side of one, the falling side of the previous), so
+//     one pass over the 81 segments gives per-segment sums A_s (rising) and
+//     C_s (falling) and filter j is A_j + C_{j+1}; then log, clamp, quantize.
 #include "internal.h"
 
 namespace dmel {
@@ -120,15 +123,24 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
                 float* __restrict__ logmel, uint8_t* __restrict__ levels) {
   __shared__ float2 zbuf[kFramesPerBlock * kSlots];
   __shared__ float2 tw[kHalf];
+  __shared__ float wr_s[kBins];
+  __shared__ float wf_s[kBins];
+  __shared__ int seg_s[kMels + 2];
   __shared__ int64_t s_base[kFramesPerBlock];
   __shared__ int s_clip[kFramesPerBlock];
   __shared__ int s_first[kFramesPerBlock];
   __shared__ int s_valid[kFramesPerBlock];
+  __shared__ int s_fast[kFramesPerBlock];
 
   const int tid = threadIdx.x;
   const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kFramesPerBlock;
 
   for (int i = tid; i < kHalf; i += kThreads) tw[i] = tabs.tw800[i];
+  for (int i = tid; i < kBins; i += kThreads) {
+    wr_s[i] = tabs.w_rise[i];
+    wf_s[i] = tabs.w_fall[i];
+  }
+  if (tid < kMels + 2) seg_s[tid] = tabs.seg_start[tid];
   if (tid < kFramesPerBlock) {
     const int64_t g = g0 + tid;
     const int valid = g < n_frames;
@@ -141,30 +153,14 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
       base = sample_off[c] + kHop * t - kHop;
       first = (t == 0);
     }
+    // the whole frame lies inside the audio and 8-byte reads are aligned
+    const int fast = valid && !first && base >= 0 && base + kWindow <= n_samples_total &&
+                     (reinterpret_cast<uintptr_t>(audio + base) & 7) == 0;
     s_valid[tid] = valid;
     s_clip[tid] = c;
     s_base[tid] = base;
     s_first[tid] = first;
-  }
-  __syncthreads();
-
-  // ---- 1. windowed samples, stored as z[m] = (x[2m], x[2m+1]) -----------
-  {
-    float* zf = reinterpret_cast<float*>(zbuf);
-    for (int it = tid; it < kFramesPerBlock * kWindow; it += kThreads) {
-      const int f = it / kWindow;
-      const int n = it - f * kWindow;
-      float v = 0.0f;
-      if (s_valid[f]) {
-        if (s_first[f] && n < kHop) {
-          if (carry != nullptr) v = carry[static_cast<int64_t>(s_clip[f]) * kHop + n];
-        } else {
-          const int64_t s = s_base[f] + n;
-          if (s >= 0 && s < n_samples_total) v = audio[s];
-        }
-      }
-      zf[2 * f * kSlots + n] = v * tabs.window[n];
-    }
+    s_fast[tid] = fast;
   }
   __syncthreads();
 
@@ -172,11 +168,45 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
   const int lane = tid & 31;   // n1 in pass A, k2 in pass B
   float2* zf = zbuf + f * kSlots;
 
-  // ---- 2a. 25-point DFTs over n2 for each n1, then twiddle ---------------
+  // ---- 1 + 2a. windowed samples, 25-point DFTs over n2 for each n1 --------
   {
     float2 x[25];
+    const int64_t base = s_base[f];
+    const float2* w2 = reinterpret_cast<const float2*>(tabs.window);
+    if (s_fast[f]) {
+      const float2* src = reinterpret_cast<const float2*>(audio + base);
 #pragma unroll
-    for (int n2 = 0; n2 < 25; ++n2) x[n2] = zf[lane + 32 * n2];
+      for (int n2 = 0; n2 < 25; ++n2) {
+        const int m = lane + 32 * n2;
+        const float2 a = src[m];
+        const float2 w = w2[m];
+        x[n2] = make_float2(a.x * w.x, a.y * w.y);
+      }
+    } else {
+      const int valid = s_valid[f], first = s_first[f];
+      const int64_t cbase = static_cast<int64_t>(s_clip[f]) * kHop;
+#pragma unroll
+      for (int n2 = 0; n2 < 25; ++n2) {
+        const int m = lane + 32 * n2;
+        float v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int n = 2 * m + h;
+          float val = 0.0f;
+          if (valid) {
+            if (first && n < kHop) {
+              if (carry != nullptr) val = carry[cbase + n];
+            } else {
+              const int64_t sidx = base + n;
+              if (sidx >= 0 && sidx < n_samples_total) val = audio[sidx];
+            }
+          }
+          v[h] = val;
+        }
+        const float2 w = w2[m];
+        x[n2] = make_float2(v[0] * w.x, v[1] * w.y);
+      }
+    }
     // n2 = 5 a + b: 5-point DFTs over a for each b
 #pragma unroll
     for (int b = 0; b < 5; ++b) dft5(x[b], x[5 + b], x[10 + b], x[15 + b], x[20 + b]);
@@ -200,7 +230,6 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
     }
 #pragma unroll
     for (int k2 = 1; k2 < 25; ++k2) y[k2] = cmul(y[k2], tw[lane * k2]);
-    __syncthreads();
 #pragma unroll
     for (int k2 = 0; k2 < 25; ++k2) zf[lane + 33 * k2] = y[k2];
   }
@@ -282,20 +311,31 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
   }
   __syncthreads();
 
-  // ---- 4. mel bands, log, clamp, quantize ---------------------------------
+  // ---- 4. mel: segment sums, then filters, log, clamp, quantize ----------
   {
-    const float* pf = reinterpret_cast<const float*>(zbuf);
+    float* pf = reinterpret_cast<float*>(zbuf);
+    constexpr int kSeg = kMels + 1;  // 81 segments
+    constexpr int kAOff = 1024;      // per-frame float offsets of A_s and C_s (past the 801 powers)
+    constexpr int kCOff = 1120;
+    for (int it = tid; it < kFramesPerBlock * kSeg; it += kThreads) {
+      const int ff = it / kSeg;
+      const int sg = it - ff * kSeg;
+      const float* p = pf + 2 * ff * kSlots;
+      float a = 0.0f, c = 0.0f;
+      for (int k = seg_s[sg]; k < seg_s[sg + 1]; ++k) {
+        a = fmaf(wr_s[k], p[k], a);
+        c = fmaf(wf_s[k], p[k], c);
+      }
+      pf[2 * ff * kSlots + kAOff + sg] = a;
+      pf[2 * ff * kSlots + kCOff + sg] = c;
+    }
+    __syncthreads();
     for (int it = tid; it < kFramesPerBlock * kMels; it += kThreads) {
       const int ff = it / kMels;
       const int j = it - ff * kMels;
       const int64_t g = g0 + ff;
       if (g >= n_frames) continue;
-      const int lo = tabs.mel_lo[j];
-      const int cnt = tabs.mel_cnt[j];
-      const float* w = tabs.mel_w + tabs.mel_off[j];
-      const float* pw = pf + 2 * ff * kSlots + lo;
-      float m = 0.0f;
-      for (int i = 0; i < cnt; ++i) m = fmaf(w[i], pw[i], m);
+      const float m = pf[2 * ff * kSlots + kAOff + j] + pf[2 * ff * kSlots + kCOff + j + 1];
       const float l = logf(fmaxf(m, kLogFloor));
       if (logmel != nullptr) logmel[g * kMels + j] = l;
       if (levels != nullptr) levels[g * kMels + j] = static_cast<uint8_t>(quantize(l));

@@ -28,11 +28,12 @@ struct FrontTables {
   const float* window;   // [1600] periodic Hann
   const float2* tw800;   // [800] exp(-2 pi i m / 800)
   const float2* tw1600;  // [401] exp(-2 pi i k / 1600)
-  const int* mel_lo;     // [80] first bin with a nonzero weight
-  const int* mel_cnt;    // [80] number of nonzero weights
-  const int* mel_off;    // [80] offset of the filter's weights in mel_w
-  const float* mel_w;    // [mel_nnz] weights, bin order
-  int mel_nnz;
+  // Mel filterbank by segment: bins [seg_start[s], seg_start[s+1]) lie
+  // between triangle edges s and s+1; such a bin feeds filter s (its rising
+  // side) with weight w_rise and filter s-1 (its falling side) with w_fall.
+  const int* seg_start;  // [82]
+  const float* w_rise;   // [801]
+  const float* w_fall;   // [801]
 };
 
 // Host-built tables, in the layout FrontTables points to (see tables.cpp).
@@ -40,11 +41,9 @@ struct HostTables {
   float window[kWindow];
   float tw800[2 * kHalf];
   float tw1600[2 * (kHalf / 2 + 1)];
-  int mel_lo[kMels];
-  int mel_cnt[kMels];
-  int mel_off[kMels];
-  float mel_w[kBins * 2];
-  int mel_nnz;
+  int seg_start[kMels + 2];
+  float w_rise[kBins];
+  float w_fall[kBins];
 };
 void build_host_tables(HostTables* t);
 

@@ -40,27 +40,23 @@ void build_host_tables(HostTables* t) {
   for (int i = 0; i < kMels + 2; ++i) edges[i] = mel_to_hz(mel_hi * i / (kMels + 1));
   edges[0] = 0.0;
   edges[kMels + 1] = kSampleRate / 2.0;
-  int nnz = 0;
-  for (int j = 0; j < kMels; ++j) {
-    const double lo = edges[j], mid = edges[j + 1], hi = edges[j + 2];
-    int first = -1, count = 0;
-    for (int k = 0; k < kBins; ++k) {
-      const double f = static_cast<double>(k) * kSampleRate / kNfft;
-      const double up = (f - lo) / (mid - lo);
-      const double down = (hi - f) / (hi - mid);
-      const double w = std::fmax(0.0, std::fmin(up, down));
-      if (w > 0.0) {
-        if (first < 0) first = k;
-        t->mel_w[nnz + count] = static_cast<float>(w);
-        ++count;
-      }
+  // segment view: bin k with edges[s] <= f < edges[s+1] (the last bin, at
+  // exactly 8000 Hz, closes segment 80)
+  int s = 0;
+  t->seg_start[0] = 0;
+  for (int k = 0; k < kBins; ++k) {
+    const double f = static_cast<double>(k) * kSampleRate / kNfft;
+    while (s < kMels && f >= edges[s + 1]) {
+      ++s;
+      t->seg_start[s] = k;
     }
-    t->mel_lo[j] = first < 0 ? 0 : first;
-    t->mel_cnt[j] = count;
-    t->mel_off[j] = nnz;
-    nnz += count;
+    const double lo = edges[s], hi = edges[s + 1];
+    const double rise = (f - lo) / (hi - lo);  // filter s, rising side
+    const double fall = (hi - f) / (hi - lo);  // filter s - 1, falling side
+    t->w_rise[k] = s < kMels ? static_cast<float>(std::fmax(0.0, rise)) : 0.0f;
+    t->w_fall[k] = s > 0 ? static_cast<float>(std::fmax(0.0, fall)) : 0.0f;
   }
-  t->mel_nnz = nnz;
+  while (s < kMels + 1) t->seg_start[++s] = kBins;
 }
 
 }  // namespace dmel
