@@ -38,12 +38,16 @@ METRIC = "audio tokens/sec (dMel frames→6144-d embeds) + achieved HBM GB/s vs 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (batch 20, stream 1000, interleave 5)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--clips", type=int, default=64)
     ap.add_argument("--minutes", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=1200, help="oracle sample: frames per worker")
+    ap.add_argument("--workload", choices=("batch", "stream", "interleave"), default="batch",
+                    help="batch: 64 x 20 min clips (default); stream: 4096 streams, one hop per step; "
+                         "interleave: 256 x 32768 audio/text positions")
+    ap.add_argument("--streams", type=int, default=4096)
     return ap.parse_args()
 
 
@@ -91,6 +95,134 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.steps is None:
+        args.steps = {"batch": 20, "stream": 1000, "interleave": 5}[args.workload]
+    if args.workload == "stream":
+        return bench_stream(args)
+    if args.workload == "interleave":
+        return bench_interleave(args)
+    return bench_batch(args)
+
+
+def _base_line(args, value, ms_step, workload, extra):
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": {"workload": workload},
+    }
+    line.update(extra)
+    return line
+
+
+def bench_stream(args):
+    """Streaming: every step each of S streams delivers one new 800-sample hop;
+    dmel_forward turns the S hops (with each stream's previous hop as carry)
+    into S tokens.  Reports per-step latency percentiles and tokens/s."""
+    dev = "cuda"
+    S = args.streams
+    K = args.steps
+    print(f"[bench] generating {S} streams x {K} hops on the GPU", file=sys.stderr, flush=True)
+    hops = synth.streaming_hops(seed=3, n_streams=S, n_steps=K + args.warmup, device=dev)
+    table = synth.table_bf16(seed=1234).to(dev)
+    rms_w = torch.ones(6144, dtype=torch.float32, device=dev)
+    gram = torch.empty((1280, 1280), dtype=torch.float32, device=dev)
+    ctx = dm.dmel_create(0)
+    dm.dmel_rms_gram(table, 6144, gram)
+    so, fo, _ = dm.clip_offsets([800] * S, dev)
+    ws = torch.empty(dm.dmel_forward_workspace_bytes(S), dtype=torch.uint8, device=dev)
+    out = torch.empty((S, 6144), dtype=torch.int16, device=dev)
+    zeros = torch.zeros((S, 800), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(k):
+        carry = zeros if k == 0 else hops[k - 1]
+        dm.dmel_forward(ctx, hops[k], S * 800, so, fo, S, S, carry, table, 6144, rms_w, gram, 1e-6, out,
+                        dm.DMEL_BF16, 6144, None, ws, ws.numel(), stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for k in range(K):
+        step(args.warmup + k)
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(K)])
+    dm.dmel_destroy(ctx)
+    line = _base_line(args, S * K / wall, wall * 1e3 / K,
+                      f"dMel streaming: {S} streams, one 800-sample hop per stream per step with an 800-sample "
+                      f"carry, {K} steps, RMSNorm on, bf16 out",
+                      {"p50_step_ms": float(np.percentile(per, 50)), "p99_step_ms": float(np.percentile(per, 99)),
+                       "steps": K})
+    line["config"].update({"streams": S, "parallelism": "single GPU"})
+    print(json.dumps(line), flush=True)
+
+
+def bench_interleave(args):
+    """Interleaved sequences: 256 x 32768 positions, 40% audio frames (dmel_forward
+    with out_rows) and 60% text rows (dmel_gather_rows) written into one bf16
+    [256, 32768, 6144] output.  One step = both calls for the whole batch."""
+    dev = "cuda"
+    lay = synth.interleave_layout(seed=4)
+    n_seq, L = lay["n_seq"], lay["seq_len"]
+    kind, seq, start, ln = lay["seg_kind"], lay["seg_seq"], lay["seg_start"], lay["seg_len"]
+    a_idx = np.nonzero(kind == 1)[0]
+    t_idx = np.nonzero(kind == 0)[0]
+    clip_frames = ln[a_idx]
+    print(f"[bench] generating {clip_frames.sum()} audio frames and the 131072-row text table", file=sys.stderr,
+          flush=True)
+    audio = synth.speech_clips(seed=4, lengths=(clip_frames * 800).tolist(), device=dev)
+    table = synth.table_bf16(seed=1234).to(dev)
+    text = synth.table_bf16(seed=1235, rows=131072, d_model=6144, device=dev)
+    a_rows = torch.from_numpy(np.concatenate([seq[i] * L + start[i] + np.arange(ln[i]) for i in a_idx])).to(dev)
+    t_pos = np.concatenate([seq[i] * L + start[i] + np.arange(ln[i]) for i in t_idx])
+    t_rows = torch.from_numpy(t_pos).to(dev)
+    ids = torch.from_numpy(lay["ids"].reshape(-1)[t_pos].astype(np.int32)).to(dev)
+    out = torch.empty((n_seq * L, 6144), dtype=torch.int16, device=dev)
+    ctx = dm.dmel_create(0)
+    so, fo, T = dm.clip_offsets((clip_frames * 800).tolist(), dev)
+    ws = torch.empty(dm.dmel_forward_workspace_bytes(T), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    n_text = t_pos.size
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dm.dmel_forward(ctx, audio, audio.numel(), so, fo, len(a_idx), T, None, table, 6144, None, None, 1e-6,
+                        out, dm.DMEL_BF16, 6144, a_rows, ws, ws.numel(), stream)
+        if ev is not None:
+            ev[1].record(stream)
+        dm.dmel_gather_rows(text, 131072, 6144, ids, n_text, out, 6144, t_rows, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in evs]).mean(axis=0)
+    dm.dmel_destroy(ctx)
+    ms = wall * 1e3 / args.steps
+    gather_bytes = n_text * 6144 * 2 * 2
+    line = _base_line(args, T / (ms * 1e-3), ms,
+                      f"dMel interleave: {n_seq} x {L} positions, {T} audio frames in {len(a_idx)} clips + "
+                      f"{n_text} text rows of a 131072x6144 bf16 table, one bf16 output, RMSNorm off",
+                      {"positions_per_s": n_seq * L / (ms * 1e-3),
+                       "kernel_ms": {"audio_forward": float(per[0]), "text_gather": float(per[1])},
+                       "text_gather_GBps": gather_bytes / (per[1] * 1e-3) / 1e9})
+    line["config"].update({"sequences": n_seq, "seq_len": L, "parallelism": "single GPU"})
+    print(json.dumps(line), flush=True)
+
+
+def bench_batch(args):
     dev = "cuda"
     n_clips = args.clips
     clip_len = int(round(args.minutes * 60 * 16000))

@@ -139,11 +139,16 @@ def bursts_clips(seed: int, n_clips: int, n_samples: int, device="cpu") -> torch
         peak = torch.amax(torch.abs(x), dim=-1, keepdim=True)
         x = torch.where(peak > 1.0, x / peak, x)
         # silent spans: exact zeros
-        mark = torch.zeros((nc, n_samples + 1), dtype=torch.int32, device=device)
+        rows, cols, vals = [], [], []
         for ci in range(nc):
             for a, b in spans[c0 + ci]:
-                mark[ci, a] += 1
-                mark[ci, b] -= 1
+                rows += [ci, ci]
+                cols += [a, b]
+                vals += [1, -1]
+        mark = torch.zeros((nc, n_samples + 1), dtype=torch.int32, device=device)
+        if rows:
+            mark.index_put_((torch.tensor(rows, device=device), torch.tensor(cols, device=device)),
+                            torch.tensor(vals, dtype=torch.int32, device=device), accumulate=True)
         silent = torch.cumsum(mark, dim=-1)[:, :n_samples] > 0
         x = torch.where(silent, torch.zeros_like(x), x)
         out[c0:c1] = x
@@ -274,3 +279,17 @@ def interleave_layout(seed: int = 4, n_seq: int = 256, seq_len: int = 32768,
         "seg_start": np.array(seg_start, dtype=np.int64), "seg_len": np.array(seg_len, dtype=np.int64),
         "ids": ids,
     }
+
+
+def streaming_hops(seed: int = 3, n_streams: int = 4096, n_steps: int = 1000, device="cpu") -> torch.Tensor:
+    """[n_steps, n_streams, 800] fp32: the hop each stream delivers at each step
+    (the bursts model, 50 s per stream at the default sizes), step-major so that
+    one step's hops are contiguous."""
+    total = n_steps * HOP
+    out = torch.empty((n_steps, n_streams, HOP), dtype=torch.float32, device=device)
+    chunk = max(1, int(2 ** 26 // max(1, total)))
+    for s0 in range(0, n_streams, chunk):
+        s1 = min(n_streams, s0 + chunk)
+        x = bursts_clips(seed * 1_000_003 + s0, s1 - s0, total, device=device)
+        out[:, s0:s1, :] = x.view(s1 - s0, n_steps, HOP).permute(1, 0, 2)
+    return out
