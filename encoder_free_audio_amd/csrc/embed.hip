@@ -29,13 +29,19 @@ namespace {
 constexpr int kEmbThreads = 1024;   // tokens per workgroup
 constexpr int kStrip = 16;          // fp32 columns per strip
 constexpr int kPitch = 20;          // floats per LDS row (80 bytes)
-constexpr int kStripsPerGroup = 4;  // strips a workgroup walks through
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest-even bf16 and packed (lo, hi): one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2_t v;
+  v[0] = lo;
+  v[1] = hi;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Clamp each byte of x to at most 15.
@@ -137,7 +143,7 @@ __global__ void __launch_bounds__(kEmbThreads)
 embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_t* __restrict__ table,
              int d_model, const float* __restrict__ rms_weight, const float* __restrict__ rms_scale,
              void* __restrict__ out, int out_f32, int64_t out_row_stride,
-             const int64_t* __restrict__ out_rows, int n_groups, int n_strips) {
+             const int64_t* __restrict__ out_rows, int n_groups, int n_strips, int strips_per_group) {
   __shared__ float4 tab4[kRows * kPitch / 4];
   float* tab = reinterpret_cast<float*>(tab4);
 
@@ -146,8 +152,8 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_
   const int64_t tb = blockIdx.x / static_cast<unsigned>(n_groups);
   const int64_t t = tb * kEmbThreads + tid;
   const bool active = t < n_tokens;
-  const int s_first = grp * kStripsPerGroup;
-  const int s_end = min(n_strips, s_first + kStripsPerGroup);
+  const int s_first = grp * strips_per_group;
+  const int s_end = min(n_strips, s_first + strips_per_group);
 
   uint4 st[kStagePer];
   stage_load(st, table, d_model, s_first * kStrip, 0, tid);
@@ -211,7 +217,7 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_
       } else {
         uint32_t w[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+        for (int i = 0; i < 8; ++i) w[i] = pack_bf16(acc[2 * i], acc[2 * i + 1]);
         uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + orow * out_row_stride + col0);
         o[0] = make_uint4(w[0], w[1], w[2], w[3]);
         o[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -376,6 +382,52 @@ rms_scale_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const flo
   }
 }
 
+// Same scale for small batches, without staging: one thread per (token, bin j)
+// reads row r_j of G straight from memory (L2-resident) and forms the bin's
+// fp32 diagonal and off-diagonal sums exactly as rms_scale_kernel does (same
+// terms, same order); the token's total is then summed in bin order in fp64 by
+// one thread.  The arithmetic is identical to rms_scale_kernel's, so a token
+// gets the same scale whichever kernel runs, whatever the batch size.
+constexpr int kDirTok = 4;                  // tokens per workgroup
+constexpr int kDirThreads = kDirTok * kMels;  // 320
+
+__global__ void __launch_bounds__(kDirThreads)
+rms_scale_direct_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const float* __restrict__ gram,
+                        int d_model, float eps, float* __restrict__ scale) {
+  __shared__ uint8_t lv_s[kDirTok][kMels];
+  __shared__ float d_s[kDirTok][kMels];
+  __shared__ float o_s[kDirTok][kMels];
+  const int tid = threadIdx.x;
+  const int tok = tid / kMels;
+  const int j = tid - tok * kMels;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kDirTok + tok;
+  const bool active = t < n_tokens;
+  if (active) {
+    const uint32_t v = levels[t * kMels + j];
+    lv_s[tok][j] = static_cast<uint8_t>(v > 15u ? 15u : v);
+  }
+  __syncthreads();
+  if (active) {
+    const int rj = kLevels * j + lv_s[tok][j];
+    const float* row = gram + static_cast<int64_t>(rj) * kRows;
+    const float diag = row[rj];
+    float off = 0.0f;
+    for (int jp = j + 1; jp < kMels; ++jp) off += row[kLevels * jp + lv_s[tok][jp]];
+    d_s[tok][j] = diag;
+    o_s[tok][j] = off;
+  }
+  __syncthreads();
+  if (active && j == 0) {
+    double total = 0.0;
+    for (int jj = 0; jj < kMels; ++jj) {
+      total += static_cast<double>(d_s[tok][jj]);
+      total += 2.0 * static_cast<double>(o_s[tok][jj]);
+    }
+    const double ms = total / static_cast<double>(d_model);
+    scale[t] = static_cast<float>(1.0 / sqrt(ms + static_cast<double>(eps)));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Row gather for text positions: out[row(i)] = table[ids[i]] (zeros for an id
 // out of range).  One 16-byte chunk per thread per iteration.
@@ -405,13 +457,34 @@ hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, const uint16_t*
                         int64_t out_row_stride, const int64_t* out_rows, hipStream_t stream) {
   if (n_tokens <= 0) return hipSuccess;
   const int n_strips = d_model / kStrip;
-  const int n_groups = (n_strips + kStripsPerGroup - 1) / kStripsPerGroup;
   const int64_t tblocks = (n_tokens + kEmbThreads - 1) / kEmbThreads;
+  // Strips per workgroup: more strips amortise the per-workgroup set-up (16 was
+  // the fastest count measured on a 1.5M-token batch), but a small batch then
+  // launches too few workgroups to fill the chip.  One workgroup fits per CU
+  // (LDS), so the cost of a count g is about rounds-of-256-workgroups x g; take
+  // the largest g within 5% of the cheapest.
+  static const int kCounts[] = {16, 8, 4, 3, 2, 1};
+  int64_t cost[6];
+  int64_t min_cost = -1;
+  for (int i = 0; i < 6; ++i) {
+    const int g = kCounts[i];
+    const int64_t wgs = tblocks * ((n_strips + g - 1) / g);
+    cost[i] = ((wgs + 255) / 256) * g;
+    if (min_cost < 0 || cost[i] < min_cost) min_cost = cost[i];
+  }
+  int best = 1;
+  for (int i = 0; i < 6; ++i) {
+    if (cost[i] * 100 <= min_cost * 105) {
+      best = kCounts[i];
+      break;
+    }
+  }
+  const int n_groups = (n_strips + best - 1) / best;
   const int64_t blocks = tblocks * n_groups;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(embed_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kEmbThreads), 0, stream, levels,
                      n_tokens, table, d_model, rms_weight, rms_scale, out, out_f32 ? 1 : 0, out_row_stride,
-                     out_rows, n_groups, n_strips);
+                     out_rows, n_groups, n_strips, best);
   return hipGetLastError();
 }
 
@@ -424,6 +497,12 @@ hipError_t launch_gram(const uint16_t* table, int d_model, float* gram, hipStrea
 hipError_t launch_rms_scale(const uint8_t* levels, int64_t n_tokens, const float* gram, int d_model,
                             float eps, float* scale, hipStream_t stream) {
   if (n_tokens <= 0) return hipSuccess;
+  if (n_tokens <= kRmsDirectMax) {
+    const int64_t blocks = (n_tokens + kDirTok - 1) / kDirTok;
+    hipLaunchKernelGGL(rms_scale_direct_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kDirThreads), 0, stream,
+                       levels, n_tokens, gram, d_model, eps, scale);
+    return hipGetLastError();
+  }
   const int64_t blocks = (n_tokens + kScaleBlock - 1) / kScaleBlock;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rms_scale_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScaleThreads), 0, stream,

@@ -59,6 +59,11 @@ hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, const uint16_t*
 
 hipError_t launch_gram(const uint16_t* table, int d_model, float* gram, hipStream_t stream);
 
+// Batches up to this many tokens take the RMSNorm-scale kernel that reads the
+// Gram matrix directly (no staging); larger ones stage it in LDS.  Both give
+// bit-identical scales.
+constexpr int64_t kRmsDirectMax = 131072;
+
 hipError_t launch_rms_scale(const uint8_t* levels, int64_t n_tokens, const float* gram, int d_model,
                             float eps, float* scale, hipStream_t stream);
 

@@ -280,3 +280,32 @@ def test_silence_and_empty(env, table):
                     None, None, 1e-6, out, dm.DMEL_BF16, 6144, None, None, 0)
     torch.cuda.synchronize()
     assert bool((out == 5).all())
+
+
+def test_scale_and_embed_independent_of_batch_size(env, table):
+    """Small batches take the direct RMSNorm-scale kernel and a different
+    strips-per-workgroup choice; a token's result must not depend on that."""
+    dm, ctx = env
+    rng = np.random.default_rng(71)
+    n_big = 131072 + 3001          # above the direct-kernel limit: staged Gram kernel
+    n_small = 4096
+    lv = P.to_dev(rng.integers(0, 16, size=(n_big, 80)).astype(np.uint8))
+    tab = table.cuda()
+    gram = torch.empty((1280, 1280), dtype=torch.float32, device="cuda")
+    dm.dmel_rms_gram(tab, 6144, gram)
+    s_big = torch.empty(n_big, dtype=torch.float32, device="cuda")
+    s_small = torch.empty(n_small, dtype=torch.float32, device="cuda")
+    dm.dmel_rms_scale(lv, n_big, gram, 6144, 1e-6, s_big)
+    dm.dmel_rms_scale(lv, n_small, gram, 6144, 1e-6, s_small)
+    torch.cuda.synchronize()
+    assert torch.equal(s_small, s_big[:n_small])
+    s = o.embed_sum(lv[:300].cpu().numpy(), _tbits(table)).astype(np.float64)
+    want = 1.0 / np.sqrt(np.mean(s * s, axis=1) + 1e-6)
+    assert np.max(np.abs(s_big[:300].cpu().numpy() - want) / want) < 1e-6
+    w = torch.ones(6144, dtype=torch.float32, device="cuda")
+    a = torch.empty((20000, 6144), dtype=torch.int16, device="cuda")
+    b = torch.empty((n_small, 6144), dtype=torch.int16, device="cuda")
+    dm.dmel_embed(lv, 20000, tab, 6144, w, s_big, a, dm.DMEL_BF16, 6144)
+    dm.dmel_embed(lv, n_small, tab, 6144, w, s_small, b, dm.DMEL_BF16, 6144)
+    torch.cuda.synchronize()
+    assert torch.equal(a[:n_small], b)
