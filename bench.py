@@ -44,9 +44,10 @@ def parse():
     ap.add_argument("--minutes", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=1200, help="oracle sample: frames per worker")
-    ap.add_argument("--workload", choices=("batch", "stream", "interleave"), default="batch",
+    ap.add_argument("--workload", choices=("batch", "stream", "interleave", "copy"), default="batch",
                     help="batch: 64 x 20 min clips (default); stream: 4096 streams, one hop per step; "
-                         "interleave: 256 x 32768 audio/text positions")
+                         "interleave: 256 x 32768 audio/text positions; copy: a plain 1 GiB device copy "
+                         "(calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--streams", type=int, default=4096)
     return ap.parse_args()
 
@@ -96,12 +97,33 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     if args.steps is None:
-        args.steps = {"batch": 20, "stream": 1000, "interleave": 5}[args.workload]
+        args.steps = {"batch": 20, "stream": 1000, "interleave": 5, "copy": 5}[args.workload]
     if args.workload == "stream":
         return bench_stream(args)
     if args.workload == "interleave":
         return bench_interleave(args)
+    if args.workload == "copy":
+        return bench_copy(args)
     return bench_batch(args)
+
+
+def bench_copy(args):
+    """A plain device-to-device copy of 1 GiB: its FETCH_SIZE / WRITE_SIZE
+    counter values, against the 1 GiB it reads and writes, scale the counter
+    readings of the front-end kernels to bytes."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    print(json.dumps({"workload": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n, "ms_per_copy": ms,
+                      "GBps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def _base_line(args, value, ms_step, workload, extra):

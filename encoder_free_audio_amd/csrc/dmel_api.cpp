@@ -131,11 +131,12 @@ int dmel_create(dmel_ctx** out, int device) {
     return fail(DMEL_ENOMEM, "host allocation failed");
   }
   dmel::build_host_tables(h);
-  // layout: window | tw800 | tw1600 | seg_start | w_rise | w_fall
+  // layout: window | tw800 | tw1600 | twa | seg_start | w_rise | w_fall
   size_t off_window = 0;
   size_t off_tw800 = round_up(off_window + sizeof(h->window), 256);
   size_t off_tw1600 = round_up(off_tw800 + sizeof(h->tw800), 256);
-  size_t off_seg = round_up(off_tw1600 + sizeof(h->tw1600), 256);
+  size_t off_twa = round_up(off_tw1600 + sizeof(h->tw1600), 256);
+  size_t off_seg = round_up(off_twa + sizeof(h->twa), 256);
   size_t off_rise = round_up(off_seg + sizeof(h->seg_start), 256);
   size_t off_fall = round_up(off_rise + sizeof(h->w_rise), 256);
   size_t total = round_up(off_fall + sizeof(h->w_fall), 256);
@@ -150,6 +151,7 @@ int dmel_create(dmel_ctx** out, int device) {
   std::memcpy(staging + off_window, h->window, sizeof(h->window));
   std::memcpy(staging + off_tw800, h->tw800, sizeof(h->tw800));
   std::memcpy(staging + off_tw1600, h->tw1600, sizeof(h->tw1600));
+  std::memcpy(staging + off_twa, h->twa, sizeof(h->twa));
   std::memcpy(staging + off_seg, h->seg_start, sizeof(h->seg_start));
   std::memcpy(staging + off_rise, h->w_rise, sizeof(h->w_rise));
   std::memcpy(staging + off_fall, h->w_fall, sizeof(h->w_fall));
@@ -172,6 +174,7 @@ int dmel_create(dmel_ctx** out, int device) {
     ctx->tabs.window = reinterpret_cast<const float*>(dev + off_window);
     ctx->tabs.tw800 = reinterpret_cast<const float2*>(dev + off_tw800);
     ctx->tabs.tw1600 = reinterpret_cast<const float2*>(dev + off_tw1600);
+    ctx->tabs.twa = reinterpret_cast<const float2*>(dev + off_twa);
     ctx->tabs.seg_start = reinterpret_cast<const int*>(dev + off_seg);
     ctx->tabs.w_rise = reinterpret_cast<const float*>(dev + off_rise);
     ctx->tabs.w_fall = reinterpret_cast<const float*>(dev + off_fall);

@@ -52,23 +52,28 @@ __device__ __forceinline__ uint32_t clamp_levels(uint32_t x) {
   return (x & ~mask) | (0x0F0F0F0Fu & mask);
 }
 
-// LDS address of the staged row that bin j selects for this lane's token.
-__device__ __forceinline__ const float4* row_ptr(const float* tab, const uint32_t (&lv)[20], int j) {
-  const uint32_t L = (lv[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-  return reinterpret_cast<const float4*>(tab + (kLevels * j + L) * kPitch);
-}
-
 // Adds bins J0..J1-1 of this lane's token into acc (bin 0 initialises it).
 // Software pipeline: the four 16-byte reads of bin j + 1 are issued, then an
 // empty asm that "modifies" the accumulators and clobbers memory pins them
 // ahead of the adds of bin j, so a wave always has the next bin's reads in
 // flight while it adds the current one, and no more than that (hoisting all
-// the reads would exhaust the registers).
+// the reads would exhaust the registers).  For J0 > 0 the LDS addresses are
+// taken from a base rebased to bin J0 through an opaque register, so that every
+// read of the range keeps its bin offset in the 16-bit immediate field (the
+// offsets of bins past 51 would overflow it, and each read would then cost two
+// extra VALU ops).
 template <int J0, int J1>
 __device__ __forceinline__ void add_bins(float (&acc)[kStrip], const float* tab, const uint32_t (&lv)[20]) {
+  uint32_t rebase = J0 * kLevels * kPitch;
+  if (J0 > 0) asm volatile("" : "+v"(rebase));
+  const float* base = tab + rebase;
+  auto row = [&](int j) {
+    const uint32_t L = (lv[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+    return reinterpret_cast<const float4*>(base + (kLevels * (j - J0) + L) * kPitch);
+  };
   float4 cur[4];
   {
-    const float4* r = row_ptr(tab, lv, J0);
+    const float4* r = row(J0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) cur[q] = r[q];
   }
@@ -76,22 +81,25 @@ __device__ __forceinline__ void add_bins(float (&acc)[kStrip], const float* tab,
   for (int j = J0; j < J1; ++j) {
     float4 nxt[4];
     if (j + 1 < J1) {
-      const float4* r = row_ptr(tab, lv, j + 1);
+      const float4* r = row(j + 1);
 #pragma unroll
       for (int q = 0; q < 4; ++q) nxt[q] = r[q];
     }
-    asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
-                 "+v"(acc[6]), "+v"(acc[7]), "+v"(acc[8]), "+v"(acc[9]), "+v"(acc[10]), "+v"(acc[11]),
-                 "+v"(acc[12]), "+v"(acc[13]), "+v"(acc[14]), "+v"(acc[15])::"memory");
+    if (j == 0) {
+      // the sum starts from the first row itself (not from +0)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (j == 0) {
-        // the sum starts from the first row itself (not from +0)
+      for (int q = 0; q < 4; ++q) {
         acc[4 * q + 0] = cur[q].x;
         acc[4 * q + 1] = cur[q].y;
         acc[4 * q + 2] = cur[q].z;
         acc[4 * q + 3] = cur[q].w;
-      } else {
+      }
+    } else {
+      asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
+                   "+v"(acc[6]), "+v"(acc[7]), "+v"(acc[8]), "+v"(acc[9]), "+v"(acc[10]), "+v"(acc[11]),
+                   "+v"(acc[12]), "+v"(acc[13]), "+v"(acc[14]), "+v"(acc[15])::"memory");
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
         acc[4 * q + 0] += cur[q].x;
         acc[4 * q + 1] += cur[q].y;
         acc[4 * q + 2] += cur[q].z;
@@ -194,8 +202,6 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_
     for (int i = 0; i < 20; ++i) asm volatile("" : "+v"(lv[i]));
     stage_load(st, table, d_model, col0, 1, tid);
     float acc[kStrip];
-#pragma unroll
-    for (int c = 0; c < kStrip; ++c) acc[c] = 0.0f;
     add_bins<0, kMels / 2>(acc, tab, lv);
     stage_store(tab, st, 1, tid);
     __syncthreads();
@@ -208,6 +214,11 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_
 #pragma unroll
         for (int c = 0; c < kStrip; ++c) acc[c] = (acc[c] * scale) * rms_weight[col0 + c];
       }
+      // Plain stores: the 16 strips of a workgroup complete each token's
+      // 128-byte lines in L2 before they are written back.  (Non-temporal
+      // stores, which would keep the output from evicting the table slices,
+      // send the 32-byte pieces to memory one by one and nearly double the
+      // bytes written.)
       if (out_f32) {
         float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + orow * out_row_stride + col0);
         o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);

@@ -121,11 +121,10 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
                 const int64_t* __restrict__ sample_off, const int64_t* __restrict__ frame_off,
                 int n_clips, int64_t n_frames, const float* __restrict__ carry,
                 float* __restrict__ logmel, uint8_t* __restrict__ levels) {
+  // Only the frames' working buffer lives in LDS (52.8 KB: three workgroups
+  // per CU); the constant tables are read from global memory (uniform indices
+  // become scalar loads, the rest hit the L1).
   __shared__ float2 zbuf[kFramesPerBlock * kSlots];
-  __shared__ float2 tw[kHalf];
-  __shared__ float wr_s[kBins];
-  __shared__ float wf_s[kBins];
-  __shared__ int seg_s[kMels + 2];
   __shared__ int64_t s_base[kFramesPerBlock];
   __shared__ int s_clip[kFramesPerBlock];
   __shared__ int s_first[kFramesPerBlock];
@@ -135,12 +134,7 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
   const int tid = threadIdx.x;
   const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kFramesPerBlock;
 
-  for (int i = tid; i < kHalf; i += kThreads) tw[i] = tabs.tw800[i];
-  for (int i = tid; i < kBins; i += kThreads) {
-    wr_s[i] = tabs.w_rise[i];
-    wf_s[i] = tabs.w_fall[i];
-  }
-  if (tid < kMels + 2) seg_s[tid] = tabs.seg_start[tid];
+  const float2* __restrict__ tw = tabs.tw800;
   if (tid < kFramesPerBlock) {
     const int64_t g = g0 + tid;
     const int valid = g < n_frames;
@@ -229,7 +223,7 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
       y[c + 20] = u4;
     }
 #pragma unroll
-    for (int k2 = 1; k2 < 25; ++k2) y[k2] = cmul(y[k2], tw[lane * k2]);
+    for (int k2 = 1; k2 < 25; ++k2) y[k2] = cmul(y[k2], tabs.twa[(k2 - 1) * 32 + lane]);
 #pragma unroll
     for (int k2 = 0; k2 < 25; ++k2) zf[lane + 33 * k2] = y[k2];
   }
@@ -289,7 +283,7 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
       const float2 zm = zbuf[ff * kSlots + (k == 0 ? 0 : kHalf - k)];
       const float2 e = make_float2(0.5f * (zk.x + zm.x), 0.5f * (zk.y - zm.y));
       const float2 o = make_float2(0.5f * (zk.y + zm.y), -0.5f * (zk.x - zm.x));
-      const float2 wo = cmul(tabs.tw1600[k], o);
+      const float2 wo = cmul(tabs.tw1600[k], o);  // L1-cached table
       const float2 x1 = cadd(e, wo), x2 = csub(e, wo);
       p_lo[m] = x1.x * x1.x + x1.y * x1.y;
       p_hi[m] = x2.x * x2.x + x2.y * x2.y;
@@ -317,17 +311,28 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
     constexpr int kSeg = kMels + 1;  // 81 segments
     constexpr int kAOff = 1024;      // per-frame float offsets of A_s and C_s (past the 801 powers)
     constexpr int kCOff = 1120;
-    for (int it = tid; it < kFramesPerBlock * kSeg; it += kThreads) {
-      const int ff = it / kSeg;
-      const int sg = it - ff * kSeg;
+    // segments s and 80 - s are paired (a narrow low band with a wide high
+    // one) so that the threads' loops are of similar length
+    constexpr int kPairs = kSeg / 2 + 1;  // 41: (0,80) .. (39,41), (40)
+    const int* __restrict__ seg = tabs.seg_start;
+    const float* __restrict__ wr = tabs.w_rise;
+    const float* __restrict__ wf = tabs.w_fall;
+    for (int it = tid; it < kFramesPerBlock * kPairs; it += kThreads) {
+      const int ff = it / kPairs;
+      const int pr = it - ff * kPairs;
       const float* p = pf + 2 * ff * kSlots;
-      float a = 0.0f, c = 0.0f;
-      for (int k = seg_s[sg]; k < seg_s[sg + 1]; ++k) {
-        a = fmaf(wr_s[k], p[k], a);
-        c = fmaf(wf_s[k], p[k], c);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int sg = h == 0 ? pr : kSeg - 1 - pr;
+        if (h == 1 && sg == pr) break;
+        float a = 0.0f, c = 0.0f;
+        for (int k = seg[sg]; k < seg[sg + 1]; ++k) {
+          a = fmaf(wr[k], p[k], a);
+          c = fmaf(wf[k], p[k], c);
+        }
+        pf[2 * ff * kSlots + kAOff + sg] = a;
+        pf[2 * ff * kSlots + kCOff + sg] = c;
       }
-      pf[2 * ff * kSlots + kAOff + sg] = a;
-      pf[2 * ff * kSlots + kCOff + sg] = c;
     }
     __syncthreads();
     for (int it = tid; it < kFramesPerBlock * kMels; it += kThreads) {

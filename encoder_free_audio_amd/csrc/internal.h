@@ -28,6 +28,7 @@ struct FrontTables {
   const float* window;   // [1600] periodic Hann
   const float2* tw800;   // [800] exp(-2 pi i m / 800)
   const float2* tw1600;  // [401] exp(-2 pi i k / 1600)
+  const float2* twa;     // [24][32]: exp(-2 pi i n1 k2 / 800) at [k2 - 1][n1]
   // Mel filterbank by segment: bins [seg_start[s], seg_start[s+1]) lie
   // between triangle edges s and s+1; such a bin feeds filter s (its rising
   // side) with weight w_rise and filter s-1 (its falling side) with w_fall.
@@ -41,6 +42,7 @@ struct HostTables {
   float window[kWindow];
   float tw800[2 * kHalf];
   float tw1600[2 * (kHalf / 2 + 1)];
+  float twa[2 * 24 * 32];
   int seg_start[kMels + 2];
   float w_rise[kBins];
   float w_fall[kBins];

@@ -34,6 +34,15 @@ void build_host_tables(HostTables* t) {
     t->tw1600[2 * k] = static_cast<float>(std::cos(two_pi * k / kNfft));
     t->tw1600[2 * k + 1] = static_cast<float>(-std::sin(two_pi * k / kNfft));
   }
+  // pass-A twiddles of the 800 = 32 x 25 decomposition, transposed so that the
+  // 32 threads of a frame read consecutive entries
+  for (int k2 = 1; k2 < 25; ++k2) {
+    for (int n1 = 0; n1 < 32; ++n1) {
+      const int m = (n1 * k2) % kHalf;
+      t->twa[2 * ((k2 - 1) * 32 + n1)] = static_cast<float>(std::cos(two_pi * m / kHalf));
+      t->twa[2 * ((k2 - 1) * 32 + n1) + 1] = static_cast<float>(-std::sin(two_pi * m / kHalf));
+    }
+  }
   // mel filter edges
   double edges[kMels + 2];
   const double mel_hi = hz_to_mel(kSampleRate / 2.0);
