@@ -131,15 +131,16 @@ int dmel_create(dmel_ctx** out, int device) {
     return fail(DMEL_ENOMEM, "host allocation failed");
   }
   dmel::build_host_tables(h);
-  // layout: window | tw800 | tw1600 | twa | seg_start | w_rise | w_fall
+  // layout: window | tw800 | tw1600 | twa | seg_start | seg_lo | seg_hi | seg_inv
   size_t off_window = 0;
   size_t off_tw800 = round_up(off_window + sizeof(h->window), 256);
   size_t off_tw1600 = round_up(off_tw800 + sizeof(h->tw800), 256);
   size_t off_twa = round_up(off_tw1600 + sizeof(h->tw1600), 256);
   size_t off_seg = round_up(off_twa + sizeof(h->twa), 256);
-  size_t off_rise = round_up(off_seg + sizeof(h->seg_start), 256);
-  size_t off_fall = round_up(off_rise + sizeof(h->w_rise), 256);
-  size_t total = round_up(off_fall + sizeof(h->w_fall), 256);
+  size_t off_lo = round_up(off_seg + sizeof(h->seg_start), 256);
+  size_t off_hi = round_up(off_lo + sizeof(h->seg_lo), 256);
+  size_t off_inv = round_up(off_hi + sizeof(h->seg_hi), 256);
+  size_t total = round_up(off_inv + sizeof(h->seg_inv), 256);
   char* staging = new (std::nothrow) char[total];
   if (staging == nullptr) {
     delete h;
@@ -153,8 +154,9 @@ int dmel_create(dmel_ctx** out, int device) {
   std::memcpy(staging + off_tw1600, h->tw1600, sizeof(h->tw1600));
   std::memcpy(staging + off_twa, h->twa, sizeof(h->twa));
   std::memcpy(staging + off_seg, h->seg_start, sizeof(h->seg_start));
-  std::memcpy(staging + off_rise, h->w_rise, sizeof(h->w_rise));
-  std::memcpy(staging + off_fall, h->w_fall, sizeof(h->w_fall));
+  std::memcpy(staging + off_lo, h->seg_lo, sizeof(h->seg_lo));
+  std::memcpy(staging + off_hi, h->seg_hi, sizeof(h->seg_hi));
+  std::memcpy(staging + off_inv, h->seg_inv, sizeof(h->seg_inv));
   int rc = DMEL_OK;
   char* dev = nullptr;
   e = hipMalloc(reinterpret_cast<void**>(&dev), total);
@@ -176,8 +178,9 @@ int dmel_create(dmel_ctx** out, int device) {
     ctx->tabs.tw1600 = reinterpret_cast<const float2*>(dev + off_tw1600);
     ctx->tabs.twa = reinterpret_cast<const float2*>(dev + off_twa);
     ctx->tabs.seg_start = reinterpret_cast<const int*>(dev + off_seg);
-    ctx->tabs.w_rise = reinterpret_cast<const float*>(dev + off_rise);
-    ctx->tabs.w_fall = reinterpret_cast<const float*>(dev + off_fall);
+    ctx->tabs.seg_lo = reinterpret_cast<const float*>(dev + off_lo);
+    ctx->tabs.seg_hi = reinterpret_cast<const float*>(dev + off_hi);
+    ctx->tabs.seg_inv = reinterpret_cast<const float*>(dev + off_inv);
     *out = ctx;
   } else {
     delete ctx;

@@ -63,13 +63,13 @@ __device__ __forceinline__ uint32_t clamp_levels(uint32_t x) {
 // offsets of bins past 51 would overflow it, and each read would then cost two
 // extra VALU ops).
 template <int J0, int J1>
-__device__ __forceinline__ void add_bins(float (&acc)[kStrip], const float* tab, const uint32_t (&lv)[20]) {
+__device__ __forceinline__ void add_bins(float (&acc)[kStrip], const float* tab, const uint32_t (&offs)[40]) {
   uint32_t rebase = J0 * kLevels * kPitch;
   if (J0 > 0) asm volatile("" : "+v"(rebase));
   const float* base = tab + rebase;
   auto row = [&](int j) {
-    const uint32_t L = (lv[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-    return reinterpret_cast<const float4*>(base + (kLevels * (j - J0) + L) * kPitch);
+    const uint32_t o = (offs[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    return reinterpret_cast<const float4*>(reinterpret_cast<const char*>(base) + o);
   };
   float4 cur[4];
   {
@@ -187,6 +187,19 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_
     if (rms_weight != nullptr) scale = rms_scale[t];
     if (out_rows != nullptr) orow = out_rows[t];
   }
+  // Byte offset of the row each bin selects, relative to its half's base (bins
+  // 0..39 from the slice start, 40..79 from bin 40), two 16-bit offsets per
+  // register: one VALU op per bin then forms the read address.
+  uint32_t offs[40];
+#pragma unroll
+  for (int i = 0; i < 40; ++i) {
+    const int j0 = 2 * i, j1 = 2 * i + 1;
+    const uint32_t L0 = (lv[j0 >> 2] >> (8 * (j0 & 3))) & 0xFFu;
+    const uint32_t L1 = (lv[j1 >> 2] >> (8 * (j1 & 3))) & 0xFFu;
+    const uint32_t o0 = (kLevels * (j0 % 40) + L0) * kPitch * 4;
+    const uint32_t o1 = (kLevels * (j1 % 40) + L1) * kPitch * 4;
+    offs[i] = o0 | (o1 << 16);
+  }
   stage_store(tab, st, 0, tid);
   __syncthreads();
 
@@ -196,18 +209,18 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_
   // the arithmetic; each half is written once its previous contents are dead.
   for (int strip = s_first; strip < s_end; ++strip) {
     const int col0 = strip * kStrip;
-    // make the levels look modified here so that the 80 row offsets are not
-    // hoisted out of the strip loop (keeping them live would spill)
+    // make the offsets look modified here so that the 80 unpacked row offsets
+    // are not hoisted out of the strip loop (keeping them live would spill)
 #pragma unroll
-    for (int i = 0; i < 20; ++i) asm volatile("" : "+v"(lv[i]));
+    for (int i = 0; i < 40; ++i) asm volatile("" : "+v"(offs[i]));
     stage_load(st, table, d_model, col0, 1, tid);
     float acc[kStrip];
-    add_bins<0, kMels / 2>(acc, tab, lv);
+    add_bins<0, kMels / 2>(acc, tab, offs);
     stage_store(tab, st, 1, tid);
     __syncthreads();
     const bool more = strip + 1 < s_end;
     if (more) stage_load(st, table, d_model, col0 + kStrip, 0, tid);
-    add_bins<kMels / 2, kMels>(acc, tab, lv);
+    add_bins<kMels / 2, kMels>(acc, tab, offs);
 
     if (active) {
       if (rms_weight != nullptr) {

@@ -315,8 +315,7 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
     // one) so that the threads' loops are of similar length
     constexpr int kPairs = kSeg / 2 + 1;  // 41: (0,80) .. (39,41), (40)
     const int* __restrict__ seg = tabs.seg_start;
-    const float* __restrict__ wr = tabs.w_rise;
-    const float* __restrict__ wf = tabs.w_fall;
+    const float bin_hz = static_cast<float>(kSampleRate) / kNfft;
     for (int it = tid; it < kFramesPerBlock * kPairs; it += kThreads) {
       const int ff = it / kPairs;
       const int pr = it - ff * kPairs;
@@ -325,10 +324,15 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
       for (int h = 0; h < 2; ++h) {
         const int sg = h == 0 ? pr : kSeg - 1 - pr;
         if (h == 1 && sg == pr) break;
+        // triangle weights of the segment's bins, from its edges
+        const float inv = tabs.seg_inv[sg];
+        const float lo = tabs.seg_lo[sg], hi = tabs.seg_hi[sg];
         float a = 0.0f, c = 0.0f;
         for (int k = seg[sg]; k < seg[sg + 1]; ++k) {
-          a = fmaf(wr[k], p[k], a);
-          c = fmaf(wf[k], p[k], c);
+          const float fk = bin_hz * static_cast<float>(k);
+          const float pk = p[k];
+          a = fmaf((fk - lo) * inv, pk, a);  // filter sg, rising side
+          c = fmaf((hi - fk) * inv, pk, c);  // filter sg - 1, falling side
         }
         pf[2 * ff * kSlots + kAOff + sg] = a;
         pf[2 * ff * kSlots + kCOff + sg] = c;

@@ -30,11 +30,13 @@ struct FrontTables {
   const float2* tw1600;  // [401] exp(-2 pi i k / 1600)
   const float2* twa;     // [24][32]: exp(-2 pi i n1 k2 / 800) at [k2 - 1][n1]
   // Mel filterbank by segment: bins [seg_start[s], seg_start[s+1]) lie
-  // between triangle edges s and s+1; such a bin feeds filter s (its rising
-  // side) with weight w_rise and filter s-1 (its falling side) with w_fall.
-  const int* seg_start;  // [82]
-  const float* w_rise;   // [801]
-  const float* w_fall;   // [801]
+  // between triangle edges s and s+1 (lo = seg_lo[s], hi = seg_hi[s]); such a
+  // bin at frequency f feeds filter s (its rising side) with weight
+  // (f - lo) / (hi - lo) and filter s-1 (its falling side) with (hi - f) / (hi - lo).
+  const int* seg_start;   // [82]
+  const float* seg_lo;    // [81] lower edge (Hz)
+  const float* seg_hi;    // [81] upper edge (Hz)
+  const float* seg_inv;   // [81] 1 / (hi - lo)
 };
 
 // Host-built tables, in the layout FrontTables points to (see tables.cpp).
@@ -44,8 +46,9 @@ struct HostTables {
   float tw1600[2 * (kHalf / 2 + 1)];
   float twa[2 * 24 * 32];
   int seg_start[kMels + 2];
-  float w_rise[kBins];
-  float w_fall[kBins];
+  float seg_lo[kMels + 1];
+  float seg_hi[kMels + 1];
+  float seg_inv[kMels + 1];
 };
 void build_host_tables(HostTables* t);
 

@@ -49,8 +49,9 @@ void build_host_tables(HostTables* t) {
   for (int i = 0; i < kMels + 2; ++i) edges[i] = mel_to_hz(mel_hi * i / (kMels + 1));
   edges[0] = 0.0;
   edges[kMels + 1] = kSampleRate / 2.0;
-  // segment view: bin k with edges[s] <= f < edges[s+1] (the last bin, at
-  // exactly 8000 Hz, closes segment 80)
+  // bin k (frequency f = 10 k Hz) lies in segment s when edges[s] <= f <
+  // edges[s+1]; the last bin, at exactly 8000 Hz, closes segment 80.  Inside
+  // segment s the triangle of filter s rises and that of filter s - 1 falls.
   int s = 0;
   t->seg_start[0] = 0;
   for (int k = 0; k < kBins; ++k) {
@@ -59,13 +60,13 @@ void build_host_tables(HostTables* t) {
       ++s;
       t->seg_start[s] = k;
     }
-    const double lo = edges[s], hi = edges[s + 1];
-    const double rise = (f - lo) / (hi - lo);  // filter s, rising side
-    const double fall = (hi - f) / (hi - lo);  // filter s - 1, falling side
-    t->w_rise[k] = s < kMels ? static_cast<float>(std::fmax(0.0, rise)) : 0.0f;
-    t->w_fall[k] = s > 0 ? static_cast<float>(std::fmax(0.0, fall)) : 0.0f;
   }
   while (s < kMels + 1) t->seg_start[++s] = kBins;
+  for (int g = 0; g <= kMels; ++g) {
+    t->seg_lo[g] = static_cast<float>(edges[g]);
+    t->seg_hi[g] = static_cast<float>(edges[g + 1]);
+    t->seg_inv[g] = static_cast<float>(1.0 / (edges[g + 1] - edges[g]));
+  }
 }
 
 }  // namespace dmel
