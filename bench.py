@@ -33,6 +33,24 @@ HBM_BYTES_PER_TOKEN = 800 * 4 + 6144 * 2    # 3,200 B audio read (800 new sample
 PEAK_ADD_TFLOPS = 256 * 64 * 2.4e9 / 1e12   # v_add_f32: 256 CUs x 64 lanes x 2.4 GHz = 39.32 T adds/s
 PEAK_HBM_GBPS = 8000.0
 METRIC = "audio tokens/sec (dMel frames→6144-d embeds) + achieved HBM GB/s vs peak"
+COUNTERS_MD = os.path.join(ROOT, "profiles", "embed_kernel_64x20min_counters.md")
+EMBED_SRC = os.path.join(ROOT, "encoder_free_audio_amd", "csrc", "embed.hip")
+
+
+def embed_traffic():
+    """Memory traffic of one embed launch on the 64 x 20 min batch, from the
+    committed counter summary - only if embed.hip is the source that was
+    measured (otherwise the figure would describe another kernel)."""
+    import hashlib
+    import re
+    try:
+        text = open(COUNTERS_MD).read()
+        want = re.search(r"embed.hip sha256: ([0-9a-f]{64})", text).group(1)
+        traffic = float(re.search(r"traffic bytes per launch: ([0-9.e+]+)", text).group(1))
+        have = hashlib.sha256(open(EMBED_SRC, "rb").read()).hexdigest()
+    except (OSError, AttributeError, ValueError):
+        return None
+    return traffic if have == want else None
 
 
 def parse():
@@ -330,7 +348,8 @@ def bench_batch(args):
         "hbm_frac": hbm / PEAK_HBM_GBPS,
         "kernel_ms": {"frontend_levels": k_front, "rms_scale": k_scale, "embed": k_embed},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_ADD_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_ADD_TFLOPS, "traffic": None},
+                     "frac": achieved / PEAK_ADD_TFLOPS,
+                     "traffic": embed_traffic() if (n_clips, clip_len) == (64, 19_200_000) else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
