@@ -127,9 +127,11 @@ def mel_to_hz(m):
     return 700.0 * (10.0 ** (np.asarray(m, dtype=np.float64) / 2595.0) - 1.0)
 
 
-def mel_edges_hz() -> np.ndarray:
-    """The 82 triangle edges in Hz (edge j, j+1, j+2 define filter j)."""
-    mels = np.linspace(hz_to_mel(F_MIN), hz_to_mel(F_MAX), N_MELS + 2)
+def mel_edges_hz(n_mels: int = N_MELS) -> np.ndarray:
+    """The n_mels + 2 triangle edges in Hz (edges j, j+1, j+2 define filter j)."""
+    if n_mels < 1:
+        raise ValueError("n_mels must be positive")
+    mels = np.linspace(hz_to_mel(F_MIN), hz_to_mel(F_MAX), n_mels + 2)
     hz = mel_to_hz(mels)
     hz[0] = F_MIN
     hz[-1] = F_MAX
@@ -140,34 +142,34 @@ def bin_frequencies() -> np.ndarray:
     return np.arange(N_BINS, dtype=np.float64) * (SAMPLE_RATE / N_FFT)
 
 
-def triangle(j: int, f) -> np.ndarray:
-    """Response of mel filter ``j`` at frequency ``f`` (Hz)."""
-    e = mel_edges_hz()
+def triangle(j: int, f, n_mels: int = N_MELS) -> np.ndarray:
+    """Response of mel filter ``j`` (of ``n_mels``) at frequency ``f`` (Hz)."""
+    e = mel_edges_hz(n_mels)
     f = np.asarray(f, dtype=np.float64)
     rise = (f - e[j]) / (e[j + 1] - e[j])
     fall = (e[j + 2] - f) / (e[j + 2] - e[j + 1])
     return np.maximum(0.0, np.minimum(rise, fall))
 
 
-def mel_filterbank() -> np.ndarray:
-    """[80, 801] fp64 filter weights H[j, k]."""
+def mel_filterbank(n_mels: int = N_MELS) -> np.ndarray:
+    """[n_mels, 801] fp64 filter weights H[j, k]."""
     freqs = bin_frequencies()
-    return np.stack([triangle(j, freqs) for j in range(N_MELS)])
+    return np.stack([triangle(j, freqs, n_mels) for j in range(n_mels)])
 
 
 # ---------------------------------------------------------------------------
 # Log-mel ("80-channel log-mel spectrogram"; reading: natural log of
 # max(M, 1e-10)).
 # ---------------------------------------------------------------------------
-def log_mel_from_frames(frames: np.ndarray) -> np.ndarray:
+def log_mel_from_frames(frames: np.ndarray, n_mels: int = N_MELS) -> np.ndarray:
     power = power_spectrum(frames)
-    mel = power @ mel_filterbank().T
+    mel = power @ mel_filterbank(n_mels).T
     return np.log(np.maximum(mel, LOG_FLOOR))
 
 
-def log_mel(x: np.ndarray, carry: np.ndarray | None = None) -> np.ndarray:
-    """[T, 80] fp64 log-mel of one clip."""
-    return log_mel_from_frames(frame_signal(x, carry))
+def log_mel(x: np.ndarray, carry: np.ndarray | None = None, n_mels: int = N_MELS) -> np.ndarray:
+    """[T, n_mels] fp64 log-mel of one clip."""
+    return log_mel_from_frames(frame_signal(x, carry), n_mels)
 
 
 # ---------------------------------------------------------------------------
@@ -177,30 +179,66 @@ def log_mel(x: np.ndarray, carry: np.ndarray | None = None) -> np.ndarray:
 # decision edges -7 + 9k/16 are exact binary fractions, and for fp32 or fp64
 # inputs every step below is exact near an edge, so the level of a given
 # value does not depend on the precision it is evaluated in.
+#
+# The same page's Coda says the serving code defaults the clamp minimum to
+# -1.5 where the released config has -7, and the config names the level
+# count (mel_vocab_size) and range (dmel_min_value, dmel_max_value) as
+# parameters.  The parametric form is the same uniform floor over [lo, hi] in
+# n_levels steps: level = min(n_levels - 1, floor((c - lo) * n_levels / (hi - lo))),
+# c = clamp(l, lo, hi), decided as the number of edges
+# e_k = lo + ((hi - lo) * k) / n_levels, k = 1 .. n_levels - 1, that c reaches,
+# with e_k evaluated in fp64 in exactly that order.  When the edges are binary
+# fractions (both page configurations) this is the exact floor formula; for
+# other ranges it differs from it only within an fp64 rounding of an edge.
 # ---------------------------------------------------------------------------
-def quantize(logmel: np.ndarray) -> np.ndarray:
-    """Levels of the reading floor((clamp(l, -7, 2) + 7) * 16 / 9), top folded to 15.
+def level_edges(lo: float = CLAMP_MIN, hi: float = CLAMP_MAX, n_levels: int = N_LEVELS) -> np.ndarray:
+    """The n_levels - 1 decision edges (value >= edge k -> level >= k)."""
+    lo, hi = float(lo), float(hi)
+    if not (np.isfinite(lo) and np.isfinite(hi) and lo < hi) or n_levels < 1:
+        raise ValueError("need finite lo < hi and n_levels >= 1")
+    k = np.arange(1, n_levels, dtype=np.float64)
+    return lo + ((hi - lo) * k) / n_levels
 
-    In exact arithmetic floor(y) >= k  <=>  y >= k  <=>  c >= -7 + 9k/16, so
-    the level is the number of edges -7 + 9k/16 (k = 1..15) that the clamped
-    value reaches.  The edges are exact binary fractions and the comparisons
-    are exact, so this evaluates the formula without any rounding, for fp32
-    and fp64 inputs alike.  (Evaluating (c + 7) * 16 / 9 in floating point
+
+def quantize(logmel: np.ndarray, lo: float = CLAMP_MIN, hi: float = CLAMP_MAX,
+             n_levels: int = N_LEVELS) -> np.ndarray:
+    """Levels of the reading floor((clamp(l, lo, hi) - lo) * n_levels / (hi - lo)), top folded.
+
+    In exact arithmetic floor(y) >= k  <=>  y >= k  <=>  c >= lo + (hi - lo) k / n,
+    so the level is the number of edges that the clamped value reaches.  The
+    comparisons are exact; with the released edges (-7 + 9k/16, exact binary
+    fractions) this evaluates the formula without any rounding, for fp32 and
+    fp64 inputs alike.  (Evaluating (c + 7) * 16 / 9 in floating point
     instead can round a value one ulp below an edge onto the edge.)
     """
+    if n_levels > 256:
+        raise ValueError("levels are bytes: at most 256")
     l = np.asarray(logmel, dtype=np.float64)
-    c = np.minimum(np.maximum(l, CLAMP_MIN), CLAMP_MAX)
-    return np.searchsorted(level_edges(), c, side="right").astype(np.uint8)
-
-
-def level_edges() -> np.ndarray:
-    """The 15 decision edges of the quantizer (value >= edge k -> level >= k)."""
-    k = np.arange(1, N_LEVELS, dtype=np.float64)
-    return CLAMP_MIN + (CLAMP_MAX - CLAMP_MIN) * k / N_LEVELS
+    c = np.minimum(np.maximum(l, float(lo)), float(hi))
+    return np.searchsorted(level_edges(lo, hi, n_levels), c, side="right").astype(np.uint8)
 
 
 def levels(x: np.ndarray, carry: np.ndarray | None = None) -> np.ndarray:
     return quantize(log_mel(x, carry))
+
+
+class Config:
+    """A front-end configuration: the released config keys n_mel_bins,
+    mel_vocab_size, dmel_min_value and dmel_max_value ("Why this is a
+    reasonable bet"); the defaults are the released values."""
+
+    def __init__(self, n_mel_bins: int = N_MELS, mel_vocab_size: int = N_LEVELS,
+                 min_value: float = CLAMP_MIN, max_value: float = CLAMP_MAX):
+        self.n_mel_bins = int(n_mel_bins)
+        self.mel_vocab_size = int(mel_vocab_size)
+        self.min_value = float(min_value)
+        self.max_value = float(max_value)
+
+
+def levels_cfg(x: np.ndarray, cfg: Config, carry: np.ndarray | None = None):
+    """(log-mel [T, n_mel_bins], levels [T, n_mel_bins]) of one clip under cfg."""
+    lm = log_mel(x, carry, cfg.n_mel_bins)
+    return lm, quantize(lm, cfg.min_value, cfg.max_value, cfg.mel_vocab_size)
 
 
 # ---------------------------------------------------------------------------
@@ -242,21 +280,27 @@ def f64_to_bf16(x: np.ndarray) -> np.ndarray:
 # Embedding bag ("A frame's 80 rows are summed into one 6144-dimensional
 # vector"; "each mel bin owns its own block of 16 rows").  Reading: row
 # r_j = 16 j + L_j; fp32 accumulation, s = E[r_0], then s = fl32(s + E[r_j])
-# for j = 1..79, in that order.
+# for j = 1..79, in that order.  With another mel_vocab_size V the block of a
+# bin has V rows (r_j = V j + L_j) and the table n_bins * V rows, as in the
+# config's nn.Embedding(n_mel_bins * mel_vocab_size -> d).
 # ---------------------------------------------------------------------------
-def table_rows(lv: np.ndarray) -> np.ndarray:
+def table_rows(lv: np.ndarray, n_levels: int = N_LEVELS) -> np.ndarray:
     lv = np.asarray(lv).astype(np.int64)
-    if lv.ndim != 2 or lv.shape[1] != N_MELS:
-        raise ValueError("levels must be [n, 80]")
-    return N_LEVELS * np.arange(N_MELS, dtype=np.int64)[None, :] + lv
+    if lv.ndim != 2:
+        raise ValueError("levels must be [n, n_bins]")
+    if n_levels == N_LEVELS and lv.shape[1] != N_MELS:
+        raise ValueError("levels must be [n, 80] for the released layout")
+    if np.any(lv >= n_levels):
+        raise ValueError("level out of range")
+    return n_levels * np.arange(lv.shape[1], dtype=np.int64)[None, :] + lv
 
 
-def embed_sum(lv: np.ndarray, table_bits: np.ndarray) -> np.ndarray:
+def embed_sum(lv: np.ndarray, table_bits: np.ndarray, n_levels: int = N_LEVELS) -> np.ndarray:
     """Sequential fp32 bag-of-bins sum: [n, d] fp32."""
     table = bf16_to_f32(table_bits)
-    rows = table_rows(lv)
+    rows = table_rows(lv, n_levels)
     s = table[rows[:, 0]].astype(np.float32, copy=True)
-    for j in range(1, N_MELS):
+    for j in range(1, rows.shape[1]):
         s = (s + table[rows[:, j]]).astype(np.float32, copy=False)
     return s
 
@@ -270,14 +314,14 @@ def rms_norm(s: np.ndarray, weight: np.ndarray, eps: float = RMS_EPS) -> np.ndar
 
 
 def embed(lv: np.ndarray, table_bits: np.ndarray, rms_weight: np.ndarray | None = None,
-          eps: float = RMS_EPS, out_dtype: str = "bf16"):
+          eps: float = RMS_EPS, out_dtype: str = "bf16", n_levels: int = N_LEVELS):
     """Audio tokens from levels.
 
     Returns ``(out, exact)``: ``out`` is bf16 bits (uint16) or fp32; ``exact``
     is the unrounded value (the fp32 sum without RMSNorm, the fp64 RMSNorm
     output with it) that tolerance checks use.
     """
-    s = embed_sum(lv, table_bits)
+    s = embed_sum(lv, table_bits, n_levels)
     if rms_weight is None:
         exact = s
         out = f32_to_bf16(s) if out_dtype == "bf16" else s.copy()
