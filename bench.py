@@ -28,7 +28,6 @@ sys.path.insert(0, ROOT)
 from encoder_free_audio_amd import dmel as dm  # noqa: E402
 from encoder_free_audio_amd import synth  # noqa: E402
 
-ADDS_PER_TOKEN = 79 * 6144                 # sequential fp32 adds of the bag-of-bins sum
 HBM_BYTES_PER_TOKEN = 800 * 4 + 6144 * 2    # 3,200 B audio read (800 new samples) + 12,288 B bf16 token write
 PEAK_ADD_TFLOPS = 256 * 64 * 2.4e9 / 1e12   # v_add_f32: 256 CUs x 64 lanes x 2.4 GHz = 39.32 T adds/s
 PEAK_HBM_GBPS = 8000.0
@@ -67,10 +66,21 @@ def parse():
                          "interleave: 256 x 32768 audio/text positions; copy: a plain 1 GiB device copy "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--streams", type=int, default=4096)
-    return ap.parse_args()
+    ap.add_argument("--config", default=None,
+                    help="batch workload with another front-end configuration, "
+                         "'n_mel_bins,mel_vocab_size,min_value,max_value' (e.g. 80,16,-1.5,2 for the serving "
+                         "code's default clamp minimum); default: the released 80,16,-7,2")
+    args = ap.parse_args()
+    if args.config is not None:
+        f = args.config.split(",")
+        if len(f) != 4:
+            ap.error("--config needs four comma-separated values")
+        args.config = {"n_mel_bins": int(f[0]), "mel_vocab_size": int(f[1]), "min_value": float(f[2]),
+                       "max_value": float(f[3])}
+    return args
 
 
-def cpu_baseline(audio_dev, clip_len, table_bits, n_clips, frames_per_worker):
+def cpu_baseline(audio_dev, clip_len, table_bits, n_clips, frames_per_worker, config=None):
     """Time the CPU oracle on a bounded sample of the same workload: the first
     frames of several clips (causal framing makes them the clip's first frames)."""
     import multiprocessing as mp
@@ -88,7 +98,7 @@ def cpu_baseline(audio_dev, clip_len, table_bits, n_clips, frames_per_worker):
     ctx = mp.get_context("fork")
     with ctx.Pool(workers) as pool:
         t0 = time.perf_counter()
-        res = pool.starmap(_oracle_job, [(s, tb) for s in segs])
+        res = pool.starmap(_oracle_job, [(s, tb, config) for s in segs])
         dt = time.perf_counter() - t0
     tokens = sum(res)
     return {"value": tokens / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
@@ -96,12 +106,13 @@ def cpu_baseline(audio_dev, clip_len, table_bits, n_clips, frames_per_worker):
                       f"RMSNorm on, bf16 out), one oracle process per core, {dt:.1f} s wall"}
 
 
-def _oracle_job(seg, tb):
+def _oracle_job(seg, tb, config=None):
     from threadpoolctl import threadpool_limits
 
     from oracle import dmel_oracle as o
+    cfg = o.Config(**config) if config is not None else None
     with threadpool_limits(1):
-        _, _, out, _ = o.forward(seg, tb, rms_weight=np.ones(tb.shape[1], dtype=np.float32))
+        _, _, out, _ = o.forward(seg, tb, rms_weight=np.ones(tb.shape[1], dtype=np.float32), cfg=cfg)
     return int(out.shape[0])
 
 
@@ -269,23 +280,27 @@ def bench_batch(args):
     T_clip = dm.dmel_num_frames(clip_len)
     n_tok = n_clips * T_clip
     d = 6144
+    cfg = args.config or dm.dmel_default_config()
+    n_bins, n_lv = cfg["n_mel_bins"], cfg["mel_vocab_size"]
+    released = cfg == dm.dmel_default_config()
+    lay = dict(n_bins=n_bins, n_levels=n_lv)
     print(f"[bench] generating {n_clips} x {args.minutes:g} min speech-like audio on the GPU", file=sys.stderr,
           flush=True)
     t0 = time.time()
     audio = synth.speech_clips(seed=2, lengths=[clip_len] * n_clips, device=dev)
-    table = synth.table_bf16(seed=1234).to(dev)
+    table = synth.table_bf16(seed=1234, rows=n_bins * n_lv).to(dev)
     rms_w = torch.ones(d, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
-    ctx = dm.dmel_create(0)
+    ctx = dm.dmel_create_config(0, cfg)
     so, fo, T = dm.clip_offsets([clip_len] * n_clips, dev)
     assert T == n_tok
     out = torch.empty((n_tok, d), dtype=torch.int16, device=dev)
     gram = torch.empty((1280, 1280), dtype=torch.float32, device=dev)
-    levels = torch.empty((n_tok, 80), dtype=torch.uint8, device=dev)
+    levels = torch.empty((n_tok, n_bins), dtype=torch.uint8, device=dev)
     scale = torch.empty(n_tok, dtype=torch.float32, device=dev)
-    dm.dmel_rms_gram(table, d, gram)   # once per table (weight preparation), outside the step
+    dm.dmel_rms_gram(table, d, gram, **lay)   # once per table (weight preparation), outside the step
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -294,10 +309,10 @@ def bench_batch(args):
         dm.dmel_levels(ctx, audio, audio.numel(), so, fo, n_clips, n_tok, None, levels, stream)
         if ev is not None:
             ev[1].record(stream)
-        dm.dmel_rms_scale(levels, n_tok, gram, d, 1e-6, scale, stream)
+        dm.dmel_rms_scale(levels, n_tok, gram, d, 1e-6, scale, stream, **lay)
         if ev is not None:
             ev[2].record(stream)
-        dm.dmel_embed(levels, n_tok, table, d, rms_w, scale, out, dm.DMEL_BF16, d, None, stream)
+        dm.dmel_embed(levels, n_tok, table, d, rms_w, scale, out, dm.DMEL_BF16, d, None, stream, **lay)
         if ev is not None:
             ev[3].record(stream)
 
@@ -315,7 +330,7 @@ def bench_batch(args):
     k_front, k_scale, k_embed = per.mean(axis=0)
     ms_step = wall * 1e3 / args.steps
     tok_s = n_tok / (ms_step * 1e-3)
-    embed_adds = ADDS_PER_TOKEN * n_tok
+    embed_adds = (n_bins - 1) * d * n_tok   # 79 x 6144 per token for the released 80 bins
     achieved = embed_adds / (k_embed * 1e-3) / 1e12
     hbm = HBM_BYTES_PER_TOKEN * n_tok / (ms_step * 1e-3) / 1e9
     print(f"[bench] per step: levels {k_front:.3f} ms, rms_scale {k_scale:.3f} ms, embed {k_embed:.3f} ms; "
@@ -324,7 +339,7 @@ def bench_batch(args):
     cpu = None
     if not args.no_cpu_baseline:
         try:
-            cpu = cpu_baseline(audio, clip_len, table, n_clips, args.cpu_frames)
+            cpu = cpu_baseline(audio, clip_len, table, n_clips, args.cpu_frames, None if released else cfg)
         except Exception as e:  # report, never hide the GPU line
             cpu = {"value": None, "unit": "tokens/s", "cores": 0, "kind": "oracle", "sample": f"failed: {e}"}
     dm.dmel_destroy(ctx)
@@ -342,14 +357,16 @@ def bench_batch(args):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"dMel forward: {n_clips} clips x {args.minutes:g} min of 16 kHz speech-like audio "
-                               f"({n_tok} tokens), table 1280x6144 bf16, fp32 sum, RMSNorm on, bf16 out",
+                               f"({n_tok} tokens), {n_bins} mel bins x {n_lv} levels over "
+                               f"[{cfg['min_value']:g}, {cfg['max_value']:g}], table {n_bins * n_lv}x6144 bf16, "
+                               f"fp32 sum, RMSNorm on, bf16 out",
                    "global_batch": n_clips, "seq_len": T_clip, "parallelism": "single GPU"},
         "hbm_achieved_GBps": hbm,
         "hbm_frac": hbm / PEAK_HBM_GBPS,
         "kernel_ms": {"frontend_levels": k_front, "rms_scale": k_scale, "embed": k_embed},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_ADD_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_ADD_TFLOPS,
-                     "traffic": embed_traffic() if (n_clips, clip_len) == (64, 19_200_000) else None},
+                     "traffic": embed_traffic() if (n_clips, clip_len) == (64, 19_200_000) and released else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -16,6 +16,7 @@
 struct dmel_ctx {
   int device = -1;
   void* dev_mem = nullptr;  // one allocation holding every constant table
+  dmel_config cfg{};
   dmel::FrontTables tabs{};
 };
 
@@ -83,6 +84,32 @@ int check_out(void* out, int32_t out_dtype, int64_t out_row_stride, int32_t widt
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Table layout accepted by the embedding kernels.
+int check_layout(int32_t n_bins, int32_t n_levels) {
+  if (n_bins < 1 || n_bins > dmel::kEmbMaxBins)
+    return fail(DMEL_ESHAPE, "n_bins must be in [1, %d] (got %d)", dmel::kEmbMaxBins, n_bins);
+  if (n_levels < 1 || n_levels > dmel::kEmbMaxLevels)
+    return fail(DMEL_ESHAPE, "n_levels must be in [1, %d] (got %d)", dmel::kEmbMaxLevels, n_levels);
+  return DMEL_OK;
+}
+
+bool released_layout(int32_t n_bins, int32_t n_levels) {
+  return n_bins == dmel::kMels && n_levels == dmel::kLevels;
+}
+
+int check_config(const dmel_config* c) {
+  if (c->n_mel_bins < 1 || c->n_mel_bins > dmel::kMaxMels)
+    return fail(DMEL_EINVAL, "n_mel_bins must be in [1, %d] (got %d)", dmel::kMaxMels, c->n_mel_bins);
+  if (c->mel_vocab_size < 1 || c->mel_vocab_size > dmel::kMaxLevels)
+    return fail(DMEL_EINVAL, "mel_vocab_size must be in [1, %d] (got %d)", dmel::kMaxLevels, c->mel_vocab_size);
+  if (!std::isfinite(c->min_value) || !std::isfinite(c->max_value) || !(c->min_value < c->max_value))
+    return fail(DMEL_EINVAL, "need finite min_value < max_value (got %g, %g)", c->min_value, c->max_value);
+  const double width = static_cast<double>(c->max_value) - static_cast<double>(c->min_value);
+  if (!(width >= 1e-6) || !(width <= 1e30))
+    return fail(DMEL_EINVAL, "max_value - min_value must be in [1e-6, 1e30] (got %g)", width);
+  return DMEL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,11 +134,35 @@ int dmel_get_params(dmel_params* out) {
 
 int64_t dmel_num_frames(int64_t n_samples) { return n_samples < 0 ? -1 : n_samples / dmel::kHop; }
 
+int dmel_default_config(dmel_config* out) {
+  if (out == nullptr) return fail(DMEL_EINVAL, "out is NULL");
+  out->n_mel_bins = dmel::kMels;
+  out->mel_vocab_size = dmel::kLevels;
+  out->min_value = dmel::kClampMin;
+  out->max_value = dmel::kClampMax;
+  return DMEL_OK;
+}
+
+int dmel_get_config(const dmel_ctx* ctx, dmel_config* out) {
+  if (ctx == nullptr || out == nullptr) return fail(DMEL_EINVAL, "ctx / out is NULL");
+  *out = ctx->cfg;
+  return DMEL_OK;
+}
+
 const char* dmel_last_error(void) { return g_last_error.c_str(); }
 
-int dmel_create(dmel_ctx** out, int device) {
+int dmel_create(dmel_ctx** out, int device) { return dmel_create_config(out, device, nullptr); }
+
+int dmel_create_config(dmel_ctx** out, int device, const dmel_config* config) {
   if (out == nullptr) return fail(DMEL_EINVAL, "out is NULL");
   *out = nullptr;
+  dmel_config cfg;
+  dmel_default_config(&cfg);
+  if (config != nullptr) {
+    int rc = check_config(config);
+    if (rc != DMEL_OK) return rc;
+    cfg = *config;
+  }
   int n_dev = 0;
   hipError_t e = hipGetDeviceCount(&n_dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
@@ -130,8 +181,8 @@ int dmel_create(dmel_ctx** out, int device) {
     (void)hipSetDevice(prev);
     return fail(DMEL_ENOMEM, "host allocation failed");
   }
-  dmel::build_host_tables(h);
-  // layout: window | tw800 | tw1600 | twa | seg_start | seg_lo | seg_hi | seg_inv
+  dmel::build_host_tables(h, cfg.n_mel_bins, cfg.mel_vocab_size, cfg.min_value, cfg.max_value);
+  // layout: window | tw800 | tw1600 | twa | seg_start | seg_lo | seg_hi | seg_inv | q_edge
   size_t off_window = 0;
   size_t off_tw800 = round_up(off_window + sizeof(h->window), 256);
   size_t off_tw1600 = round_up(off_tw800 + sizeof(h->tw800), 256);
@@ -140,7 +191,8 @@ int dmel_create(dmel_ctx** out, int device) {
   size_t off_lo = round_up(off_seg + sizeof(h->seg_start), 256);
   size_t off_hi = round_up(off_lo + sizeof(h->seg_lo), 256);
   size_t off_inv = round_up(off_hi + sizeof(h->seg_hi), 256);
-  size_t total = round_up(off_inv + sizeof(h->seg_inv), 256);
+  size_t off_qe = round_up(off_inv + sizeof(h->seg_inv), 256);
+  size_t total = round_up(off_qe + sizeof(h->q_edge), 256);
   char* staging = new (std::nothrow) char[total];
   if (staging == nullptr) {
     delete h;
@@ -157,6 +209,7 @@ int dmel_create(dmel_ctx** out, int device) {
   std::memcpy(staging + off_lo, h->seg_lo, sizeof(h->seg_lo));
   std::memcpy(staging + off_hi, h->seg_hi, sizeof(h->seg_hi));
   std::memcpy(staging + off_inv, h->seg_inv, sizeof(h->seg_inv));
+  std::memcpy(staging + off_qe, h->q_edge, sizeof(h->q_edge));
   int rc = DMEL_OK;
   char* dev = nullptr;
   e = hipMalloc(reinterpret_cast<void**>(&dev), total);
@@ -181,6 +234,13 @@ int dmel_create(dmel_ctx** out, int device) {
     ctx->tabs.seg_lo = reinterpret_cast<const float*>(dev + off_lo);
     ctx->tabs.seg_hi = reinterpret_cast<const float*>(dev + off_hi);
     ctx->tabs.seg_inv = reinterpret_cast<const float*>(dev + off_inv);
+    ctx->tabs.q_edge = reinterpret_cast<const float*>(dev + off_qe);
+    ctx->tabs.n_mels = cfg.n_mel_bins;
+    ctx->tabs.n_levels = cfg.mel_vocab_size;
+    ctx->tabs.q_lo = cfg.min_value;
+    ctx->tabs.q_hi = cfg.max_value;
+    ctx->tabs.q_scale = static_cast<float>(cfg.mel_vocab_size / (static_cast<double>(cfg.max_value) - cfg.min_value));
+    ctx->cfg = cfg;
     *out = ctx;
   } else {
     delete ctx;
@@ -231,33 +291,42 @@ int dmel_levels(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "frontend launch");
 }
 
-int dmel_rms_gram(const uint16_t* table, int32_t d_model, float* gram, void* stream) {
-  int rc = check_table(table, d_model);
+int dmel_rms_gram(const uint16_t* table, int32_t n_bins, int32_t n_levels, int32_t d_model, float* gram,
+                  void* stream) {
+  int rc = check_layout(n_bins, n_levels);
+  if (rc != DMEL_OK) return rc;
+  rc = check_table(table, d_model);
   if (rc != DMEL_OK) return rc;
   if (gram == nullptr) return fail(DMEL_EINVAL, "gram is NULL");
   if (!aligned(gram, 4)) return fail(DMEL_EALIGN, "gram is not 4-byte aligned");
-  hipError_t e = dmel::launch_gram(table, d_model, gram, static_cast<hipStream_t>(stream));
+  hipError_t e = dmel::launch_gram(table, n_bins, n_levels, d_model, gram, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "gram launch");
 }
 
-int dmel_rms_scale(const uint8_t* levels, int64_t n_tokens, const float* gram, int32_t d_model, float eps,
-                   float* scale, void* stream) {
+int dmel_rms_scale(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels, const float* gram,
+                   int32_t d_model, float eps, float* scale, void* stream) {
   if (n_tokens < 0) return fail(DMEL_EINVAL, "n_tokens is negative");
+  int rc = check_layout(n_bins, n_levels);
+  if (rc != DMEL_OK) return rc;
   if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(DMEL_EINVAL, "eps must be finite and >= 0");
   if (d_model <= 0) return fail(DMEL_ESHAPE, "d_model must be positive");
   if (n_tokens == 0) return DMEL_OK;
   if (levels == nullptr || gram == nullptr || scale == nullptr) return fail(DMEL_EINVAL, "NULL pointer argument");
-  if (!aligned(levels, 16)) return fail(DMEL_EALIGN, "levels is not 16-byte aligned");
+  if (released_layout(n_bins, n_levels) && !aligned(levels, 16))
+    return fail(DMEL_EALIGN, "levels is not 16-byte aligned");
   if (!aligned(gram, 4) || !aligned(scale, 4)) return fail(DMEL_EALIGN, "gram / scale not 4-byte aligned");
-  hipError_t e = dmel::launch_rms_scale(levels, n_tokens, gram, d_model, eps, scale, static_cast<hipStream_t>(stream));
+  hipError_t e = dmel::launch_rms_scale(levels, n_tokens, n_bins, n_levels, gram, d_model, eps, scale,
+                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "rms_scale launch");
 }
 
-int dmel_embed(const uint8_t* levels, int64_t n_tokens, const uint16_t* table, int32_t d_model,
-               const float* rms_weight, const float* rms_scale, void* out, int32_t out_dtype,
+int dmel_embed(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels, const uint16_t* table,
+               int32_t d_model, const float* rms_weight, const float* rms_scale, void* out, int32_t out_dtype,
                int64_t out_row_stride, const int64_t* out_rows, void* stream) {
   if (n_tokens < 0) return fail(DMEL_EINVAL, "n_tokens is negative");
-  int rc = check_table(table, d_model);
+  int rc = check_layout(n_bins, n_levels);
+  if (rc != DMEL_OK) return rc;
+  rc = check_table(table, d_model);
   if (rc != DMEL_OK) return rc;
   rc = check_out(out, out_dtype, out_row_stride, d_model, out_rows);
   if (rc != DMEL_OK) return rc;
@@ -266,8 +335,9 @@ int dmel_embed(const uint8_t* levels, int64_t n_tokens, const uint16_t* table, i
     return fail(DMEL_EALIGN, "rms_weight / rms_scale not 4-byte aligned");
   if (n_tokens == 0) return DMEL_OK;
   if (levels == nullptr) return fail(DMEL_EINVAL, "levels is NULL");
-  if (!aligned(levels, 16)) return fail(DMEL_EALIGN, "levels is not 16-byte aligned");
-  hipError_t e = dmel::launch_embed(levels, n_tokens, table, d_model, rms_weight, rms_scale, out,
+  if (released_layout(n_bins, n_levels) && !aligned(levels, 16))
+    return fail(DMEL_EALIGN, "levels is not 16-byte aligned");
+  hipError_t e = dmel::launch_embed(levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, out,
                                     out_dtype == DMEL_F32, out_row_stride, out_rows, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "embed launch");
 }
@@ -286,6 +356,9 @@ int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_tota
   int rc = check_audio(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, out, "out");
   if (rc != DMEL_OK) return rc;
   if (carry != nullptr && !aligned(carry, 4)) return fail(DMEL_EALIGN, "carry is not 4-byte aligned");
+  const int32_t n_bins = ctx->cfg.n_mel_bins, n_levels = ctx->cfg.mel_vocab_size;
+  rc = check_layout(n_bins, n_levels);
+  if (rc != DMEL_OK) return rc;
   rc = check_table(table, d_model);
   if (rc != DMEL_OK) return rc;
   rc = check_out(out, out_dtype, out_row_stride, d_model, out_rows);
@@ -302,6 +375,7 @@ int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_tota
   if (workspace == nullptr) return fail(DMEL_EINVAL, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(DMEL_EALIGN, "workspace is not 256-byte aligned");
   auto* levels = static_cast<uint8_t*>(workspace);
+  // levels [n, n_bins] (n_bins <= 80), then the scales
   auto* scale = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                          round_up(static_cast<size_t>(n_frames_total) * dmel::kMels, 256));
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -309,11 +383,11 @@ int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_tota
                                        n_frames_total, carry, nullptr, levels, s);
   if (e != hipSuccess) return hip_fail(e, "frontend launch");
   if (rms_weight != nullptr) {
-    e = dmel::launch_rms_scale(levels, n_frames_total, gram, d_model, eps, scale, s);
+    e = dmel::launch_rms_scale(levels, n_frames_total, n_bins, n_levels, gram, d_model, eps, scale, s);
     if (e != hipSuccess) return hip_fail(e, "rms_scale launch");
   }
-  e = dmel::launch_embed(levels, n_frames_total, table, d_model, rms_weight, rms_weight ? scale : nullptr, out,
-                         out_dtype == DMEL_F32, out_row_stride, out_rows, s);
+  e = dmel::launch_embed(levels, n_frames_total, n_bins, n_levels, table, d_model, rms_weight,
+                         rms_weight ? scale : nullptr, out, out_dtype == DMEL_F32, out_row_stride, out_rows, s);
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "embed launch");
 }
 

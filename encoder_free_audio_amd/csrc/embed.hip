@@ -21,6 +21,14 @@
 //  * per bin a lane issues four 16-byte LDS reads and 16 adds; accumulators
 //    stay in registers; the epilogue applies the RMSNorm scale and weight and
 //    rounds to bf16.
+//
+// Other layouts (a config with n_mel_bins <= 80 bins of mel_vocab_size <= 16
+// rows each, table row n_levels * bin + level) run in the same 80 x 16 row
+// space: table row V * b + l is staged at LDS row 16 * b + l, every other LDS
+// row holds -0.0, and the bins past n_bins select level 0 of their (empty)
+// block.  Adding -0.0 leaves every fp32 value unchanged (x + -0 = x, also for
+// x = +0 and -0), so the padded sum is bit-identical to the sum over the
+// n_bins real bins.
 #include "internal.h"
 
 namespace dmel {
@@ -42,6 +50,24 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   v[0] = lo;
   v[1] = hi;
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Levels of token t for any layout, as 80 bytes (bin j in byte j % 4 of word
+// j / 4): read byte by byte from a [n, n_bins] array, clamped to vmax; bins
+// past n_bins read as level 0.
+__device__ __forceinline__ void load_levels_any(uint32_t (&lv)[20], const uint8_t* levels, int64_t t, int n_bins,
+                                                uint32_t vmax) {
+  const uint8_t* p = levels + t * n_bins;
+#pragma unroll
+  for (int i = 0; i < 20; ++i) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = 4 * i + b;
+      if (j < n_bins) w |= min(static_cast<uint32_t>(p[j]), vmax) << (8 * b);
+    }
+    lv[i] = w;
+  }
 }
 
 // Clamp each byte of x to at most 15.
@@ -117,15 +143,29 @@ constexpr int kHalfRows = kRows / 2;                   // bins 0..39 | bins 40..
 constexpr int kStageItems = kHalfRows * 2;             // 16-byte chunks per half strip (1280)
 constexpr int kStagePer = (kStageItems + kEmbThreads - 1) / kEmbThreads;  // 2
 
-// Global -> registers: this thread's chunks of half `half` of the strip at col0.
+// Global -> registers: this thread's chunks of half `half` of the strip at
+// col0.  kAny: LDS row 16 b + l takes table row n_levels * b + l, or -0.0
+// where (b, l) is outside the n_bins x n_levels layout.
+template <bool kAny>
 __device__ __forceinline__ void stage_load(uint4 (&st)[kStagePer], const uint16_t* table, int d_model, int col0,
-                                           int half, int tid) {
+                                           int half, int tid, int n_bins, int n_levels) {
 #pragma unroll
   for (int k = 0; k < kStagePer; ++k) {
     const int i = tid + k * kEmbThreads;
     if (i < kStageItems) {
       const int row = half * kHalfRows + (i >> 1);
-      st[k] = *reinterpret_cast<const uint4*>(table + static_cast<int64_t>(row) * d_model + col0 + 8 * (i & 1));
+      int src = row;
+      bool real = true;
+      if (kAny) {
+        const int b = row >> 4, l = row & 15;
+        real = b < n_bins && l < n_levels;
+        src = b * n_levels + l;
+      }
+      if (real) {
+        st[k] = *reinterpret_cast<const uint4*>(table + static_cast<int64_t>(src) * d_model + col0 + 8 * (i & 1));
+      } else {
+        st[k] = make_uint4(0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u);  // bf16 -0.0
+      }
     }
   }
 }
@@ -147,10 +187,13 @@ __device__ __forceinline__ void stage_store(float* tab, const uint4 (&st)[kStage
   }
 }
 
+// kAny = false: the released layout (levels [n, 80], 16-byte aligned, table
+// [1280, d]); true: any n_bins <= 80, n_levels <= 16 (see the top of the file).
+template <bool kAny>
 __global__ void __launch_bounds__(kEmbThreads)
-embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_t* __restrict__ table,
-             int d_model, const float* __restrict__ rms_weight, const float* __restrict__ rms_scale,
-             void* __restrict__ out, int out_f32, int64_t out_row_stride,
+embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels,
+             const uint16_t* __restrict__ table, int d_model, const float* __restrict__ rms_weight,
+             const float* __restrict__ rms_scale, void* __restrict__ out, int out_f32, int64_t out_row_stride,
              const int64_t* __restrict__ out_rows, int n_groups, int n_strips, int strips_per_group) {
   __shared__ float4 tab4[kRows * kPitch / 4];
   float* tab = reinterpret_cast<float*>(tab4);
@@ -164,10 +207,12 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_
   const int s_end = min(n_strips, s_first + strips_per_group);
 
   uint4 st[kStagePer];
-  stage_load(st, table, d_model, s_first * kStrip, 0, tid);
+  stage_load<kAny>(st, table, d_model, s_first * kStrip, 0, tid, n_bins, n_levels);
 
   uint32_t lv[20];
-  if (active) {
+  if (active && kAny) {
+    load_levels_any(lv, levels, t, n_bins, static_cast<uint32_t>(n_levels - 1));
+  } else if (active) {
     const uint4* p = reinterpret_cast<const uint4*>(levels + t * kMels);
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
@@ -213,14 +258,15 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_
     // are not hoisted out of the strip loop (keeping them live would spill)
 #pragma unroll
     for (int i = 0; i < 40; ++i) asm volatile("" : "+v"(offs[i]));
-    stage_load(st, table, d_model, col0, 1, tid);
+    stage_load<kAny>(st, table, d_model, col0, 1, tid, n_bins, n_levels);
     float acc[kStrip];
     add_bins<0, kMels / 2>(acc, tab, offs);
     stage_store(tab, st, 1, tid);
     __syncthreads();
     const bool more = strip + 1 < s_end;
-    if (more) stage_load(st, table, d_model, col0 + kStrip, 0, tid);
-    add_bins<kMels / 2, kMels>(acc, tab, offs);
+    if (more) stage_load<kAny>(st, table, d_model, col0 + kStrip, 0, tid, n_bins, n_levels);
+    // (a layout of at most 40 bins has nothing but -0.0 rows in this half)
+    if (!kAny || n_bins > kMels / 2) add_bins<kMels / 2, kMels>(acc, tab, offs);
 
     if (active) {
       if (rms_weight != nullptr) {
@@ -256,11 +302,13 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const uint16_
 // ---------------------------------------------------------------------------
 // Gram matrix G = E E^T (fp64 accumulation of exact bf16 products, stored
 // fp32).  One workgroup per 16 x 16 block (bin j rows x bin j' rows), j <= j'.
+// G is indexed in the 80 x 16 row space (16 * bin + level) for every layout;
+// rows outside the n_bins x n_levels layout are zero.
 // ---------------------------------------------------------------------------
 constexpr int kGramChunk = 256;
 
 __global__ void __launch_bounds__(256)
-gram_kernel(const uint16_t* __restrict__ table, int d_model, float* __restrict__ gram) {
+gram_kernel(const uint16_t* __restrict__ table, int n_bins, int n_levels, int d_model, float* __restrict__ gram) {
   __shared__ float a_s[16][kGramChunk + 1];
   __shared__ float b_s[16][kGramChunk + 1];
   // blockIdx.x enumerates the upper-triangle pairs (j, j')
@@ -280,9 +328,9 @@ gram_kernel(const uint16_t* __restrict__ table, int d_model, float* __restrict__
     for (int i = tid; i < 16 * kGramChunk; i += 256) {
       const int r = i / kGramChunk, c = i - r * kGramChunk;
       float va = 0.0f, vb = 0.0f;
-      if (c < width) {
-        va = bf16_to_f32(table[static_cast<int64_t>(kLevels * j + r) * d_model + c0 + c]);
-        vb = bf16_to_f32(table[static_cast<int64_t>(kLevels * jp + r) * d_model + c0 + c]);
+      if (c < width && r < n_levels) {
+        if (j < n_bins) va = bf16_to_f32(table[static_cast<int64_t>(n_levels * j + r) * d_model + c0 + c]);
+        if (jp < n_bins) vb = bf16_to_f32(table[static_cast<int64_t>(n_levels * jp + r) * d_model + c0 + c]);
       }
       a_s[r][c] = va;
       b_s[r][c] = vb;
@@ -330,8 +378,8 @@ __device__ __forceinline__ void row_terms(float (&off)[kScaleTok], const float* 
 }
 
 __global__ void __launch_bounds__(kScaleThreads)
-rms_scale_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const float* __restrict__ gram,
-                 int d_model, float eps, float* __restrict__ scale) {
+rms_scale_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels,
+                 const float* __restrict__ gram, int d_model, float eps, float* __restrict__ scale) {
   __shared__ float g_s[16 * kGPitch];  // 83 KB
   const int tid = threadIdx.x;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kScaleBlock + tid;
@@ -341,7 +389,9 @@ rms_scale_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const flo
   for (int k = 0; k < kScaleTok; ++k) {
     const int64_t t = t0 + static_cast<int64_t>(k) * kScaleThreads;
     total[k] = 0.0;
-    if (t < n_tokens) {
+    if (t < n_tokens && (n_bins != kMels || n_levels != kLevels)) {
+      load_levels_any(rot[k], levels, t, n_bins, static_cast<uint32_t>(n_levels - 1));
+    } else if (t < n_tokens) {
       const uint4* p = reinterpret_cast<const uint4*>(levels + t * kMels);
 #pragma unroll
       for (int i = 0; i < 5; ++i) {
@@ -416,8 +466,8 @@ constexpr int kDirTok = 4;                  // tokens per workgroup
 constexpr int kDirThreads = kDirTok * kMels;  // 320
 
 __global__ void __launch_bounds__(kDirThreads)
-rms_scale_direct_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, const float* __restrict__ gram,
-                        int d_model, float eps, float* __restrict__ scale) {
+rms_scale_direct_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels,
+                        const float* __restrict__ gram, int d_model, float eps, float* __restrict__ scale) {
   __shared__ uint8_t lv_s[kDirTok][kMels];
   __shared__ float d_s[kDirTok][kMels];
   __shared__ float o_s[kDirTok][kMels];
@@ -427,8 +477,10 @@ rms_scale_direct_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, co
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kDirTok + tok;
   const bool active = t < n_tokens;
   if (active) {
-    const uint32_t v = levels[t * kMels + j];
-    lv_s[tok][j] = static_cast<uint8_t>(v > 15u ? 15u : v);
+    // bins past n_bins take level 0 of their (zero) block of G
+    const uint32_t vmax = static_cast<uint32_t>(n_levels - 1);
+    const uint32_t v = j < n_bins ? levels[t * n_bins + j] : 0u;
+    lv_s[tok][j] = static_cast<uint8_t>(v > vmax ? vmax : v);
   }
   __syncthreads();
   if (active) {
@@ -476,9 +528,10 @@ gather_rows_kernel(const uint16_t* __restrict__ table, int64_t n_table_rows, int
 
 }  // namespace
 
-hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, const uint16_t* table, int d_model,
-                        const float* rms_weight, const float* rms_scale, void* out, bool out_f32,
-                        int64_t out_row_stride, const int64_t* out_rows, hipStream_t stream) {
+hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
+                        const uint16_t* table, int d_model, const float* rms_weight, const float* rms_scale,
+                        void* out, bool out_f32, int64_t out_row_stride, const int64_t* out_rows,
+                        hipStream_t stream) {
   if (n_tokens <= 0) return hipSuccess;
   const int n_strips = d_model / kStrip;
   const int64_t tblocks = (n_tokens + kEmbThreads - 1) / kEmbThreads;
@@ -506,31 +559,38 @@ hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, const uint16_t*
   const int n_groups = (n_strips + best - 1) / best;
   const int64_t blocks = tblocks * n_groups;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(embed_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kEmbThreads), 0, stream, levels,
-                     n_tokens, table, d_model, rms_weight, rms_scale, out, out_f32 ? 1 : 0, out_row_stride,
-                     out_rows, n_groups, n_strips, best);
+  if (n_bins == kMels && n_levels == kLevels) {
+    hipLaunchKernelGGL(embed_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kEmbThreads), 0, stream,
+                       levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, out,
+                       out_f32 ? 1 : 0, out_row_stride, out_rows, n_groups, n_strips, best);
+  } else {
+    hipLaunchKernelGGL(embed_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kEmbThreads), 0, stream,
+                       levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, out,
+                       out_f32 ? 1 : 0, out_row_stride, out_rows, n_groups, n_strips, best);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_gram(const uint16_t* table, int d_model, float* gram, hipStream_t stream) {
+hipError_t launch_gram(const uint16_t* table, int n_bins, int n_levels, int d_model, float* gram,
+                       hipStream_t stream) {
   const int pairs = kMels * (kMels + 1) / 2;
-  hipLaunchKernelGGL(gram_kernel, dim3(pairs), dim3(256), 0, stream, table, d_model, gram);
+  hipLaunchKernelGGL(gram_kernel, dim3(pairs), dim3(256), 0, stream, table, n_bins, n_levels, d_model, gram);
   return hipGetLastError();
 }
 
-hipError_t launch_rms_scale(const uint8_t* levels, int64_t n_tokens, const float* gram, int d_model,
-                            float eps, float* scale, hipStream_t stream) {
+hipError_t launch_rms_scale(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
+                            const float* gram, int d_model, float eps, float* scale, hipStream_t stream) {
   if (n_tokens <= 0) return hipSuccess;
   if (n_tokens <= kRmsDirectMax) {
     const int64_t blocks = (n_tokens + kDirTok - 1) / kDirTok;
     hipLaunchKernelGGL(rms_scale_direct_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kDirThreads), 0, stream,
-                       levels, n_tokens, gram, d_model, eps, scale);
+                       levels, n_tokens, n_bins, n_levels, gram, d_model, eps, scale);
     return hipGetLastError();
   }
   const int64_t blocks = (n_tokens + kScaleBlock - 1) / kScaleBlock;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rms_scale_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScaleThreads), 0, stream,
-                     levels, n_tokens, gram, d_model, eps, scale);
+                     levels, n_tokens, n_bins, n_levels, gram, d_model, eps, scale);
   return hipGetLastError();
 }
 

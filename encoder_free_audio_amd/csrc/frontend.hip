@@ -1,5 +1,8 @@
 // Front end: framing + Hann window + 1600-point real FFT + power + sparse mel
-// projection + log + clamp + 16-level quantizer, fused in one kernel.
+// projection + log + clamp + 16-level quantizer, fused in one kernel.  The
+// filter count and the quantizer's range and level count come from the
+// context's configuration (released values: 80 filters, [-7, 2], 16 levels;
+// the same page's Coda gives -1.5 as the serving code's default minimum).
 //
 // "Inside Inkling: Audio Design", Part 1: 16 kHz mono audio becomes an
 // 80-channel log-mel spectrogram (hop 800, window 1600) whose 80 values per
@@ -104,15 +107,18 @@ __device__ __forceinline__ int clip_of(const int64_t* frame_off, int n_clips, in
   return lo;
 }
 
-// Exact level of a log-mel value: the number of edges -7 + 9k/16 (k = 1..15)
-// that the clamped value reaches, i.e. floor((c + 7) * 16 / 9) without rounding.
-__device__ __forceinline__ int quantize(float l) {
-  const float c = fminf(fmaxf(l, kClampMin), kClampMax);
-  int q = static_cast<int>((c - kClampMin) * (16.0f / 9.0f));
-  q = q > 15 ? 15 : q;
-  // the estimate is within one of the exact level; the edges are exact in fp32
-  if (q > 0 && c < kClampMin + 0.5625f * static_cast<float>(q)) --q;
-  if (q < 15 && c >= kClampMin + 0.5625f * static_cast<float>(q + 1)) ++q;
+// Exact level of a log-mel value: the number of quantizer edges k = 1 .. V-1
+// that the clamped value reaches, i.e. floor((c - lo) * V / (hi - lo)) capped
+// at V - 1, decided by exact comparisons (the released edges -7 + 9k/16 are
+// exact in fp32; other edges are stored rounded up, see FrontTables).
+__device__ __forceinline__ int quantize(float l, const FrontTables& t) {
+  const float c = fminf(fmaxf(l, t.q_lo), t.q_hi);
+  const int vmax = t.n_levels - 1;
+  int q = static_cast<int>((c - t.q_lo) * t.q_scale);
+  q = q < 0 ? 0 : (q > vmax ? vmax : q);
+  // the estimate is within one or two of the exact level
+  while (q > 0 && c < t.q_edge[q]) --q;
+  while (q < vmax && c >= t.q_edge[q + 1]) ++q;
   return q;
 }
 
@@ -308,21 +314,23 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
   // ---- 4. mel: segment sums, then filters, log, clamp, quantize ----------
   {
     float* pf = reinterpret_cast<float*>(zbuf);
-    constexpr int kSeg = kMels + 1;  // 81 segments
+    const int n_mels = tabs.n_mels;
+    const int n_seg = n_mels + 1;    // 81 segments for 80 filters
     constexpr int kAOff = 1024;      // per-frame float offsets of A_s and C_s (past the 801 powers)
-    constexpr int kCOff = 1120;
-    // segments s and 80 - s are paired (a narrow low band with a wide high
-    // one) so that the threads' loops are of similar length
-    constexpr int kPairs = kSeg / 2 + 1;  // 41: (0,80) .. (39,41), (40)
+    constexpr int kCOff = kAOff + kMaxMels + 8;
+    static_assert(kCOff + kMaxMels + 1 <= 2 * kSlots, "segment sums must fit the frame's buffer");
+    // segments s and n_seg - 1 - s are paired (a narrow low band with a wide
+    // high one) so that the threads' loops are of similar length
+    const int n_pairs = (n_seg + 1) / 2;  // 41: (0,80) .. (39,41), (40)
     const int* __restrict__ seg = tabs.seg_start;
     const float bin_hz = static_cast<float>(kSampleRate) / kNfft;
-    for (int it = tid; it < kFramesPerBlock * kPairs; it += kThreads) {
-      const int ff = it / kPairs;
-      const int pr = it - ff * kPairs;
+    for (int it = tid; it < kFramesPerBlock * n_pairs; it += kThreads) {
+      const int ff = it / n_pairs;
+      const int pr = it - ff * n_pairs;
       const float* p = pf + 2 * ff * kSlots;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int sg = h == 0 ? pr : kSeg - 1 - pr;
+        const int sg = h == 0 ? pr : n_seg - 1 - pr;
         if (h == 1 && sg == pr) break;
         // triangle weights of the segment's bins, from its edges
         const float inv = tabs.seg_inv[sg];
@@ -339,15 +347,15 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
       }
     }
     __syncthreads();
-    for (int it = tid; it < kFramesPerBlock * kMels; it += kThreads) {
-      const int ff = it / kMels;
-      const int j = it - ff * kMels;
+    for (int it = tid; it < kFramesPerBlock * n_mels; it += kThreads) {
+      const int ff = it / n_mels;
+      const int j = it - ff * n_mels;
       const int64_t g = g0 + ff;
       if (g >= n_frames) continue;
       const float m = pf[2 * ff * kSlots + kAOff + j] + pf[2 * ff * kSlots + kCOff + j + 1];
       const float l = logf(fmaxf(m, kLogFloor));
-      if (logmel != nullptr) logmel[g * kMels + j] = l;
-      if (levels != nullptr) levels[g * kMels + j] = static_cast<uint8_t>(quantize(l));
+      if (logmel != nullptr) logmel[g * n_mels + j] = l;
+      if (levels != nullptr) levels[g * n_mels + j] = static_cast<uint8_t>(quantize(l, tabs));
     }
   }
 }

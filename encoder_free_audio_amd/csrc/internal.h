@@ -23,6 +23,13 @@ constexpr float kClampMin = -7.0f;
 constexpr float kClampMax = 2.0f;
 constexpr float kLogFloor = 1e-10f;
 
+// Configurable front end (the config keys n_mel_bins, mel_vocab_size,
+// dmel_min_value, dmel_max_value): limits of what the kernels support.
+constexpr int kMaxMels = 128;        // filters of the front end
+constexpr int kMaxLevels = 256;      // quantizer levels (levels are bytes)
+constexpr int kEmbMaxBins = kMels;   // the embedding's LDS slice holds 80 bins
+constexpr int kEmbMaxLevels = kLevels;  // ... of up to 16 rows each
+
 // Device-resident constant tables of a context.
 struct FrontTables {
   const float* window;   // [1600] periodic Hann
@@ -33,10 +40,19 @@ struct FrontTables {
   // between triangle edges s and s+1 (lo = seg_lo[s], hi = seg_hi[s]); such a
   // bin at frequency f feeds filter s (its rising side) with weight
   // (f - lo) / (hi - lo) and filter s-1 (its falling side) with (hi - f) / (hi - lo).
-  const int* seg_start;   // [82]
-  const float* seg_lo;    // [81] lower edge (Hz)
-  const float* seg_hi;    // [81] upper edge (Hz)
-  const float* seg_inv;   // [81] 1 / (hi - lo)
+  const int* seg_start;   // [n_mels + 2] (82 for the released 80 filters)
+  const float* seg_lo;    // [n_mels + 1] lower edge (Hz)
+  const float* seg_hi;    // [n_mels + 1] upper edge (Hz)
+  const float* seg_inv;   // [n_mels + 1] 1 / (hi - lo)
+  // Quantizer: level = number of edges k = 1 .. n_levels - 1 that the clamped
+  // value c reaches.  q_edge[k] is the smallest fp32 value >= the fp64 edge
+  // lo + ((hi - lo) * k) / n_levels, so the fp32 test c >= q_edge[k] is the
+  // exact comparison with the fp64 edge.
+  const float* q_edge;    // [n_levels + 1]
+  int n_mels;             // filters, 1 .. 128
+  int n_levels;           // 1 .. 256
+  float q_lo, q_hi;       // clamp range
+  float q_scale;          // n_levels / (hi - lo), for the first estimate
 };
 
 // Host-built tables, in the layout FrontTables points to (see tables.cpp).
@@ -45,12 +61,14 @@ struct HostTables {
   float tw800[2 * kHalf];
   float tw1600[2 * (kHalf / 2 + 1)];
   float twa[2 * 24 * 32];
-  int seg_start[kMels + 2];
-  float seg_lo[kMels + 1];
-  float seg_hi[kMels + 1];
-  float seg_inv[kMels + 1];
+  int seg_start[kMaxMels + 2];
+  float seg_lo[kMaxMels + 1];
+  float seg_hi[kMaxMels + 1];
+  float seg_inv[kMaxMels + 1];
+  float q_edge[kMaxLevels + 1];
 };
-void build_host_tables(HostTables* t);
+// n_mels in [1, 128], n_levels in [1, 256], lo < hi (validated by the caller).
+void build_host_tables(HostTables* t, int n_mels, int n_levels, float lo, float hi);
 
 // Kernel launchers (all enqueue on `stream` and return the launch status).
 hipError_t launch_frontend(const FrontTables& tabs, const float* audio, int64_t n_samples_total,
@@ -58,19 +76,25 @@ hipError_t launch_frontend(const FrontTables& tabs, const float* audio, int64_t 
                            int64_t n_frames, const float* carry, float* logmel, uint8_t* levels,
                            hipStream_t stream);
 
-hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, const uint16_t* table, int d_model,
-                        const float* rms_weight, const float* rms_scale, void* out, bool out_f32,
-                        int64_t out_row_stride, const int64_t* out_rows, hipStream_t stream);
+// Embedding-side layout: levels [n, n_bins] (1 <= n_bins <= 80), table rows
+// n_levels * bin + level (1 <= n_levels <= 16).  Internally every kernel works
+// in the released 80 x 16 row space (row 16 * bin + level): missing bins read
+// a row of -0.0 (an exact no-op in the fp32 sum, and 0 in the Gram matrix).
+hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
+                        const uint16_t* table, int d_model, const float* rms_weight, const float* rms_scale,
+                        void* out, bool out_f32, int64_t out_row_stride, const int64_t* out_rows,
+                        hipStream_t stream);
 
-hipError_t launch_gram(const uint16_t* table, int d_model, float* gram, hipStream_t stream);
+hipError_t launch_gram(const uint16_t* table, int n_bins, int n_levels, int d_model, float* gram,
+                       hipStream_t stream);
 
 // Batches up to this many tokens take the RMSNorm-scale kernel that reads the
 // Gram matrix directly (no staging); larger ones stage it in LDS.  Both give
 // bit-identical scales.
 constexpr int64_t kRmsDirectMax = 131072;
 
-hipError_t launch_rms_scale(const uint8_t* levels, int64_t n_tokens, const float* gram, int d_model,
-                            float eps, float* scale, hipStream_t stream);
+hipError_t launch_rms_scale(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
+                            const float* gram, int d_model, float eps, float* scale, hipStream_t stream);
 
 hipError_t launch_gather_rows(const uint16_t* table, int64_t n_table_rows, int d_model,
                               const int32_t* ids, int64_t n, uint16_t* out, int64_t out_row_stride,

@@ -9,7 +9,10 @@
 //    final real-spectrum split, exp(-2 pi i k / 1600);
 //  * 80 triangular filters on the HTK mel scale m(f) = 2595 log10(1 + f / 700),
 //    82 edges equally spaced in mel from 0 Hz to 8000 Hz (outer edges set to
-//    exactly 0 and 8000 Hz), unit peak, evaluated at bin frequencies 10 k Hz.
+//    exactly 0 and 8000 Hz), unit peak, evaluated at bin frequencies 10 k Hz
+//    (n_mel_bins filters and n_mel_bins + 2 edges in general);
+//  * uniform quantizer over the clamp range [lo, hi] in n_levels steps, whose
+//    edges are lo + ((hi - lo) * k) / n_levels evaluated in fp64.
 #include <cmath>
 
 #include "internal.h"
@@ -21,7 +24,7 @@ double hz_to_mel(double f) { return 2595.0 * std::log10(1.0 + f / 700.0); }
 double mel_to_hz(double m) { return 700.0 * (std::pow(10.0, m / 2595.0) - 1.0); }
 }  // namespace
 
-void build_host_tables(HostTables* t) {
+void build_host_tables(HostTables* t, int n_mels, int n_levels, float lo, float hi) {
   const double two_pi = 2.0 * M_PI;
   for (int n = 0; n < kWindow; ++n) {
     t->window[n] = static_cast<float>(0.5 - 0.5 * std::cos(two_pi * n / kWindow));
@@ -44,29 +47,41 @@ void build_host_tables(HostTables* t) {
     }
   }
   // mel filter edges
-  double edges[kMels + 2];
+  double edges[kMaxMels + 2];
   const double mel_hi = hz_to_mel(kSampleRate / 2.0);
-  for (int i = 0; i < kMels + 2; ++i) edges[i] = mel_to_hz(mel_hi * i / (kMels + 1));
+  for (int i = 0; i < n_mels + 2; ++i) edges[i] = mel_to_hz(mel_hi * i / (n_mels + 1));
   edges[0] = 0.0;
-  edges[kMels + 1] = kSampleRate / 2.0;
+  edges[n_mels + 1] = kSampleRate / 2.0;
   // bin k (frequency f = 10 k Hz) lies in segment s when edges[s] <= f <
-  // edges[s+1]; the last bin, at exactly 8000 Hz, closes segment 80.  Inside
-  // segment s the triangle of filter s rises and that of filter s - 1 falls.
+  // edges[s+1]; the last bin, at exactly 8000 Hz, closes the last segment.
+  // Inside segment s the triangle of filter s rises and that of filter s - 1
+  // falls.
   int s = 0;
   t->seg_start[0] = 0;
   for (int k = 0; k < kBins; ++k) {
     const double f = static_cast<double>(k) * kSampleRate / kNfft;
-    while (s < kMels && f >= edges[s + 1]) {
+    while (s < n_mels && f >= edges[s + 1]) {
       ++s;
       t->seg_start[s] = k;
     }
   }
-  while (s < kMels + 1) t->seg_start[++s] = kBins;
-  for (int g = 0; g <= kMels; ++g) {
+  while (s < n_mels + 1) t->seg_start[++s] = kBins;
+  for (int g = 0; g <= n_mels; ++g) {
     t->seg_lo[g] = static_cast<float>(edges[g]);
     t->seg_hi[g] = static_cast<float>(edges[g + 1]);
     t->seg_inv[g] = static_cast<float>(1.0 / (edges[g + 1] - edges[g]));
   }
+  // quantizer edges, rounded up to fp32 so that an fp32 comparison with them
+  // is the exact comparison with the fp64 edge
+  const double dlo = lo, dhi = hi;
+  t->q_edge[0] = lo;
+  for (int k = 1; k < n_levels; ++k) {
+    const double e = dlo + ((dhi - dlo) * k) / n_levels;
+    float f = static_cast<float>(e);
+    if (static_cast<double>(f) < e) f = std::nextafter(f, INFINITY);
+    t->q_edge[k] = f;
+  }
+  t->q_edge[n_levels] = hi;
 }
 
 }  // namespace dmel

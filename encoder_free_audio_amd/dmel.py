@@ -25,9 +25,9 @@ _STATUS = {0: "DMEL_OK", -1: "DMEL_EINVAL", -2: "DMEL_ESHAPE", -3: "DMEL_EDTYPE"
            -5: "DMEL_EHIP", -6: "DMEL_ENOMEM", -7: "DMEL_ESTATE"}
 
 # Every symbol include/dmel.h declares.
-EXPORTS = ("dmel_get_params", "dmel_num_frames", "dmel_last_error", "dmel_create", "dmel_destroy",
-           "dmel_frames", "dmel_levels", "dmel_rms_gram", "dmel_rms_scale", "dmel_embed",
-           "dmel_forward_workspace_bytes", "dmel_forward", "dmel_gather_rows")
+EXPORTS = ("dmel_get_params", "dmel_num_frames", "dmel_last_error", "dmel_default_config", "dmel_create",
+           "dmel_create_config", "dmel_get_config", "dmel_destroy", "dmel_frames", "dmel_levels", "dmel_rms_gram",
+           "dmel_rms_scale", "dmel_embed", "dmel_forward_workspace_bytes", "dmel_forward", "dmel_gather_rows")
 
 
 class DmelError(RuntimeError):
@@ -43,6 +43,11 @@ class DmelParams(ctypes.Structure):
                 ("n_levels", ctypes.c_int32), ("n_rows", ctypes.c_int32), ("clamp_min", ctypes.c_float),
                 ("clamp_max", ctypes.c_float), ("log_floor", ctypes.c_float), ("f_min_hz", ctypes.c_float),
                 ("f_max_hz", ctypes.c_float)]
+
+
+class DmelConfig(ctypes.Structure):
+    _fields_ = [("n_mel_bins", ctypes.c_int32), ("mel_vocab_size", ctypes.c_int32), ("min_value", ctypes.c_float),
+                ("max_value", ctypes.c_float)]
 
 
 _lib_handle = None
@@ -70,13 +75,16 @@ def lib() -> ctypes.CDLL:
             "dmel_get_params": (ctypes.c_int, [ctypes.POINTER(DmelParams)]),
             "dmel_num_frames": (_I64, [_I64]),
             "dmel_last_error": (ctypes.c_char_p, []),
+            "dmel_default_config": (ctypes.c_int, [ctypes.POINTER(DmelConfig)]),
             "dmel_create": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.c_int]),
+            "dmel_create_config": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.c_int, ctypes.POINTER(DmelConfig)]),
+            "dmel_get_config": (ctypes.c_int, [_P, ctypes.POINTER(DmelConfig)]),
             "dmel_destroy": (ctypes.c_int, [_P]),
             "dmel_frames": (ctypes.c_int, [_P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _P]),
             "dmel_levels": (ctypes.c_int, [_P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _P]),
-            "dmel_rms_gram": (ctypes.c_int, [_P, _I32, _P, _P]),
-            "dmel_rms_scale": (ctypes.c_int, [_P, _I64, _P, _I32, _F, _P, _P]),
-            "dmel_embed": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _P, _P, _I32, _I64, _P, _P]),
+            "dmel_rms_gram": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P]),
+            "dmel_rms_scale": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _F, _P, _P]),
+            "dmel_embed": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _I64, _P, _P]),
             "dmel_forward_workspace_bytes": (_SZ, [_I64]),
             "dmel_forward": (ctypes.c_int, [_P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _I32, _P, _P, _F,
                                             _P, _I32, _I64, _P, _P, _SZ, _P]),
@@ -131,11 +139,35 @@ def dmel_last_error() -> str:
     return lib().dmel_last_error().decode(errors="replace")
 
 
+def dmel_default_config() -> dict:
+    c = DmelConfig()
+    _check("dmel_default_config", lib().dmel_default_config(ctypes.byref(c)))
+    return {name: getattr(c, name) for name, _ in DmelConfig._fields_}
+
+
 def dmel_create(device: int = 0) -> int:
     """Returns the context handle (an int) for HIP device ``device``."""
     h = _P()
     _check("dmel_create", lib().dmel_create(ctypes.byref(h), int(device)))
     return h.value
+
+
+def dmel_create_config(device: int = 0, config: dict | None = None) -> int:
+    """Context with the configuration ``config`` (keys of DmelConfig; None: released)."""
+    h = _P()
+    c = None
+    if config is not None:
+        c = DmelConfig(int(config["n_mel_bins"]), int(config["mel_vocab_size"]), float(config["min_value"]),
+                       float(config["max_value"]))
+    _check("dmel_create_config",
+           lib().dmel_create_config(ctypes.byref(h), int(device), ctypes.byref(c) if c is not None else None))
+    return h.value
+
+
+def dmel_get_config(ctx) -> dict:
+    c = DmelConfig()
+    _check("dmel_get_config", lib().dmel_get_config(ctx, ctypes.byref(c)))
+    return {name: getattr(c, name) for name, _ in DmelConfig._fields_}
 
 
 def dmel_destroy(ctx: int) -> None:
@@ -156,20 +188,24 @@ def dmel_levels(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_f
                                             _ptr(levels), _stream(stream)))
 
 
-def dmel_rms_gram(table, d_model, gram, stream=None) -> None:
-    _check("dmel_rms_gram", lib().dmel_rms_gram(_ptr(table), int(d_model), _ptr(gram), _stream(stream)))
+# The table layout (n_bins, n_levels) of the next three calls is keyword-only
+# here and defaults to the released 80 x 16; the C arguments keep their order.
+def dmel_rms_gram(table, d_model, gram, stream=None, *, n_bins=80, n_levels=16) -> None:
+    _check("dmel_rms_gram", lib().dmel_rms_gram(_ptr(table), int(n_bins), int(n_levels), int(d_model), _ptr(gram),
+                                                _stream(stream)))
 
 
-def dmel_rms_scale(levels, n_tokens, gram, d_model, eps, scale, stream=None) -> None:
-    _check("dmel_rms_scale", lib().dmel_rms_scale(_ptr(levels), int(n_tokens), _ptr(gram), int(d_model),
-                                                  float(eps), _ptr(scale), _stream(stream)))
+def dmel_rms_scale(levels, n_tokens, gram, d_model, eps, scale, stream=None, *, n_bins=80, n_levels=16) -> None:
+    _check("dmel_rms_scale", lib().dmel_rms_scale(_ptr(levels), int(n_tokens), int(n_bins), int(n_levels),
+                                                  _ptr(gram), int(d_model), float(eps), _ptr(scale),
+                                                  _stream(stream)))
 
 
 def dmel_embed(levels, n_tokens, table, d_model, rms_weight, rms_scale, out, out_dtype, out_row_stride,
-               out_rows=None, stream=None) -> None:
-    _check("dmel_embed", lib().dmel_embed(_ptr(levels), int(n_tokens), _ptr(table), int(d_model),
-                                          _ptr(rms_weight), _ptr(rms_scale), _ptr(out), int(out_dtype),
-                                          int(out_row_stride), _ptr(out_rows), _stream(stream)))
+               out_rows=None, stream=None, *, n_bins=80, n_levels=16) -> None:
+    _check("dmel_embed", lib().dmel_embed(_ptr(levels), int(n_tokens), int(n_bins), int(n_levels), _ptr(table),
+                                          int(d_model), _ptr(rms_weight), _ptr(rms_scale), _ptr(out),
+                                          int(out_dtype), int(out_row_stride), _ptr(out_rows), _stream(stream)))
 
 
 def dmel_forward_workspace_bytes(n_frames_total: int) -> int:

@@ -77,8 +77,26 @@ typedef struct dmel_params {
   float f_max_hz;       /* 8000 */
 } dmel_params;
 
-/* Opaque per-device context: holds the window, FFT twiddles and the sparse
- * mel filterbank, uploaded once to the device it was created on. */
+/* Front-end configuration, the released config's keys ("Why this is a
+ * reasonable bet": n_mel_bins 80, mel_vocab_size 16, dmel_min_value -7.0,
+ * dmel_max_value 2.0; the Coda "What I don't know yet" gives -1.5 as the
+ * serving code's default minimum).  The quantizer is the same uniform floor
+ * for every configuration: with c = clamp(x, min_value, max_value) and V =
+ * mel_vocab_size, level = number of edges e_k = min + ((max - min) * k) / V
+ * (k = 1 .. V-1, evaluated in fp64) with c >= e_k, i.e.
+ * min(V - 1, floor((c - min) * V / (max - min))) decided exactly.  The
+ * filterbank has n_mel_bins HTK triangles over 0..8000 Hz (n_mel_bins + 2
+ * edges equally spaced in mel). */
+typedef struct dmel_config {
+  int32_t n_mel_bins;      /* filters, 1..128 (the embedding accepts up to 80) */
+  int32_t mel_vocab_size;  /* levels per bin, 1..256 (the embedding accepts up to 16) */
+  float min_value;         /* clamp range: finite, min_value < max_value, */
+  float max_value;         /* 1e-6 <= max_value - min_value <= 1e30 */
+} dmel_config;
+
+/* Opaque per-device context: holds the window, FFT twiddles, the sparse
+ * mel filterbank and the quantizer edges of its configuration, uploaded once
+ * to the device it was created on. */
 typedef struct dmel_ctx dmel_ctx;
 
 /* Fills *out with the constants above.  DMEL_EINVAL if out is NULL. */
@@ -93,11 +111,23 @@ int64_t dmel_num_frames(int64_t n_samples);
 /* Thread-local description of the last failure in this thread ("" if none). */
 const char* dmel_last_error(void);
 
+/* Fills *out with the released configuration (80, 16, -7.0, 2.0).
+ * DMEL_EINVAL if out is NULL. */
+int dmel_default_config(dmel_config* out);
+
 /* Creates a context on HIP device `device`: allocates and uploads the constant
  * tables (about 30 KB), synchronously.  The only call that allocates device
  * memory.  The caller's current device is left unchanged.
  * Errors: DMEL_EINVAL (out NULL, bad device), DMEL_ENOMEM, DMEL_EHIP. */
 int dmel_create(dmel_ctx** out, int device);
+
+/* As dmel_create, with the front end configured by *config (NULL: the
+ * released configuration).  Errors: as dmel_create, and DMEL_EINVAL for a
+ * configuration outside the ranges of dmel_config. */
+int dmel_create_config(dmel_ctx** out, int device, const dmel_config* config);
+
+/* The configuration a context was created with.  DMEL_EINVAL on NULL. */
+int dmel_get_config(const dmel_ctx* ctx, dmel_config* out);
 
 /* Frees a context (NULL is a no-op).  Work already enqueued with it must have
  * completed. */
@@ -107,7 +137,8 @@ int dmel_destroy(dmel_ctx* ctx);
  *  audio      fp32 [n_samples_total], 4-byte aligned
  *  carry      fp32 [n_clips, 800] or NULL: the samples that precede each clip
  *             (the previous hop of a stream); NULL means zeros
- *  logmel     fp32 [n_frames_total, 80] out, row-major
+ *  logmel     fp32 [n_frames_total, n_mel_bins] out, row-major (n_mel_bins of
+ *             the context's configuration: 80 by default)
  * Frames are independent; the result depends only on each frame's 1600
  * samples.  Arithmetic is fp32.
  * Errors: DMEL_EINVAL, DMEL_ESHAPE (n_frames_total > n_samples_total / 800),
@@ -118,38 +149,50 @@ int dmel_frames(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total
 
 /* Levels of every frame ("each of the 80 mel energies in a frame is quantized
  * to one of 16 levels", Part 1; clamp range [-7, 2], "Why this is a reasonable
- * bet").  Same audio arguments as dmel_frames.
- *  levels     uint8 [n_frames_total, 80] out, values 0..15.
+ * bet"; the quantizer of the context's configuration, see dmel_config).  Same
+ * audio arguments as dmel_frames.
+ *  levels     uint8 [n_frames_total, n_mel_bins] out, values 0..mel_vocab_size-1.
  * The level is decided exactly from the fp32 log-mel value that dmel_frames
  * returns for the same input. */
 int dmel_levels(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total,
                 const int64_t* sample_off, const int64_t* frame_off, int32_t n_clips,
                 int64_t n_frames_total, const float* carry, uint8_t* levels, void* stream);
 
+/* Table layout of the embedding calls: n_bins bins (1..80) of n_levels rows
+ * each (1..16), table row n_levels * bin + level; the released layout is
+ * n_bins = 80, n_levels = 16 (row 16 * bin + level, 1280 rows).  Other values
+ * give DMEL_ESHAPE. */
+
 /* Gram matrix of the table, G[r][r'] = sum_c E[r][c] * E[r'][c], accumulated
  * in fp64 and stored as fp32, for the RMSNorm of dmel_embed / dmel_forward.
- *  table      bf16 [1280, d_model], 16-byte aligned, row-major
- *  gram       fp32 [1280, 1280] out (both triangles are written)
+ *  table      bf16 [n_bins * n_levels, d_model], 16-byte aligned, row-major
+ *  gram       fp32 [1280, 1280] out (both triangles are written), indexed by
+ *             16 * bin + level whatever the layout; entries of (bin, level)
+ *             pairs outside the layout are 0
  * Recompute whenever the table's contents change.  d_model % 16 == 0. */
-int dmel_rms_gram(const uint16_t* table, int32_t d_model, float* gram, void* stream);
+int dmel_rms_gram(const uint16_t* table, int32_t n_bins, int32_t n_levels, int32_t d_model, float* gram,
+                  void* stream);
 
 /* Per-token RMSNorm scale r_t = 1 / sqrt(|s_t|^2 / d_model + eps), where
  * |s_t|^2 = sum_{j,j'} G[16 j + L_tj][16 j' + L_tj'] is the squared norm of
- * the exact sum of the token's 80 rows (the "optional RMSNorm" of Part 1).
+ * the exact sum of the token's n_bins rows (the "optional RMSNorm" of Part 1).
  * It differs from the norm of the fp32-rounded sum by about 1e-7 relative.
- *  levels     uint8 [n_tokens, 80], 16-byte aligned; values > 15 read as 15
- *  gram       fp32 [1280, 1280] from dmel_rms_gram
+ *  levels     uint8 [n_tokens, n_bins] (16-byte aligned for the released
+ *             layout); values >= n_levels read as n_levels - 1
+ *  gram       fp32 [1280, 1280] from dmel_rms_gram with the same layout
  *  scale      fp32 [n_tokens] out
  * Errors: DMEL_EINVAL (eps < 0 or not finite), DMEL_EALIGN, DMEL_ESHAPE. */
-int dmel_rms_scale(const uint8_t* levels, int64_t n_tokens, const float* gram, int32_t d_model,
-                   float eps, float* scale, void* stream);
+int dmel_rms_scale(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels,
+                   const float* gram, int32_t d_model, float eps, float* scale, void* stream);
 
 /* Bag-of-bins embedding ("A frame's 80 rows are summed into one 6144-dimensional
  * vector, with an optional RMSNorm", Part 1; "each mel bin owns its own block of
  * 16 rows", "Why this is a reasonable bet").
- *  levels     uint8 [n_tokens, 80], 16-byte aligned; values > 15 read as 15, so
- *             no table read is out of bounds
- *  table      bf16 [1280, d_model], 16-byte aligned; row 16 * bin + level
+ *  levels     uint8 [n_tokens, n_bins] (16-byte aligned for the released
+ *             layout); values >= n_levels read as n_levels - 1, so no table
+ *             read is out of bounds
+ *  table      bf16 [n_bins * n_levels, d_model], 16-byte aligned; row
+ *             n_levels * bin + level (16 * bin + level when released)
  *  d_model    multiple of 16, 16 <= d_model <= 65536
  *  rms_weight fp32 [d_model] or NULL (NULL: no RMSNorm)
  *  rms_scale  fp32 [n_tokens] from dmel_rms_scale; required iff rms_weight
@@ -158,12 +201,13 @@ int dmel_rms_scale(const uint8_t* levels, int64_t n_tokens, const float* gram, i
  *             out + row * out_row_stride elements; 16-byte aligned, and
  *             out_row_stride * element size must be a multiple of 16 bytes
  *  out_rows   int64 [n_tokens] or NULL; rows must be distinct and in range
- * Token value: s = E[r_0], then s = fl32(s + E[r_j]) for j = 1..79, exactly
- * (bit-identical to that sequential fp32 sum); with RMSNorm, y = s * r * w in
- * fp32. */
-int dmel_embed(const uint8_t* levels, int64_t n_tokens, const uint16_t* table, int32_t d_model,
-               const float* rms_weight, const float* rms_scale, void* out, int32_t out_dtype,
-               int64_t out_row_stride, const int64_t* out_rows, void* stream);
+ * Token value: s = E[r_0], then s = fl32(s + E[r_j]) for j = 1..n_bins-1,
+ * exactly (bit-identical to that sequential fp32 sum); with RMSNorm,
+ * y = s * r * w in fp32. */
+int dmel_embed(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels,
+               const uint16_t* table, int32_t d_model, const float* rms_weight, const float* rms_scale,
+               void* out, int32_t out_dtype, int64_t out_row_stride, const int64_t* out_rows,
+               void* stream);
 
 /* Bytes of device workspace dmel_forward needs for n_frames_total frames
  * (levels plus per-token scales, each 256-byte aligned).  0 for a negative count. */
@@ -171,8 +215,10 @@ size_t dmel_forward_workspace_bytes(int64_t n_frames_total);
 
 /* End to end: audio -> levels -> tokens, i.e. dmel_levels, then (when
  * rms_weight is non-NULL) dmel_rms_scale with `gram`, then dmel_embed, on one
- * stream.  Audio arguments as dmel_frames, table/output arguments as
- * dmel_embed.  `workspace` is device memory of at least
+ * stream, with the table layout of the context's configuration (n_bins =
+ * n_mel_bins, n_levels = mel_vocab_size; DMEL_ESHAPE when that is not an
+ * embedding layout).  Audio arguments as dmel_frames, table/output arguments
+ * as dmel_embed.  `workspace` is device memory of at least
  * dmel_forward_workspace_bytes(n_frames_total) bytes, 256-byte aligned; it
  * holds intermediates only and may be reused once the call's work is done.
  * gram is required iff rms_weight is non-NULL. */

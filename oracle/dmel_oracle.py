@@ -288,8 +288,6 @@ def table_rows(lv: np.ndarray, n_levels: int = N_LEVELS) -> np.ndarray:
     lv = np.asarray(lv).astype(np.int64)
     if lv.ndim != 2:
         raise ValueError("levels must be [n, n_bins]")
-    if n_levels == N_LEVELS and lv.shape[1] != N_MELS:
-        raise ValueError("levels must be [n, 80] for the released layout")
     if np.any(lv >= n_levels):
         raise ValueError("level out of range")
     return n_levels * np.arange(lv.shape[1], dtype=np.int64)[None, :] + lv
@@ -332,11 +330,11 @@ def embed(lv: np.ndarray, table_bits: np.ndarray, rms_weight: np.ndarray | None 
 
 
 def forward(x: np.ndarray, table_bits: np.ndarray, rms_weight=None, eps: float = RMS_EPS,
-            out_dtype: str = "bf16", carry=None):
-    """One clip end to end: audio -> log-mel -> levels -> tokens."""
-    lm = log_mel(x, carry)
-    lv = quantize(lm)
-    out, exact = embed(lv, table_bits, rms_weight, eps, out_dtype)
+            out_dtype: str = "bf16", carry=None, cfg: Config | None = None):
+    """One clip end to end: audio -> log-mel -> levels -> tokens (cfg: None = released)."""
+    cfg = cfg or Config()
+    lm, lv = levels_cfg(x, cfg, carry)
+    out, exact = embed(lv, table_bits, rms_weight, eps, out_dtype, n_levels=cfg.mel_vocab_size)
     return lm, lv, out, exact
 
 

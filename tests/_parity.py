@@ -2,11 +2,13 @@
 run the CPU oracle on the same arrays, and compare to the stated bars.
 
 Bars (per element):
-* log-mel: |gpu - oracle| <= 1e-3 on values clamped to [-7, 2]; where the
-  oracle is below -7 the GPU value only has to be <= -7 + 1e-3.
+* log-mel: |gpu - oracle| <= 1e-3 on values clamped to [-7, 2] (or the
+  configuration's clamp range); where the oracle is below the minimum the
+  GPU value only has to be <= minimum + 1e-3.
 * levels: equal, except where the oracle's log-mel lies within 1e-3 of a
-  decision edge -7 + 9k/16 (those are counted); and always equal to the
-  oracle's quantizer applied to the GPU's own fp32 log-mel.
+  decision edge (-7 + 9k/16 for the released quantizer) (those are
+  counted); and always equal to the oracle's quantizer applied to the GPU's
+  own fp32 log-mel.
 * embedding without RMSNorm: bit-exact given the same levels.
 * RMSNorm: fp32 output within 1e-5 relative of the oracle's fp64 value; bf16
   output equal, or one ulp apart where the oracle value is within 1e-5
@@ -37,11 +39,11 @@ def offsets(lengths):
     return dm.clip_offsets(lengths, DEV)
 
 
-def gpu_frames(ctx, audio_flat: torch.Tensor, lengths, carry=None):
-    """(logmel fp32 [T,80], levels u8 [T,80]) from the HIP path, as numpy."""
+def gpu_frames(ctx, audio_flat: torch.Tensor, lengths, carry=None, n_mels=80):
+    """(logmel fp32 [T,n_mels], levels u8 [T,n_mels]) from the HIP path, as numpy."""
     so, fo, T = offsets(lengths)
-    lm = torch.empty((max(T, 1), 80), dtype=torch.float32, device=DEV)
-    lv = torch.empty((max(T, 1), 80), dtype=torch.uint8, device=DEV)
+    lm = torch.empty((max(T, 1), n_mels), dtype=torch.float32, device=DEV)
+    lv = torch.empty((max(T, 1), n_mels), dtype=torch.uint8, device=DEV)
     n = audio_flat.numel()
     dm.dmel_frames(ctx, audio_flat, n, so, fo, len(lengths), T, carry, lm)
     dm.dmel_levels(ctx, audio_flat, n, so, fo, len(lengths), T, carry, lv)
@@ -50,8 +52,9 @@ def gpu_frames(ctx, audio_flat: torch.Tensor, lengths, carry=None):
 
 
 def gpu_embed(levels_np, table_bits: torch.Tensor, d_model, out_dtype="bf16", rms_weight=None, eps=1e-6,
-              gram=None):
-    n = levels_np.shape[0]
+              gram=None, n_levels=16):
+    n, n_bins = levels_np.shape
+    lay = dict(n_bins=n_bins, n_levels=n_levels)
     lv = to_dev(levels_np.astype(np.uint8))
     table = table_bits.to(DEV)
     dt = dm.DMEL_BF16 if out_dtype == "bf16" else dm.DMEL_F32
@@ -63,36 +66,44 @@ def gpu_embed(levels_np, table_bits: torch.Tensor, d_model, out_dtype="bf16", rm
         w = to_dev(np.asarray(rms_weight, dtype=np.float32))
         if gram is None:
             gram = torch.empty((1280, 1280), dtype=torch.float32, device=DEV)
-            dm.dmel_rms_gram(table, d_model, gram)
+            dm.dmel_rms_gram(table, d_model, gram, **lay)
         scale = torch.empty(max(n, 1), dtype=torch.float32, device=DEV)
-        dm.dmel_rms_scale(lv, n, gram, d_model, eps, scale)
-    dm.dmel_embed(lv, n, table, d_model, w, scale, out, dt, d_model)
+        dm.dmel_rms_scale(lv, n, gram, d_model, eps, scale, **lay)
+    dm.dmel_embed(lv, n, table, d_model, w, scale, out, dt, d_model, **lay)
     torch.cuda.synchronize()
     res = out[:n].cpu().numpy()
     return res.view(np.uint16) if dt == dm.DMEL_BF16 else res
 
 
-def check_logmel(gpu_lm, ora_lm):
+def check_logmel(gpu_lm, ora_lm, lo=o.CLAMP_MIN, hi=o.CLAMP_MAX):
     g = np.asarray(gpu_lm, dtype=np.float64)
     r = np.asarray(ora_lm, dtype=np.float64)
-    gc = np.clip(g, o.CLAMP_MIN, o.CLAMP_MAX)
-    rc = np.clip(r, o.CLAMP_MIN, o.CLAMP_MAX)
+    assert g.shape == r.shape
+    gc = np.clip(g, lo, hi)
+    rc = np.clip(r, lo, hi)
     err = np.abs(gc - rc)
     assert err.max(initial=0.0) <= LOGMEL_TOL, f"clamped log-mel error {err.max()}"
-    below = r < o.CLAMP_MIN
+    below = r < lo
     if below.any():
-        assert g[below].max() <= o.CLAMP_MIN + LOGMEL_TOL
-    above = r >= o.CLAMP_MIN
+        assert g[below].max() <= lo + LOGMEL_TOL
+    above = r >= lo
     return float(err.max(initial=0.0)), float(np.abs(g - r)[above].max(initial=0.0))
 
 
-def check_levels(gpu_lv, ora_lm, ora_lv, gpu_lm=None):
-    """Returns (elements in the edge band, forgiven mismatches, frames affected)."""
+def check_levels(gpu_lv, ora_lm, ora_lv, gpu_lm=None, cfg=None):
+    """Returns (elements in the edge band, forgiven mismatches, frames affected).
+
+    cfg: an oracle Config for a non-released quantizer (None: released)."""
+    cfg = cfg or o.Config()
+    q = (cfg.min_value, cfg.max_value, cfg.mel_vocab_size)
     gpu_lv = np.asarray(gpu_lv)
     ora_lv = np.asarray(ora_lv)
     assert gpu_lv.shape == ora_lv.shape
-    assert gpu_lv.max(initial=0) <= 15
-    edges = o.level_edges()
+    assert gpu_lv.max(initial=0) <= cfg.mel_vocab_size - 1
+    edges = o.level_edges(*q)
+    if edges.size == 0:
+        assert np.array_equal(gpu_lv, ora_lv)
+        return 0, 0, 0
     d = np.min(np.abs(np.asarray(ora_lm, dtype=np.float64)[..., None] - edges), axis=-1)
     band = d <= LOGMEL_TOL
     mism = gpu_lv != ora_lv
@@ -102,7 +113,7 @@ def check_levels(gpu_lv, ora_lm, ora_lv, gpu_lm=None):
     assert np.all(np.abs(gpu_lv.astype(int) - ora_lv.astype(int))[mism] == 1)
     if gpu_lm is not None:
         # the same decision taken on the GPU's own fp32 value: exact
-        same = o.quantize(np.asarray(gpu_lm, dtype=np.float32))
+        same = o.quantize(np.asarray(gpu_lm, dtype=np.float32), *q)
         assert np.array_equal(same, gpu_lv)
     frames = int(np.any(mism, axis=-1).sum()) if mism.ndim == 2 else int(mism.any())
     return int(band.sum()), int(mism.sum()), frames

@@ -30,7 +30,7 @@ def _header_symbols():
 
 def test_exports_every_header_symbol(dm):
     syms = _header_symbols()
-    assert len(syms) >= 13
+    assert len(syms) >= 16
     assert sorted(dm.EXPORTS) == syms
     out = subprocess.run(["nm", "-D", "--defined-only", dm.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (dmel_\w+)", out))
@@ -46,6 +46,31 @@ def test_params_match_the_method(dm):
     assert p["clamp_min"] == o.CLAMP_MIN and p["clamp_max"] == o.CLAMP_MAX
     assert abs(p["log_floor"] - o.LOG_FLOOR) < 1e-17
     assert p["f_min_hz"] == o.F_MIN and p["f_max_hz"] == o.F_MAX
+
+
+def test_default_config_is_the_released_one(dm):
+    c = dm.dmel_default_config()
+    cfg = o.Config()
+    assert c == {"n_mel_bins": cfg.n_mel_bins, "mel_vocab_size": cfg.mel_vocab_size,
+                 "min_value": cfg.min_value, "max_value": cfg.max_value}
+
+
+def test_config_validation(dm):
+    # rejected in host code before any HIP call
+    E = dm.DmelError
+    good = dict(n_mel_bins=80, mel_vocab_size=16, min_value=-1.5, max_value=2.0)
+    bad = [dict(n_mel_bins=0), dict(n_mel_bins=129), dict(mel_vocab_size=0), dict(mel_vocab_size=257),
+           dict(min_value=2.0), dict(min_value=3.0), dict(min_value=float("nan")), dict(max_value=float("inf")),
+           dict(min_value=1.0, max_value=1.0 + 2.0 ** -23)]
+    for kw in bad:
+        c = dict(good)
+        c.update(kw)
+        with pytest.raises(E) as e:
+            dm.dmel_create_config(0, c)
+        assert _code(e) == -1, (kw, str(e.value))
+    with pytest.raises(E) as e:
+        dm.dmel_get_config(None)
+    assert _code(e) == -1
 
 
 def test_num_frames(dm):
@@ -112,13 +137,19 @@ def test_validation_embed(dm):
     ok = dict(levels=FAKE, n_tokens=10, table=FAKE, d_model=6144, rms_weight=None, rms_scale=None, out=FAKE,
               out_dtype=0, out_row_stride=6144)
 
+    ok.update(n_bins=80, n_levels=16)
+
     def call(**kw):
         a = dict(ok)
         a.update(kw)
         dm.dmel_embed(a["levels"], a["n_tokens"], a["table"], a["d_model"], a["rms_weight"], a["rms_scale"],
-                      a["out"], a["out_dtype"], a["out_row_stride"])
+                      a["out"], a["out_dtype"], a["out_row_stride"], n_bins=a["n_bins"], n_levels=a["n_levels"])
 
     cases = [
+        (dict(n_bins=0), -2),
+        (dict(n_bins=81), -2),
+        (dict(n_levels=0), -2),
+        (dict(n_levels=17), -2),
         (dict(n_tokens=-1), -1),
         (dict(d_model=100), -2),
         (dict(d_model=0), -2),
@@ -147,6 +178,12 @@ def test_validation_other_entry_points(dm):
     assert _code(e) == -1
     with pytest.raises(E) as e:
         dm.dmel_rms_gram(FAKE, 6008, FAKE)
+    assert _code(e) == -2
+    with pytest.raises(E) as e:
+        dm.dmel_rms_gram(FAKE, 6144, FAKE, n_bins=81)
+    assert _code(e) == -2
+    with pytest.raises(E) as e:
+        dm.dmel_rms_scale(FAKE, 5, FAKE, 6144, 1e-6, FAKE, n_levels=32)
     assert _code(e) == -2
     with pytest.raises(E) as e:
         dm.dmel_rms_scale(FAKE, 5, FAKE, 6144, -1.0, FAKE)

@@ -1,8 +1,9 @@
 """The library's host-built constant tables (csrc/tables.cpp, compiled here with
-the host compiler alone) against the oracle's independently built window and
-filterbank: the window, the FFT twiddles and the mel filterbank in the
-segment form the kernel uses, with the weights evaluated as the kernel
-evaluates them (fp32, from each segment's edges)."""
+the host compiler alone) against the oracle's independently built window,
+filterbank and quantizer: the window, the FFT twiddles, the mel filterbank in
+the segment form the kernel uses, with the weights evaluated as the kernel
+evaluates them (fp32, from each segment's edges), and the quantizer edges,
+for the released configuration and others."""
 
 import os
 import shutil
@@ -18,23 +19,31 @@ CSRC = os.path.join(ROOT, "encoder_free_audio_amd", "csrc")
 
 DRIVER = r"""
 #include <cstdio>
+#include <cstdlib>
 #include "internal.h"
-int main() {
+int main(int argc, char** argv) {
   static dmel::HostTables t;
-  dmel::build_host_tables(&t);
+  const int n_mels = std::atoi(argv[1]), n_levels = std::atoi(argv[2]);
+  const float lo = std::strtof(argv[3], nullptr), hi = std::strtof(argv[4], nullptr);
+  dmel::build_host_tables(&t, n_mels, n_levels, lo, hi);
   for (int i = 0; i < dmel::kWindow; ++i) std::printf("w %d %.9g\n", i, t.window[i]);
   for (int i = 0; i < dmel::kHalf; ++i) std::printf("t8 %d %.9g %.9g\n", i, t.tw800[2 * i], t.tw800[2 * i + 1]);
   for (int i = 0; i <= dmel::kHalf / 2; ++i) std::printf("t16 %d %.9g %.9g\n", i, t.tw1600[2 * i], t.tw1600[2 * i + 1]);
   for (int i = 0; i < 24 * 32; ++i) std::printf("ta %d %.9g %.9g\n", i, t.twa[2 * i], t.twa[2 * i + 1]);
-  for (int i = 0; i < dmel::kMels + 2; ++i) std::printf("ss %d %d\n", i, t.seg_start[i]);
-  for (int i = 0; i <= dmel::kMels; ++i) std::printf("sg %d %.9g %.9g %.9g\n", i, t.seg_lo[i], t.seg_hi[i], t.seg_inv[i]);
+  for (int i = 0; i < n_mels + 2; ++i) std::printf("ss %d %d\n", i, t.seg_start[i]);
+  for (int i = 0; i <= n_mels; ++i) std::printf("sg %d %.9g %.9g %.9g\n", i, t.seg_lo[i], t.seg_hi[i], t.seg_inv[i]);
+  for (int i = 0; i <= n_levels; ++i) std::printf("qe %d %.9g\n", i, t.q_edge[i]);
   return 0;
 }
 """
 
 
+CONFIGS = [(80, 16, -7.0, 2.0), (80, 16, -1.5, 2.0), (40, 8, -5.0, 1.0), (128, 10, -7.0, 2.0),
+           (1, 1, -7.0, 2.0), (64, 256, -3.0, 4.5)]
+
+
 @pytest.fixture(scope="module")
-def tables(tmp_path_factory):
+def dump_exe(tmp_path_factory):
     gxx = shutil.which("g++")
     if gxx is None:
         pytest.skip("no host C++ compiler")
@@ -46,12 +55,21 @@ def tables(tmp_path_factory):
     subprocess.run([gxx, "-O1", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
                     "-I", CSRC, "-I", os.path.join(ROOT, "include"), str(src), os.path.join(CSRC, "tables.cpp"),
                     "-o", str(exe)], check=True, capture_output=True)
-    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
-    t = {"w": {}, "t8": {}, "t16": {}, "ta": {}, "ss": {}, "sg": {}}
+    return exe
+
+
+def _dump(exe, cfg):
+    out = subprocess.run([str(exe)] + [repr(v) for v in cfg], check=True, capture_output=True, text=True).stdout
+    t = {"w": {}, "t8": {}, "t16": {}, "ta": {}, "ss": {}, "sg": {}, "qe": {}}
     for line in out.splitlines():
         k, i, *v = line.split()
         t[k][int(i)] = [float(x) for x in v]
     return t
+
+
+@pytest.fixture(scope="module")
+def tables(dump_exe):
+    return _dump(dump_exe, CONFIGS[0])
 
 
 def test_window(tables):
@@ -73,23 +91,52 @@ def test_twiddles(tables):
     assert np.max(np.abs(ta[..., 0] + 1j * ta[..., 1] - want)) < 1e-7
 
 
-def test_segment_filterbank_matches_oracle(tables):
-    H = o.mel_filterbank()
-    starts = [tables["ss"][i][0] for i in range(82)]
-    assert starts[0] == 0 and starts[81] == 801 and all(a <= b for a, b in zip(starts, starts[1:]))
-    G = np.zeros((80, 801))
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_segment_filterbank_matches_oracle(dump_exe, cfg):
+    tables = _dump(dump_exe, cfg)
+    n = cfg[0]
+    H = o.mel_filterbank(n)
+    starts = [tables["ss"][i][0] for i in range(n + 2)]
+    assert starts[0] == 0 and starts[n + 1] == 801 and all(a <= b for a, b in zip(starts, starts[1:]))
+    G = np.zeros((n, 801))
+    tol = np.zeros((n, 801))
     bin_hz = np.float32(16000.0 / 1600.0)
-    for s in range(81):
+    for s in range(n + 1):
         lo, hi, inv = (np.float32(v) for v in tables["sg"][s])
         for k in range(int(starts[s]), int(starts[s + 1])):
             fk = np.float32(bin_hz * np.float32(k))
             rise = np.float32(np.float32(fk - lo) * inv)
             fall = np.float32(np.float32(hi - fk) * inv)
-            if s < 80:
+            # fp32 rounding of f, the edges, 1/(hi - lo), the difference and
+            # the product: a few ulps of (f + hi) / (hi - lo)
+            bound = 4.0 * 2.0 ** -24 * (float(fk) + float(hi)) * float(inv) + 1e-12
+            if s < n:
                 G[s, k] += rise
+                tol[s, k] = bound
             if s > 0:
                 G[s - 1, k] += fall
+                tol[s - 1, k] = bound
     # every bin lies between the edges of its segment, and the weights agree
     # with the oracle's fp64 triangles to fp32 rounding
-    assert np.max(np.abs(G - H)) < 2e-6
+    assert np.all(np.abs(G - H) <= tol)
+    assert np.max(np.abs(G - H)) < 2e-5
     assert np.array_equal(G > 1e-6, H > 1e-6)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_quantizer_edges_match_oracle(dump_exe, cfg):
+    n_mels, n_lv, lo, hi = cfg
+    t = _dump(dump_exe, cfg)
+    q = np.array([t["qe"][i][0] for i in range(n_lv + 1)], dtype=np.float32)
+    assert q[0] == np.float32(lo) and q[-1] == np.float32(hi)
+    e = o.level_edges(lo, hi, n_lv)
+    # each stored edge is the smallest fp32 value >= the oracle's fp64 edge
+    inner = q[1:-1].astype(np.float64)
+    below = np.nextafter(q[1:-1], np.float32(-np.inf)).astype(np.float64)
+    assert np.all(inner >= e) and np.all(below < e)
+    # hence the fp32 comparison decides as the oracle does on fp32 inputs
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.uniform(lo - 1, hi + 1, 20000).astype(np.float32), q, below.astype(np.float32)])
+    c = np.minimum(np.maximum(x, np.float32(lo)), np.float32(hi))
+    lv = (c[:, None] >= q[None, 1:-1]).sum(axis=1)
+    assert np.array_equal(lv, o.quantize(x.astype(np.float64), lo, hi, n_lv))
