@@ -61,10 +61,13 @@ def parse():
     ap.add_argument("--minutes", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=1200, help="oracle sample: frames per worker")
-    ap.add_argument("--workload", choices=("batch", "stream", "interleave", "copy"), default="batch",
+    ap.add_argument("--workload", choices=("batch", "stream", "interleave", "copy", "shortconv", "shortconv_decode"),
+                    default="batch",
                     help="batch: 64 x 20 min clips (default); stream: 4096 streams, one hop per step; "
                          "interleave: 256 x 32768 audio/text positions; copy: a plain 1 GiB device copy "
-                         "(calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+                         "(calibrates the FETCH_SIZE / WRITE_SIZE counters); shortconv: the decoder's width-4 "
+                         "short convolution over 64 requests x 24,000 tokens x 6144 channels (prefill); "
+                         "shortconv_decode: 4096 requests, one token per step, state carried")
     ap.add_argument("--streams", type=int, default=4096)
     ap.add_argument("--config", default=None,
                     help="batch workload with another front-end configuration, "
@@ -126,14 +129,109 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     if args.steps is None:
-        args.steps = {"batch": 20, "stream": 1000, "interleave": 5, "copy": 5}[args.workload]
+        args.steps = {"batch": 20, "stream": 1000, "interleave": 5, "copy": 5, "shortconv": 20,
+                      "shortconv_decode": 1000}[args.workload]
     if args.workload == "stream":
         return bench_stream(args)
     if args.workload == "interleave":
         return bench_interleave(args)
     if args.workload == "copy":
         return bench_copy(args)
+    if args.workload in ("shortconv", "shortconv_decode"):
+        return bench_shortconv(args)
     return bench_batch(args)
+
+
+def cpu_baseline_shortconv(x, w, st, S, L, decode):
+    """The short-convolution oracle (fp64, one process) on a bounded sample of
+    the same workload (about 10 s of CPU work): 8 requests x 8000 tokens of the
+    prefill, or up to 8000 decode steps of 8 requests."""
+    from oracle import shortconv_oracle as sc  # noqa: E402  (test infrastructure)
+
+    C = x.shape[1]
+    n_req, n_tok = 8, 8000
+    if decode:
+        n_tok = min(n_tok, x.shape[0] // S)
+        xs = x[: n_tok * S].view(n_tok, S, C)[:, :n_req].permute(1, 0, 2).reshape(n_req * n_tok, C)
+    else:
+        xs = x.view(S, L, C)[:n_req, :n_tok].reshape(n_req * n_tok, C)
+    xb = xs.cpu().numpy().view(np.uint16)
+    stb = st[:n_req].cpu().numpy().view(np.uint16)
+    wn = w.cpu().numpy().astype(np.float64)
+    off = np.arange(0, n_req * n_tok + 1, n_tok)
+    t0 = time.perf_counter()
+    sc.shortconv(xb, off, wn, stb)
+    dt = time.perf_counter() - t0
+    return {"value": n_req * n_tok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_req} requests x {n_tok} tokens x {C} channels ({'decode steps' if decode else 'prefill'}), "
+                      f"state in and out, one process, {dt:.1f} s wall"}
+
+
+def bench_shortconv(args):
+    """The decoder's short convolution (width 4, per-request state): prefill of
+    64 requests x 24,000 tokens x 6144 channels, or decode steps of one token
+    for each of 4096 requests with the state carried in two buffers.  Inputs
+    bf16 ~ N(0, 1), taps ~ U(-0.5, 0.5), bf16 output."""
+    dev = "cuda"
+    C = 6144
+    decode = args.workload == "shortconv_decode"
+    S, L = (args.streams, 1) if decode else (64, 24000)
+    T = S * L
+    n_x = T if not decode else T * args.steps
+    x = synth.activations_bf16(seed=90, n_tokens=n_x, channels=C, device=dev)
+    w = synth.shortconv_weight(seed=91, channels=C).to(dev)
+    st = [synth.activations_bf16(seed=92, n_tokens=S * 3, channels=C, device=dev).view(S, 3, C),
+          torch.empty((S, 3, C), dtype=torch.int16, device=dev)]
+    off = torch.arange(0, T + 1, L, dtype=torch.int64, device=dev)
+    y = torch.empty((T, C), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(k, ev=None):
+        xk = x[(k % (n_x // T)) * T: (k % (n_x // T) + 1) * T]
+        if ev is not None:
+            ev[0].record(stream)
+        dm.dmel_shortconv(xk, T, C, off, S, w, st[k % 2], st[(k + 1) % 2], y, dm.DMEL_BF16, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(k, events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per = np.array([e[0].elapsed_time(e[1]) for e in events])
+    k_ms = float(per.mean())
+    ms_step = wall * 1e3 / args.steps
+    bytes_launch = T * C * 2 * 2 + S * 3 * C * 2 * 2 + C * 16 + (S + 1) * 8
+    achieved = bytes_launch / (k_ms * 1e-3) / 1e9
+    line = {
+        "metric": "short-convolution tokens/s (width 4, 6144 channels, per-request state)",
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": (f"shortconv decode: {S} requests x 1 token per step, state carried" if decode else
+                                f"shortconv prefill: {S} requests x {L} tokens") + f", {C} channels, bf16 in/out",
+                   "global_batch": S, "seq_len": L, "parallelism": "single GPU"},
+        "kernel_ms": {"shortconv": k_ms, "p50": float(np.percentile(per, 50)), "p99": float(np.percentile(per, 99))},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_shortconv(x, w, st[0], S, L, decode),
+    }
+    print(f"[bench] shortconv kernel {k_ms:.4f} ms per launch ({bytes_launch / 1e9:.3f} GB algorithmic), "
+          f"wall {ms_step:.4f} ms per step", file=sys.stderr, flush=True)
+    print(json.dumps(line), flush=True)
 
 
 def bench_copy(args):

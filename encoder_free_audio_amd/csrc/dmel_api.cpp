@@ -97,6 +97,13 @@ bool released_layout(int32_t n_bins, int32_t n_levels) {
   return n_bins == dmel::kMels && n_levels == dmel::kLevels;
 }
 
+// [a, a + na) and [b, b + nb) share a byte (empty ranges never do).
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
 int check_config(const dmel_config* c) {
   if (c->n_mel_bins < 1 || c->n_mel_bins > dmel::kMaxMels)
     return fail(DMEL_EINVAL, "n_mel_bins must be in [1, %d] (got %d)", dmel::kMaxMels, c->n_mel_bins);
@@ -404,6 +411,37 @@ int dmel_gather_rows(const uint16_t* table, int64_t n_table_rows, int32_t d_mode
   hipError_t e = dmel::launch_gather_rows(table, n_table_rows, d_model, ids, n, out, out_row_stride, out_rows,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "gather_rows launch");
+}
+
+int dmel_shortconv(const uint16_t* x, int64_t n_tokens, int32_t channels, const int64_t* seq_off, int32_t n_seqs,
+                   const float* weight, const uint16_t* state_in, uint16_t* state_out, void* y, int32_t y_dtype,
+                   void* stream) {
+  if (n_tokens < 0 || n_seqs < 0) return fail(DMEL_EINVAL, "negative count");
+  if (channels < 8 || channels > (1 << 20) || channels % 8 != 0)
+    return fail(DMEL_ESHAPE, "channels must be a multiple of 8 in [8, 1048576] (got %d)", channels);
+  if (n_tokens > 0 && n_seqs == 0) return fail(DMEL_ESHAPE, "tokens given but n_seqs is 0");
+  if (y_dtype != DMEL_BF16 && y_dtype != DMEL_F32) return fail(DMEL_EDTYPE, "unsupported y_dtype %d", y_dtype);
+  if (n_tokens == 0 && (state_out == nullptr || n_seqs == 0)) return DMEL_OK;
+  if (seq_off == nullptr) return fail(DMEL_EINVAL, "seq_off is NULL");
+  if (n_tokens > 0 && (x == nullptr || y == nullptr || weight == nullptr))
+    return fail(DMEL_EINVAL, "x / y / weight is NULL");
+  if (!aligned(seq_off, 8)) return fail(DMEL_EALIGN, "seq_off is not 8-byte aligned");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(weight, 16) || !aligned(state_in, 16) ||
+      !aligned(state_out, 16))
+    return fail(DMEL_EALIGN, "x, y, weight and the state arrays must be 16-byte aligned");
+  const size_t C = static_cast<size_t>(channels), T = static_cast<size_t>(n_tokens), S = static_cast<size_t>(n_seqs);
+  const size_t bx = T * C * 2, by = T * C * (y_dtype == DMEL_F32 ? 4 : 2), bs = S * 3 * C * 2, bw = C * 16,
+               bo = (S + 1) * 8;
+  // written buffers must not share memory with anything the kernel reads or writes
+  if (overlaps(y, by, x, bx) || overlaps(y, by, state_in, bs) || overlaps(y, by, state_out, bs) ||
+      overlaps(y, by, weight, bw) || overlaps(y, by, seq_off, bo))
+    return fail(DMEL_EINVAL, "y overlaps another argument");
+  if (overlaps(state_out, bs, x, bx) || overlaps(state_out, bs, state_in, bs) || overlaps(state_out, bs, weight, bw) ||
+      overlaps(state_out, bs, seq_off, bo))
+    return fail(DMEL_EINVAL, "state_out overlaps another argument (use two state buffers in turn)");
+  hipError_t e = dmel::launch_shortconv(x, n_tokens, channels, seq_off, n_seqs, weight, state_in, state_out, y,
+                                        y_dtype == DMEL_F32, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "shortconv launch");
 }
 
 }  // extern "C"

@@ -96,6 +96,12 @@ constexpr int64_t kRmsDirectMax = 131072;
 hipError_t launch_rms_scale(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
                             const float* gram, int d_model, float eps, float* scale, hipStream_t stream);
 
+// Short convolution (width 4, residual) over ragged requests with per-request
+// state; channels % 8 == 0.
+hipError_t launch_shortconv(const uint16_t* x, int64_t n_tokens, int channels, const int64_t* seq_off, int n_seqs,
+                            const float* weight, const uint16_t* state_in, uint16_t* state_out, void* y,
+                            bool y_f32, hipStream_t stream);
+
 hipError_t launch_gather_rows(const uint16_t* table, int64_t n_table_rows, int d_model,
                               const int32_t* ids, int64_t n, uint16_t* out, int64_t out_row_stride,
                               const int64_t* out_rows, hipStream_t stream);

@@ -27,7 +27,8 @@ _STATUS = {0: "DMEL_OK", -1: "DMEL_EINVAL", -2: "DMEL_ESHAPE", -3: "DMEL_EDTYPE"
 # Every symbol include/dmel.h declares.
 EXPORTS = ("dmel_get_params", "dmel_num_frames", "dmel_last_error", "dmel_default_config", "dmel_create",
            "dmel_create_config", "dmel_get_config", "dmel_destroy", "dmel_frames", "dmel_levels", "dmel_rms_gram",
-           "dmel_rms_scale", "dmel_embed", "dmel_forward_workspace_bytes", "dmel_forward", "dmel_gather_rows")
+           "dmel_rms_scale", "dmel_embed", "dmel_forward_workspace_bytes", "dmel_forward", "dmel_gather_rows",
+           "dmel_shortconv")
 
 
 class DmelError(RuntimeError):
@@ -89,6 +90,7 @@ def lib() -> ctypes.CDLL:
             "dmel_forward": (ctypes.c_int, [_P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _I32, _P, _P, _F,
                                             _P, _I32, _I64, _P, _P, _SZ, _P]),
             "dmel_gather_rows": (ctypes.c_int, [_P, _I64, _I32, _P, _I64, _P, _I64, _P, _P]),
+            "dmel_shortconv": (ctypes.c_int, [_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _I32, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(h, name)
@@ -228,6 +230,13 @@ def dmel_gather_rows(table, n_table_rows, d_model, ids, n, out, out_row_stride, 
     _check("dmel_gather_rows", lib().dmel_gather_rows(_ptr(table), int(n_table_rows), int(d_model), _ptr(ids),
                                                       int(n), _ptr(out), int(out_row_stride), _ptr(out_rows),
                                                       _stream(stream)))
+
+
+def dmel_shortconv(x, n_tokens, channels, seq_off, n_seqs, weight, state_in, state_out, y, y_dtype,
+                   stream=None) -> None:
+    _check("dmel_shortconv", lib().dmel_shortconv(_ptr(x), int(n_tokens), int(channels), _ptr(seq_off), int(n_seqs),
+                                                  _ptr(weight), _ptr(state_in), _ptr(state_out), _ptr(y),
+                                                  int(y_dtype), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -293,3 +293,25 @@ def streaming_hops(seed: int = 3, n_streams: int = 4096, n_steps: int = 1000, de
         x = bursts_clips(seed * 1_000_003 + s0, s1 - s0, total, device=device)
         out[:, s0:s1, :] = x.view(s1 - s0, n_steps, HOP).permute(1, 0, 2)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Decoder short convolution: bf16 activations ~ N(0, std) (the residual-branch
+# and key / value projection outputs it is applied to), weights ~ U(-0.5, 0.5)
+# per channel and tap, and ragged request lengths.
+# ---------------------------------------------------------------------------
+def activations_bf16(seed: int, n_tokens: int, channels: int, std: float = 1.0, device="cpu") -> torch.Tensor:
+    """[n_tokens, channels] bf16 bit patterns in an int16 tensor."""
+    return table_bf16(seed, rows=n_tokens, d_model=channels, std=std, device=device)
+
+
+def shortconv_weight(seed: int, channels: int, width: int = 4) -> torch.Tensor:
+    """[channels, width] fp32 taps ~ U(-0.5, 0.5)."""
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy(rng.uniform(-0.5, 0.5, (channels, width)).astype(np.float32))
+
+
+def request_lengths(seed: int, n: int, lo: int = 0, hi: int = 200) -> list:
+    """n request lengths ~ U{lo..hi} (empty requests included when lo = 0)."""
+    rng = np.random.default_rng(seed)
+    return [int(v) for v in rng.integers(lo, hi + 1, n)]

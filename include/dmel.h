@@ -241,6 +241,36 @@ int dmel_gather_rows(const uint16_t* table, int64_t n_table_rows, int32_t d_mode
                      const int32_t* ids, int64_t n, uint16_t* out, int64_t out_row_stride,
                      const int64_t* out_rows, void* stream);
 
+/* Short convolution of the decoder over a batch of requests ("Inside Inkling:
+ * Audio Design", Part 3 - Inference, "Short convolutions": per-channel causal
+ * convolution of width 4 with a residual,
+ *     y[t][c] = x[t][c] + sum_{d=0}^{3} w[c][d] * x[t-d][c];
+ * "Where audio touches the serving path": each request keeps a small
+ * convolution state).
+ *  x          bf16 [n_tokens, channels]; request s is rows
+ *             seq_off[s] .. seq_off[s+1] (seq_off: int64 [n_seqs + 1],
+ *             seq_off[0] = 0, non-decreasing, seq_off[n_seqs] = n_tokens;
+ *             requests may be empty)
+ *  weight     fp32 [channels, 4]: weight[c][d] multiplies x[t-d][c]
+ *  state_in   bf16 [n_seqs, 3, channels] or NULL (zeros): the three inputs
+ *             before each request's first token, oldest first
+ *  state_out  bf16 [n_seqs, 3, channels] or NULL: receives the last three
+ *             inputs of [state_in, request tokens] (an empty request keeps
+ *             its state); must not overlap any other argument - callers that
+ *             carry the state alternate two buffers
+ *  y          y_dtype (DMEL_BF16 / DMEL_F32) [n_tokens, channels]; must not
+ *             overlap any other argument
+ * channels % 8 == 0; x, y, weight and the states 16-byte aligned.
+ * Arithmetic is fp32: a = w0 x[t]; a = fma(w1, x[t-1], a); a = fma(w2,
+ * x[t-2], a); a = fma(w3, x[t-3], a); y = x[t] + a, rounded to nearest-even
+ * for bf16 output.  Offsets that break the rules above give unspecified
+ * values but no out-of-bounds access.
+ * Errors: DMEL_EINVAL (NULL where data is needed, overlapping buffers),
+ * DMEL_ESHAPE, DMEL_EDTYPE, DMEL_EALIGN, DMEL_EHIP. */
+int dmel_shortconv(const uint16_t* x, int64_t n_tokens, int32_t channels, const int64_t* seq_off,
+                   int32_t n_seqs, const float* weight, const uint16_t* state_in, uint16_t* state_out,
+                   void* y, int32_t y_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -215,11 +215,45 @@ def test_validation_other_entry_points(dm):
     assert _code(e) in (-1, -5)
 
 
+def test_validation_shortconv(dm):
+    E = dm.DmelError
+    C, T, S = 64, 10, 2
+    ok = dict(x=FAKE, n_tokens=T, channels=C, seq_off=FAKE, n_seqs=S, weight=FAKE + (1 << 16),
+              state_in=None, state_out=None, y=FAKE + (1 << 18), y_dtype=0)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        dm.dmel_shortconv(a["x"], a["n_tokens"], a["channels"], a["seq_off"], a["n_seqs"], a["weight"],
+                          a["state_in"], a["state_out"], a["y"], a["y_dtype"])
+
+    cases = [
+        (dict(n_tokens=-1), -1),
+        (dict(channels=12), -2),
+        (dict(channels=0), -2),
+        (dict(n_seqs=0), -2),
+        (dict(y_dtype=3), -3),
+        (dict(seq_off=None), -1),
+        (dict(y=None), -1),
+        (dict(weight=None), -1),
+        (dict(x=FAKE + 8), -4),
+        (dict(seq_off=FAKE + 4), -4),
+        (dict(y=FAKE + 96), -1),                      # overlaps x (1280 bytes from FAKE)
+        (dict(state_in=FAKE + (1 << 19), state_out=FAKE + (1 << 19)), -1),   # in place
+        (dict(state_out=FAKE), -1),                   # overlaps x
+    ]
+    for kw, code in cases:
+        with pytest.raises(E) as e:
+            call(**kw)
+        assert _code(e) == code, (kw, str(e.value))
+
+
 def test_zero_work_is_a_noop(dm):
     # T = 0 (short audio) and n_tokens = 0 need no pointers and no GPU
     dm.dmel_embed(None, 0, FAKE, 6144, None, None, FAKE, 0, 6144)
     dm.dmel_rms_scale(None, 0, None, 6144, 1e-6, None)
     dm.dmel_gather_rows(None, 0, 16, None, 0, FAKE, 16)
+    dm.dmel_shortconv(None, 0, 64, None, 3, None, None, None, None, 0)
 
 
 def test_missing_library_fails_loudly(tmp_path):
