@@ -339,6 +339,70 @@ def forward(x: np.ndarray, table_bits: np.ndarray, rms_weight=None, eps: float =
 
 
 # ---------------------------------------------------------------------------
+# Backward (training the front end jointly with the model: "Inside Inkling:
+# Audio Design", Coda, the front ends are frozen in post-training and training
+# them is experimental; the survey's next row).  The pages give no backward;
+# it is the derivative of the forward above.
+#
+# RMSNorm: y = s * r * w with r = 1 / sqrt(mean(s^2) + eps), so for an
+# upstream gradient dy
+#     ds = r * (w * dy) - (r^3 / D) * (sum_c w_c dy_c s_c) * s
+#     dw = sum_t dy_t * s_t * r_t
+# (evaluated in fp64 from the fp32 sum s).
+#
+# Embedding bag: dE[row] = sum of ds_t over the (t, j) with row r_tj = row.
+# Reading of the summation order (the pages give none; a fixed order makes the
+# result reproducible and checkable bit for bit): tokens are taken in
+# segments of SEGMENT consecutive tokens; within a segment each row sums its
+# tokens' gradients in increasing token order in fp32 starting from +0; the
+# result is then (start + partial_0) + partial_1 + ... in segment order in
+# fp32, where start is +0 or, when accumulating, the existing gradient.
+# ---------------------------------------------------------------------------
+SEGMENT = 65536
+
+
+def rms_backward(lv: np.ndarray, table_bits: np.ndarray, weight, dy, eps: float = RMS_EPS,
+                 n_levels: int = N_LEVELS):
+    """(ds fp64 [n, d], dw fp64 [d], s fp32 [n, d], r fp64 [n]) for levels lv and upstream dy."""
+    s = embed_sum(lv, table_bits, n_levels)
+    ds, dw, r = rms_backward_from_sum(s, weight, dy, eps)
+    return ds, dw, s, r
+
+
+def rms_backward_from_sum(s, weight, dy, eps: float = RMS_EPS):
+    """(ds, dw, r) of y = s * w / sqrt(mean(s^2) + eps) for rows s, in fp64."""
+    s64 = np.asarray(s, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    g = np.asarray(dy, dtype=np.float64)
+    d = s64.shape[1]
+    r = 1.0 / np.sqrt(np.mean(s64 * s64, axis=1) + eps)
+    dot = np.sum(w[None, :] * g * s64, axis=1)
+    ds = r[:, None] * (w[None, :] * g) - (r ** 3 / d)[:, None] * dot[:, None] * s64
+    dw = np.sum(g * s64 * r[:, None], axis=0)
+    return ds, dw, r
+
+
+def embed_backward(lv: np.ndarray, dsum, n_levels: int = N_LEVELS, dtable=None, segment: int = SEGMENT):
+    """fp32 [n_bins * n_levels, d] gradient of the table in the fixed order above.
+
+    dsum: [n, d] gradient with respect to the fp32 sum (fp32 values, or bf16
+    values given as fp32).  dtable: existing gradient to accumulate into."""
+    g = np.asarray(dsum, dtype=np.float32)
+    rows = table_rows(np.minimum(np.asarray(lv), n_levels - 1), n_levels)
+    n, n_bins = rows.shape
+    d = g.shape[1]
+    total = np.zeros((n_bins * n_levels, d), dtype=np.float32) if dtable is None else \
+        np.array(dtable, dtype=np.float32, copy=True)
+    for s0 in range(0, n, segment):
+        part = np.zeros_like(total)
+        for t in range(s0, min(n, s0 + segment)):
+            # the token's rows are distinct (one per bin): one fp32 add each
+            part[rows[t]] = part[rows[t]] + g[t][None, :]
+        total = total + part
+    return total
+
+
+# ---------------------------------------------------------------------------
 # Serving-path placement ("Where audio touches the serving path": one audio
 # item is a sentinel expanded into f frame positions).  An interleaved
 # sequence is a list of segments in order; a text segment contributes one
