@@ -1,0 +1,500 @@
+// Backward of the bag-of-bins embedding and of its RMSNorm.
+//
+// The pages give no backward ("Inside Inkling: Audio Design", Coda: the
+// front ends are frozen in post-training, training them is experimental); it
+// is the derivative of the forward in embed.hip:
+//   y = s * r * w,  r = 1 / sqrt(mean(s^2) + eps)   (r from dmel_rms_scale)
+//   ds = r * (w * dy) - (r^3 / D) * (sum_c w_c dy_c s_c) * s
+//   dw = sum_t dy_t * s_t * r_t
+//   dE[row] = sum of ds_t over the (t, j) whose selected row r_tj is row.
+//
+// Table gradient order (fixed, so that the result is reproducible and equal
+// bit for bit to the sequential definition): tokens in segments of 65536;
+// inside a segment every row sums its tokens' gradients in increasing token
+// order in fp32 from +0; the segment partials are then added in order to +0
+// (or to the existing gradient when accumulating).
+//
+// Kernels:
+//  * bucket_kernel - for each chunk of 64 tokens and each bin, a stable
+//    counting sort of the chunk's tokens by level (one wave per (chunk, bin),
+//    lane = token, a ballot per level): the LDS byte addresses of the tokens'
+//    gradient rows, grouped by level, and the 17 group starts (32-bit words,
+//    so that the scatter reads them with scalar loads).
+//  * scatter_kernel - a workgroup owns one segment, 16 bins (one wave each)
+//    and 256 columns (4 per lane); per chunk it stages the 64 x 256 gradient
+//    tile in LDS, then each wave walks its bin's level groups in token order
+//    and adds the tile rows into 16 x 4 accumulators in registers (one
+//    ds_read_b128 and four v_add_f32 per token); the group lists are uniform,
+//    so they come through scalar loads.  Workgroups that share a tile (the
+//    bin groups of one segment and strip) are placed on the same XCD.
+//  * combine_kernel - the segment partials, in order.
+//  * rms_dot_kernel / rms_ds_kernel - the RMSNorm backward: the forward sum
+//    is recomputed exactly as embed_kernel computes it (embed_core.h); the
+//    first pass forms sum_c w_c dy_c s_c per token and per-workgroup partial
+//    sums of dy * s * r per column, the second pass writes ds.
+#include "embed_core.h"
+
+namespace dmel {
+namespace {
+
+constexpr int kChunk = 64;                   // tokens per staged tile
+constexpr int kSegChunks = kBwdSegment / kChunk;
+constexpr int kBwdCols = 256;                // columns per workgroup (4 per lane)
+constexpr int kBwdBins = 16;                 // bins per workgroup (one per wave)
+constexpr int kBwdThreads = 64 * kBwdBins;   // 1024
+constexpr int kOffPitch = 17;                // group starts per (chunk, bin): 16 levels + end
+
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+bucket_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels, int64_t n_pairs,
+              uint32_t* __restrict__ lists, uint32_t* __restrict__ starts) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (pair >= n_pairs) return;  // whole wave; no barriers in this kernel
+  const int64_t chunk = pair / n_bins;
+  const int j = static_cast<int>(pair - chunk * n_bins);
+  const int64_t t = chunk * kChunk + lane;
+  uint32_t L = 0xFFu;  // no group
+  if (t < n_tokens) {
+    L = levels[t * n_bins + j];
+    L = L < static_cast<uint32_t>(n_levels - 1) ? L : static_cast<uint32_t>(n_levels - 1);
+  }
+  uint32_t* lst = lists + pair * kChunk;
+  uint32_t* st = starts + pair * kOffPitch;
+  uint32_t base = 0;
+  for (int l = 0; l < n_levels; ++l) {
+    const uint64_t m = __ballot(L == static_cast<uint32_t>(l));
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    if (L == static_cast<uint32_t>(l)) lst[base + rank] = static_cast<uint32_t>(lane * kBwdCols * 4);
+    if (lane == 0) st[l] = base;
+    base += static_cast<uint32_t>(__popcll(m));
+  }
+  if (lane == 0) {
+    for (int l = n_levels; l <= 16; ++l) st[l] = base;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <bool kBf16>
+__device__ __forceinline__ void tile_load(float4 (&r)[4], const void* g, int64_t n_tokens, int d_model, int64_t t0,
+                                          int c_strip, int tid) {
+  // 64 rows x 256 columns; item i = row * 64 + (4-column group)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + k * kBwdThreads;
+    const int row = i >> 6, cg = i & 63;
+    const int64_t t = t0 + row;
+    const int c = c_strip + 4 * cg;
+    r[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (t < n_tokens && c < d_model) {
+      if (kBf16) {
+        const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g) + t * d_model + c);
+        r[k] = make_float4(bf16_to_f32(q.x & 0xFFFFu), bf16_to_f32(q.x >> 16), bf16_to_f32(q.y & 0xFFFFu),
+                           bf16_to_f32(q.y >> 16));
+      } else {
+        r[k] = *reinterpret_cast<const float4*>(static_cast<const float*>(g) + t * d_model + c);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void tile_store(float4* tile, const float4 (&r)[4], int tid) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) tile[tid + k * kBwdThreads] = r[k];
+}
+
+__device__ __forceinline__ void add4(float4& a, const float4& v) {
+  a.x += v.x;
+  a.y += v.y;
+  a.z += v.z;
+  a.w += v.w;
+}
+
+// Adds the tokens of one level group (list entries k .. e-1, token order).
+__device__ __forceinline__ void add_group(float4& acc, const char* tile_lane, const uint32_t* __restrict__ lst, int k,
+                                          int e) {
+  for (; k + 4 <= e; k += 4) {
+    const float4 v0 = *reinterpret_cast<const float4*>(tile_lane + lst[k]);
+    const float4 v1 = *reinterpret_cast<const float4*>(tile_lane + lst[k + 1]);
+    const float4 v2 = *reinterpret_cast<const float4*>(tile_lane + lst[k + 2]);
+    const float4 v3 = *reinterpret_cast<const float4*>(tile_lane + lst[k + 3]);
+    add4(acc, v0);
+    add4(acc, v1);
+    add4(acc, v2);
+    add4(acc, v3);
+  }
+  for (; k < e; ++k) add4(acc, *reinterpret_cast<const float4*>(tile_lane + lst[k]));
+}
+
+// Workgroup (segment, bin group, strip); see the file comment.  Writes the
+// segment's partial sums to part (or, with a single segment, the final
+// gradient to out: out = (accumulate ? out : 0) + partial).
+template <bool kBf16>
+__global__ void __launch_bounds__(kBwdThreads)
+scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_levels, int d_model,
+               const uint32_t* __restrict__ lists, const uint32_t* __restrict__ starts, int64_t n_chunks,
+               int n_groups, int n_strips, int64_t n_outer, float* __restrict__ part, float* __restrict__ out,
+               int single, int accumulate) {
+  __shared__ float4 tile[kChunk * kBwdCols / 4];  // 64 KB
+  // blockIdx -> (outer = segment * n_strips + strip, bin group); the bin
+  // groups of one outer index are 8 apart, so they land on the same XCD
+  const int64_t bid = blockIdx.x;
+  const int grp = static_cast<int>((bid >> 3) % n_groups);
+  const int64_t outer = ((bid >> 3) / n_groups) * 8 + (bid & 7);
+  if (outer >= n_outer) return;  // before any barrier: the whole workgroup leaves
+  const int strip = static_cast<int>(outer % n_strips);
+  const int64_t seg = outer / n_strips;
+
+  const int tid = threadIdx.x;
+  // the wave index, made explicitly uniform so that the group lists come
+  // through scalar loads
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int j = grp * kBwdBins + wave;
+  const bool bin_ok = j < n_bins;
+  const int c_strip = strip * kBwdCols;
+  const int c0 = c_strip + 4 * lane;
+  const int64_t ch0 = seg * kSegChunks;
+  const int64_t ch1 = min(ch0 + kSegChunks, n_chunks);
+
+  float4 acc[16];
+#pragma unroll
+  for (int l = 0; l < 16; ++l) acc[l] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+
+  float4 r[4];
+  tile_load<kBf16>(r, g, n_tokens, d_model, ch0 * kChunk, c_strip, tid);
+  const char* tile_lane = reinterpret_cast<const char*>(tile) + lane * 16;
+  for (int64_t ch = ch0; ch < ch1; ++ch) {
+    tile_store(tile, r, tid);
+    __syncthreads();
+    if (ch + 1 < ch1) tile_load<kBf16>(r, g, n_tokens, d_model, (ch + 1) * kChunk, c_strip, tid);
+    if (bin_ok) {
+      const int64_t pair = ch * n_bins + j;
+      const uint32_t* lst = lists + pair * kChunk;
+      const uint32_t* st = starts + pair * kOffPitch;
+#pragma unroll
+      for (int l = 0; l < 16; ++l) {
+        if (l < n_levels) add_group(acc[l], tile_lane, lst, static_cast<int>(st[l]), static_cast<int>(st[l + 1]));
+      }
+    }
+    __syncthreads();  // the tile is overwritten next
+  }
+
+  if (!bin_ok || c0 >= d_model) return;
+#pragma unroll
+  for (int l = 0; l < 16; ++l) {
+    if (l < n_levels) {
+      const int64_t row = static_cast<int64_t>(j) * n_levels + l;
+      if (single) {
+        float4* o = reinterpret_cast<float4*>(out + row * d_model + c0);
+        float4 v = accumulate ? *o : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        add4(v, acc[l]);
+        *o = v;
+      } else {
+        const int64_t rows = static_cast<int64_t>(n_bins) * n_levels;
+        *reinterpret_cast<float4*>(part + (seg * rows + row) * d_model + c0) = acc[l];
+      }
+    }
+  }
+}
+
+// Zero fill (kept out of hipMemsetAsync so that a caller may capture the
+// calls in a graph).
+__global__ void __launch_bounds__(256) zero_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0.0f;
+}
+
+hipError_t zero_fill(float* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+// out[i] = (accumulate ? out[i] : 0) + part[0][i] + part[1][i] + ... in order.
+__global__ void __launch_bounds__(256)
+combine_kernel(const float* __restrict__ part, int64_t n_seg, int64_t n4, float* __restrict__ out, int accumulate) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    float4 v = accumulate ? reinterpret_cast<const float4*>(out)[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int64_t s = 0; s < n_seg; ++s) add4(v, reinterpret_cast<const float4*>(part)[s * n4 + i]);
+    reinterpret_cast<float4*>(out)[i] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm backward.  Workgroups as embed_kernel: 1024 tokens (one per lane)
+// and a group of 16-column strips.
+// ---------------------------------------------------------------------------
+template <bool kDyBf16>
+__device__ __forceinline__ void load_dy(float (&gr)[kStrip], const void* dy, int64_t t, int d_model, int col0,
+                                        bool active) {
+  if (!active) {
+#pragma unroll
+    for (int c = 0; c < kStrip; ++c) gr[c] = 0.0f;
+    return;
+  }
+  if (kDyBf16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(dy) + t * d_model + col0);
+    const uint4 a = p[0], b = p[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      gr[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+      gr[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(dy) + t * d_model + col0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = p[q];
+      gr[4 * q] = v.x;
+      gr[4 * q + 1] = v.y;
+      gr[4 * q + 2] = v.z;
+      gr[4 * q + 3] = v.w;
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Pass 1: per token, sum_c w_c dy_c s_c over the workgroup's strips (dot_part
+// [n_tokens, n_groups]); per column, sum over the workgroup's tokens of
+// dy * s * r (dw_part [token blocks, d_model]).
+template <bool kAny, bool kDyBf16>
+__global__ void __launch_bounds__(kEmbThreads)
+rms_dot_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels,
+               const uint16_t* __restrict__ table, int d_model, const float* __restrict__ rms_weight,
+               const float* __restrict__ rms_scale, const void* __restrict__ dy, float* __restrict__ dot_part,
+               float* __restrict__ dw_part, int n_groups, int n_strips, int strips_per_group) {
+  __shared__ float4 tab4[kRows * kPitch / 4];
+  __shared__ float red[kEmbThreads / 64][kStrip];
+  float* tab = reinterpret_cast<float*>(tab4);
+  const int tid = threadIdx.x;
+  const int grp = static_cast<int>(blockIdx.x % static_cast<unsigned>(n_groups));
+  const int64_t tb = blockIdx.x / static_cast<unsigned>(n_groups);
+  const int64_t t = tb * kEmbThreads + tid;
+  const bool active = t < n_tokens;
+  const int s_first = grp * strips_per_group;
+  const int s_end = min(n_strips, s_first + strips_per_group);
+  uint32_t offs[40];
+  token_offsets<kAny>(offs, levels, t, active, n_bins, n_levels);
+  const float r = active ? rms_scale[t] : 0.0f;
+  float dot = 0.0f;
+  sum_strips<kAny>(tab, table, d_model, s_first, s_end, tid, n_bins, n_levels, offs,
+                   [&](int col0, float (&acc)[kStrip]) {
+                     float gr[kStrip];
+                     load_dy<kDyBf16>(gr, dy, t, d_model, col0, active);
+                     float q[kStrip];
+#pragma unroll
+                     for (int c = 0; c < kStrip; ++c) {
+                       dot = fmaf(rms_weight[col0 + c] * gr[c], acc[c], dot);
+                       q[c] = (gr[c] * acc[c]) * r;
+                     }
+#pragma unroll
+                     for (int c = 0; c < kStrip; ++c) q[c] = wave_sum(q[c]);
+                     if ((tid & 63) == 0) {
+#pragma unroll
+                       for (int c = 0; c < kStrip; ++c) red[tid >> 6][c] = q[c];
+                     }
+                     __syncthreads();
+                     if (tid < kStrip) {
+                       float v = 0.0f;
+#pragma unroll
+                       for (int w = 0; w < kEmbThreads / 64; ++w) v += red[w][tid];
+                       dw_part[tb * d_model + col0 + tid] = v;
+                     }
+                   });
+  if (active) dot_part[t * n_groups + grp] = dot;
+}
+
+// Pass 2: ds = r (w dy) - (r^3 / D) dot s, written fp32.
+template <bool kAny, bool kDyBf16>
+__global__ void __launch_bounds__(kEmbThreads)
+rms_ds_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels,
+              const uint16_t* __restrict__ table, int d_model, const float* __restrict__ rms_weight,
+              const float* __restrict__ rms_scale, const void* __restrict__ dy, const float* __restrict__ dot_part,
+              float* __restrict__ ds, int n_groups, int n_strips, int strips_per_group) {
+  __shared__ float4 tab4[kRows * kPitch / 4];
+  float* tab = reinterpret_cast<float*>(tab4);
+  const int tid = threadIdx.x;
+  const int grp = static_cast<int>(blockIdx.x % static_cast<unsigned>(n_groups));
+  const int64_t tb = blockIdx.x / static_cast<unsigned>(n_groups);
+  const int64_t t = tb * kEmbThreads + tid;
+  const bool active = t < n_tokens;
+  const int s_first = grp * strips_per_group;
+  const int s_end = min(n_strips, s_first + strips_per_group);
+  uint32_t offs[40];
+  token_offsets<kAny>(offs, levels, t, active, n_bins, n_levels);
+  float r = 0.0f, coef = 0.0f;
+  if (active) {
+    r = rms_scale[t];
+    float dot = 0.0f;
+    for (int g = 0; g < n_groups; ++g) dot += dot_part[t * n_groups + g];
+    coef = ((r * r) * r) / static_cast<float>(d_model) * dot;
+  }
+  sum_strips<kAny>(tab, table, d_model, s_first, s_end, tid, n_bins, n_levels, offs,
+                   [&](int col0, float (&acc)[kStrip]) {
+                     if (!active) return;
+                     float gr[kStrip];
+                     load_dy<kDyBf16>(gr, dy, t, d_model, col0, true);
+                     float o[kStrip];
+#pragma unroll
+                     for (int c = 0; c < kStrip; ++c) o[c] = fmaf(-coef, acc[c], r * (rms_weight[col0 + c] * gr[c]));
+                     float4* p = reinterpret_cast<float4*>(ds + t * d_model + col0);
+                     p[0] = make_float4(o[0], o[1], o[2], o[3]);
+                     p[1] = make_float4(o[4], o[5], o[6], o[7]);
+                     p[2] = make_float4(o[8], o[9], o[10], o[11]);
+                     p[3] = make_float4(o[12], o[13], o[14], o[15]);
+                   });
+}
+
+// dw[c] = (accumulate ? dw[c] : 0) + sum over token blocks, in order.
+__global__ void __launch_bounds__(256)
+dw_reduce_kernel(const float* __restrict__ dw_part, int64_t n_blocks, int d_model, float* __restrict__ dw,
+                 int accumulate) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= d_model) return;
+  float v = 0.0f;
+  for (int64_t b = 0; b < n_blocks; ++b) v += dw_part[b * d_model + c];
+  dw[c] = accumulate ? dw[c] + v : v;
+}
+
+// strips per workgroup for the recompute passes (as launch_embed chooses)
+int strips_per_group(int64_t tblocks, int n_strips) {
+  static const int kCounts[] = {16, 8, 4, 3, 2, 1};
+  int64_t cost[6];
+  int64_t min_cost = -1;
+  for (int i = 0; i < 6; ++i) {
+    const int g = kCounts[i];
+    const int64_t wgs = tblocks * ((n_strips + g - 1) / g);
+    cost[i] = ((wgs + 255) / 256) * g;
+    if (min_cost < 0 || cost[i] < min_cost) min_cost = cost[i];
+  }
+  for (int i = 0; i < 6; ++i)
+    if (cost[i] * 100 <= min_cost * 105) return kCounts[i];
+  return 1;
+}
+
+}  // namespace
+
+size_t bwd_layout(int64_t n_tokens, int n_bins, int n_levels, int d_model, size_t* off_starts, size_t* off_part) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const size_t n_chunks = static_cast<size_t>((n_tokens + kChunk - 1) / kChunk);
+  const size_t pairs = n_chunks * static_cast<size_t>(n_bins);
+  const size_t n_seg = (n_chunks + kSegChunks - 1) / kSegChunks;
+  const size_t b_lists = up(pairs * kChunk * sizeof(uint32_t));
+  const size_t b_starts = up(pairs * kOffPitch * sizeof(uint32_t));
+  const size_t b_part = n_seg > 1 ? up(n_seg * static_cast<size_t>(n_bins) * n_levels * d_model * sizeof(float)) : 0;
+  if (off_starts) *off_starts = b_lists;
+  if (off_part) *off_part = b_lists + b_starts;
+  return b_lists + b_starts + b_part;
+}
+
+hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels, const void* dsum,
+                                 bool dsum_bf16, int d_model, float* dtable, bool accumulate, void* workspace,
+                                 hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(n_bins) * n_levels;
+  if (n_tokens <= 0) {
+    if (accumulate) return hipSuccess;
+    return zero_fill(dtable, rows * d_model, stream);
+  }
+  size_t off_starts = 0, off_part = 0;
+  bwd_layout(n_tokens, n_bins, n_levels, d_model, &off_starts, &off_part);
+  auto* lists = static_cast<uint32_t*>(workspace);
+  auto* starts = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + off_starts);
+  auto* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_part);
+  const int64_t n_chunks = (n_tokens + kChunk - 1) / kChunk;
+  const int64_t n_pairs = n_chunks * n_bins;
+  const int64_t n_seg = (n_chunks + kSegChunks - 1) / kSegChunks;
+  const int64_t bblocks = (n_pairs + 3) / 4;
+  if (bblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bucket_kernel, dim3(static_cast<unsigned>(bblocks)), dim3(256), 0, stream, levels, n_tokens,
+                     n_bins, n_levels, n_pairs, lists, starts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_groups = (n_bins + kBwdBins - 1) / kBwdBins;
+  const int n_strips = (d_model + kBwdCols - 1) / kBwdCols;
+  const int64_t n_outer = n_seg * n_strips;
+  const int64_t blocks = ((n_outer + 7) / 8) * 8 * n_groups;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int single = n_seg == 1;
+  if (dsum_bf16) {
+    hipLaunchKernelGGL(scatter_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kBwdThreads), 0, stream, dsum,
+                       n_tokens, n_bins, n_levels, d_model, lists, starts, n_chunks, n_groups, n_strips, n_outer,
+                       part, dtable, single, accumulate ? 1 : 0);
+  } else {
+    hipLaunchKernelGGL(scatter_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kBwdThreads), 0, stream,
+                       dsum, n_tokens, n_bins, n_levels, d_model, lists, starts, n_chunks, n_groups, n_strips,
+                       n_outer, part, dtable, single, accumulate ? 1 : 0);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess || single) return e;
+  const int64_t n4 = rows * d_model / 4;
+  int64_t cblocks = (n4 + 255) / 256;
+  if (cblocks > 65536) cblocks = 65536;
+  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(cblocks)), dim3(256), 0, stream, part, n_seg, n4,
+                     dtable, accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+size_t rms_bwd_layout(int64_t n_tokens, int d_model, size_t* off_dw) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const int n_strips = d_model / kStrip;
+  const int64_t tblocks = (n_tokens + kEmbThreads - 1) / kEmbThreads;
+  const int g = strips_per_group(tblocks, n_strips);
+  const int n_groups = (n_strips + g - 1) / g;
+  const size_t b_dot = up(static_cast<size_t>(n_tokens) * n_groups * sizeof(float));
+  const size_t b_dw = up(static_cast<size_t>(tblocks) * d_model * sizeof(float));
+  if (off_dw) *off_dw = b_dot;
+  return b_dot + b_dw;
+}
+
+hipError_t launch_rms_backward(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
+                               const uint16_t* table, int d_model, const float* rms_weight, const float* rms_scale,
+                               const void* dy, bool dy_bf16, float* ds, float* dweight, bool accumulate_dweight,
+                               void* workspace, hipStream_t stream) {
+  if (n_tokens <= 0) {
+    if (dweight == nullptr || accumulate_dweight) return hipSuccess;
+    return zero_fill(dweight, d_model, stream);
+  }
+  size_t off_dw = 0;
+  rms_bwd_layout(n_tokens, d_model, &off_dw);
+  auto* dot_part = static_cast<float*>(workspace);
+  auto* dw_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_dw);
+  const int n_strips = d_model / kStrip;
+  const int64_t tblocks = (n_tokens + kEmbThreads - 1) / kEmbThreads;
+  const int g = strips_per_group(tblocks, n_strips);
+  const int n_groups = (n_strips + g - 1) / g;
+  const int64_t blocks = tblocks * n_groups;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const bool any = !(n_bins == kMels && n_levels == kLevels);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kEmbThreads);
+#define DMEL_RMS_PASS(KERNEL, ...)                                                                           \
+  do {                                                                                                       \
+    if (any && dy_bf16) hipLaunchKernelGGL((KERNEL<true, true>), grid, block, 0, stream, __VA_ARGS__);       \
+    else if (any) hipLaunchKernelGGL((KERNEL<true, false>), grid, block, 0, stream, __VA_ARGS__);            \
+    else if (dy_bf16) hipLaunchKernelGGL((KERNEL<false, true>), grid, block, 0, stream, __VA_ARGS__);        \
+    else hipLaunchKernelGGL((KERNEL<false, false>), grid, block, 0, stream, __VA_ARGS__);                    \
+  } while (0)
+  DMEL_RMS_PASS(rms_dot_kernel, levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, dy,
+                dot_part, dw_part, n_groups, n_strips, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  DMEL_RMS_PASS(rms_ds_kernel, levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, dy,
+                dot_part, ds, n_groups, n_strips, g);
+#undef DMEL_RMS_PASS
+  e = hipGetLastError();
+  if (e != hipSuccess || dweight == nullptr) return e;
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((d_model + 255) / 256), dim3(256), 0, stream, dw_part, tblocks, d_model,
+                     dweight, accumulate_dweight ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace dmel

@@ -444,4 +444,85 @@ int dmel_shortconv(const uint16_t* x, int64_t n_tokens, int32_t channels, const 
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "shortconv launch");
 }
 
+size_t dmel_embed_backward_workspace_bytes(int64_t n_tokens, int32_t n_bins, int32_t n_levels, int32_t d_model) {
+  if (n_tokens < 0 || n_bins < 1 || n_bins > dmel::kEmbMaxBins || n_levels < 1 || n_levels > dmel::kEmbMaxLevels ||
+      d_model < 16)
+    return 0;
+  return dmel::bwd_layout(n_tokens, n_bins, n_levels, d_model, nullptr, nullptr);
+}
+
+int dmel_embed_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels, const void* dsum,
+                        int32_t dsum_dtype, int32_t d_model, float* dtable, int32_t accumulate, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (n_tokens < 0) return fail(DMEL_EINVAL, "n_tokens is negative");
+  int rc = check_layout(n_bins, n_levels);
+  if (rc != DMEL_OK) return rc;
+  if (d_model < 16 || d_model > 65536 || d_model % 16 != 0)
+    return fail(DMEL_ESHAPE, "d_model must be a multiple of 16 in [16, 65536] (got %d)", d_model);
+  if (dsum_dtype != DMEL_BF16 && dsum_dtype != DMEL_F32) return fail(DMEL_EDTYPE, "unsupported dsum_dtype %d", dsum_dtype);
+  if (dtable == nullptr) return fail(DMEL_EINVAL, "dtable is NULL");
+  if (!aligned(dtable, 16)) return fail(DMEL_EALIGN, "dtable is not 16-byte aligned");
+  const size_t need = dmel_embed_backward_workspace_bytes(n_tokens, n_bins, n_levels, d_model);
+  if (workspace_bytes < need)
+    return fail(DMEL_ENOMEM, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  if (n_tokens > 0) {
+    if (levels == nullptr || dsum == nullptr || workspace == nullptr)
+      return fail(DMEL_EINVAL, "levels / dsum / workspace is NULL");
+    if (!aligned(dsum, 16)) return fail(DMEL_EALIGN, "dsum is not 16-byte aligned");
+    if (!aligned(workspace, 256)) return fail(DMEL_EALIGN, "workspace is not 256-byte aligned");
+    const size_t T = static_cast<size_t>(n_tokens), D = static_cast<size_t>(d_model);
+    const size_t b_tab = static_cast<size_t>(n_bins) * n_levels * D * 4;
+    const size_t b_ds = T * D * (dsum_dtype == DMEL_F32 ? 4 : 2);
+    if (overlaps(dtable, b_tab, dsum, b_ds) || overlaps(dtable, b_tab, levels, T * n_bins) ||
+        overlaps(dtable, b_tab, workspace, need) || overlaps(workspace, need, dsum, b_ds) ||
+        overlaps(workspace, need, levels, T * n_bins))
+      return fail(DMEL_EINVAL, "dtable / workspace overlap another argument");
+  }
+  hipError_t e = dmel::launch_embed_backward(levels, n_tokens, n_bins, n_levels, dsum, dsum_dtype == DMEL_BF16, d_model,
+                                             dtable, accumulate != 0, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "embed backward launch");
+}
+
+size_t dmel_rms_backward_workspace_bytes(int64_t n_tokens, int32_t d_model) {
+  if (n_tokens < 0 || d_model < 16 || d_model % 16 != 0) return 0;
+  return dmel::rms_bwd_layout(n_tokens, d_model, nullptr);
+}
+
+int dmel_rms_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels, const uint16_t* table,
+                      int32_t d_model, const float* rms_weight, const float* rms_scale, const void* dy, int32_t dy_dtype,
+                      float* dsum, float* dweight, int32_t accumulate_dweight, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (n_tokens < 0) return fail(DMEL_EINVAL, "n_tokens is negative");
+  int rc = check_layout(n_bins, n_levels);
+  if (rc != DMEL_OK) return rc;
+  rc = check_table(table, d_model);
+  if (rc != DMEL_OK) return rc;
+  if (dy_dtype != DMEL_BF16 && dy_dtype != DMEL_F32) return fail(DMEL_EDTYPE, "unsupported dy_dtype %d", dy_dtype);
+  if (rms_weight == nullptr) return fail(DMEL_EINVAL, "rms_weight is NULL");
+  if (!aligned(rms_weight, 4)) return fail(DMEL_EALIGN, "rms_weight is not 4-byte aligned");
+  if (dweight != nullptr && !aligned(dweight, 4)) return fail(DMEL_EALIGN, "dweight is not 4-byte aligned");
+  const size_t need = dmel_rms_backward_workspace_bytes(n_tokens, d_model);
+  if (workspace_bytes < need)
+    return fail(DMEL_ENOMEM, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  if (n_tokens > 0) {
+    if (levels == nullptr || rms_scale == nullptr || dy == nullptr || dsum == nullptr || workspace == nullptr)
+      return fail(DMEL_EINVAL, "levels / rms_scale / dy / dsum / workspace is NULL");
+    if (released_layout(n_bins, n_levels) && !aligned(levels, 16))
+      return fail(DMEL_EALIGN, "levels is not 16-byte aligned");
+    if (!aligned(dy, 16) || !aligned(dsum, 16) || !aligned(rms_scale, 4))
+      return fail(DMEL_EALIGN, "dy / dsum must be 16-byte aligned, rms_scale 4-byte aligned");
+    if (!aligned(workspace, 256)) return fail(DMEL_EALIGN, "workspace is not 256-byte aligned");
+    const size_t T = static_cast<size_t>(n_tokens), D = static_cast<size_t>(d_model);
+    const size_t b_ds = T * D * 4, b_dy = T * D * (dy_dtype == DMEL_F32 ? 4 : 2);
+    if (overlaps(dsum, b_ds, dy, b_dy) || overlaps(dsum, b_ds, workspace, need) || overlaps(dsum, b_ds, levels, T * n_bins) ||
+        overlaps(dsum, b_ds, rms_scale, T * 4) || overlaps(dsum, b_ds, dweight, D * 4) ||
+        overlaps(workspace, need, dy, b_dy) || overlaps(dweight, D * 4, workspace, need))
+      return fail(DMEL_EINVAL, "dsum / dweight / workspace overlap another argument");
+  }
+  hipError_t e = dmel::launch_rms_backward(levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, dy,
+                                           dy_dtype == DMEL_BF16, dsum, dweight, accumulate_dweight != 0, workspace,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "rms backward launch");
+}
+
 }  // extern "C"

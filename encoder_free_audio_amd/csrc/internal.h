@@ -102,6 +102,20 @@ hipError_t launch_shortconv(const uint16_t* x, int64_t n_tokens, int channels, c
                             const float* weight, const uint16_t* state_in, uint16_t* state_out, void* y,
                             bool y_f32, hipStream_t stream);
 
+// Backward of the embedding (table gradient in a fixed order: token order
+// within segments of kBwdSegment tokens, then the segment partials in order)
+// and of its RMSNorm.
+constexpr int64_t kBwdSegment = 65536;
+size_t bwd_layout(int64_t n_tokens, int n_bins, int n_levels, int d_model, size_t* off_starts, size_t* off_part);
+hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels, const void* dsum,
+                                 bool dsum_bf16, int d_model, float* dtable, bool accumulate, void* workspace,
+                                 hipStream_t stream);
+size_t rms_bwd_layout(int64_t n_tokens, int d_model, size_t* off_dw);
+hipError_t launch_rms_backward(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
+                               const uint16_t* table, int d_model, const float* rms_weight, const float* rms_scale,
+                               const void* dy, bool dy_bf16, float* ds, float* dweight, bool accumulate_dweight,
+                               void* workspace, hipStream_t stream);
+
 hipError_t launch_gather_rows(const uint16_t* table, int64_t n_table_rows, int d_model,
                               const int32_t* ids, int64_t n, uint16_t* out, int64_t out_row_stride,
                               const int64_t* out_rows, hipStream_t stream);

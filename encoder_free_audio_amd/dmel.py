@@ -28,7 +28,8 @@ _STATUS = {0: "DMEL_OK", -1: "DMEL_EINVAL", -2: "DMEL_ESHAPE", -3: "DMEL_EDTYPE"
 EXPORTS = ("dmel_get_params", "dmel_num_frames", "dmel_last_error", "dmel_default_config", "dmel_create",
            "dmel_create_config", "dmel_get_config", "dmel_destroy", "dmel_frames", "dmel_levels", "dmel_rms_gram",
            "dmel_rms_scale", "dmel_embed", "dmel_forward_workspace_bytes", "dmel_forward", "dmel_gather_rows",
-           "dmel_shortconv")
+           "dmel_shortconv", "dmel_embed_backward_workspace_bytes", "dmel_embed_backward",
+           "dmel_rms_backward_workspace_bytes", "dmel_rms_backward")
 
 
 class DmelError(RuntimeError):
@@ -91,6 +92,11 @@ def lib() -> ctypes.CDLL:
                                             _P, _I32, _I64, _P, _P, _SZ, _P]),
             "dmel_gather_rows": (ctypes.c_int, [_P, _I64, _I32, _P, _I64, _P, _I64, _P, _P]),
             "dmel_shortconv": (ctypes.c_int, [_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _I32, _P]),
+            "dmel_embed_backward_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32]),
+            "dmel_embed_backward": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _I32, _P, _I32, _P, _SZ, _P]),
+            "dmel_rms_backward_workspace_bytes": (_SZ, [_I64, _I32]),
+            "dmel_rms_backward": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _P, _P, _I32, _P,
+                                                 _SZ, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(h, name)
@@ -237,6 +243,31 @@ def dmel_shortconv(x, n_tokens, channels, seq_off, n_seqs, weight, state_in, sta
     _check("dmel_shortconv", lib().dmel_shortconv(_ptr(x), int(n_tokens), int(channels), _ptr(seq_off), int(n_seqs),
                                                   _ptr(weight), _ptr(state_in), _ptr(state_out), _ptr(y),
                                                   int(y_dtype), _stream(stream)))
+
+
+def dmel_embed_backward_workspace_bytes(n_tokens, n_bins, n_levels, d_model) -> int:
+    return int(lib().dmel_embed_backward_workspace_bytes(int(n_tokens), int(n_bins), int(n_levels), int(d_model)))
+
+
+def dmel_embed_backward(levels, n_tokens, n_bins, n_levels, dsum, dsum_dtype, d_model, dtable, accumulate, workspace,
+                        workspace_bytes, stream=None) -> None:
+    _check("dmel_embed_backward", lib().dmel_embed_backward(_ptr(levels), int(n_tokens), int(n_bins), int(n_levels),
+                                                            _ptr(dsum), int(dsum_dtype), int(d_model), _ptr(dtable),
+                                                            int(accumulate), _ptr(workspace), int(workspace_bytes),
+                                                            _stream(stream)))
+
+
+def dmel_rms_backward_workspace_bytes(n_tokens, d_model) -> int:
+    return int(lib().dmel_rms_backward_workspace_bytes(int(n_tokens), int(d_model)))
+
+
+def dmel_rms_backward(levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, dy, dy_dtype, dsum,
+                      dweight, accumulate_dweight, workspace, workspace_bytes, stream=None) -> None:
+    _check("dmel_rms_backward", lib().dmel_rms_backward(_ptr(levels), int(n_tokens), int(n_bins), int(n_levels),
+                                                        _ptr(table), int(d_model), _ptr(rms_weight), _ptr(rms_scale),
+                                                        _ptr(dy), int(dy_dtype), _ptr(dsum), _ptr(dweight),
+                                                        int(accumulate_dweight), _ptr(workspace),
+                                                        int(workspace_bytes), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -271,6 +271,58 @@ int dmel_shortconv(const uint16_t* x, int64_t n_tokens, int32_t channels, const 
                    int32_t n_seqs, const float* weight, const uint16_t* state_in, uint16_t* state_out,
                    void* y, int32_t y_dtype, void* stream);
 
+/* Backward of the front end's trainable parts, for training it jointly with
+ * the model (the pages give no backward; "Inside Inkling: Audio Design",
+ * Coda, says the front ends are frozen in post-training and training them is
+ * experimental).  It is the derivative of dmel_embed:
+ *   with RMSNorm, y = s * r * w, r = 1 / sqrt(mean(s^2) + eps):
+ *     ds = r * (w * dy) - (r^3 / D) * (sum_c w_c dy_c s_c) * s
+ *     dw = sum_t dy_t * s_t * r_t
+ *   without it, ds = dy;
+ *   the table gradient: dtable[row] = sum of ds_t over the (t, bin) whose
+ *   selected row is row. */
+
+/* Bytes of workspace dmel_embed_backward needs (0 for invalid sizes). */
+size_t dmel_embed_backward_workspace_bytes(int64_t n_tokens, int32_t n_bins, int32_t n_levels, int32_t d_model);
+
+/* Table gradient of the bag-of-bins embedding.
+ *  levels     uint8 [n_tokens, n_bins]; values >= n_levels read as n_levels - 1
+ *  dsum       dsum_dtype (DMEL_F32, or DMEL_BF16 for an upstream bf16
+ *             gradient without RMSNorm) [n_tokens, d_model], 16-byte aligned:
+ *             the gradient with respect to each token's fp32 sum
+ *  dtable     fp32 [n_bins * n_levels, d_model] out (row n_levels * bin + level),
+ *             16-byte aligned; overwritten, or added to when accumulate != 0
+ *  workspace  device memory, 256-byte aligned, >= the size above
+ * Summation order (fixed, so results repeat bit for bit): tokens are taken in
+ * segments of 65536 consecutive tokens; inside a segment each row sums its
+ * tokens' gradients in increasing token order in fp32 starting from +0; the
+ * segment partials are then added in segment order in fp32 to +0 (or to the
+ * existing dtable when accumulating).  d_model % 16 == 0; n_bins <= 80,
+ * n_levels <= 16.  dtable and workspace must not overlap other arguments. */
+int dmel_embed_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels,
+                        const void* dsum, int32_t dsum_dtype, int32_t d_model, float* dtable,
+                        int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace dmel_rms_backward needs (0 for invalid sizes). */
+size_t dmel_rms_backward_workspace_bytes(int64_t n_tokens, int32_t d_model);
+
+/* Backward of the RMSNorm of dmel_embed: the gradient with respect to each
+ * token's fp32 sum and to the RMSNorm weight.  The sums are recomputed from
+ * the levels and the table exactly as dmel_embed computes them.
+ *  levels, table, rms_weight, rms_scale   as given to dmel_embed (rms_scale from
+ *             dmel_rms_scale)
+ *  dy         dy_dtype [n_tokens, d_model], 16-byte aligned: upstream gradient
+ *  dsum       fp32 [n_tokens, d_model] out, 16-byte aligned
+ *  dweight    fp32 [d_model] out or NULL; overwritten, or added to when
+ *             accumulate_dweight != 0
+ *  workspace  device memory, 256-byte aligned, >= the size above
+ * fp32 arithmetic in a fixed order (results repeat bit for bit). */
+int dmel_rms_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels,
+                      const uint16_t* table, int32_t d_model, const float* rms_weight,
+                      const float* rms_scale, const void* dy, int32_t dy_dtype, float* dsum,
+                      float* dweight, int32_t accumulate_dweight, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,253 @@
+"""GPU parity of the backward (table gradient of the bag-of-bins embedding and
+the RMSNorm backward) through the C ABI against the oracle.
+
+Bars:
+* table gradient: bit-exact against the oracle's fixed-order definition
+  (fp32, token order inside segments of 65536 tokens, segments in order),
+  for fp32 and bf16 token gradients, every layout, accumulate on and off;
+  repeated runs give identical bits.
+* RMSNorm backward, fp32 arithmetic against the oracle's fp64:
+  |ds - ds_exact| <= 1e-5 * (|r w dy| + (r^3 / D) * sum_c |w_c dy_c s_c| * |s|)
+  + 1e-30 per element: the two terms of ds, each a few fp32 roundings away
+  from exact, where the dot product sum_c w_c dy_c s_c is an fp32 sum over D
+  columns whose rounding error is bounded by a multiple of the sum of its
+  terms' magnitudes (not of the sum itself, which may cancel).  The sums s are
+  recomputed bit-identically to the forward, so r is the forward's.  dw per
+  column within 1e-5 * sum_t |dy s r|.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dmel_oracle as o
+from encoder_free_audio_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from encoder_free_audio_amd import dmel
+    return dmel
+
+
+def gpu_embed_backward(dm, lv, g, n_levels, dtable_in=None, bf16=False):
+    n, n_bins = lv.shape
+    d = g.shape[1]
+    lvd = torch.from_numpy(np.ascontiguousarray(lv)).cuda()
+    if bf16:
+        gd = torch.from_numpy(np.ascontiguousarray(g).view(np.int16)).cuda()
+    else:
+        gd = torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).cuda()
+    rows = n_bins * n_levels
+    dt = torch.full((rows, d), float("nan"), dtype=torch.float32, device="cuda") if dtable_in is None else \
+        torch.from_numpy(np.ascontiguousarray(dtable_in, dtype=np.float32)).cuda()
+    wsb = dm.dmel_embed_backward_workspace_bytes(n, n_bins, n_levels, d)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    dm.dmel_embed_backward(lvd, n, n_bins, n_levels, gd, dm.DMEL_BF16 if bf16 else dm.DMEL_F32, d, dt,
+                           0 if dtable_in is None else 1, ws, wsb)
+    torch.cuda.synchronize()
+    return dt.cpu().numpy()
+
+
+@pytest.mark.parametrize("n_bins,n_levels", [(80, 16), (40, 8), (3, 5), (64, 16), (17, 1)])
+@pytest.mark.parametrize("n,d", [(2 * 64 + 37, 272), (1, 16), (64, 6144)])
+def test_table_gradient_bit_exact(dm, n_bins, n_levels, n, d):
+    rng = np.random.default_rng(n_bins * 1000 + n_levels * 10 + n + d)
+    print(f"case: table gradient {n_bins}x{n_levels} n={n} d={d}", flush=True)
+    lv = rng.integers(0, n_levels + 3, (n, n_bins)).astype(np.uint8)   # some levels >= n_levels: clamped
+    g = rng.standard_normal((n, d)).astype(np.float32)
+    got = gpu_embed_backward(dm, lv, g, n_levels)
+    want = o.embed_backward(lv, g, n_levels)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # accumulate into an existing gradient
+    base = rng.standard_normal(want.shape).astype(np.float32)
+    got = gpu_embed_backward(dm, lv, g, n_levels, dtable_in=base)
+    want = o.embed_backward(lv, g, n_levels, dtable=base)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_table_gradient_bf16_input(dm):
+    rng = np.random.default_rng(7)
+    n, d = 700, 128
+    lv = rng.integers(0, 16, (n, 80)).astype(np.uint8)
+    bits = o.f32_to_bf16(rng.standard_normal((n, d)).astype(np.float32))
+    got = gpu_embed_backward(dm, lv, bits, 16, bf16=True)
+    want = o.embed_backward(lv, o.bf16_to_f32(bits), 16)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_table_gradient_empty_batch(dm):
+    d = 32
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    dt = torch.full((1280, d), 5.0, dtype=torch.float32, device="cuda")
+    dm.dmel_embed_backward(None, 0, 80, 16, None, dm.DMEL_F32, d, dt, 1, ws, 0)
+    torch.cuda.synchronize()
+    assert bool((dt == 5.0).all())
+    dm.dmel_embed_backward(None, 0, 80, 16, None, dm.DMEL_F32, d, dt, 0, ws, 0)
+    torch.cuda.synchronize()
+    assert bool((dt == 0.0).all())
+
+
+def test_segment_order_golden(dm, golden_dir):
+    # the hand-worked case across the 65536-token segment boundary: one row
+    with open(os.path.join(golden_dir, "embed_backward_order.json")) as f:
+        c = json.load(f)
+    n, d = o.SEGMENT + 2, 16
+    print(f"case: segment boundary n={n}", flush=True)
+    lv = np.zeros((n, 1), dtype=np.uint8)
+    g = np.zeros((n, d), dtype=np.float32)
+    g[o.SEGMENT - 2: o.SEGMENT + 2, 0] = np.array(c["terms"], dtype=np.float32)
+    got = gpu_embed_backward(dm, lv, g, 1)
+    assert got[0, 0] == c["segments_of_two"]          # 2 tokens each side of the boundary
+    assert np.array_equal(got, o.embed_backward(lv, g, 1))
+
+
+def test_multi_segment_and_determinism(dm):
+    rng = np.random.default_rng(8)
+    n, d = 2 * o.SEGMENT + 777, 32
+    print(f"case: three segments n={n}", flush=True)
+    lv = rng.integers(0, 16, (n, 80)).astype(np.uint8)
+    g = rng.standard_normal((n, d)).astype(np.float32)
+    got = gpu_embed_backward(dm, lv, g, 16)
+    again = gpu_embed_backward(dm, lv, g, 16)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+    want = o.embed_backward(lv, g, 16)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def _rms_case(dm, lv, n_levels, d, dy_bf16, seed, accumulate=False):
+    rng = np.random.default_rng(seed)
+    n, n_bins = lv.shape
+    table = synth.table_bf16(seed=seed, rows=n_bins * n_levels, d_model=d)
+    tb = table.numpy().view(np.uint16)
+    w = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    dy32 = rng.standard_normal((n, d)).astype(np.float32)
+    if dy_bf16:
+        dy_bits = o.f32_to_bf16(dy32)
+        dy = o.bf16_to_f32(dy_bits)
+        dyd = torch.from_numpy(dy_bits.view(np.int16)).cuda()
+    else:
+        dy = dy32
+        dyd = torch.from_numpy(dy32).cuda()
+    lay = dict(n_bins=n_bins, n_levels=n_levels)
+    lvd = torch.from_numpy(np.ascontiguousarray(lv)).cuda()
+    td = table.cuda()
+    wd = torch.from_numpy(w).cuda()
+    gram = torch.empty((1280, 1280), dtype=torch.float32, device="cuda")
+    dm.dmel_rms_gram(td, d, gram, **lay)
+    scale = torch.empty(n, dtype=torch.float32, device="cuda")
+    dm.dmel_rms_scale(lvd, n, gram, d, 1e-6, scale, **lay)
+    ds = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    dw0 = rng.standard_normal(d).astype(np.float32)
+    dw = torch.from_numpy(dw0.copy()).cuda()
+    wsb = dm.dmel_rms_backward_workspace_bytes(n, d)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    dm.dmel_rms_backward(lvd, n, n_bins, n_levels, td, d, wd, scale, dyd, dm.DMEL_BF16 if dy_bf16 else dm.DMEL_F32,
+                         ds, dw, 1 if accumulate else 0, ws, wsb)
+    torch.cuda.synchronize()
+    ds_want, dw_want, s, r = o.rms_backward(lv, tb, w, dy, n_levels=n_levels)
+    if accumulate:
+        dw_want = dw_want + dw0.astype(np.float64)
+    s64 = s.astype(np.float64)
+    dot_abs = np.sum(np.abs(w[None, :].astype(np.float64) * dy * s64), axis=1)
+    tol = 1e-5 * (np.abs(r[:, None] * w[None, :] * dy) + (r ** 3 / d * dot_abs)[:, None] * np.abs(s64)) + 1e-30
+    got = ds.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ds_want) <= tol), f"max excess {np.max(np.abs(got - ds_want) - tol)}"
+    dw_tol = 1e-5 * np.sum(np.abs(dy * s64 * r[:, None]), axis=0) + (np.abs(dw0) * 1e-7 if accumulate else 0)
+    assert np.all(np.abs(dw.cpu().numpy() - dw_want) <= dw_tol + 1e-30)
+    return ds
+
+
+@pytest.mark.parametrize("n_bins,n_levels", [(80, 16), (40, 8)])
+@pytest.mark.parametrize("dy_bf16", [False, True])
+def test_rms_backward(dm, n_bins, n_levels, dy_bf16):
+    rng = np.random.default_rng(11 + n_bins)
+    for n, d in ((2 * 1024 + 37, 256), (300, 6144)):
+        print(f"case: rms backward {n_bins}x{n_levels} dy_bf16={dy_bf16} n={n} d={d}", flush=True)
+        lv = rng.integers(0, n_levels, (n, n_bins)).astype(np.uint8)
+        _rms_case(dm, lv, n_levels, d, dy_bf16, seed=n + d, accumulate=(n == 300))
+
+
+def test_rms_then_table_gradient_chain(dm):
+    # the gradient flows through both calls; the table gradient of the GPU's
+    # ds equals the oracle's fixed-order sum of that ds bit for bit
+    rng = np.random.default_rng(12)
+    n, d = 1500, 128
+    lv = rng.integers(0, 16, (n, 80)).astype(np.uint8)
+    ds = _rms_case(dm, lv, 16, d, True, seed=99)
+    wsb = dm.dmel_embed_backward_workspace_bytes(n, 80, 16, d)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    dt = torch.empty((1280, d), dtype=torch.float32, device="cuda")
+    dm.dmel_embed_backward(torch.from_numpy(lv).cuda(), n, 80, 16, ds, dm.DMEL_F32, d, dt, 0, ws, wsb)
+    torch.cuda.synchronize()
+    want = o.embed_backward(lv, ds.cpu().numpy(), 16)
+    assert np.array_equal(dt.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_full_size_backward_sampled(dm):
+    # the 64 x 20 min batch (1,536,000 tokens, speech-like levels), bf16 dy:
+    # RMSNorm backward then the table gradient; sampled checks
+    n_clips, clip_len, d = 64, 19_200_000, 6144
+    print("case: backward on 64 x 20 min", flush=True)
+    audio = synth.speech_clips(seed=2, lengths=[clip_len] * n_clips, device="cuda")
+    ctx = dm.dmel_create(0)
+    so, fo, T = dm.clip_offsets([clip_len] * n_clips, "cuda")
+    lv = torch.empty((T, 80), dtype=torch.uint8, device="cuda")
+    dm.dmel_levels(ctx, audio, audio.numel(), so, fo, n_clips, T, None, lv)
+    del audio
+    table = synth.table_bf16(seed=1234).cuda()
+    w = torch.ones(d, dtype=torch.float32, device="cuda")
+    gram = torch.empty((1280, 1280), dtype=torch.float32, device="cuda")
+    dm.dmel_rms_gram(table, d, gram)
+    scale = torch.empty(T, dtype=torch.float32, device="cuda")
+    dm.dmel_rms_scale(lv, T, gram, d, 1e-6, scale)
+    dy = synth.activations_bf16(seed=21, n_tokens=T, channels=d, std=1e-3, device="cuda")
+    ds = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    dw = torch.empty(d, dtype=torch.float32, device="cuda")
+    wsb = dm.dmel_rms_backward_workspace_bytes(T, d)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    dm.dmel_rms_backward(lv, T, 80, 16, table, d, w, scale, dy, dm.DMEL_BF16, ds, dw, 0, ws, wsb)
+    del ws
+    wsb2 = dm.dmel_embed_backward_workspace_bytes(T, 80, 16, d)
+    ws2 = torch.empty(wsb2, dtype=torch.uint8, device="cuda")
+    dt = torch.empty((1280, d), dtype=torch.float32, device="cuda")
+    dm.dmel_embed_backward(lv, T, 80, 16, ds, dm.DMEL_F32, d, dt, 0, ws2, wsb2)
+    torch.cuda.synchronize()
+    dm.dmel_destroy(ctx)
+    assert bool(torch.isfinite(ds).all()) and bool(torch.isfinite(dt).all())
+    tb = table.cpu().numpy().view(np.uint16)
+    # sampled tokens: ds against the oracle
+    rng = np.random.default_rng(22)
+    picks = np.concatenate([rng.integers(0, T, 24), [0, T - 1]])
+    lvs = lv[torch.from_numpy(picks).cuda()].cpu().numpy()
+    dys = o.bf16_to_f32(dy[torch.from_numpy(picks).cuda()].cpu().numpy().view(np.uint16))
+    ds_want, _, s, r = o.rms_backward(lvs, tb, np.ones(d, np.float32), dys)
+    s64 = s.astype(np.float64)
+    dot_abs = np.sum(np.abs(dys * s64), axis=1)
+    tol = 1e-5 * (np.abs(r[:, None] * dys) + (r ** 3 / d * dot_abs)[:, None] * np.abs(s64)) + 1e-30
+    got = ds[torch.from_numpy(picks).cuda()].cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ds_want) <= tol)
+    # sampled rows and columns of the table gradient: the fixed-order sum of
+    # the GPU's ds over the tokens that selected the row
+    lv_np = lv.cpu().numpy()
+    cols = np.array([0, 1, 777, 6143])
+    for row in (16 * 0 + 15, 16 * 40 + 12, 16 * 79 + 9, 16 * 7 + 0):
+        j, l = divmod(row, 16)
+        toks = np.nonzero(np.minimum(lv_np[:, j], 15) == l)[0]
+        vals = ds[torch.from_numpy(toks).cuda()][:, torch.from_numpy(cols).cuda()].cpu().numpy() \
+            if toks.size else np.zeros((0, cols.size), np.float32)
+        total = np.zeros(cols.size, np.float32)
+        for s0 in range(0, T, o.SEGMENT):
+            seg = vals[(toks >= s0) & (toks < s0 + o.SEGMENT)]
+            part = np.cumsum(np.concatenate([np.zeros((1, cols.size), np.float32), seg]), axis=0,
+                             dtype=np.float32)[-1]
+            total = (total + part).astype(np.float32)
+        got = dt[row, torch.from_numpy(cols).cuda()].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), total.view(np.uint32)), (row, toks.size)
