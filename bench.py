@@ -61,13 +61,15 @@ def parse():
     ap.add_argument("--minutes", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=1200, help="oracle sample: frames per worker")
-    ap.add_argument("--workload", choices=("batch", "stream", "interleave", "copy", "shortconv", "shortconv_decode"),
+    ap.add_argument("--workload", choices=("batch", "stream", "interleave", "copy", "shortconv", "shortconv_decode",
+                                           "backward"),
                     default="batch",
                     help="batch: 64 x 20 min clips (default); stream: 4096 streams, one hop per step; "
                          "interleave: 256 x 32768 audio/text positions; copy: a plain 1 GiB device copy "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters); shortconv: the decoder's width-4 "
                          "short convolution over 64 requests x 24,000 tokens x 6144 channels (prefill); "
-                         "shortconv_decode: 4096 requests, one token per step, state carried")
+                         "shortconv_decode: 4096 requests, one token per step, state carried; backward: the "
+                         "RMSNorm and table-gradient backward of the 64 x 20 min batch")
     ap.add_argument("--streams", type=int, default=4096)
     ap.add_argument("--config", default=None,
                     help="batch workload with another front-end configuration, "
@@ -130,7 +132,7 @@ def main():
         sys.exit(1)
     if args.steps is None:
         args.steps = {"batch": 20, "stream": 1000, "interleave": 5, "copy": 5, "shortconv": 20,
-                      "shortconv_decode": 1000}[args.workload]
+                      "shortconv_decode": 1000, "backward": 5}[args.workload]
     if args.workload == "stream":
         return bench_stream(args)
     if args.workload == "interleave":
@@ -139,7 +141,116 @@ def main():
         return bench_copy(args)
     if args.workload in ("shortconv", "shortconv_decode"):
         return bench_shortconv(args)
+    if args.workload == "backward":
+        return bench_backward(args)
     return bench_batch(args)
+
+
+def bench_backward(args):
+    """Backward of the front end's trainable parts on the 64 x 20 min batch:
+    the RMSNorm backward (dmel_rms_backward: two passes that recompute the
+    forward sum) and the table gradient (dmel_embed_backward: level sort,
+    fixed-order scatter, segment combine), from a bf16 upstream gradient
+    ~ N(0, 1e-3).  One step = both calls; the levels come from the front end
+    before the timed region."""
+    dev = "cuda"
+    n_clips = args.clips
+    clip_len = int(round(args.minutes * 60 * 16000))
+    d = 6144
+    audio = synth.speech_clips(seed=2, lengths=[clip_len] * n_clips, device=dev)
+    ctx = dm.dmel_create(0)
+    so, fo, T = dm.clip_offsets([clip_len] * n_clips, dev)
+    lv = torch.empty((T, 80), dtype=torch.uint8, device=dev)
+    dm.dmel_levels(ctx, audio, audio.numel(), so, fo, n_clips, T, None, lv)
+    torch.cuda.synchronize()
+    del audio
+    table = synth.table_bf16(seed=1234).to(dev)
+    w = torch.ones(d, dtype=torch.float32, device=dev)
+    gram = torch.empty((1280, 1280), dtype=torch.float32, device=dev)
+    dm.dmel_rms_gram(table, d, gram)
+    scale = torch.empty(T, dtype=torch.float32, device=dev)
+    dm.dmel_rms_scale(lv, T, gram, d, 1e-6, scale)
+    dy = synth.activations_bf16(seed=21, n_tokens=T, channels=d, std=1e-3, device=dev)
+    ds = torch.empty((T, d), dtype=torch.float32, device=dev)
+    dw = torch.empty(d, dtype=torch.float32, device=dev)
+    dt = torch.empty((1280, d), dtype=torch.float32, device=dev)
+    wb1 = dm.dmel_rms_backward_workspace_bytes(T, d)
+    wb2 = dm.dmel_embed_backward_workspace_bytes(T, 80, 16, d)
+    ws = torch.empty(max(wb1, wb2), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dm.dmel_rms_backward(lv, T, 80, 16, table, d, w, scale, dy, dm.DMEL_BF16, ds, dw, 0, ws, wb1, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        dm.dmel_embed_backward(lv, T, 80, 16, ds, dm.DMEL_F32, d, dt, 0, ws, wb2, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(2)] for e in events])
+    k_rms, k_tab = per.mean(axis=0)
+    ms_step = wall * 1e3 / args.steps
+    # the table gradient adds every token's gradient into one row per bin:
+    # 80 x 6144 fp32 adds per token
+    adds = 80 * d * T
+    achieved = adds / (k_tab * 1e-3) / 1e12
+    print(f"[bench] backward per step: rms {k_rms:.3f} ms, table gradient {k_tab:.3f} ms; wall {ms_step:.3f} ms",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_backward(lv, table, dy, d)
+    dm.dmel_destroy(ctx)
+    line = {
+        "metric": "backward tokens/s (RMSNorm + table gradient of the dMel embedding)",
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"dMel backward: {n_clips} clips x {args.minutes:g} min ({T} tokens), table "
+                               f"1280x6144, bf16 upstream gradient, RMSNorm backward + fixed-order table gradient",
+                   "global_batch": n_clips, "seq_len": T // n_clips, "parallelism": "single GPU"},
+        "kernel_ms": {"rms_backward": float(k_rms), "table_gradient": float(k_tab)},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_ADD_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_ADD_TFLOPS, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_backward(lv, table, dy, d):
+    """The oracle's backward (fp64 RMSNorm backward, fixed-order fp32 table
+    gradient) on a bounded sample: the first 3000 tokens, one process."""
+    from oracle import dmel_oracle as o  # noqa: E402  (test infrastructure)
+
+    n = 3000
+    lvs = lv[:n].cpu().numpy()
+    tb = table.cpu().numpy().view(np.uint16)
+    dys = o.bf16_to_f32(dy[:n].cpu().numpy().view(np.uint16))
+    t0 = time.perf_counter()
+    ds, _, _, _ = o.rms_backward(lvs, tb, np.ones(d, np.float32), dys)
+    o.embed_backward(lvs, ds.astype(np.float32))
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} tokens of the batch, RMSNorm backward + table gradient, one process, "
+                      f"{dt:.1f} s wall"}
 
 
 def cpu_baseline_shortconv(x, w, st, S, L, decode):
