@@ -15,13 +15,14 @@
 // (or to the existing gradient when accumulating).
 //
 // Kernels:
-//  * bucket_kernel - for each chunk of 64 tokens and each bin, a stable
+//  * bucket_kernel - for each chunk of 128 tokens and each bin, a stable
 //    counting sort of the chunk's tokens by level (one wave per (chunk, bin),
-//    lane = token, a ballot per level): the LDS byte addresses of the tokens'
-//    gradient rows, grouped by level, and the 17 group starts (32-bit words,
-//    so that the scatter reads them with scalar loads).
+//    64 tokens per ballot): the LDS byte addresses of the tokens' gradient
+//    rows, grouped by level, each group padded to a multiple of four entries
+//    with the address of a row of -0.0, and the 17 group starts (32-bit
+//    words, so that the scatter reads them with scalar loads).
 //  * scatter_kernel - a workgroup owns one segment, 16 bins (one wave each)
-//    and 256 columns (4 per lane); per chunk it stages the 64 x 256 gradient
+//    and 256 columns (4 per lane); per chunk it stages the 128 x 256 gradient
 //    tile in LDS, then each wave walks its bin's level groups in token order
 //    and adds the tile rows into 16 x 4 accumulators in registers (one
 //    ds_read_b128 and four v_add_f32 per token); the group lists are uniform,
@@ -37,12 +38,19 @@
 namespace dmel {
 namespace {
 
-constexpr int kChunk = 64;                   // tokens per staged tile
+constexpr int kChunk = 128;                  // tokens per staged tile
+constexpr int kRounds = kChunk / 64;         // waves of 64 tokens per chunk in the level sort
 constexpr int kSegChunks = kBwdSegment / kChunk;
 constexpr int kBwdCols = 256;                // columns per workgroup (4 per lane)
 constexpr int kBwdBins = 16;                 // bins per workgroup (one per wave)
 constexpr int kBwdThreads = 64 * kBwdBins;   // 1024
+constexpr int kTileItems = kChunk * kBwdCols / 4 / kBwdThreads;  // float4 per thread per tile (8)
+constexpr int kListPitch = kChunk + 3 * 16;  // entries per (chunk, bin): groups padded to multiples of 4
 constexpr int kOffPitch = 17;                // group starts per (chunk, bin): 16 levels + end
+// LDS byte address of the tile row that holds -0.0 (after the kChunk token
+// rows): adding it is an exact no-op, so level groups are padded with it to
+// whole groups of four and the scatter needs no remainder loop.
+constexpr uint32_t kNegZeroRow = kChunk * kBwdCols * 4;
 
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
@@ -53,22 +61,33 @@ bucket_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, 
   if (pair >= n_pairs) return;  // whole wave; no barriers in this kernel
   const int64_t chunk = pair / n_bins;
   const int j = static_cast<int>(pair - chunk * n_bins);
-  const int64_t t = chunk * kChunk + lane;
-  uint32_t L = 0xFFu;  // no group
-  if (t < n_tokens) {
-    L = levels[t * n_bins + j];
-    L = L < static_cast<uint32_t>(n_levels - 1) ? L : static_cast<uint32_t>(n_levels - 1);
+  uint32_t L[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t t = chunk * kChunk + r * 64 + lane;
+    L[r] = 0xFFu;  // no group
+    if (t < n_tokens) {
+      const uint32_t v = levels[t * n_bins + j];
+      L[r] = v < static_cast<uint32_t>(n_levels - 1) ? v : static_cast<uint32_t>(n_levels - 1);
+    }
   }
-  uint32_t* lst = lists + pair * kChunk;
+  uint32_t* lst = lists + pair * kListPitch;
   uint32_t* st = starts + pair * kOffPitch;
   uint32_t base = 0;
   for (int l = 0; l < n_levels; ++l) {
-    const uint64_t m = __ballot(L == static_cast<uint32_t>(l));
-    const uint32_t rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-    if (L == static_cast<uint32_t>(l)) lst[base + rank] = static_cast<uint32_t>(lane * kBwdCols * 4);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const uint64_t m = __ballot(L[r] == static_cast<uint32_t>(l));
+      const uint32_t rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+      if (L[r] == static_cast<uint32_t>(l)) lst[base + cnt + rank] = static_cast<uint32_t>((r * 64 + lane) * kBwdCols * 4);
+      cnt += static_cast<uint32_t>(__popcll(m));
+    }
+    const uint32_t padded = (cnt + 3u) & ~3u;
+    if (static_cast<uint32_t>(lane) < padded - cnt) lst[base + cnt + lane] = kNegZeroRow;
     if (lane == 0) st[l] = base;
-    base += static_cast<uint32_t>(__popcll(m));
+    base += padded;
   }
   if (lane == 0) {
     for (int l = n_levels; l <= 16; ++l) st[l] = base;
@@ -77,11 +96,11 @@ bucket_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, 
 
 // ---------------------------------------------------------------------------
 template <bool kBf16>
-__device__ __forceinline__ void tile_load(float4 (&r)[4], const void* g, int64_t n_tokens, int d_model, int64_t t0,
-                                          int c_strip, int tid) {
-  // 64 rows x 256 columns; item i = row * 64 + (4-column group)
+__device__ __forceinline__ void tile_load(float4 (&r)[kTileItems], const void* g, int64_t n_tokens, int d_model,
+                                          int64_t t0, int c_strip, int tid) {
+  // kChunk rows x 256 columns; item i = row * 64 + (4-column group)
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kTileItems; ++k) {
     const int i = tid + k * kBwdThreads;
     const int row = i >> 6, cg = i & 63;
     const int64_t t = t0 + row;
@@ -99,9 +118,9 @@ __device__ __forceinline__ void tile_load(float4 (&r)[4], const void* g, int64_t
   }
 }
 
-__device__ __forceinline__ void tile_store(float4* tile, const float4 (&r)[4], int tid) {
+__device__ __forceinline__ void tile_store(float4* tile, const float4 (&r)[kTileItems], int tid) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) tile[tid + k * kBwdThreads] = r[k];
+  for (int k = 0; k < kTileItems; ++k) tile[tid + k * kBwdThreads] = r[k];
 }
 
 __device__ __forceinline__ void add4(float4& a, const float4& v) {
@@ -111,10 +130,11 @@ __device__ __forceinline__ void add4(float4& a, const float4& v) {
   a.w += v.w;
 }
 
-// Adds the tokens of one level group (list entries k .. e-1, token order).
+// Adds the tokens of one level group (list entries k .. e-1, token order; the
+// group is padded to a multiple of four with the -0.0 row).
 __device__ __forceinline__ void add_group(float4& acc, const char* tile_lane, const uint32_t* __restrict__ lst, int k,
                                           int e) {
-  for (; k + 4 <= e; k += 4) {
+  for (; k < e; k += 4) {
     const float4 v0 = *reinterpret_cast<const float4*>(tile_lane + lst[k]);
     const float4 v1 = *reinterpret_cast<const float4*>(tile_lane + lst[k + 1]);
     const float4 v2 = *reinterpret_cast<const float4*>(tile_lane + lst[k + 2]);
@@ -124,7 +144,6 @@ __device__ __forceinline__ void add_group(float4& acc, const char* tile_lane, co
     add4(acc, v2);
     add4(acc, v3);
   }
-  for (; k < e; ++k) add4(acc, *reinterpret_cast<const float4*>(tile_lane + lst[k]));
 }
 
 // Workgroup (segment, bin group, strip); see the file comment.  Writes the
@@ -136,7 +155,7 @@ scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_l
                const uint32_t* __restrict__ lists, const uint32_t* __restrict__ starts, int64_t n_chunks,
                int n_groups, int n_strips, int64_t n_outer, float* __restrict__ part, float* __restrict__ out,
                int single, int accumulate) {
-  __shared__ float4 tile[kChunk * kBwdCols / 4];  // 64 KB
+  __shared__ float4 tile[(kChunk + 1) * kBwdCols / 4];  // 128 KB of token rows + the -0.0 row
   // blockIdx -> (outer = segment * n_strips + strip, bin group); the bin
   // groups of one outer index are 8 apart, so they land on the same XCD
   const int64_t bid = blockIdx.x;
@@ -161,7 +180,8 @@ scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_l
 #pragma unroll
   for (int l = 0; l < 16; ++l) acc[l] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 
-  float4 r[4];
+  if (tid < kBwdCols / 4) tile[kChunk * kBwdCols / 4 + tid] = make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
+  float4 r[kTileItems];
   tile_load<kBf16>(r, g, n_tokens, d_model, ch0 * kChunk, c_strip, tid);
   const char* tile_lane = reinterpret_cast<const char*>(tile) + lane * 16;
   for (int64_t ch = ch0; ch < ch1; ++ch) {
@@ -170,7 +190,7 @@ scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_l
     if (ch + 1 < ch1) tile_load<kBf16>(r, g, n_tokens, d_model, (ch + 1) * kChunk, c_strip, tid);
     if (bin_ok) {
       const int64_t pair = ch * n_bins + j;
-      const uint32_t* lst = lists + pair * kChunk;
+      const uint32_t* lst = lists + pair * kListPitch;
       const uint32_t* st = starts + pair * kOffPitch;
 #pragma unroll
       for (int l = 0; l < 16; ++l) {
@@ -389,7 +409,7 @@ size_t bwd_layout(int64_t n_tokens, int n_bins, int n_levels, int d_model, size_
   const size_t n_chunks = static_cast<size_t>((n_tokens + kChunk - 1) / kChunk);
   const size_t pairs = n_chunks * static_cast<size_t>(n_bins);
   const size_t n_seg = (n_chunks + kSegChunks - 1) / kSegChunks;
-  const size_t b_lists = up(pairs * kChunk * sizeof(uint32_t));
+  const size_t b_lists = up(pairs * kListPitch * sizeof(uint32_t));
   const size_t b_starts = up(pairs * kOffPitch * sizeof(uint32_t));
   const size_t b_part = n_seg > 1 ? up(n_seg * static_cast<size_t>(n_bins) * n_levels * d_model * sizeof(float)) : 0;
   if (off_starts) *off_starts = b_lists;
