@@ -62,14 +62,15 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=1200, help="oracle sample: frames per worker")
     ap.add_argument("--workload", choices=("batch", "stream", "interleave", "copy", "shortconv", "shortconv_decode",
-                                           "backward"),
+                                           "backward", "hmlp"),
                     default="batch",
                     help="batch: 64 x 20 min clips (default); stream: 4096 streams, one hop per step; "
                          "interleave: 256 x 32768 audio/text positions; copy: a plain 1 GiB device copy "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters); shortconv: the decoder's width-4 "
                          "short convolution over 64 requests x 24,000 tokens x 6144 channels (prefill); "
                          "shortconv_decode: 4096 requests, one token per step, state carried; backward: the "
-                         "RMSNorm and table-gradient backward of the 64 x 20 min batch")
+                         "RMSNorm and table-gradient backward of the 64 x 20 min batch; hmlp: the four-stage "
+                         "image front end over 32 images of 1280 x 1280 (32768 patches of 40 x 40)")
     ap.add_argument("--streams", type=int, default=4096)
     ap.add_argument("--config", default=None,
                     help="batch workload with another front-end configuration, "
@@ -132,7 +133,7 @@ def main():
         sys.exit(1)
     if args.steps is None:
         args.steps = {"batch": 20, "stream": 1000, "interleave": 5, "copy": 5, "shortconv": 20,
-                      "shortconv_decode": 1000, "backward": 5}[args.workload]
+                      "shortconv_decode": 1000, "backward": 5, "hmlp": 10}[args.workload]
     if args.workload == "stream":
         return bench_stream(args)
     if args.workload == "interleave":
@@ -143,6 +144,8 @@ def main():
         return bench_shortconv(args)
     if args.workload == "backward":
         return bench_backward(args)
+    if args.workload == "hmlp":
+        return bench_hmlp(args)
     return bench_batch(args)
 
 
@@ -233,6 +236,107 @@ def bench_backward(args):
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+
+
+def bench_hmlp(args):
+    """hMLP image front end: 32 bf16 images of 1280 x 1280 (32768 patches),
+    widths 1536, 1536, 1536, 6144, bf16 out.  One step = dmel_hmlp_forward.
+    The stage-2 GEMM (the dominant launch: 302 MFLOP per patch) is also timed
+    alone through dmel_hmlp_stage for the roofline."""
+    dev = "cuda"
+    n, H, W, hidden, d = 32, 1280, 1280, 1536, 6144
+    P = n * (H // 40) * (W // 40)
+    images = synth.table_bf16(seed=5, rows=n * H * W, d_model=3, std=1.0, device=dev)
+    rng = np.random.default_rng(6)
+    shapes = [(hidden, 75), (hidden, 4 * hidden), (hidden, 4 * hidden), (d, 4 * hidden)]
+    ws = []
+    for nn_, k in shapes:
+        ws.append(synth.table_bf16(seed=int(rng.integers(1 << 30)), rows=nn_, d_model=k, std=1.0 / np.sqrt(k)).to(dev))
+        ws.append(torch.from_numpy((rng.standard_normal(nn_) * 0.1).astype(np.float32)).to(dev))
+    out = torch.empty((P, d), dtype=torch.int16, device=dev)
+    wsb = dm.dmel_hmlp_workspace_bytes(n, H, W, hidden)
+    wsp = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dm.dmel_hmlp_forward(images, n, H, W, *ws, hidden, d, out, dm.DMEL_BF16, wsp, wsb, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = wall * 1e3 / args.steps
+    ms_ev = e0.elapsed_time(e1) / args.steps
+    # stage 2 alone (same kernel, same shape as inside the forward)
+    x2 = torch.empty((P * 16, 4 * hidden), dtype=torch.int16, device=dev)
+    x2.view(torch.bfloat16).normal_()
+    y2 = torch.empty((P * 16, hidden), dtype=torch.int16, device=dev)
+    for _ in range(2):
+        dm.dmel_hmlp_stage(x2, P * 16, 4 * hidden, ws[2], ws[3], hidden, 1, y2, dm.DMEL_BF16, stream)
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(5):
+        dm.dmel_hmlp_stage(x2, P * 16, 4 * hidden, ws[2], ws[3], hidden, 1, y2, dm.DMEL_BF16, stream)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    k2 = f0.elapsed_time(f1) / 5
+    flops2 = 2.0 * P * 16 * (4 * hidden) * hidden
+    achieved = flops2 / (k2 * 1e-3) / 1e12
+    flops_all = 2.0 * P * (64 * 75 * hidden + 16 * 4 * hidden * hidden + 4 * 4 * hidden * hidden + 4 * hidden * d)
+    print(f"[bench] hmlp step {ms_ev:.3f} ms (events), wall {ms_step:.3f} ms; stage-2 GEMM {k2:.3f} ms "
+          f"= {achieved:.0f} TFLOP/s; whole stem {flops_all / (ms_ev * 1e-3) / 1e12:.0f} TFLOP/s",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_hmlp(images, ws, H, W)
+    line = {
+        "metric": "image patches/s (hMLP front end, 40 x 40 patches -> 6144-d)",
+        "value": P / (ms_step * 1e-3),
+        "unit": "patches/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"hMLP stem: {n} images x {H} x {W} ({P} patches), widths {hidden}/{hidden}/{hidden}/"
+                               f"{d}, bf16 matrix-core products, fp32 accumulation, bf16 out",
+                   "global_batch": n, "seq_len": P // n, "parallelism": "single GPU"},
+        "kernel_ms": {"forward": ms_ev, "stage2_gemm": k2},
+        "tflops_stem": flops_all / (ms_ev * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_hmlp(images, ws, H, W):
+    """The hMLP oracle (fp64) on a bounded sample: the first 8 patches of the
+    first image, one process."""
+    from oracle import hmlp_oracle as ho  # noqa: E402  (test infrastructure)
+
+    img = images[: H * W].view(1, H, W, 3)[:, :40, :320, :].contiguous().cpu().numpy().view(np.uint16)
+    wn = [(ws[2 * i].cpu().numpy().view(np.uint16), ws[2 * i + 1].cpu().numpy()) for i in range(4)]
+    t0 = time.perf_counter()
+    ho.hmlp(img, wn)
+    dt = time.perf_counter() - t0
+    return {"value": 8 / dt, "unit": "patches/s", "cores": 1, "kind": "oracle",
+            "sample": f"8 patches (a 40 x 320 strip of the first image), full widths, one process, {dt:.1f} s wall"}
 
 
 def cpu_baseline_backward(lv, table, dy, d):

@@ -525,4 +525,61 @@ int dmel_rms_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, i
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "rms backward launch");
 }
 
+size_t dmel_hmlp_workspace_bytes(int32_t n_images, int32_t height, int32_t width, int32_t hidden) {
+  if (n_images < 0 || height < 0 || width < 0 || height % 40 || width % 40 || hidden < 128 || hidden % 128) return 0;
+  const int64_t P = static_cast<int64_t>(n_images) * (height / 40) * (width / 40);
+  return dmel::hmlp_layout(P, hidden, nullptr);
+}
+
+int dmel_hmlp_stage(const uint16_t* x, int64_t n_rows, int32_t k, const uint16_t* weight, const float* bias, int32_t n,
+                    int32_t gelu, void* y, int32_t y_dtype, void* stream) {
+  if (n_rows < 0) return fail(DMEL_EINVAL, "n_rows is negative");
+  if (k < 32 || k % 32 != 0 || k > (1 << 20)) return fail(DMEL_ESHAPE, "k must be a positive multiple of 32 (got %d)", k);
+  if (n < 128 || n % 128 != 0 || n > (1 << 20)) return fail(DMEL_ESHAPE, "n must be a positive multiple of 128 (got %d)", n);
+  if (y_dtype != DMEL_BF16 && y_dtype != DMEL_F32) return fail(DMEL_EDTYPE, "unsupported y_dtype %d", y_dtype);
+  if (n_rows == 0) return DMEL_OK;
+  if (x == nullptr || weight == nullptr || bias == nullptr || y == nullptr) return fail(DMEL_EINVAL, "NULL argument");
+  if (!aligned(x, 16) || !aligned(weight, 16) || !aligned(bias, 4) || !aligned(y, 4))
+    return fail(DMEL_EALIGN, "x and weight must be 16-byte aligned, bias and y 4-byte aligned");
+  const size_t by = static_cast<size_t>(n_rows) * n * (y_dtype == DMEL_F32 ? 4 : 2);
+  if (overlaps(y, by, x, static_cast<size_t>(n_rows) * k * 2) || overlaps(y, by, weight, static_cast<size_t>(n) * k * 2) ||
+      overlaps(y, by, bias, static_cast<size_t>(n) * 4))
+    return fail(DMEL_EINVAL, "y overlaps another argument");
+  hipError_t e = dmel::launch_gemm_bf16(x, weight, bias, y, n_rows, n, k, gelu != 0, y_dtype == DMEL_F32,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "hmlp stage launch");
+}
+
+int dmel_hmlp_forward(const uint16_t* images, int32_t n_images, int32_t height, int32_t width, const uint16_t* w1,
+                      const float* b1, const uint16_t* w2, const float* b2, const uint16_t* w3, const float* b3,
+                      const uint16_t* w4, const float* b4, int32_t hidden, int32_t d_model, void* out, int32_t out_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_images < 0 || height < 0 || width < 0) return fail(DMEL_EINVAL, "negative size");
+  if (height % 40 || width % 40) return fail(DMEL_ESHAPE, "height and width must be multiples of 40 (got %d x %d)", height, width);
+  if (hidden < 128 || hidden % 128 || hidden > 16384) return fail(DMEL_ESHAPE, "hidden must be a multiple of 128 in [128, 16384]");
+  if (d_model < 128 || d_model % 128 || d_model > 65536) return fail(DMEL_ESHAPE, "d_model must be a multiple of 128 in [128, 65536]");
+  if (out_dtype != DMEL_BF16 && out_dtype != DMEL_F32) return fail(DMEL_EDTYPE, "unsupported out_dtype %d", out_dtype);
+  const int64_t P = static_cast<int64_t>(n_images) * (height / 40) * (width / 40);
+  if (P == 0) return DMEL_OK;
+  const uint16_t* w[4] = {w1, w2, w3, w4};
+  const float* b[4] = {b1, b2, b3, b4};
+  for (int i = 0; i < 4; ++i) {
+    if (w[i] == nullptr || b[i] == nullptr) return fail(DMEL_EINVAL, "stage %d weight or bias is NULL", i + 1);
+    if (!aligned(w[i], 16) || !aligned(b[i], 4)) return fail(DMEL_EALIGN, "stage %d weight must be 16-byte aligned", i + 1);
+  }
+  if (images == nullptr || out == nullptr || workspace == nullptr) return fail(DMEL_EINVAL, "images / out / workspace is NULL");
+  if (!aligned(images, 2) || !aligned(out, 4) || !aligned(workspace, 256))
+    return fail(DMEL_EALIGN, "images 2-byte, out 4-byte, workspace 256-byte aligned");
+  const size_t need = dmel::hmlp_layout(P, hidden, nullptr);
+  if (workspace_bytes < need)
+    return fail(DMEL_ENOMEM, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  const size_t bo = static_cast<size_t>(P) * d_model * (out_dtype == DMEL_F32 ? 4 : 2);
+  const size_t bi = static_cast<size_t>(n_images) * height * width * 3 * 2;
+  if (overlaps(out, bo, images, bi) || overlaps(out, bo, workspace, need) || overlaps(workspace, need, images, bi))
+    return fail(DMEL_EINVAL, "out / workspace overlap another argument");
+  hipError_t e = dmel::launch_hmlp(images, n_images, height, width, w, b, hidden, d_model, out, out_dtype == DMEL_F32,
+                                   workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "hmlp launch");
+}
+
 }  // extern "C"

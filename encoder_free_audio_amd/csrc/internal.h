@@ -116,6 +116,14 @@ hipError_t launch_rms_backward(const uint8_t* levels, int64_t n_tokens, int n_bi
                                const void* dy, bool dy_bf16, float* ds, float* dweight, bool accumulate_dweight,
                                void* workspace, hipStream_t stream);
 
+// hMLP image front end (four stages over 40 x 40 patches) and its stage GEMM.
+size_t hmlp_layout(int64_t n_patches, int hidden, size_t* off);
+hipError_t launch_hmlp(const uint16_t* images, int n_images, int height, int width, const uint16_t* const w[4],
+                       const float* const b[4], int hidden, int d_model, void* out, bool out_f32, void* workspace,
+                       hipStream_t stream);
+hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, const float* bias, void* C, int64_t M, int N, int K,
+                            bool gelu, bool out_f32, hipStream_t stream);
+
 hipError_t launch_gather_rows(const uint16_t* table, int64_t n_table_rows, int d_model,
                               const int32_t* ids, int64_t n, uint16_t* out, int64_t out_row_stride,
                               const int64_t* out_rows, hipStream_t stream);

@@ -29,7 +29,8 @@ EXPORTS = ("dmel_get_params", "dmel_num_frames", "dmel_last_error", "dmel_defaul
            "dmel_create_config", "dmel_get_config", "dmel_destroy", "dmel_frames", "dmel_levels", "dmel_rms_gram",
            "dmel_rms_scale", "dmel_embed", "dmel_forward_workspace_bytes", "dmel_forward", "dmel_gather_rows",
            "dmel_shortconv", "dmel_embed_backward_workspace_bytes", "dmel_embed_backward",
-           "dmel_rms_backward_workspace_bytes", "dmel_rms_backward")
+           "dmel_rms_backward_workspace_bytes", "dmel_rms_backward", "dmel_hmlp_workspace_bytes",
+           "dmel_hmlp_forward", "dmel_hmlp_stage")
 
 
 class DmelError(RuntimeError):
@@ -95,6 +96,10 @@ def lib() -> ctypes.CDLL:
             "dmel_embed_backward_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32]),
             "dmel_embed_backward": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _I32, _P, _I32, _P, _SZ, _P]),
             "dmel_rms_backward_workspace_bytes": (_SZ, [_I64, _I32]),
+            "dmel_hmlp_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+            "dmel_hmlp_forward": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P,
+                                                 _I32, _P, _SZ, _P]),
+            "dmel_hmlp_stage": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _I32, _I32, _P, _I32, _P]),
             "dmel_rms_backward": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _P, _P, _I32, _P,
                                                  _SZ, _P]),
         }
@@ -268,6 +273,23 @@ def dmel_rms_backward(levels, n_tokens, n_bins, n_levels, table, d_model, rms_we
                                                         _ptr(dy), int(dy_dtype), _ptr(dsum), _ptr(dweight),
                                                         int(accumulate_dweight), _ptr(workspace),
                                                         int(workspace_bytes), _stream(stream)))
+
+
+def dmel_hmlp_workspace_bytes(n_images, height, width, hidden) -> int:
+    return int(lib().dmel_hmlp_workspace_bytes(int(n_images), int(height), int(width), int(hidden)))
+
+
+def dmel_hmlp_forward(images, n_images, height, width, w1, b1, w2, b2, w3, b3, w4, b4, hidden, d_model, out, out_dtype,
+                      workspace, workspace_bytes, stream=None) -> None:
+    _check("dmel_hmlp_forward", lib().dmel_hmlp_forward(_ptr(images), int(n_images), int(height), int(width), _ptr(w1),
+                                                        _ptr(b1), _ptr(w2), _ptr(b2), _ptr(w3), _ptr(b3), _ptr(w4),
+                                                        _ptr(b4), int(hidden), int(d_model), _ptr(out), int(out_dtype),
+                                                        _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def dmel_hmlp_stage(x, n_rows, k, weight, bias, n, gelu, y, y_dtype, stream=None) -> None:
+    _check("dmel_hmlp_stage", lib().dmel_hmlp_stage(_ptr(x), int(n_rows), int(k), _ptr(weight), _ptr(bias), int(n),
+                                                    int(gelu), _ptr(y), int(y_dtype), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

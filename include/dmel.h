@@ -323,6 +323,47 @@ int dmel_rms_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, i
                       float* dweight, int32_t accumulate_dweight, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* hMLP image front end: one d_model-wide embedding per 40 x 40 pixel patch
+ * ("Inside Inkling: Audio Design", Part 1, "Why this is a reasonable bet": a
+ * 4-layer hMLP over 40x40 patches; "Why Thinking Machines Built Inkling
+ * Without a Vision Encoder": a four-stage hMLP stem per 40 x 40 tile).  The
+ * pages give no widths or merge pattern; read as: stage 1 maps each 5 x 5 x 3
+ * sub-patch, flattened (row, column, channel), to `hidden` channels; stages
+ * 2-4 map the 2 x 2 neighbouring outputs of the previous stage, concatenated
+ * in (row, column) order, to hidden, hidden and d_model channels; each stage
+ * adds its bias, stages 1-3 apply the exact GELU x * Phi(x), and the hidden
+ * activations are rounded to bf16 (nearest even).  Matrix-core bf16 products
+ * with fp32 accumulation. */
+
+/* Bytes of workspace dmel_hmlp_forward needs (0 for invalid sizes). */
+size_t dmel_hmlp_workspace_bytes(int32_t n_images, int32_t height, int32_t width, int32_t hidden);
+
+/* Patch embeddings of a batch of images.
+ *  images   bf16 [n_images, height, width, 3] (height-width-channel), sides
+ *           multiples of 40
+ *  w1, b1   bf16 [hidden, 75], fp32 [hidden]
+ *  w2, b2   bf16 [hidden, 4 * hidden], fp32 [hidden]
+ *  w3, b3   bf16 [hidden, 4 * hidden], fp32 [hidden]
+ *  w4, b4   bf16 [d_model, 4 * hidden], fp32 [d_model]; weights 16-byte aligned
+ *  out      out_dtype [n_images * height/40 * width/40, d_model]: patches
+ *           image by image, row-major over the patch grid
+ *  workspace  device memory, 256-byte aligned, >= dmel_hmlp_workspace_bytes
+ * hidden and d_model are multiples of 128.  Errors: DMEL_EINVAL, DMEL_ESHAPE,
+ * DMEL_EDTYPE, DMEL_EALIGN, DMEL_ENOMEM (workspace too small), DMEL_EHIP. */
+int dmel_hmlp_forward(const uint16_t* images, int32_t n_images, int32_t height, int32_t width,
+                      const uint16_t* w1, const float* b1, const uint16_t* w2, const float* b2,
+                      const uint16_t* w3, const float* b3, const uint16_t* w4, const float* b4,
+                      int32_t hidden, int32_t d_model, void* out, int32_t out_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* One hMLP stage on its own: y = x weight^T + bias, then GELU when gelu != 0.
+ *  x       bf16 [n_rows, k], 16-byte aligned (k % 32 == 0)
+ *  weight  bf16 [n, k], 16-byte aligned (n % 128 == 0); bias fp32 [n]
+ *  y       y_dtype [n_rows, n] (bf16 rounded to nearest even, or fp32) */
+int dmel_hmlp_stage(const uint16_t* x, int64_t n_rows, int32_t k, const uint16_t* weight,
+                    const float* bias, int32_t n, int32_t gelu, void* y, int32_t y_dtype,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif
