@@ -177,10 +177,193 @@ gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, cons
   }
 }
 
+// ---- large-tile GEMM -------------------------------------------------------
+// C[M, N] = A[M, K] B[N, K]^T + bias (then GELU) for N % 256 == 0 and
+// K % 64 == 0.  Workgroup tile 256 x 256, K step 64, four waves as 2 x 2, each
+// owning 4 x 4 MFMA tiles of 32 x 32 (256 fp32 accumulators per lane: one wave
+// per SIMD, accumulators in AGPRs).
+//  * Operands go from global memory straight into LDS (16-byte
+//    global_load_lds; no register staging), two stages of 64 KB, the next
+//    K step's loads in flight while the current one is multiplied.
+//  * LDS rows are 128 bytes (64 bf16 of K); the 16-byte chunk c of row r sits
+//    in slot c ^ (r & 7), so the fragment reads of 8 consecutive rows at one
+//    chunk hit 8 different slots (all 32 banks).  A lane of the DMA load writes
+//    slot (lane & 7) of row (lane >> 3) of its 8-row block, so it fetches
+//    logical chunk (lane & 7) ^ (lane >> 3).
+//  * Tile order: workgroup b runs on XCD b % 8.  Each XCD takes a contiguous
+//    range of tiles in row-panel-major order, so the ~32 workgroups resident on
+//    one XCD share A row panels (all N / 256 column tiles of a panel) and B
+//    column panels in that XCD's L2.
+//  * Rows past M load row M - 1 (in bounds) and are not written.
+constexpr int kBT = 256;                      // tile rows / columns
+constexpr int kBTK = 64;                      // K step
+constexpr int kRowBytes = kBTK * 2;           // 128-byte LDS rows
+constexpr int kTileBytes = kBT * kRowBytes;   // 32 KB per operand tile
+constexpr int kStageBytes = 2 * kTileBytes;   // A + B
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <bool kGelu, bool kOutF32>
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const float* __restrict__ bias,
+               void* __restrict__ C, int64_t M, int N, int K, int tiles_n, int64_t n_tiles) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int64_t b = blockIdx.x;
+  const int64_t q = n_tiles / 8, rem = n_tiles % 8;
+  const int64_t x = b % 8;
+  const int64_t tile = x * q + (x < rem ? x : rem) + b / 8;
+  const int64_t bm = tile / tiles_n;
+  const int bn = static_cast<int>(tile - bm * tiles_n);
+  const int64_t row0 = bm * kBT;
+  const int col0 = bn * kBT;
+
+  // this lane's DMA sources: rows wave * 64 + 8 j + (lane >> 3) of the A and B
+  // tiles, logical chunk (lane & 7) ^ (lane >> 3); byte offsets from the tiles'
+  // first rows (< 2^32: 256 rows of at most 2^21 bytes)
+  const int lr = lane >> 3, lc = (lane & 7) ^ lr;
+  uint32_t aoff[8], boff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = wave * 64 + 8 * j + lr;
+    const int64_t ra = row0 + r < M ? r : M - 1 - row0;
+    aoff[j] = static_cast<uint32_t>(ra * K * 2 + lc * 16);
+    boff[j] = static_cast<uint32_t>(static_cast<int64_t>(r) * K * 2 + lc * 16);
+  }
+  const char* Ab = reinterpret_cast<const char*>(A + row0 * K);
+  const char* Bb = reinterpret_cast<const char*>(B + static_cast<int64_t>(col0) * K);
+  auto issue = [&](int stage, int k0) {
+    char* sa = smem + stage * kStageBytes + wave * 64 * kRowBytes;
+    char* sb = sa + kTileBytes;
+    const char* ga = Ab + static_cast<int64_t>(k0) * 2;
+    const char* gb = Bb + static_cast<int64_t>(k0) * 2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_global_load_lds(ga + aoff[j], (lds_void_t*)(sa + j * 8 * kRowBytes), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_global_load_lds(gb + boff[j], (lds_void_t*)(sb + j * 8 * kRowBytes), 16, 0, 0);
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][c][i] = 0.0f;
+
+  const int nk = K / kBTK;
+  issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int s = kt & 1;
+    // this wave's loads of stage s have landed; the barrier makes every wave's
+    // visible and ends every wave's reads of stage s ^ 1 (from step kt - 1)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 1 < nk) issue(s ^ 1, (kt + 1) * kBTK);
+    const char* sa = smem + s * kStageBytes + (wm * 128 + (lane & 31)) * kRowBytes;
+    const char* sb = smem + s * kStageBytes + kTileBytes + (wn * 128 + (lane & 31)) * kRowBytes;
+    // fragments of sub-step kk + 1 are read while sub-step kk multiplies
+    bf16x8_t fa[2][4], fb[2][4];
+    auto frag = [&](int kk, int buf) {
+      const int off = ((2 * kk + (lane >> 5)) ^ (lane & 7)) << 4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) fa[buf][t] = *reinterpret_cast<const bf16x8_t*>(sa + t * 32 * kRowBytes + off);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) fb[buf][t] = *reinterpret_cast<const bf16x8_t*>(sb + t * 32 * kRowBytes + off);
+    };
+    frag(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < kBTK / 16; ++kk) {
+      if (kk + 1 < kBTK / 16) frag(kk + 1, (kk + 1) & 1);
+      // keep those reads here, ahead of this sub-step's products, so they
+      // return while the matrix core works through the sixteen products: an
+      // empty asm that clobbers memory (loads stay above it) and "modifies"
+      // this sub-step's fragments (the products stay below it)
+      const int cb = kk & 1;
+      asm volatile("" : "+v"(fa[cb][0]), "+v"(fa[cb][1]), "+v"(fa[cb][2]), "+v"(fa[cb][3]), "+v"(fb[cb][0]),
+                   "+v"(fb[cb][1]), "+v"(fb[cb][2]), "+v"(fb[cb][3])::"memory");
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][a], fb[kk & 1][c], acc[a][c], 0, 0, 0);
+    }
+  }
+
+  // Epilogue through LDS, a quarter of the wave's 128 x 128 block (32 rows) at
+  // a time: the accumulators go to a wave-private 32 x 128 fp32 area (row
+  // pitch 136 floats: the two row groups of one store land in different bank
+  // halves), then each lane reads 4 consecutive columns of a row back, so a
+  // half-wave writes one row's 128 outputs as one contiguous piece.  Lane
+  // layout of a 32 x 32 accumulator: column lane & 31, rows
+  // 8 (i / 4) + 4 (lane / 32) + i % 4.
+  constexpr int kEpPitch = 136;
+  __syncthreads();  // every wave is done with the operand stages
+  float* ep = reinterpret_cast<float*>(smem) + wave * 32 * kEpPitch;
+  const int cl = 4 * (lane & 31);
+  const int col = col0 + wn * 128 + cl;
+  const float4 bb = make_float4(bias[col], bias[col + 1], bias[col + 2], bias[col + 3]);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        ep[(8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * kEpPitch + c * 32 + (lane & 31)] = acc[a][c][i];
+#pragma unroll 4
+    for (int pr = 0; pr < 16; ++pr) {
+      const int r = 2 * pr + (lane >> 5);
+      const int64_t row = row0 + wm * 128 + a * 32 + r;
+      float4 v = *reinterpret_cast<const float4*>(ep + r * kEpPitch + cl);
+      v.x += bb.x;
+      v.y += bb.y;
+      v.z += bb.z;
+      v.w += bb.w;
+      if (kGelu) {
+        v.x = 0.5f * v.x * (1.0f + erff(v.x * 0.70710678118654752f));
+        v.y = 0.5f * v.y * (1.0f + erff(v.y * 0.70710678118654752f));
+        v.z = 0.5f * v.z * (1.0f + erff(v.z * 0.70710678118654752f));
+        v.w = 0.5f * v.w * (1.0f + erff(v.w * 0.70710678118654752f));
+      }
+      if (row < M) {
+        if (kOutF32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(C) + row * N + col) = v;
+        } else {
+          const uint2 h = make_uint2(static_cast<uint32_t>(to_bf16(v.x)) | static_cast<uint32_t>(to_bf16(v.y)) << 16,
+                                     static_cast<uint32_t>(to_bf16(v.z)) | static_cast<uint32_t>(to_bf16(v.w)) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + row * N + col) = h;
+        }
+      }
+    }
+  }
+}
+
 hipError_t gemm(const uint16_t* A, const uint16_t* B, const float* bias, void* C, int64_t M, int N, int K, bool gelu,
                 bool out_f32, hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  // (the large-tile kernel stores 16 or 8 bytes per lane: C 16-byte aligned)
+  if (N % kBT == 0 && K % kBTK == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0) {
+    const int tiles_n = N / kBT;
+    const int64_t n_tiles = ((M + kBT - 1) / kBT) * tiles_n;
+    if (n_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(n_tiles)), block(kGemmThreads);
+    if (gelu && !out_f32) {
+      hipLaunchKernelGGL((gemm256_kernel<true, false>), grid, block, 0, stream, A, B, bias, C, M, N, K, tiles_n, n_tiles);
+    } else if (gelu) {
+      hipLaunchKernelGGL((gemm256_kernel<true, true>), grid, block, 0, stream, A, B, bias, C, M, N, K, tiles_n, n_tiles);
+    } else if (!out_f32) {
+      hipLaunchKernelGGL((gemm256_kernel<false, false>), grid, block, 0, stream, A, B, bias, C, M, N, K, tiles_n, n_tiles);
+    } else {
+      hipLaunchKernelGGL((gemm256_kernel<false, true>), grid, block, 0, stream, A, B, bias, C, M, N, K, tiles_n, n_tiles);
+    }
+    return hipGetLastError();
+  }
   const int64_t blocks = ((M + kBM - 1) / kBM) * (N / kBN);
-  if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gemm_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kGemmThreads), 0, stream, A, B, bias, C, M,
                      N, K, gelu ? 1 : 0, out_f32 ? 1 : 0);

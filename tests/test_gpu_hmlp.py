@@ -123,7 +123,8 @@ def to_spatial(rows, n, H, W, level):
     return out.reshape(n, ph * side, pw * side, C)
 
 
-@pytest.mark.parametrize("M,K,N", [(300, 96, 128), (128 * 3 + 5, 6144, 256), (64, 512, 1536), (1, 32, 128)])
+@pytest.mark.parametrize("M,K,N", [(300, 96, 128), (128 * 3 + 5, 6144, 256), (64, 512, 1536), (1, 32, 128),
+                                   (1000, 192, 768), (257, 64, 512), (2048, 128, 1792)])
 @pytest.mark.parametrize("gelu", [0, 1])
 def test_stage_gemm(dm, M, K, N, gelu):
     print(f"case: stage GEMM M={M} K={K} N={N} gelu={gelu}", flush=True)
