@@ -40,6 +40,30 @@ __device__ __forceinline__ uint16_t to_bf16(float v) {
   return static_cast<uint16_t>(__builtin_bit_cast(uint32_t, __builtin_convertvector(x, hb16x2_t)) & 0xFFFFu);
 }
 
+// GELU(x) = x Phi(x) with Phi(x) = erfc(-x / sqrt(2)) / 2, branch free.  For
+// z >= 0, erfc(z) = t exp(P(t) - z^2) with t = 1 / (1 + z / 2): the form of
+// the Chebyshev erfc approximation in Press et al., Numerical Recipes, with a
+// degree-9 polynomial P fitted to ln(erfc(z) / t) + z^2 over t in (0, 1]
+// (largest fit error 8e-8).  This fp32 evaluation is within 3.8e-7 absolute
+// of the exact GELU over [-9, 9] (1.3e-6 relative for x >= -3), well inside
+// the accumulation tolerance of every stage.
+__device__ __forceinline__ float gelu(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+  float p = 1.767219591e-01f;
+  p = fmaf(p, t, -8.499431527e-01f);
+  p = fmaf(p, t, 1.544073511e+00f);
+  p = fmaf(p, t, -1.195862089e+00f);
+  p = fmaf(p, t, 3.181210659e-01f);
+  p = fmaf(p, t, -2.015549787e-01f);
+  p = fmaf(p, t, 1.002275065e-01f);
+  p = fmaf(p, t, 3.736856663e-01f);
+  p = fmaf(p, t, 1.000042885e+00f);
+  p = fmaf(p, t, -1.265512293e+00f);
+  const float ec = t * __builtin_amdgcn_exp2f(fmaf(-z, z, p) * 1.44269504088896341f);
+  return x * (x >= 0.0f ? fmaf(-0.5f, ec, 1.0f) : 0.5f * ec);
+}
+
 // Morton index m (0..63) of an 8 x 8 grid -> (y, x): bits y2 x2 y1 x1 y0 x0.
 __device__ __forceinline__ void demorton8(int m, int& y, int& x) {
   y = ((m >> 5) & 1) << 2 | ((m >> 3) & 1) << 1 | ((m >> 1) & 1);
@@ -166,7 +190,7 @@ gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, cons
         const int64_t row = row0 + wm * 64 + a * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
         if (row >= M) continue;
         float v = acc[a][b][i] + bb;
-        if (gelu) v = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+        if (gelu) v = dmel::gelu(v);
         if (out_f32) {
           static_cast<float*>(C)[row * N + col] = v;
         } else {
@@ -179,26 +203,34 @@ gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, cons
 
 // ---- large-tile GEMM -------------------------------------------------------
 // C[M, N] = A[M, K] B[N, K]^T + bias (then GELU) for N % 256 == 0 and
-// K % 64 == 0.  Workgroup tile 256 x 256, K step 64, four waves as 2 x 2, each
-// owning 4 x 4 MFMA tiles of 32 x 32 (256 fp32 accumulators per lane: one wave
-// per SIMD, accumulators in AGPRs).
+// K % 32 == 0.  Workgroup tile 256 x 256, four waves as 2 x 2, each owning
+// 4 x 4 MFMA tiles of 32 x 32 (256 fp32 accumulators per lane: one wave per
+// SIMD, accumulators in AGPRs).
 //  * Operands go from global memory straight into LDS (16-byte
-//    global_load_lds; no register staging), two stages of 64 KB, the next
-//    K step's loads in flight while the current one is multiplied.
-//  * LDS rows are 128 bytes (64 bf16 of K); the 16-byte chunk c of row r sits
-//    in slot c ^ (r & 7), so the fragment reads of 8 consecutive rows at one
-//    chunk hit 8 different slots (all 32 banks).  A lane of the DMA load writes
-//    slot (lane & 7) of row (lane >> 3) of its 8-row block, so it fetches
-//    logical chunk (lane & 7) ^ (lane >> 3).
+//    global_load_lds, no register staging) through a ring of four stages of
+//    K = 32 (32 KB each); the loads of step k + 3 are issued during step k (a
+//    fifth stage measured no faster).
+//  * LDS rows are 64 bytes (32 bf16 of K); the 16-byte chunk c of row r sits
+//    in slot c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3: the fragment reads of
+//    any 8 or 16 consecutive rows at one chunk then touch every bank at most
+//    once (rows of equal r % 2, and of equal r % 4, get distinct slots).  A
+//    lane of the DMA load writes slot lane & 3 of row lane >> 2 of its 16-row
+//    block, so it fetches logical chunk (lane & 3) ^ f(row).
+//  * One barrier per K step, between its two 16-deep sub-steps: it certifies
+//    the next step's stage (after this wave's wait for its loads) and frees
+//    the stage read in the previous step for the next loads.  The fragments of
+//    the sub-step after it were read before it, so the matrix core does not
+//    wait for the barrier's LDS reads.
 //  * Tile order: workgroup b runs on XCD b % 8.  Each XCD takes a contiguous
 //    range of tiles in row-panel-major order, so the ~32 workgroups resident on
 //    one XCD share A row panels (all N / 256 column tiles of a panel) and B
 //    column panels in that XCD's L2.
 //  * Rows past M load row M - 1 (in bounds) and are not written.
 constexpr int kBT = 256;                      // tile rows / columns
-constexpr int kBTK = 64;                      // K step
-constexpr int kRowBytes = kBTK * 2;           // 128-byte LDS rows
-constexpr int kTileBytes = kBT * kRowBytes;   // 32 KB per operand tile
+constexpr int kBTK = 32;                      // K step
+constexpr int kNStages = 4;
+constexpr int kRowBytes = kBTK * 2;           // 64-byte LDS rows
+constexpr int kTileBytes = kBT * kRowBytes;   // 16 KB per operand tile
 constexpr int kStageBytes = 2 * kTileBytes;   // A + B
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -207,7 +239,7 @@ template <bool kGelu, bool kOutF32>
 __global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const float* __restrict__ bias,
                void* __restrict__ C, int64_t M, int N, int K, int tiles_n, int64_t n_tiles) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kNStages * kStageBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -221,33 +253,63 @@ gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, c
   const int64_t row0 = bm * kBT;
   const int col0 = bn * kBT;
 
-  // this lane's DMA sources: rows wave * 64 + 8 j + (lane >> 3) of the A and B
-  // tiles, logical chunk (lane & 7) ^ (lane >> 3); byte offsets from the tiles'
+  // this lane's DMA sources: rows wave * 64 + 16 j + (lane >> 2) of the A and B
+  // tiles, logical chunk (lane & 3) ^ f(row); byte offsets from the tiles'
   // first rows (< 2^32: 256 rows of at most 2^21 bytes)
-  const int lr = lane >> 3, lc = (lane & 7) ^ lr;
-  uint32_t aoff[8], boff[8];
+  const int lr = lane >> 2;
+  uint32_t aoff[4], boff[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = wave * 64 + 8 * j + lr;
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave * 64 + 16 * j + lr;
+    const int lc = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
     const int64_t ra = row0 + r < M ? r : M - 1 - row0;
     aoff[j] = static_cast<uint32_t>(ra * K * 2 + lc * 16);
     boff[j] = static_cast<uint32_t>(static_cast<int64_t>(r) * K * 2 + lc * 16);
   }
   const char* Ab = reinterpret_cast<const char*>(A + row0 * K);
   const char* Bb = reinterpret_cast<const char*>(B + static_cast<int64_t>(col0) * K);
-  auto issue = [&](int stage, int k0) {
-    char* sa = smem + stage * kStageBytes + wave * 64 * kRowBytes;
+  auto issue = [&](int kt) {
+    char* sa = smem + (kt % kNStages) * kStageBytes + wave * 64 * kRowBytes;
     char* sb = sa + kTileBytes;
-    const char* ga = Ab + static_cast<int64_t>(k0) * 2;
-    const char* gb = Bb + static_cast<int64_t>(k0) * 2;
+    const char* ga = Ab + static_cast<int64_t>(kt) * (kBTK * 2);
+    const char* gb = Bb + static_cast<int64_t>(kt) * (kBTK * 2);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_global_load_lds(ga + aoff[j], (lds_void_t*)(sa + j * 8 * kRowBytes), 16, 0, 0);
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(ga + aoff[j], (lds_void_t*)(sa + j * 16 * kRowBytes), 16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_global_load_lds(gb + boff[j], (lds_void_t*)(sb + j * 8 * kRowBytes), 16, 0, 0);
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(gb + boff[j], (lds_void_t*)(sb + j * 16 * kRowBytes), 16, 0, 0);
+  };
+  // Wait until this wave's loads of the stage needed next have landed (loads
+  // complete in order; `later` more steps' loads may stay in flight), then
+  // meet the other waves.  One asm with a memory clobber, so no LDS access
+  // moves across it and no fence adds a wait for every load in flight.
+  auto sync_stage = [&](int later) {
+    if (later == 3) {
+      asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+    } else if (later == 2) {
+      asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+    } else if (later == 1) {
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
   };
 
+  // fragments of sub-step (k, h): rows (lane & 31) + 32 t of this wave's
+  // 128-row blocks, logical chunk 2 h + (lane >> 5)
+  const int frow = (lane & 31) * kRowBytes;
+  const int fsw = (((lane & 31) >> 1) ^ ((lane & 31) >> 3)) & 3;  // f(row): the block offsets are multiples of 32
+  bf16x8_t fa[2][4], fb[2][4];
+  auto frag = [&](int kt, int h, int buf) {
+    const char* sa = smem + (kt % kNStages) * kStageBytes + wm * 128 * kRowBytes + frow;
+    const char* sb = smem + (kt % kNStages) * kStageBytes + kTileBytes + wn * 128 * kRowBytes + frow;
+    const int off = ((2 * h + (lane >> 5)) ^ fsw) << 4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) fa[buf][t] = *reinterpret_cast<const bf16x8_t*>(sa + t * 32 * kRowBytes + off);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) fb[buf][t] = *reinterpret_cast<const bf16x8_t*>(sb + t * 32 * kRowBytes + off);
+  };
   f32x16_t acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -255,45 +317,67 @@ gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, c
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][c][i] = 0.0f;
+  // Issue order per sub-step: wait for this sub-step's fragments, issue the
+  // next sub-step's eight LDS reads, then the sixteen products, so the reads
+  // return while the matrix core works (and at most eight are in flight).
+  // pin(buf), an empty asm that "modifies" the fragments of buffer buf and
+  // clobbers memory, makes the wave wait for them there and keeps the next
+  // reads below it; scheduling barriers keep each group of products between
+  // the reads before it and the wait after it.
+  auto pin = [&](int buf) {
+    asm volatile("" : "+v"(fa[buf][0]), "+v"(fa[buf][1]), "+v"(fa[buf][2]), "+v"(fa[buf][3]), "+v"(fb[buf][0]),
+                 "+v"(fb[buf][1]), "+v"(fb[buf][2]), "+v"(fb[buf][3])::"memory");
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][a], fb[buf][c], acc[a][c], 0, 0, 0);
+  };
 
+  // The ring always advances by one stage per K step: past the last step the
+  // loads repeat the last step's data into a stage nobody reads again, so the
+  // number of loads in flight (and so every wait) is the same in every step.
   const int nk = K / kBTK;
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int s = kt & 1;
-    // this wave's loads of stage s have landed; the barrier makes every wave's
-    // visible and ends every wave's reads of stage s ^ 1 (from step kt - 1)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < nk) issue(s ^ 1, (kt + 1) * kBTK);
-    const char* sa = smem + s * kStageBytes + (wm * 128 + (lane & 31)) * kRowBytes;
-    const char* sb = smem + s * kStageBytes + kTileBytes + (wn * 128 + (lane & 31)) * kRowBytes;
-    // fragments of sub-step kk + 1 are read while sub-step kk multiplies
-    bf16x8_t fa[2][4], fb[2][4];
-    auto frag = [&](int kk, int buf) {
-      const int off = ((2 * kk + (lane >> 5)) ^ (lane & 7)) << 4;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) fa[buf][t] = *reinterpret_cast<const bf16x8_t*>(sa + t * 32 * kRowBytes + off);
+  for (int i = 0; i < kNStages - 1; ++i) issue(min(i, nk - 1));
+  sync_stage(kNStages - 2);
+  frag(0, 0, 0);
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    pin(0);
+    frag(kt, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0);
+    __builtin_amdgcn_sched_barrier(0);
+    pin(1);
+    // stage kt + 1 certified; stage kt - 1 (read in the previous step) free
+    sync_stage(kNStages - 3);
+    issue(min(kt + kNStages - 1, nk - 1));
+    frag(kt + 1, 0, 0);
+    mma(1);
+    // after the barrier the products start at once; the next sub-step's eight
+    // LDS reads (early, so they are back by the next step) and the eight DMA
+    // loads go between them
 #pragma unroll
-      for (int t = 0; t < 4; ++t) fb[buf][t] = *reinterpret_cast<const bf16x8_t*>(sb + t * 32 * kRowBytes + off);
-    };
-    frag(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < kBTK / 16; ++kk) {
-      if (kk + 1 < kBTK / 16) frag(kk + 1, (kk + 1) & 1);
-      // keep those reads here, ahead of this sub-step's products, so they
-      // return while the matrix core works through the sixteen products: an
-      // empty asm that clobbers memory (loads stay above it) and "modifies"
-      // this sub-step's fragments (the products stay below it)
-      const int cb = kk & 1;
-      asm volatile("" : "+v"(fa[cb][0]), "+v"(fa[cb][1]), "+v"(fa[cb][2]), "+v"(fa[cb][3]), "+v"(fb[cb][0]),
-                   "+v"(fb[cb][1]), "+v"(fb[cb][2]), "+v"(fb[cb][3])::"memory");
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][a], fb[kk & 1][c], acc[a][c], 0, 0, 0);
+    for (int m = 0; m < 8; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global (DMA) load
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
+  pin(0);
+  frag(nk - 1, 1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(0);
+  __builtin_amdgcn_sched_barrier(0);
+  pin(1);
+  mma(1);
 
   // Epilogue through LDS, a quarter of the wave's 128 x 128 block (32 rows) at
   // a time: the accumulators go to a wave-private 32 x 128 fp32 area (row
@@ -325,10 +409,10 @@ gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, c
       v.z += bb.z;
       v.w += bb.w;
       if (kGelu) {
-        v.x = 0.5f * v.x * (1.0f + erff(v.x * 0.70710678118654752f));
-        v.y = 0.5f * v.y * (1.0f + erff(v.y * 0.70710678118654752f));
-        v.z = 0.5f * v.z * (1.0f + erff(v.z * 0.70710678118654752f));
-        v.w = 0.5f * v.w * (1.0f + erff(v.w * 0.70710678118654752f));
+        v.x = gelu(v.x);
+        v.y = gelu(v.y);
+        v.z = gelu(v.z);
+        v.w = gelu(v.w);
       }
       if (row < M) {
         if (kOutF32) {
