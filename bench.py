@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=1200, help="oracle sample: frames per worker")
     ap.add_argument("--workload", choices=("batch", "stream", "interleave", "copy", "shortconv", "shortconv_decode",
-                                           "backward", "hmlp"),
+                                           "backward", "hmlp", "dft_gemm"),
                     default="batch",
                     help="batch: 64 x 20 min clips (default); stream: 4096 streams, one hop per step; "
                          "interleave: 256 x 32768 audio/text positions; copy: a plain 1 GiB device copy "
@@ -133,7 +133,7 @@ def main():
         sys.exit(1)
     if args.steps is None:
         args.steps = {"batch": 20, "stream": 1000, "interleave": 5, "copy": 5, "shortconv": 20,
-                      "shortconv_decode": 1000, "backward": 5, "hmlp": 10}[args.workload]
+                      "shortconv_decode": 1000, "backward": 5, "hmlp": 10, "dft_gemm": 3}[args.workload]
     if args.workload == "stream":
         return bench_stream(args)
     if args.workload == "interleave":
@@ -146,6 +146,8 @@ def main():
         return bench_backward(args)
     if args.workload == "hmlp":
         return bench_hmlp(args)
+    if args.workload == "dft_gemm":
+        return bench_dft_gemm(args)
     return bench_batch(args)
 
 
@@ -239,6 +241,80 @@ def bench_backward(args):
 
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+
+
+def bench_dft_gemm(args):
+    """The two ways to the log-mel of the 64 x 20 min batch (1,536,000 frames):
+    the mixed-radix FFT staged in LDS (dmel_frames) and the DFT as one bf16x3
+    matrix-core product (dmel_frames_dft_gemm: split frames, GEMM over
+    K = 4800 into 1792 fp32 columns, power + mel + log).  A step = one call of
+    each, timed separately with HIP events.  `value` is the DFT-as-GEMM
+    variant's frames/s; the FFT's is beside it."""
+    dev = "cuda"
+    n_clips = args.clips
+    clip_len = int(round(args.minutes * 60 * 16000))
+    audio = synth.speech_clips(seed=2, lengths=[clip_len] * n_clips, device=dev)
+    ctx = dm.dmel_create(0)
+    so, fo, T = dm.clip_offsets([clip_len] * n_clips, dev)
+    lm_fft = torch.empty((T, 80), dtype=torch.float32, device=dev)
+    lm_mm = torch.empty((T, 80), dtype=torch.float32, device=dev)
+    mat = torch.empty(dm.dmel_dft_matrix_bytes(), dtype=torch.uint8, device=dev)
+    wsb = dm.dmel_frames_dft_gemm_workspace_bytes(T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    dm.dmel_dft_matrix(mat, stream)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dm.dmel_frames(ctx, audio, audio.numel(), so, fo, n_clips, T, None, lm_fft, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        dm.dmel_frames_dft_gemm(ctx, audio, audio.numel(), so, fo, n_clips, T, None, mat, lm_mm, ws, wsb, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(2)] for e in events])
+    ms_fft, ms_mm = per.mean(axis=0)
+    a, b = np.clip(lm_fft.cpu().numpy(), -7, 2), np.clip(lm_mm.cpu().numpy(), -7, 2)
+    diff = float(np.abs(a - b).max())
+    flops_mm = 2.0 * 1792 * 4800 * T
+    achieved = flops_mm / (ms_mm * 1e-3) / 1e12
+    print(f"[bench] log-mel of {T} frames: LDS FFT {ms_fft:.3f} ms, DFT as GEMM {ms_mm:.3f} ms "
+          f"({ms_mm / ms_fft:.1f}x); max |difference| of the clamped log-mel {diff:.2e}", file=sys.stderr, flush=True)
+    dm.dmel_destroy(ctx)
+    line = {
+        "metric": "audio frames/s (log-mel of 16 kHz audio, DFT as a bf16x3 matrix-core product)",
+        "value": T / (ms_mm * 1e-3),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": float(ms_mm),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"log-mel of {n_clips} speech-like clips x {args.minutes:g} min ({T} frames): "
+                               f"framing, 1600-point DFT as a [T, 4800] x [4800, 1792] bf16 product, power, "
+                               f"80 mel filters, log",
+                   "global_batch": n_clips, "seq_len": T // n_clips, "parallelism": "single GPU"},
+        "kernel_ms": {"lds_fft_frames": float(ms_fft), "dft_gemm_frames": float(ms_mm)},
+        "fft_frames_per_s": T / (ms_fft * 1e-3),
+        "max_clamped_logmel_difference": diff,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def bench_hmlp(args):

@@ -286,6 +286,39 @@ int dmel_frames(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "frontend launch");
 }
 
+size_t dmel_dft_matrix_bytes(void) { return dmel::dft_matrix_bytes(); }
+
+int dmel_dft_matrix(void* matrix, void* stream) {
+  if (matrix == nullptr) return fail(DMEL_EINVAL, "matrix is NULL");
+  if (!aligned(matrix, 256)) return fail(DMEL_EALIGN, "matrix is not 256-byte aligned");
+  hipError_t e = dmel::launch_dft_matrix(static_cast<uint16_t*>(matrix), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "dft matrix launch");
+}
+
+size_t dmel_frames_dft_gemm_workspace_bytes(int64_t n_frames_total) {
+  return n_frames_total < 0 ? 0 : dmel::dft_gemm_workspace_bytes(n_frames_total);
+}
+
+int dmel_frames_dft_gemm(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total, const int64_t* sample_off,
+                         const int64_t* frame_off, int32_t n_clips, int64_t n_frames_total, const float* carry,
+                         const void* matrix, float* logmel, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_audio(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, logmel, "logmel");
+  if (rc != DMEL_OK) return rc;
+  if (carry != nullptr && !aligned(carry, 4)) return fail(DMEL_EALIGN, "carry is not 4-byte aligned");
+  if (n_frames_total > 0x7FFFFFFF) return fail(DMEL_ESHAPE, "at most 2^31 - 1 frames per call");
+  const size_t need = dmel::dft_gemm_workspace_bytes(n_frames_total);
+  if (workspace_bytes < need)
+    return fail(DMEL_ENOMEM, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  if (n_frames_total == 0) return DMEL_OK;
+  if (matrix == nullptr || workspace == nullptr) return fail(DMEL_EINVAL, "matrix / workspace is NULL");
+  if (!aligned(matrix, 256) || !aligned(workspace, 256))
+    return fail(DMEL_EALIGN, "matrix and workspace must be 256-byte aligned");
+  hipError_t e = dmel::launch_dft_gemm_frames(ctx->tabs, audio, n_samples_total, sample_off, frame_off, n_clips,
+                                              n_frames_total, carry, static_cast<const uint16_t*>(matrix), logmel,
+                                              workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "dft gemm launch");
+}
+
 int dmel_levels(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total, const int64_t* sample_off,
                 const int64_t* frame_off, int32_t n_clips, int64_t n_frames_total, const float* carry,
                 uint8_t* levels, void* stream) {

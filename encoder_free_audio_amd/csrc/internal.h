@@ -124,6 +124,15 @@ hipError_t launch_hmlp(const uint16_t* images, int n_images, int height, int wid
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, const float* bias, void* C, int64_t M, int N, int K,
                             bool gelu, bool out_f32, hipStream_t stream);
 
+// Log-mel through the DFT as a matrix-core product (dft_gemm.hip).
+size_t dft_matrix_bytes();
+size_t dft_gemm_workspace_bytes(int64_t n_frames);
+hipError_t launch_dft_matrix(uint16_t* B, hipStream_t stream);
+hipError_t launch_dft_gemm_frames(const FrontTables& tabs, const float* audio, int64_t n_samples_total,
+                                  const int64_t* sample_off, const int64_t* frame_off, int n_clips, int64_t n_frames,
+                                  const float* carry, const uint16_t* B, float* logmel, void* workspace,
+                                  hipStream_t stream);
+
 hipError_t launch_gather_rows(const uint16_t* table, int64_t n_table_rows, int d_model,
                               const int32_t* ids, int64_t n, uint16_t* out, int64_t out_row_stride,
                               const int64_t* out_rows, hipStream_t stream);

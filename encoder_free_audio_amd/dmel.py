@@ -30,7 +30,8 @@ EXPORTS = ("dmel_get_params", "dmel_num_frames", "dmel_last_error", "dmel_defaul
            "dmel_rms_scale", "dmel_embed", "dmel_forward_workspace_bytes", "dmel_forward", "dmel_gather_rows",
            "dmel_shortconv", "dmel_embed_backward_workspace_bytes", "dmel_embed_backward",
            "dmel_rms_backward_workspace_bytes", "dmel_rms_backward", "dmel_hmlp_workspace_bytes",
-           "dmel_hmlp_forward", "dmel_hmlp_stage")
+           "dmel_hmlp_forward", "dmel_hmlp_stage", "dmel_dft_matrix_bytes", "dmel_dft_matrix",
+           "dmel_frames_dft_gemm_workspace_bytes", "dmel_frames_dft_gemm")
 
 
 class DmelError(RuntimeError):
@@ -102,6 +103,10 @@ def lib() -> ctypes.CDLL:
             "dmel_hmlp_stage": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _I32, _I32, _P, _I32, _P]),
             "dmel_rms_backward": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _P, _P, _I32, _P,
                                                  _SZ, _P]),
+            "dmel_dft_matrix_bytes": (_SZ, []),
+            "dmel_dft_matrix": (ctypes.c_int, [_P, _P]),
+            "dmel_frames_dft_gemm_workspace_bytes": (_SZ, [_I64]),
+            "dmel_frames_dft_gemm": (ctypes.c_int, [_P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(h, name)
@@ -192,6 +197,26 @@ def dmel_frames(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_f
     _check("dmel_frames", lib().dmel_frames(ctx, _ptr(audio), int(n_samples_total), _ptr(sample_off),
                                             _ptr(frame_off), int(n_clips), int(n_frames_total), _ptr(carry),
                                             _ptr(logmel), _stream(stream)))
+
+
+def dmel_dft_matrix_bytes() -> int:
+    return int(lib().dmel_dft_matrix_bytes())
+
+
+def dmel_dft_matrix(matrix, stream=None) -> None:
+    _check("dmel_dft_matrix", lib().dmel_dft_matrix(_ptr(matrix), _stream(stream)))
+
+
+def dmel_frames_dft_gemm_workspace_bytes(n_frames_total: int) -> int:
+    return int(lib().dmel_frames_dft_gemm_workspace_bytes(int(n_frames_total)))
+
+
+def dmel_frames_dft_gemm(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, carry, matrix,
+                         logmel, workspace, workspace_bytes, stream=None) -> None:
+    _check("dmel_frames_dft_gemm",
+           lib().dmel_frames_dft_gemm(ctx, _ptr(audio), int(n_samples_total), _ptr(sample_off), _ptr(frame_off),
+                                      int(n_clips), int(n_frames_total), _ptr(carry), _ptr(matrix), _ptr(logmel),
+                                      _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def dmel_levels(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, carry, levels,

@@ -278,3 +278,47 @@ def test_product_path_does_not_touch_the_oracle():
                     text = f.read()
                 assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), fn
                 assert "dmel_oracle" not in text, fn
+
+
+def test_dft_gemm_validation(dm):
+    # sizes and rejections of the DFT-as-GEMM front end, in host code
+    assert dm.dmel_dft_matrix_bytes() == 1792 * 4800 * 2 + 1792 * 4
+    assert dm.dmel_frames_dft_gemm_workspace_bytes(0) == 0
+    assert dm.dmel_frames_dft_gemm_workspace_bytes(1) == 9728 + 7168
+    assert dm.dmel_frames_dft_gemm_workspace_bytes(1000) == 9_600_000 + 7_168_000
+    assert dm.dmel_frames_dft_gemm_workspace_bytes(-1) == 0
+    E = dm.DmelError
+    lib = dm.lib()
+    with pytest.raises(E) as e:
+        dm._check("dmel_dft_matrix", lib.dmel_dft_matrix(None, None))
+    assert _code(e) == -1
+    with pytest.raises(E) as e:
+        dm._check("dmel_dft_matrix", lib.dmel_dft_matrix(8, None))
+    assert _code(e) == -4
+    # (fake, aligned device addresses: every check fails before any HIP call)
+    args = dict(audio=256, n=1600, so=512, fo=768, clips=1, frames=2, carry=None, mat=1024, lm=2048, ws=4096,
+                wsb=10 ** 6)
+
+    def call(ctx=None, **kw):
+        a = dict(args)
+        a.update(kw)
+        return lib.dmel_frames_dft_gemm(ctx, a["audio"], a["n"], a["so"], a["fo"], a["clips"], a["frames"],
+                                        a["carry"], a["mat"], a["lm"], a["ws"], a["wsb"], None)
+    assert call() == -1                                   # NULL context
+    ctx = dm.dmel_create(0) if dm_has_gpu() else None
+    if ctx is not None:
+        try:
+            assert call(ctx, frames=3) == -2              # more frames than the audio holds
+            assert call(ctx, wsb=100) == -6               # workspace too small
+            assert call(ctx, mat=None) == -1
+            assert call(ctx, mat=1030) == -4
+        finally:
+            dm.dmel_destroy(ctx)
+
+
+def dm_has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
