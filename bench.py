@@ -33,20 +33,24 @@ PEAK_ADD_TFLOPS = 256 * 64 * 2.4e9 / 1e12   # v_add_f32: 256 CUs x 64 lanes x 2.
 PEAK_HBM_GBPS = 8000.0
 METRIC = "audio tokens/sec (dMel frames→6144-d embeds) + achieved HBM GB/s vs peak"
 COUNTERS_MD = os.path.join(ROOT, "profiles", "embed_kernel_64x20min_counters.md")
-EMBED_SRC = os.path.join(ROOT, "encoder_free_audio_amd", "csrc", "embed.hip")
+EMBED_SRCS = [os.path.join(ROOT, "encoder_free_audio_amd", "csrc", f) for f in ("embed.hip", "embed_core.h")]
 
 
 def embed_traffic():
     """Memory traffic of one embed launch on the 64 x 20 min batch, from the
-    committed counter summary - only if embed.hip is the source that was
-    measured (otherwise the figure would describe another kernel)."""
+    committed counter summary - only if embed.hip and embed_core.h are the
+    sources that were measured (otherwise the figure would describe another
+    kernel)."""
     import hashlib
     import re
     try:
         text = open(COUNTERS_MD).read()
-        want = re.search(r"embed.hip sha256: ([0-9a-f]{64})", text).group(1)
+        want = re.search(r"embed.hip \+ embed_core.h sha256: ([0-9a-f]{64})", text).group(1)
         traffic = float(re.search(r"traffic bytes per launch: ([0-9.e+]+)", text).group(1))
-        have = hashlib.sha256(open(EMBED_SRC, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for f in EMBED_SRCS:
+            h.update(open(f, "rb").read())
+        have = h.hexdigest()
     except (OSError, AttributeError, ValueError):
         return None
     return traffic if have == want else None
@@ -60,7 +64,7 @@ def parse():
     ap.add_argument("--clips", type=int, default=64)
     ap.add_argument("--minutes", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-frames", type=int, default=1200, help="oracle sample: frames per worker")
+    ap.add_argument("--cpu-frames", type=int, default=10000, help="oracle sample: frames per worker")
     ap.add_argument("--workload", choices=("batch", "stream", "interleave", "copy", "shortconv", "shortconv_decode",
                                            "backward", "hmlp", "dft_gemm"),
                     default="batch",
