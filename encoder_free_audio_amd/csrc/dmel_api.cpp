@@ -355,7 +355,7 @@ int dmel_rms_scale(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int3
   if (released_layout(n_bins, n_levels) && !aligned(levels, 16))
     return fail(DMEL_EALIGN, "levels is not 16-byte aligned");
   if (!aligned(gram, 4) || !aligned(scale, 4)) return fail(DMEL_EALIGN, "gram / scale not 4-byte aligned");
-  hipError_t e = dmel::launch_rms_scale(levels, n_tokens, n_bins, n_levels, gram, d_model, eps, scale,
+  hipError_t e = dmel::launch_rms_scale(levels, n_tokens, n_bins, n_levels, gram, d_model, eps, scale, nullptr,
                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "rms_scale launch");
 }
@@ -385,7 +385,8 @@ int dmel_embed(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t 
 size_t dmel_forward_workspace_bytes(int64_t n_frames_total) {
   if (n_frames_total < 0) return 0;
   const size_t n = static_cast<size_t>(n_frames_total);
-  return round_up(n * dmel::kMels, 256) + round_up(n * sizeof(float), 256);
+  return round_up(n * dmel::kMels, 256) + round_up(n * sizeof(float), 256) +
+         round_up(dmel::rms_partials_bytes(n_frames_total), 256);
 }
 
 int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total, const int64_t* sample_off,
@@ -423,7 +424,10 @@ int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_tota
                                        n_frames_total, carry, nullptr, levels, s);
   if (e != hipSuccess) return hip_fail(e, "frontend launch");
   if (rms_weight != nullptr) {
-    e = dmel::launch_rms_scale(levels, n_frames_total, n_bins, n_levels, gram, d_model, eps, scale, s);
+    void* partials = static_cast<char*>(workspace) + round_up(static_cast<size_t>(n_frames_total) * dmel::kMels, 256) +
+                     round_up(static_cast<size_t>(n_frames_total) * sizeof(float), 256);
+    e = dmel::launch_rms_scale(levels, n_frames_total, n_bins, n_levels, gram, d_model, eps, scale,
+                               dmel::rms_partials_bytes(n_frames_total) > 0 ? partials : nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "rms_scale launch");
   }
   e = dmel::launch_embed(levels, n_frames_total, n_bins, n_levels, table, d_model, rms_weight,

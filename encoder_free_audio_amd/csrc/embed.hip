@@ -315,7 +315,7 @@ constexpr int kDirThreads = kDirTok * kMels;  // 320
 __global__ void __launch_bounds__(kDirThreads)
 rms_scale_direct_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels,
                         const float* __restrict__ gram, int d_model, float eps, float* __restrict__ scale) {
-  __shared__ uint8_t lv_s[kDirTok][kMels];
+  __shared__ __attribute__((aligned(16))) uint8_t lv_s[kDirTok][kMels];
   __shared__ float d_s[kDirTok][kMels];
   __shared__ float o_s[kDirTok][kMels];
   const int tid = threadIdx.x;
@@ -334,14 +334,29 @@ rms_scale_direct_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, in
     const int rj = kLevels * j + lv_s[tok][j];
     const float* row = gram + static_cast<int64_t>(rj) * kRows;
     const float diag = row[rj];
+    // all lookups are issued at once (their addresses are independent) and
+    // added in bin order; the terms of bins jp <= j are +0.0, which leave the
+    // sum at +0.0 until its first real term (a sum that starts at +0.0 never
+    // becomes -0.0), exactly as the staged kernel's masked terms
+    uint32_t lw[20];
+#pragma unroll
+    for (int i = 0; i < 20; ++i) lw[i] = reinterpret_cast<const uint32_t*>(lv_s[tok])[i];
+    float v[kMels];
+#pragma unroll
+    for (int jp = 0; jp < kMels; ++jp) {
+      const uint32_t L = (lw[jp >> 2] >> (8 * (jp & 3))) & 0xFFu;
+      v[jp] = jp > j ? row[kLevels * jp + L] : 0.0f;
+    }
     float off = 0.0f;
-    for (int jp = j + 1; jp < kMels; ++jp) off += row[kLevels * jp + lv_s[tok][jp]];
+#pragma unroll
+    for (int jp = 0; jp < kMels; ++jp) off += v[jp];
     d_s[tok][j] = diag;
     o_s[tok][j] = off;
   }
   __syncthreads();
   if (active && j == 0) {
     double total = 0.0;
+#pragma unroll 16
     for (int jj = 0; jj < kMels; ++jj) {
       total += static_cast<double>(d_s[tok][jj]);
       total += 2.0 * static_cast<double>(o_s[tok][jj]);
@@ -349,6 +364,87 @@ rms_scale_direct_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, in
     const double ms = total / static_cast<double>(d_model);
     scale[t] = static_cast<float>(1.0 / sqrt(ms + static_cast<double>(eps)));
   }
+}
+
+// Same scale for small batches with a workspace, bin-parallel: a workgroup
+// takes one bin j and 1024 tokens (one per thread), stages the 16 rows of bin
+// j of the upper triangle of G in LDS (as rms_scale_kernel does) and writes
+// each token's diagonal term and fp32 off-diagonal sum of bin j (same terms,
+// same order) to part[j][token]; rms_total_kernel then adds the 80 bins of
+// each token in bin order in fp64.  Identical arithmetic again, so the scale
+// does not depend on the kernel that computed it.  The token's levels stay in
+// registers as 80 bytes; the lookups run over a static bin index jp = 0..79
+// (terms of bins jp <= j are +0.0, which leave the sum at +0.0 until its first
+// real term: a sum that starts at +0.0 never becomes -0.0), so every byte
+// index is static and all lookups are independent.
+constexpr int kBinTok = 1024;
+
+template <bool kAny>
+__global__ void __launch_bounds__(kBinTok)
+rms_bin_partials_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels,
+                        const float* __restrict__ gram, int n_chunks, float2* __restrict__ part) {
+  __shared__ float g_s[16 * kGPitch];              // 83 KB
+  const int tid = threadIdx.x;
+  const int j = static_cast<int>(blockIdx.x / static_cast<unsigned>(n_chunks));  // heavy (small) bins first
+  const int64_t t = static_cast<int64_t>(blockIdx.x % static_cast<unsigned>(n_chunks)) * kBinTok + tid;
+  const bool active = t < n_tokens;
+  const int c0 = kLevels * j;
+  const int width = kRows - c0;
+  for (int i = tid; i < 16 * width; i += kBinTok) {
+    const int r = i / width;
+    const int c = i - r * width;
+    g_s[r * kGPitch + c] = gram[static_cast<int64_t>(c0 + r) * kRows + c0 + c];
+  }
+  uint32_t lw[20];
+  if (active && kAny) {
+    load_levels_any(lw, levels, t, n_bins, static_cast<uint32_t>(n_levels - 1));
+  } else if (active) {
+    const uint4* p = reinterpret_cast<const uint4*>(levels + t * kMels);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const uint4 q = p[i];
+      lw[4 * i + 0] = clamp_levels(q.x);
+      lw[4 * i + 1] = clamp_levels(q.y);
+      lw[4 * i + 2] = clamp_levels(q.z);
+      lw[4 * i + 3] = clamp_levels(q.w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 20; ++i) lw[i] = 0;
+  }
+  __syncthreads();
+  if (!active) return;
+  uint32_t lj = 0;
+#pragma unroll
+  for (int jp = 0; jp < kMels; ++jp) lj = jp == j ? (lw[jp >> 2] >> (8 * (jp & 3))) & 0xFFu : lj;
+  const float* row = g_s + lj * kGPitch - c0;   // row[16 jp + L] = G[16 j + lj][16 jp + L]
+  float v[kMels];
+#pragma unroll
+  for (int jp = 0; jp < kMels; ++jp) {
+    const uint32_t L = (lw[jp >> 2] >> (8 * (jp & 3))) & 0xFFu;
+    // (the address stays inside the staged rows for every jp)
+    const float g = row[jp > j ? kLevels * jp + static_cast<int>(L) : c0];
+    v[jp] = jp > j ? g : 0.0f;
+  }
+  float off = 0.0f;
+#pragma unroll
+  for (int jp = 0; jp < kMels; ++jp) off += v[jp];
+  part[static_cast<int64_t>(j) * n_tokens + t] = make_float2(row[c0 + lj], off);
+}
+
+__global__ void __launch_bounds__(256)
+rms_total_kernel(const float2* __restrict__ part, int64_t n_tokens, int d_model, float eps, float* __restrict__ scale) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= n_tokens) return;
+  double total = 0.0;
+#pragma unroll 16
+  for (int j = 0; j < kMels; ++j) {
+    const float2 v = part[static_cast<int64_t>(j) * n_tokens + t];
+    total += static_cast<double>(v.x);
+    total += 2.0 * static_cast<double>(v.y);
+  }
+  const double ms = total / static_cast<double>(d_model);
+  scale[t] = static_cast<float>(1.0 / sqrt(ms + static_cast<double>(eps)));
 }
 
 // ---------------------------------------------------------------------------
@@ -387,17 +483,18 @@ hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, int n_bins, int
   // launches too few workgroups to fill the chip.  One workgroup fits per CU
   // (LDS), so the cost of a count g is about rounds-of-256-workgroups x g; take
   // the largest g within 5% of the cheapest.
-  static const int kCounts[] = {16, 8, 4, 3, 2, 1};
-  int64_t cost[6];
+  static const int kCounts[] = {16, 12, 8, 6, 4, 3, 2, 1};
+  constexpr int kNCounts = sizeof(kCounts) / sizeof(kCounts[0]);
+  int64_t cost[kNCounts];
   int64_t min_cost = -1;
-  for (int i = 0; i < 6; ++i) {
+  for (int i = 0; i < kNCounts; ++i) {
     const int g = kCounts[i];
     const int64_t wgs = tblocks * ((n_strips + g - 1) / g);
     cost[i] = ((wgs + 255) / 256) * g;
     if (min_cost < 0 || cost[i] < min_cost) min_cost = cost[i];
   }
   int best = 1;
-  for (int i = 0; i < 6; ++i) {
+  for (int i = 0; i < kNCounts; ++i) {
     if (cost[i] * 100 <= min_cost * 105) {
       best = kCounts[i];
       break;
@@ -425,9 +522,31 @@ hipError_t launch_gram(const uint16_t* table, int n_bins, int n_levels, int d_mo
   return hipGetLastError();
 }
 
+size_t rms_partials_bytes(int64_t n_tokens) {
+  return n_tokens > 0 && n_tokens <= kRmsDirectMax ? static_cast<size_t>(n_tokens) * kMels * sizeof(float2) : 0;
+}
+
 hipError_t launch_rms_scale(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
-                            const float* gram, int d_model, float eps, float* scale, hipStream_t stream) {
+                            const float* gram, int d_model, float eps, float* scale, void* partials,
+                            hipStream_t stream) {
   if (n_tokens <= 0) return hipSuccess;
+  if (n_tokens <= kRmsDirectMax && partials != nullptr) {
+    const int n_chunks = static_cast<int>((n_tokens + kBinTok - 1) / kBinTok);
+    auto* part = static_cast<float2*>(partials);
+    const dim3 grid(static_cast<unsigned>(n_chunks * kMels));
+    if (n_bins == kMels && n_levels == kLevels) {
+      hipLaunchKernelGGL(rms_bin_partials_kernel<false>, grid, dim3(kBinTok), 0, stream, levels, n_tokens, n_bins,
+                         n_levels, gram, n_chunks, part);
+    } else {
+      hipLaunchKernelGGL(rms_bin_partials_kernel<true>, grid, dim3(kBinTok), 0, stream, levels, n_tokens, n_bins,
+                         n_levels, gram, n_chunks, part);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(rms_total_kernel, dim3(static_cast<unsigned>((n_tokens + 255) / 256)), dim3(256), 0, stream,
+                       part, n_tokens, d_model, eps, scale);
+    return hipGetLastError();
+  }
   if (n_tokens <= kRmsDirectMax) {
     const int64_t blocks = (n_tokens + kDirTok - 1) / kDirTok;
     hipLaunchKernelGGL(rms_scale_direct_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kDirThreads), 0, stream,

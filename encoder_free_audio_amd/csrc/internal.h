@@ -88,13 +88,17 @@ hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, int n_bins, int
 hipError_t launch_gram(const uint16_t* table, int n_bins, int n_levels, int d_model, float* gram,
                        hipStream_t stream);
 
-// Batches up to this many tokens take the RMSNorm-scale kernel that reads the
-// Gram matrix directly (no staging); larger ones stage it in LDS.  Both give
-// bit-identical scales.
+// Batches up to this many tokens take a small-batch RMSNorm-scale path: with
+// a partials buffer (rms_partials_bytes), a bin-parallel kernel that stages G
+// in LDS plus an in-order total; without one, a kernel that reads the Gram
+// matrix directly.  Larger batches stage G in LDS per token block.  All three
+// give bit-identical scales.
 constexpr int64_t kRmsDirectMax = 131072;
 
+size_t rms_partials_bytes(int64_t n_tokens);  // 0 above kRmsDirectMax
 hipError_t launch_rms_scale(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
-                            const float* gram, int d_model, float eps, float* scale, hipStream_t stream);
+                            const float* gram, int d_model, float eps, float* scale, void* partials,
+                            hipStream_t stream);
 
 // Short convolution (width 4, residual) over ragged requests with per-request
 // state; channels % 8 == 0.

@@ -210,7 +210,9 @@ int dmel_embed(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t 
                void* stream);
 
 /* Bytes of device workspace dmel_forward needs for n_frames_total frames
- * (levels plus per-token scales, each 256-byte aligned).  0 for a negative count. */
+ * (levels plus per-token scales, and for batches of at most 131,072 frames
+ * 640 bytes per frame of RMSNorm partial sums; each part 256-byte aligned).
+ * 0 for a negative count. */
 size_t dmel_forward_workspace_bytes(int64_t n_frames_total);
 
 /* End to end: audio -> levels -> tokens, i.e. dmel_levels, then (when

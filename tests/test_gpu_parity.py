@@ -309,3 +309,48 @@ def test_scale_and_embed_independent_of_batch_size(env, table):
     dm.dmel_embed(lv, n_small, tab, 6144, w, s_small, b, dm.DMEL_BF16, 6144)
     torch.cuda.synchronize()
     assert torch.equal(a[:n_small], b)
+
+
+@pytest.mark.parametrize("cfg", [None, {"n_mel_bins": 40, "mel_vocab_size": 8, "min_value": -5.0, "max_value": 1.0}])
+def test_forward_rmsnorm_small_batch_paths(env, table, cfg):
+    """dmel_forward on a small batch takes the bin-parallel RMSNorm-scale path
+    (its workspace holds the partial sums); the same tokens through
+    dmel_levels -> dmel_rms_scale (direct kernel) -> dmel_embed, and the
+    staged kernel on a batch above the small-batch limit, give the same bits."""
+    dm, ctx0 = env
+    ctx = ctx0 if cfg is None else dm.dmel_create_config(0, cfg)
+    try:
+        nb = 80 if cfg is None else cfg["n_mel_bins"]
+        nl = 16 if cfg is None else cfg["mel_vocab_size"]
+        print(f"case: forward with RMSNorm, small batch, config {cfg}", flush=True)
+        x = synth.bursts_clips(seed=5, n_clips=6, n_samples=480000).cuda()
+        so, fo, T = P.offsets([480000] * 6)
+        tab = (table if cfg is None else synth.table_bf16(seed=78, rows=nb * nl, d_model=6144)).cuda()
+        gram = torch.empty((1280, 1280), dtype=torch.float32, device="cuda")
+        dm.dmel_rms_gram(tab, 6144, gram, n_bins=nb, n_levels=nl)
+        w = (torch.rand(6144, generator=torch.Generator().manual_seed(5)) + 0.5).cuda()
+        out = torch.empty((T, 6144), dtype=torch.int16, device="cuda")
+        ws = torch.empty(dm.dmel_forward_workspace_bytes(T), dtype=torch.uint8, device="cuda")
+        dm.dmel_forward(ctx, x.reshape(-1), x.numel(), so, fo, 6, T, None, tab, 6144, w, gram, 1e-6, out,
+                        dm.DMEL_BF16, 6144, None, ws, ws.numel())
+        lv = torch.empty((T, nb), dtype=torch.uint8, device="cuda")
+        dm.dmel_levels(ctx, x.reshape(-1), x.numel(), so, fo, 6, T, None, lv)
+        sc = torch.empty(T, dtype=torch.float32, device="cuda")
+        dm.dmel_rms_scale(lv, T, gram, 6144, 1e-6, sc, n_bins=nb, n_levels=nl)
+        ref = torch.empty((T, 6144), dtype=torch.int16, device="cuda")
+        dm.dmel_embed(lv, T, tab, 6144, w, sc, ref, dm.DMEL_BF16, 6144, n_bins=nb, n_levels=nl)
+        # the staged kernel: the same levels repeated past the small-batch limit
+        reps = 131072 // T + 1
+        big = lv.repeat(reps, 1)
+        sc_big = torch.empty(big.shape[0], dtype=torch.float32, device="cuda")
+        dm.dmel_rms_scale(big, big.shape[0], gram, 6144, 1e-6, sc_big, n_bins=nb, n_levels=nl)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        assert torch.equal(sc, sc_big[:T])
+        # the forward's scales sit in its workspace after the levels
+        off = (T * 80 + 255) // 256 * 256
+        assert torch.equal(ws[off: off + 4 * T].view(torch.float32), sc)
+    finally:
+        if cfg is not None:
+            torch.cuda.synchronize()
+            dm.dmel_destroy(ctx)
