@@ -157,8 +157,9 @@ def main():
 
 def bench_backward(args):
     """Backward of the front end's trainable parts on the 64 x 20 min batch:
-    the RMSNorm backward (dmel_rms_backward: two passes that recompute the
-    forward sum) and the table gradient (dmel_embed_backward: level sort,
+    the RMSNorm backward (dmel_rms_backward with the larger workspace: a first
+    pass that recomputes the forward sum and keeps it, a second that streams
+    it) and the table gradient (dmel_embed_backward: level sort,
     fixed-order scatter, segment combine), from a bf16 upstream gradient
     ~ N(0, 1e-3).  One step = both calls; the levels come from the front end
     before the timed region."""
@@ -183,7 +184,7 @@ def bench_backward(args):
     ds = torch.empty((T, d), dtype=torch.float32, device=dev)
     dw = torch.empty(d, dtype=torch.float32, device=dev)
     dt = torch.empty((1280, d), dtype=torch.float32, device=dev)
-    wb1 = dm.dmel_rms_backward_workspace_bytes(T, d)
+    wb1 = dm.dmel_rms_backward_stored_workspace_bytes(T, d)   # keeps the sums between the two passes
     wb2 = dm.dmel_embed_backward_workspace_bytes(T, 80, 16, d)
     ws = torch.empty(max(wb1, wb2), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()

@@ -33,6 +33,8 @@
 //    is recomputed exactly as embed_kernel computes it (embed_core.h); the
 //    first pass forms sum_c w_c dy_c s_c per token and per-workgroup partial
 //    sums of dy * s * r per column, the second pass writes ds.
+#include <algorithm>
+
 #include "embed_core.h"
 
 namespace dmel {
@@ -286,13 +288,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Pass 1: per token, sum_c w_c dy_c s_c over the workgroup's strips (dot_part
 // [n_tokens, n_groups]); per column, sum over the workgroup's tokens of
-// dy * s * r (dw_part [token blocks, d_model]).
+// dy * s * r (dw_part [token blocks, d_model]); with s_out, the sums s
+// themselves (fp32 [n_tokens, d_model]) for the streaming second pass.
 template <bool kAny, bool kDyBf16>
 __global__ void __launch_bounds__(kEmbThreads)
 rms_dot_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels,
                const uint16_t* __restrict__ table, int d_model, const float* __restrict__ rms_weight,
                const float* __restrict__ rms_scale, const void* __restrict__ dy, float* __restrict__ dot_part,
-               float* __restrict__ dw_part, int n_groups, int n_strips, int strips_per_group) {
+               float* __restrict__ dw_part, float* __restrict__ s_out, int n_groups, int n_strips,
+               int strips_per_group) {
   __shared__ float4 tab4[kRows * kPitch / 4];
   __shared__ float red[kEmbThreads / 64][kStrip];
   float* tab = reinterpret_cast<float*>(tab4);
@@ -309,6 +313,13 @@ rms_dot_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins,
   float dot = 0.0f;
   sum_strips<kAny>(tab, table, d_model, s_first, s_end, tid, n_bins, n_levels, offs,
                    [&](int col0, float (&acc)[kStrip]) {
+                     if (s_out != nullptr && active) {
+                       float4* so = reinterpret_cast<float4*>(s_out + t * d_model + col0);
+                       so[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                       so[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+                       so[2] = make_float4(acc[8], acc[9], acc[10], acc[11]);
+                       so[3] = make_float4(acc[12], acc[13], acc[14], acc[15]);
+                     }
                      float gr[kStrip];
                      load_dy<kDyBf16>(gr, dy, t, d_model, col0, active);
                      float q[kStrip];
@@ -373,6 +384,54 @@ rms_ds_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, 
                      p[2] = make_float4(o[8], o[9], o[10], o[11]);
                      p[3] = make_float4(o[12], o[13], o[14], o[15]);
                    });
+}
+
+// Second pass from stored sums (when the workspace holds them): the per-token
+// factor (r^3 / D) dot, then ds = r (w dy) - factor s as a stream over the
+// stored sums: the same expressions, in the same order, as rms_ds_kernel.
+__global__ void __launch_bounds__(256)
+rms_coef_kernel(const float* __restrict__ dot_part, const float* __restrict__ rms_scale, int64_t n_tokens,
+                int n_groups, int d_model, float* __restrict__ coef) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= n_tokens) return;
+  const float r = rms_scale[t];
+  float dot = 0.0f;
+  for (int g = 0; g < n_groups; ++g) dot += dot_part[t * n_groups + g];
+  coef[t] = ((r * r) * r) / static_cast<float>(d_model) * dot;
+}
+
+template <bool kDyBf16>
+__global__ void __launch_bounds__(256)
+rms_ds_stream_kernel(const float* __restrict__ s, const void* __restrict__ dy, const float* __restrict__ rms_weight,
+                     const float* __restrict__ rms_scale, const float* __restrict__ coef, int64_t n_tokens,
+                     int d_model, float* __restrict__ ds) {
+  const int q4 = d_model / 4;
+  const int64_t total = n_tokens * q4;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t t = i / q4;
+    const int c = static_cast<int>(i - t * q4) * 4;
+    const float r = rms_scale[t], cf = coef[t];
+    const float4 sv = reinterpret_cast<const float4*>(s)[i];
+    float gr[4];
+    if (kDyBf16) {
+      const uint2 h = reinterpret_cast<const uint2*>(dy)[i];
+      gr[0] = bf16_to_f32(h.x & 0xFFFFu);
+      gr[1] = bf16_to_f32(h.x >> 16);
+      gr[2] = bf16_to_f32(h.y & 0xFFFFu);
+      gr[3] = bf16_to_f32(h.y >> 16);
+    } else {
+      const float4 g = reinterpret_cast<const float4*>(dy)[i];
+      gr[0] = g.x;
+      gr[1] = g.y;
+      gr[2] = g.z;
+      gr[3] = g.w;
+    }
+    const float4 w = *reinterpret_cast<const float4*>(rms_weight + c);
+    reinterpret_cast<float4*>(ds)[i] =
+        make_float4(fmaf(-cf, sv.x, r * (w.x * gr[0])), fmaf(-cf, sv.y, r * (w.y * gr[1])),
+                    fmaf(-cf, sv.z, r * (w.z * gr[2])), fmaf(-cf, sv.w, r * (w.w * gr[3])));
+  }
 }
 
 // dw[c] = (accumulate ? dw[c] : 0) + sum over token blocks, in order.
@@ -476,10 +535,18 @@ size_t rms_bwd_layout(int64_t n_tokens, int d_model, size_t* off_dw) {
   return b_dot + b_dw;
 }
 
+// The larger workspace of the stored-sum second pass: the layout above, then
+// the sums fp32 [n_tokens, d_model], then the per-token factors.
+size_t rms_bwd_stored_bytes(int64_t n_tokens, int d_model) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const size_t n = static_cast<size_t>(n_tokens);
+  return rms_bwd_layout(n_tokens, d_model, nullptr) + up(n * d_model * sizeof(float)) + up(n * sizeof(float));
+}
+
 hipError_t launch_rms_backward(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
                                const uint16_t* table, int d_model, const float* rms_weight, const float* rms_scale,
                                const void* dy, bool dy_bf16, float* ds, float* dweight, bool accumulate_dweight,
-                               void* workspace, hipStream_t stream) {
+                               void* workspace, bool stored, hipStream_t stream) {
   if (n_tokens <= 0) {
     if (dweight == nullptr || accumulate_dweight) return hipSuccess;
     return zero_fill(dweight, d_model, stream);
@@ -503,12 +570,31 @@ hipError_t launch_rms_backward(const uint8_t* levels, int64_t n_tokens, int n_bi
     else if (dy_bf16) hipLaunchKernelGGL((KERNEL<false, true>), grid, block, 0, stream, __VA_ARGS__);        \
     else hipLaunchKernelGGL((KERNEL<false, false>), grid, block, 0, stream, __VA_ARGS__);                    \
   } while (0)
+  const size_t base = rms_bwd_layout(n_tokens, d_model, nullptr);
+  float* s_store = stored ? reinterpret_cast<float*>(static_cast<char*>(workspace) + base) : nullptr;
   DMEL_RMS_PASS(rms_dot_kernel, levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, dy,
-                dot_part, dw_part, n_groups, n_strips, g);
+                dot_part, dw_part, s_store, n_groups, n_strips, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  DMEL_RMS_PASS(rms_ds_kernel, levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, dy,
-                dot_part, ds, n_groups, n_strips, g);
+  if (stored) {
+    const size_t b_s = (static_cast<size_t>(n_tokens) * d_model * sizeof(float) + 255) / 256 * 256;
+    auto* coef = reinterpret_cast<float*>(static_cast<char*>(workspace) + base + b_s);
+    hipLaunchKernelGGL(rms_coef_kernel, dim3(static_cast<unsigned>((n_tokens + 255) / 256)), dim3(256), 0, stream,
+                       dot_part, rms_scale, n_tokens, n_groups, d_model, coef);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t items = n_tokens * (d_model / 4);
+    const unsigned sb = static_cast<unsigned>(std::min<int64_t>((items + 255) / 256, 256 * 64));
+    if (dy_bf16) {
+      hipLaunchKernelGGL(rms_ds_stream_kernel<true>, dim3(sb), dim3(256), 0, stream, s_store, dy, rms_weight,
+                         rms_scale, coef, n_tokens, d_model, ds);
+    } else {
+      hipLaunchKernelGGL(rms_ds_stream_kernel<false>, dim3(sb), dim3(256), 0, stream, s_store, dy, rms_weight,
+                         rms_scale, coef, n_tokens, d_model, ds);
+    }
+  } else {
+    DMEL_RMS_PASS(rms_ds_kernel, levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, dy,
+                  dot_part, ds, n_groups, n_strips, g);
+  }
 #undef DMEL_RMS_PASS
   e = hipGetLastError();
   if (e != hipSuccess || dweight == nullptr) return e;

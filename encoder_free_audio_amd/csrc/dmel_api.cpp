@@ -525,6 +525,11 @@ size_t dmel_rms_backward_workspace_bytes(int64_t n_tokens, int32_t d_model) {
   return dmel::rms_bwd_layout(n_tokens, d_model, nullptr);
 }
 
+size_t dmel_rms_backward_stored_workspace_bytes(int64_t n_tokens, int32_t d_model) {
+  if (n_tokens < 0 || d_model < 16 || d_model % 16 != 0) return 0;
+  return dmel::rms_bwd_stored_bytes(n_tokens, d_model);
+}
+
 int dmel_rms_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels, const uint16_t* table,
                       int32_t d_model, const float* rms_weight, const float* rms_scale, const void* dy, int32_t dy_dtype,
                       float* dsum, float* dweight, int32_t accumulate_dweight, void* workspace, size_t workspace_bytes,
@@ -538,9 +543,13 @@ int dmel_rms_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, i
   if (rms_weight == nullptr) return fail(DMEL_EINVAL, "rms_weight is NULL");
   if (!aligned(rms_weight, 4)) return fail(DMEL_EALIGN, "rms_weight is not 4-byte aligned");
   if (dweight != nullptr && !aligned(dweight, 4)) return fail(DMEL_EALIGN, "dweight is not 4-byte aligned");
-  const size_t need = dmel_rms_backward_workspace_bytes(n_tokens, d_model);
-  if (workspace_bytes < need)
-    return fail(DMEL_ENOMEM, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  const size_t need_min = dmel_rms_backward_workspace_bytes(n_tokens, d_model);
+  if (workspace_bytes < need_min)
+    return fail(DMEL_ENOMEM, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need_min);
+  // a workspace that can hold the sums selects the stored-sum second pass
+  const size_t need_stored = dmel_rms_backward_stored_workspace_bytes(n_tokens, d_model);
+  const bool stored = n_tokens > 0 && workspace_bytes >= need_stored;
+  const size_t need = stored ? need_stored : need_min;
   if (n_tokens > 0) {
     if (levels == nullptr || rms_scale == nullptr || dy == nullptr || dsum == nullptr || workspace == nullptr)
       return fail(DMEL_EINVAL, "levels / rms_scale / dy / dsum / workspace is NULL");
@@ -558,7 +567,7 @@ int dmel_rms_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, i
   }
   hipError_t e = dmel::launch_rms_backward(levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, dy,
                                            dy_dtype == DMEL_BF16, dsum, dweight, accumulate_dweight != 0, workspace,
-                                           static_cast<hipStream_t>(stream));
+                                           stored, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "rms backward launch");
 }
 

@@ -115,10 +115,13 @@ hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_
                                  bool dsum_bf16, int d_model, float* dtable, bool accumulate, void* workspace,
                                  hipStream_t stream);
 size_t rms_bwd_layout(int64_t n_tokens, int d_model, size_t* off_dw);
+size_t rms_bwd_stored_bytes(int64_t n_tokens, int d_model);
+// stored: the workspace holds rms_bwd_stored_bytes (the first pass keeps the
+// sums, the second streams them) instead of recomputing the sums twice.
 hipError_t launch_rms_backward(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
                                const uint16_t* table, int d_model, const float* rms_weight, const float* rms_scale,
                                const void* dy, bool dy_bf16, float* ds, float* dweight, bool accumulate_dweight,
-                               void* workspace, hipStream_t stream);
+                               void* workspace, bool stored, hipStream_t stream);
 
 // hMLP image front end (four stages over 40 x 40 patches) and its stage GEMM.
 size_t hmlp_layout(int64_t n_patches, int hidden, size_t* off);

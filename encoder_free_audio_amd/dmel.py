@@ -29,7 +29,8 @@ EXPORTS = ("dmel_get_params", "dmel_num_frames", "dmel_last_error", "dmel_defaul
            "dmel_create_config", "dmel_get_config", "dmel_destroy", "dmel_frames", "dmel_levels", "dmel_rms_gram",
            "dmel_rms_scale", "dmel_embed", "dmel_forward_workspace_bytes", "dmel_forward", "dmel_gather_rows",
            "dmel_shortconv", "dmel_embed_backward_workspace_bytes", "dmel_embed_backward",
-           "dmel_rms_backward_workspace_bytes", "dmel_rms_backward", "dmel_hmlp_workspace_bytes",
+           "dmel_rms_backward_workspace_bytes", "dmel_rms_backward_stored_workspace_bytes", "dmel_rms_backward",
+           "dmel_hmlp_workspace_bytes",
            "dmel_hmlp_forward", "dmel_hmlp_stage", "dmel_dft_matrix_bytes", "dmel_dft_matrix",
            "dmel_frames_dft_gemm_workspace_bytes", "dmel_frames_dft_gemm")
 
@@ -97,6 +98,7 @@ def lib() -> ctypes.CDLL:
             "dmel_embed_backward_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32]),
             "dmel_embed_backward": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _I32, _P, _I32, _P, _SZ, _P]),
             "dmel_rms_backward_workspace_bytes": (_SZ, [_I64, _I32]),
+            "dmel_rms_backward_stored_workspace_bytes": (_SZ, [_I64, _I32]),
             "dmel_hmlp_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
             "dmel_hmlp_forward": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P,
                                                  _I32, _P, _SZ, _P]),
@@ -289,6 +291,10 @@ def dmel_embed_backward(levels, n_tokens, n_bins, n_levels, dsum, dsum_dtype, d_
 
 def dmel_rms_backward_workspace_bytes(n_tokens, d_model) -> int:
     return int(lib().dmel_rms_backward_workspace_bytes(int(n_tokens), int(d_model)))
+
+
+def dmel_rms_backward_stored_workspace_bytes(n_tokens, d_model) -> int:
+    return int(lib().dmel_rms_backward_stored_workspace_bytes(int(n_tokens), int(d_model)))
 
 
 def dmel_rms_backward(levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, dy, dy_dtype, dsum,

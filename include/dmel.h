@@ -308,6 +308,13 @@ int dmel_embed_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins,
 /* Bytes of workspace dmel_rms_backward needs (0 for invalid sizes). */
 size_t dmel_rms_backward_workspace_bytes(int64_t n_tokens, int32_t d_model);
 
+/* Bytes of workspace with which dmel_rms_backward keeps the fp32 sums between
+ * its passes (the above + n_tokens * d_model * 4 + n_tokens * 4, each part
+ * 256-byte aligned; 0 for invalid sizes).  With at least this much, the second
+ * pass streams the stored sums instead of recomputing them; the results are
+ * the same bits either way. */
+size_t dmel_rms_backward_stored_workspace_bytes(int64_t n_tokens, int32_t d_model);
+
 /* Backward of the RMSNorm of dmel_embed: the gradient with respect to each
  * token's fp32 sum and to the RMSNorm weight.  The sums are recomputed from
  * the levels and the table exactly as dmel_embed computes them.
@@ -317,7 +324,9 @@ size_t dmel_rms_backward_workspace_bytes(int64_t n_tokens, int32_t d_model);
  *  dsum       fp32 [n_tokens, d_model] out, 16-byte aligned
  *  dweight    fp32 [d_model] out or NULL; overwritten, or added to when
  *             accumulate_dweight != 0
- *  workspace  device memory, 256-byte aligned, >= the size above
+ *  workspace  device memory, 256-byte aligned, >= dmel_rms_backward_workspace_bytes
+ *             (>= dmel_rms_backward_stored_workspace_bytes: the sums are kept,
+ *             not recomputed, for the second pass)
  * fp32 arithmetic in a fixed order (results repeat bit for bit). */
 int dmel_rms_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels,
                       const uint16_t* table, int32_t d_model, const float* rms_weight,

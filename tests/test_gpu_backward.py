@@ -162,6 +162,17 @@ def _rms_case(dm, lv, n_levels, d, dy_bf16, seed, accumulate=False):
     assert np.all(np.abs(got - ds_want) <= tol), f"max excess {np.max(np.abs(got - ds_want) - tol)}"
     dw_tol = 1e-5 * np.sum(np.abs(dy * s64 * r[:, None]), axis=0) + (np.abs(dw0) * 1e-7 if accumulate else 0)
     assert np.all(np.abs(dw.cpu().numpy() - dw_want) <= dw_tol + 1e-30)
+    # with the larger workspace the second pass streams the stored sums: same bits
+    wsb2 = dm.dmel_rms_backward_stored_workspace_bytes(n, d)
+    assert wsb2 >= wsb + 4 * n * d
+    ws2 = torch.empty(wsb2, dtype=torch.uint8, device="cuda")
+    ds2 = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    dw2 = torch.from_numpy(dw0.copy()).cuda()
+    dm.dmel_rms_backward(lvd, n, n_bins, n_levels, td, d, wd, scale, dyd, dm.DMEL_BF16 if dy_bf16 else dm.DMEL_F32,
+                         ds2, dw2, 1 if accumulate else 0, ws2, wsb2)
+    torch.cuda.synchronize()
+    assert torch.equal(ds2.view(torch.int32), ds.view(torch.int32))
+    assert torch.equal(dw2.view(torch.int32), dw.view(torch.int32))
     return ds
 
 
@@ -211,7 +222,7 @@ def test_full_size_backward_sampled(dm):
     dy = synth.activations_bf16(seed=21, n_tokens=T, channels=d, std=1e-3, device="cuda")
     ds = torch.empty((T, d), dtype=torch.float32, device="cuda")
     dw = torch.empty(d, dtype=torch.float32, device="cuda")
-    wsb = dm.dmel_rms_backward_workspace_bytes(T, d)
+    wsb = dm.dmel_rms_backward_stored_workspace_bytes(T, d)   # the path bench.py times
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     dm.dmel_rms_backward(lv, T, 80, 16, table, d, w, scale, dy, dm.DMEL_BF16, ds, dw, 0, ws, wsb)
     del ws
