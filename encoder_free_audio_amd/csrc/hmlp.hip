@@ -208,8 +208,8 @@ gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, cons
 // SIMD, accumulators in AGPRs).
 //  * Operands go from global memory straight into LDS (16-byte
 //    global_load_lds, no register staging) through a ring of four stages of
-//    K = 32 (32 KB each); the loads of step k + 3 are issued during step k (a
-//    fifth stage measured no faster).
+//    K = 32 (32 KB each); the loads of step k + 3 are issued during steps k
+//    and k + 1 (a fifth stage measured no faster).
 //  * LDS rows are 64 bytes (32 bf16 of K); the 16-byte chunk c of row r sits
 //    in slot c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3: the fragment reads of
 //    any 8 or 16 consecutive rows at one chunk then touch every bank at most
@@ -268,6 +268,13 @@ gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, c
   }
   const char* Ab = reinterpret_cast<const char*>(A + row0 * K);
   const char* Bb = reinterpret_cast<const char*>(B + static_cast<int64_t>(col0) * K);
+  auto issue_half = [&](int kt, int h) {
+    char* sa = smem + (kt % kNStages) * kStageBytes + wave * 64 * kRowBytes + h * kTileBytes;
+    const char* ga = (h == 0 ? Ab : Bb) + static_cast<int64_t>(kt) * (kBTK * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(ga + (h == 0 ? aoff[j] : boff[j]), (lds_void_t*)(sa + j * 16 * kRowBytes), 16, 0, 0);
+  };
   auto issue = [&](int kt) {
     char* sa = smem + (kt % kNStages) * kStageBytes + wave * 64 * kRowBytes;
     char* sb = sa + kTileBytes;
@@ -344,30 +351,39 @@ gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, c
   for (int i = 0; i < kNStages - 1; ++i) issue(min(i, nk - 1));
   sync_stage(kNStages - 2);
   frag(0, 0, 0);
+  // Each stage's loads are split over two sub-steps: its A half after the
+  // barrier of step k (between the products of the second sub-step), its B
+  // half in the first sub-step of step k + 1, so the DMA traffic is spread
+  // over the whole step.  (In step 0 the B half repeats the prologue's loads of
+  // stage 2 with the same data; the wait below then waits a little longer.)
+  // Loads complete in order, so before the barrier of step k the loads of
+  // stage k + 2 are the only ones that may still be in flight.
   for (int kt = 0; kt + 1 < nk; ++kt) {
     pin(0);
     frag(kt, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
+    issue_half(min(kt + kNStages - 2, nk - 1), 1);
     mma(0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     pin(1);
-    // stage kt + 1 certified; stage kt - 1 (read in the previous step) free
     sync_stage(kNStages - 3);
-    issue(min(kt + kNStages - 1, nk - 1));
+    issue_half(min(kt + kNStages - 1, nk - 1), 0);
     frag(kt + 1, 0, 0);
     mma(1);
-    // after the barrier the products start at once; the next sub-step's eight
-    // LDS reads (early, so they are back by the next step) and the eight DMA
-    // loads go between them
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global (DMA) load
+    for (int m = 0; m < 4; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
