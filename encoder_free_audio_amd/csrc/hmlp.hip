@@ -235,11 +235,31 @@ constexpr int kStageBytes = 2 * kTileBytes;   // A + B
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <bool kGelu, bool kOutF32>
-__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// kWM = 4 (the one launched): eight waves (4 x 2) of 2 x 4 MFMA tiles, two
+// waves per SIMD, so one wave's epilogue arithmetic, loads and barrier waits
+// overlap the other's products.  kWM = 2: four waves (2 x 2) of 4 x 4 tiles,
+// one wave per SIMD (fewer LDS fragment reads per product; measured slower
+// for every hMLP and DFT shape).
+constexpr int kEpPitch = 136;   // epilogue LDS row pitch (floats)
+
+template <int kWM>
+constexpr int smem_bytes() {
+  return kNStages * kStageBytes > 2 * kWM * 32 * kEpPitch * 4 ? kNStages * kStageBytes : 2 * kWM * 32 * kEpPitch * 4;
+}
+
+template <int kWM>
+struct GemmShape {
+  static constexpr int TM = 8 / kWM;     // MFMA tile rows per wave
+  static constexpr int RW = 128 / kWM;   // tile rows each wave loads per operand
+  static constexpr int NJ = RW / 16;     // DMA instructions per operand per stage
+};
+
+template <int kWM, bool kGelu, bool kOutF32>
+__global__ void __launch_bounds__(128 * kWM) __attribute__((amdgpu_waves_per_eu(kWM / 2, kWM / 2)))
 gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const float* __restrict__ bias,
                void* __restrict__ C, int64_t M, int N, int K, int tiles_n, int64_t n_tiles) {
-  __shared__ __attribute__((aligned(1024))) char smem[kNStages * kStageBytes];
+  using G = GemmShape<kWM>;
+  __shared__ __attribute__((aligned(1024))) char smem[smem_bytes<kWM>()];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -253,14 +273,14 @@ gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, c
   const int64_t row0 = bm * kBT;
   const int col0 = bn * kBT;
 
-  // this lane's DMA sources: rows wave * 64 + 16 j + (lane >> 2) of the A and B
-  // tiles, logical chunk (lane & 3) ^ f(row); byte offsets from the tiles'
+  // this lane's DMA sources: rows wave * G::RW + 16 j + (lane >> 2) of the A and
+  // B tiles, logical chunk (lane & 3) ^ f(row); byte offsets from the tiles'
   // first rows (< 2^32: 256 rows of at most 2^21 bytes)
   const int lr = lane >> 2;
-  uint32_t aoff[4], boff[4];
+  uint32_t aoff[4], boff[4];   // (first G::NJ used; a fixed size keeps the arrays capturable by the lambdas)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = wave * 64 + 16 * j + lr;
+  for (int j = 0; j < G::NJ; ++j) {
+    const int r = wave * G::RW + 16 * j + lr;
     const int lc = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
     const int64_t ra = row0 + r < M ? r : M - 1 - row0;
     aoff[j] = static_cast<uint32_t>(ra * K * 2 + lc * 16);
@@ -269,22 +289,22 @@ gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, c
   const char* Ab = reinterpret_cast<const char*>(A + row0 * K);
   const char* Bb = reinterpret_cast<const char*>(B + static_cast<int64_t>(col0) * K);
   auto issue_half = [&](int kt, int h) {
-    char* sa = smem + (kt % kNStages) * kStageBytes + wave * 64 * kRowBytes + h * kTileBytes;
+    char* sa = smem + (kt % kNStages) * kStageBytes + wave * G::RW * kRowBytes + h * kTileBytes;
     const char* ga = (h == 0 ? Ab : Bb) + static_cast<int64_t>(kt) * (kBTK * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < G::NJ; ++j)
       __builtin_amdgcn_global_load_lds(ga + (h == 0 ? aoff[j] : boff[j]), (lds_void_t*)(sa + j * 16 * kRowBytes), 16, 0, 0);
   };
   auto issue = [&](int kt) {
-    char* sa = smem + (kt % kNStages) * kStageBytes + wave * 64 * kRowBytes;
+    char* sa = smem + (kt % kNStages) * kStageBytes + wave * G::RW * kRowBytes;
     char* sb = sa + kTileBytes;
     const char* ga = Ab + static_cast<int64_t>(kt) * (kBTK * 2);
     const char* gb = Bb + static_cast<int64_t>(kt) * (kBTK * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < G::NJ; ++j)
       __builtin_amdgcn_global_load_lds(ga + aoff[j], (lds_void_t*)(sa + j * 16 * kRowBytes), 16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < G::NJ; ++j)
       __builtin_amdgcn_global_load_lds(gb + boff[j], (lds_void_t*)(sb + j * 16 * kRowBytes), 16, 0, 0);
   };
   // Wait until this wave's loads of the stage needed next have landed (loads
@@ -292,34 +312,39 @@ gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, c
   // meet the other waves.  One asm with a memory clobber, so no LDS access
   // moves across it and no fence adds a wait for every load in flight.
   auto sync_stage = [&](int later) {
-    if (later == 3) {
+    const int n = later * 2 * G::NJ;   // loads of `later` stages
+    if (n == 24) {
       asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
-    } else if (later == 2) {
+    } else if (n == 16) {
       asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-    } else if (later == 1) {
+    } else if (n == 12) {
+      asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+    } else if (n == 8) {
       asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    } else if (n == 4) {
+      asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
   };
 
   // fragments of sub-step (k, h): rows (lane & 31) + 32 t of this wave's
-  // 128-row blocks, logical chunk 2 h + (lane >> 5)
+  // blocks (32 G::TM rows of A, 128 rows of B), logical chunk 2 h + (lane >> 5)
   const int frow = (lane & 31) * kRowBytes;
   const int fsw = (((lane & 31) >> 1) ^ ((lane & 31) >> 3)) & 3;  // f(row): the block offsets are multiples of 32
-  bf16x8_t fa[2][4], fb[2][4];
+  bf16x8_t fa[2][G::TM], fb[2][4];
   auto frag = [&](int kt, int h, int buf) {
-    const char* sa = smem + (kt % kNStages) * kStageBytes + wm * 128 * kRowBytes + frow;
+    const char* sa = smem + (kt % kNStages) * kStageBytes + wm * 32 * G::TM * kRowBytes + frow;
     const char* sb = smem + (kt % kNStages) * kStageBytes + kTileBytes + wn * 128 * kRowBytes + frow;
     const int off = ((2 * h + (lane >> 5)) ^ fsw) << 4;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) fa[buf][t] = *reinterpret_cast<const bf16x8_t*>(sa + t * 32 * kRowBytes + off);
+    for (int t = 0; t < G::TM; ++t) fa[buf][t] = *reinterpret_cast<const bf16x8_t*>(sa + t * 32 * kRowBytes + off);
 #pragma unroll
     for (int t = 0; t < 4; ++t) fb[buf][t] = *reinterpret_cast<const bf16x8_t*>(sb + t * 32 * kRowBytes + off);
   };
-  f32x16_t acc[4][4];
+  f32x16_t acc[G::TM][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < G::TM; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -332,12 +357,17 @@ gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, c
   // reads below it; scheduling barriers keep each group of products between
   // the reads before it and the wait after it.
   auto pin = [&](int buf) {
-    asm volatile("" : "+v"(fa[buf][0]), "+v"(fa[buf][1]), "+v"(fa[buf][2]), "+v"(fa[buf][3]), "+v"(fb[buf][0]),
-                 "+v"(fb[buf][1]), "+v"(fb[buf][2]), "+v"(fb[buf][3])::"memory");
+    if constexpr (G::TM == 4) {
+      asm volatile("" : "+v"(fa[buf][0]), "+v"(fa[buf][1]), "+v"(fa[buf][2]), "+v"(fa[buf][3]), "+v"(fb[buf][0]),
+                   "+v"(fb[buf][1]), "+v"(fb[buf][2]), "+v"(fb[buf][3])::"memory");
+    } else {
+      asm volatile("" : "+v"(fa[buf][0]), "+v"(fa[buf][1]), "+v"(fb[buf][0]), "+v"(fb[buf][1]), "+v"(fb[buf][2]),
+                   "+v"(fb[buf][3])::"memory");
+    }
   };
   auto mma = [&](int buf) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < G::TM; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][a], fb[buf][c], acc[a][c], 0, 0, 0);
@@ -365,9 +395,9 @@ gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, c
     issue_half(min(kt + kNStages - 2, nk - 1), 1);
     mma(0);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    for (int m = 0; m < G::NJ; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);            // two MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // one global (DMA) load
     }
     __builtin_amdgcn_sched_barrier(0);
     pin(1);
@@ -376,14 +406,14 @@ gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, c
     frag(kt + 1, 0, 0);
     mma(1);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int m = 0; m < G::TM + 4; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    for (int m = 0; m < G::NJ; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, (3 * G::TM - 4) / G::NJ, 0);  // MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                // one global (DMA) load
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -402,14 +432,13 @@ gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, c
   // half-wave writes one row's 128 outputs as one contiguous piece.  Lane
   // layout of a 32 x 32 accumulator: column lane & 31, rows
   // 8 (i / 4) + 4 (lane / 32) + i % 4.
-  constexpr int kEpPitch = 136;
   __syncthreads();  // every wave is done with the operand stages
   float* ep = reinterpret_cast<float*>(smem) + wave * 32 * kEpPitch;
   const int cl = 4 * (lane & 31);
   const int col = col0 + wn * 128 + cl;
   const float4 bb = make_float4(bias[col], bias[col + 1], bias[col + 2], bias[col + 3]);
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
+  for (int a = 0; a < G::TM; ++a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -418,7 +447,7 @@ gemm256_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, c
 #pragma unroll 4
     for (int pr = 0; pr < 16; ++pr) {
       const int r = 2 * pr + (lane >> 5);
-      const int64_t row = row0 + wm * 128 + a * 32 + r;
+      const int64_t row = row0 + wm * 32 * G::TM + a * 32 + r;
       float4 v = *reinterpret_cast<const float4*>(ep + r * kEpPitch + cl);
       v.x += bb.x;
       v.y += bb.y;
@@ -451,15 +480,18 @@ hipError_t gemm(const uint16_t* A, const uint16_t* B, const float* bias, void* C
     const int tiles_n = N / kBT;
     const int64_t n_tiles = ((M + kBT - 1) / kBT) * tiles_n;
     if (n_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const dim3 grid(static_cast<unsigned>(n_tiles)), block(kGemmThreads);
+    const dim3 grid(static_cast<unsigned>(n_tiles));
+    // eight waves (two per SIMD): measured faster than four waves of 4 x 4
+    // tiles for every stage shape (the stem 19.9 -> 17.8 ms)
+    const dim3 block(512);
     if (gelu && !out_f32) {
-      hipLaunchKernelGGL((gemm256_kernel<true, false>), grid, block, 0, stream, A, B, bias, C, M, N, K, tiles_n, n_tiles);
+      hipLaunchKernelGGL((gemm256_kernel<4, true, false>), grid, block, 0, stream, A, B, bias, C, M, N, K, tiles_n, n_tiles);
     } else if (gelu) {
-      hipLaunchKernelGGL((gemm256_kernel<true, true>), grid, block, 0, stream, A, B, bias, C, M, N, K, tiles_n, n_tiles);
+      hipLaunchKernelGGL((gemm256_kernel<4, true, true>), grid, block, 0, stream, A, B, bias, C, M, N, K, tiles_n, n_tiles);
     } else if (!out_f32) {
-      hipLaunchKernelGGL((gemm256_kernel<false, false>), grid, block, 0, stream, A, B, bias, C, M, N, K, tiles_n, n_tiles);
+      hipLaunchKernelGGL((gemm256_kernel<4, false, false>), grid, block, 0, stream, A, B, bias, C, M, N, K, tiles_n, n_tiles);
     } else {
-      hipLaunchKernelGGL((gemm256_kernel<false, true>), grid, block, 0, stream, A, B, bias, C, M, N, K, tiles_n, n_tiles);
+      hipLaunchKernelGGL((gemm256_kernel<4, false, true>), grid, block, 0, stream, A, B, bias, C, M, N, K, tiles_n, n_tiles);
     }
     return hipGetLastError();
   }
