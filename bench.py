@@ -130,7 +130,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs the dMel front end on one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards by clips with no collective, see DESIGN.md", file=sys.stderr)
+              "clips, streams and sequences are independent, so more GPUs would each take a share of the clips "
+              "with no collective during the forward", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

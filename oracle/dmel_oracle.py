@@ -341,7 +341,7 @@ def forward(x: np.ndarray, table_bits: np.ndarray, rms_weight=None, eps: float =
 # ---------------------------------------------------------------------------
 # Backward (training the front end jointly with the model: "Inside Inkling:
 # Audio Design", Coda, the front ends are frozen in post-training and training
-# them is experimental; the survey's next row).  The pages give no backward;
+# them is experimental).  The pages give no backward;
 # it is the derivative of the forward above.
 #
 # RMSNorm: y = s * r * w with r = 1 / sqrt(mean(s^2) + eps), so for an
