@@ -97,6 +97,18 @@ __device__ __forceinline__ void dft8(float2 (&v)[8]) {
   v[7] = csub(e3, w3o);
 }
 
+// Orders the LDS accesses of one wavefront.  Every frame's buffer is written
+// and read only by its own 32 threads, which lie in one wavefront, and a
+// wavefront's LDS operations complete in issue order; so between the FFT
+// passes it is enough to keep the compiler from moving memory operations
+// across this point, and the four wavefronts of a workgroup run those passes
+// without waiting for each other.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Clip of global frame g: the largest c with frame_off[c] <= g.
 __device__ __forceinline__ int clip_of(const int64_t* frame_off, int n_clips, int64_t g) {
   int lo = 0, hi = n_clips;
@@ -131,49 +143,35 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
   // per CU); the constant tables are read from global memory (uniform indices
   // become scalar loads, the rest hit the L1).
   __shared__ float2 zbuf[kFramesPerBlock * kSlots];
-  __shared__ int64_t s_base[kFramesPerBlock];
-  __shared__ int s_clip[kFramesPerBlock];
-  __shared__ int s_first[kFramesPerBlock];
-  __shared__ int s_valid[kFramesPerBlock];
-  __shared__ int s_fast[kFramesPerBlock];
 
   const int tid = threadIdx.x;
-  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kFramesPerBlock;
-
-  const float2* __restrict__ tw = tabs.tw800;
-  if (tid < kFramesPerBlock) {
-    const int64_t g = g0 + tid;
-    const int valid = g < n_frames;
-    int c = 0;
-    int64_t base = 0;
-    int first = 0;
-    if (valid) {
-      c = clip_of(frame_off, n_clips, g);
-      const int64_t t = g - frame_off[c];
-      base = sample_off[c] + kHop * t - kHop;
-      first = (t == 0);
-    }
-    // the whole frame lies inside the audio and 8-byte reads are aligned
-    const int fast = valid && !first && base >= 0 && base + kWindow <= n_samples_total &&
-                     (reinterpret_cast<uintptr_t>(audio + base) & 7) == 0;
-    s_valid[tid] = valid;
-    s_clip[tid] = c;
-    s_base[tid] = base;
-    s_first[tid] = first;
-    s_fast[tid] = fast;
-  }
-  __syncthreads();
-
   const int f = tid >> 5;      // frame within the block
   const int lane = tid & 31;   // n1 in pass A, k2 in pass B
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kFramesPerBlock;
   float2* zf = zbuf + f * kSlots;
+  const float2* __restrict__ tw = tabs.tw800;
+
+  // the frame's clip and first sample (each of its 32 threads finds them)
+  const int64_t g = g0 + f;
+  const bool valid = g < n_frames;
+  int clip = 0;
+  int64_t base = 0;
+  bool first = false;
+  if (valid) {
+    clip = clip_of(frame_off, n_clips, g);
+    const int64_t t = g - frame_off[clip];
+    base = sample_off[clip] + kHop * t - kHop;
+    first = (t == 0);
+  }
+  // the whole frame lies inside the audio and 8-byte reads are aligned
+  const bool fast = valid && !first && base >= 0 && base + kWindow <= n_samples_total &&
+                    (reinterpret_cast<uintptr_t>(audio + base) & 7) == 0;
 
   // ---- 1 + 2a. windowed samples, 25-point DFTs over n2 for each n1 --------
   {
     float2 x[25];
-    const int64_t base = s_base[f];
     const float2* w2 = reinterpret_cast<const float2*>(tabs.window);
-    if (s_fast[f]) {
+    if (fast) {
       const float2* src = reinterpret_cast<const float2*>(audio + base);
 #pragma unroll
       for (int n2 = 0; n2 < 25; ++n2) {
@@ -183,8 +181,7 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
         x[n2] = make_float2(a.x * w.x, a.y * w.y);
       }
     } else {
-      const int valid = s_valid[f], first = s_first[f];
-      const int64_t cbase = static_cast<int64_t>(s_clip[f]) * kHop;
+      const int64_t cbase = static_cast<int64_t>(clip) * kHop;
 #pragma unroll
       for (int n2 = 0; n2 < 25; ++n2) {
         const int m = lane + 32 * n2;
@@ -233,7 +230,7 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
 #pragma unroll
     for (int k2 = 0; k2 < 25; ++k2) zf[lane + 33 * k2] = y[k2];
   }
-  __syncthreads();
+  wave_sync();
 
   // ---- 2b. 32-point DFTs over n1 for each k2 ---------------------------
   {
@@ -259,7 +256,7 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
     // 4-point DFTs over q for each r: output k1 = r + 8 s
 #pragma unroll
     for (int r = 0; r < 8; ++r) dft4(v[0][r], v[1][r], v[2][r], v[3][r]);
-    __syncthreads();
+    wave_sync();
     if (active) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
@@ -268,25 +265,23 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
       }
     }
   }
-  __syncthreads();
+  wave_sync();
 
   // ---- 3. real-spectrum split and power ---------------------------------
   // E[k] = (Z[k] + conj Z[800-k]) / 2, O[k] = (Z[k] - conj Z[800-k]) / 2i,
-  // X[k] = E + W1600^k O and X[800-k] = conj(E - W1600^k O), k = 0..400.
-  constexpr int kPairs = kHalf / 2 + 1;  // 401
-  constexpr int kItems = kFramesPerBlock * kPairs;
-  constexpr int kPer = (kItems + kThreads - 1) / kThreads;
+  // X[k] = E + W1600^k O and X[800-k] = conj(E - W1600^k O), k = 0..400;
+  // the frame's thread `lane` takes k = lane + 32 m.
+  constexpr int kPairs = kHalf / 2 + 1;            // 401
+  constexpr int kPer = (kPairs + 31) / 32;         // 13
   float p_lo[kPer], p_hi[kPer];
 #pragma unroll
   for (int m = 0; m < kPer; ++m) {
-    const int it = tid + kThreads * m;
+    const int k = lane + 32 * m;
     p_lo[m] = 0.0f;
     p_hi[m] = 0.0f;
-    if (it < kItems) {
-      const int ff = it / kPairs;
-      const int k = it - ff * kPairs;
-      const float2 zk = zbuf[ff * kSlots + k];
-      const float2 zm = zbuf[ff * kSlots + (k == 0 ? 0 : kHalf - k)];
+    if (k < kPairs) {
+      const float2 zk = zf[k];
+      const float2 zm = zf[k == 0 ? 0 : kHalf - k];
       const float2 e = make_float2(0.5f * (zk.x + zm.x), 0.5f * (zk.y - zm.y));
       const float2 o = make_float2(0.5f * (zk.y + zm.y), -0.5f * (zk.x - zm.x));
       const float2 wo = cmul(tabs.tw1600[k], o);  // L1-cached table
@@ -295,21 +290,19 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
       p_hi[m] = x2.x * x2.x + x2.y * x2.y;
     }
   }
-  __syncthreads();
+  wave_sync();
   {
-    float* pf = reinterpret_cast<float*>(zbuf);
+    float* pw = reinterpret_cast<float*>(zf);  // the frame's 801 powers
 #pragma unroll
     for (int m = 0; m < kPer; ++m) {
-      const int it = tid + kThreads * m;
-      if (it < kItems) {
-        const int ff = it / kPairs;
-        const int k = it - ff * kPairs;
-        pf[2 * ff * kSlots + k] = p_lo[m];
-        pf[2 * ff * kSlots + kHalf - k] = p_hi[m];
+      const int k = lane + 32 * m;
+      if (k < kPairs) {
+        pw[k] = p_lo[m];
+        pw[kHalf - k] = p_hi[m];
       }
     }
   }
-  __syncthreads();
+  __syncthreads();  // the mel step works across the block's frames
 
   // ---- 4. mel: segment sums, then filters, log, clamp, quantize ----------
   {
@@ -324,9 +317,12 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
     const int n_pairs = (n_seg + 1) / 2;  // 41: (0,80) .. (39,41), (40)
     const int* __restrict__ seg = tabs.seg_start;
     const float bin_hz = static_cast<float>(kSampleRate) / kNfft;
+    // pair-major order: the lanes of a wavefront take neighbouring pairs, whose
+    // segments have similar lengths, so their loops run about the same count
+    static_assert(kFramesPerBlock == 8, "pair-major order assumes 8 frames");
     for (int it = tid; it < kFramesPerBlock * n_pairs; it += kThreads) {
-      const int ff = it / n_pairs;
-      const int pr = it - ff * n_pairs;
+      const int pr = it >> 3;
+      const int ff = it & 7;
       const float* p = pf + 2 * ff * kSlots;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -336,26 +332,56 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
         const float inv = tabs.seg_inv[sg];
         const float lo = tabs.seg_lo[sg], hi = tabs.seg_hi[sg];
         float a = 0.0f, c = 0.0f;
-        for (int k = seg[sg]; k < seg[sg + 1]; ++k) {
-          const float fk = bin_hz * static_cast<float>(k);
-          const float pk = p[k];
-          a = fmaf((fk - lo) * inv, pk, a);  // filter sg, rising side
-          c = fmaf((hi - fk) * inv, pk, c);  // filter sg - 1, falling side
+        const int k0 = seg[sg], k1 = seg[sg + 1];
+        float fk = bin_hz * static_cast<float>(k0);  // 10 k Hz, exact
+        // four bins per step, their reads issued together, then one step over
+        // the last 0..3 bins whose reads past the segment (at most index 802,
+        // inside the frame's slots) are dropped
+        int k = k0;
+        for (; k + 4 <= k1; k += 4) {
+          float q[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) q[i] = p[k + i];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            a = fmaf(fk - lo, q[i], a);  // filter sg, rising side
+            c = fmaf(hi - fk, q[i], c);  // filter sg - 1, falling side
+            fk += bin_hz;
+          }
         }
-        pf[2 * ff * kSlots + kAOff + sg] = a;
-        pf[2 * ff * kSlots + kCOff + sg] = c;
+        if (k < k1) {
+          float q[3];
+#pragma unroll
+          for (int i = 0; i < 3; ++i) q[i] = p[k + i];
+#pragma unroll
+          for (int i = 0; i < 3; ++i) {
+            const float pk = k + i < k1 ? q[i] : 0.0f;
+            a = fmaf(fk - lo, pk, a);
+            c = fmaf(hi - fk, pk, c);
+            fk += bin_hz;
+          }
+        }
+        pf[2 * ff * kSlots + kAOff + sg] = a * inv;
+        pf[2 * ff * kSlots + kCOff + sg] = c * inv;
       }
     }
     __syncthreads();
-    for (int it = tid; it < kFramesPerBlock * n_mels; it += kThreads) {
-      const int ff = it / n_mels;
+    // output it = ff * n_mels + j of the block; ff = floor((it + 0.5) / n_mels)
+    // in fp32 is exact: it < 1024 puts the product within 1.3e-4 of the
+    // quotient, whose distance to an integer is at least 0.5 / 128
+    const int64_t n_valid = n_frames - g0 < kFramesPerBlock ? n_frames - g0 : kFramesPerBlock;
+    const int n_out = static_cast<int>(n_valid) * n_mels;
+    const float inv_n = 1.0f / static_cast<float>(n_mels);
+    float* lm_out = logmel != nullptr ? logmel + g0 * n_mels : nullptr;
+    uint8_t* lv_out = levels != nullptr ? levels + g0 * n_mels : nullptr;
+    for (int it = tid; it < n_out; it += kThreads) {
+      const int ff = static_cast<int>((static_cast<float>(it) + 0.5f) * inv_n);
       const int j = it - ff * n_mels;
-      const int64_t g = g0 + ff;
-      if (g >= n_frames) continue;
       const float m = pf[2 * ff * kSlots + kAOff + j] + pf[2 * ff * kSlots + kCOff + j + 1];
-      const float l = logf(fmaxf(m, kLogFloor));
-      if (logmel != nullptr) logmel[g * n_mels + j] = l;
-      if (levels != nullptr) levels[g * n_mels + j] = static_cast<uint8_t>(quantize(l, tabs));
+      // ln m = ln 2 * log2 m with the hardware log2 (about 1 ulp; m >= 1e-10 is normal)
+      const float l = 0.69314718055994531f * __builtin_amdgcn_logf(fmaxf(m, kLogFloor));
+      if (lm_out != nullptr) lm_out[it] = l;
+      if (lv_out != nullptr) lv_out[it] = static_cast<uint8_t>(quantize(l, tabs));
     }
   }
 }
