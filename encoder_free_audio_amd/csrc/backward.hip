@@ -132,19 +132,36 @@ __device__ __forceinline__ void add4(float4& a, const float4& v) {
   a.w += v.w;
 }
 
-// Adds the tokens of one level group (list entries k .. e-1, token order; the
-// group is padded to a multiple of four with the -0.0 row).
-__device__ __forceinline__ void add_group(float4& acc, const char* tile_lane, const uint32_t* __restrict__ lst, int k,
-                                          int e) {
-  for (; k < e; k += 4) {
-    const float4 v0 = *reinterpret_cast<const float4*>(tile_lane + lst[k]);
-    const float4 v1 = *reinterpret_cast<const float4*>(tile_lane + lst[k + 1]);
-    const float4 v2 = *reinterpret_cast<const float4*>(tile_lane + lst[k + 2]);
-    const float4 v3 = *reinterpret_cast<const float4*>(tile_lane + lst[k + 3]);
-    add4(acc, v0);
-    add4(acc, v1);
-    add4(acc, v2);
-    add4(acc, v3);
+// Adds one chunk of this wave's bin: the list's groups of four entries in
+// order (level l's groups, in token order, before level l + 1's), each into
+// acc[l].  The scalar read of a group's entries is issued one group ahead, so
+// that it is answered while the previous group's tile rows are read and each
+// group waits once, for its own rows.
+__device__ __forceinline__ void add_chunk(float4 (&acc)[16], const char* tile_lane, const uint32_t* __restrict__ lst,
+                                          const uint32_t* __restrict__ st) {
+  uint32_t bound[17];
+#pragma unroll
+  for (int l = 0; l <= 16; ++l) bound[l] = st[l];
+  const int end = static_cast<int>(bound[16]);  // >= 4: a chunk holds at least one token
+  uint4 an = *reinterpret_cast<const uint4*>(lst);
+  int k = 0;
+#pragma unroll
+  for (int l = 0; l < 16; ++l) {
+    const int e = static_cast<int>(bound[l + 1]);
+    for (; k < e; k += 4) {
+      const uint4 a = an;
+      // the next group's entries (the last group's again at the end: always
+      // inside the list)
+      an = *reinterpret_cast<const uint4*>(lst + (k + 4 < end ? k + 4 : end - 4));
+      const float4 v0 = *reinterpret_cast<const float4*>(tile_lane + a.x);
+      const float4 v1 = *reinterpret_cast<const float4*>(tile_lane + a.y);
+      const float4 v2 = *reinterpret_cast<const float4*>(tile_lane + a.z);
+      const float4 v3 = *reinterpret_cast<const float4*>(tile_lane + a.w);
+      add4(acc[l], v0);
+      add4(acc[l], v1);
+      add4(acc[l], v2);
+      add4(acc[l], v3);
+    }
   }
 }
 
@@ -192,12 +209,7 @@ scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_l
     if (ch + 1 < ch1) tile_load<kBf16>(r, g, n_tokens, d_model, (ch + 1) * kChunk, c_strip, tid);
     if (bin_ok) {
       const int64_t pair = ch * n_bins + j;
-      const uint32_t* lst = lists + pair * kListPitch;
-      const uint32_t* st = starts + pair * kOffPitch;
-#pragma unroll
-      for (int l = 0; l < 16; ++l) {
-        if (l < n_levels) add_group(acc[l], tile_lane, lst, static_cast<int>(st[l]), static_cast<int>(st[l + 1]));
-      }
+      add_chunk(acc, tile_lane, lists + pair * kListPitch, starts + pair * kOffPitch);
     }
     __syncthreads();  // the tile is overwritten next
   }
