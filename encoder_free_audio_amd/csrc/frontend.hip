@@ -163,20 +163,54 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
     base = sample_off[clip] + kHop * t - kHop;
     first = (t == 0);
   }
-  // the whole frame lies inside the audio and 8-byte reads are aligned
-  const bool fast = valid && !first && base >= 0 && base + kWindow <= n_samples_total &&
-                    (reinterpret_cast<uintptr_t>(audio + base) & 7) == 0;
+  // Samples [0, 800) of the frame come from `lo` (the audio, or for a clip's
+  // first frame its carry, or zeros without one) and [800, 1600) from `hi`
+  // (the audio), whenever the frame lies inside the audio, which offsets that
+  // describe the audio always give; other frames check every sample.
+  const float* lo = nullptr;
+  const float* hi = nullptr;
+  bool inside = false;
+  if (valid && base + kHop >= 0 && base + kWindow <= n_samples_total && (first || base >= 0)) {
+    inside = true;
+    hi = audio + (base + kHop);
+    if (!first) lo = audio + base;
+    else if (carry != nullptr) lo = carry + static_cast<int64_t>(clip) * kHop;
+  }
+  // the usual case: both sources present and 8-byte aligned
+  const bool paired = inside && lo != nullptr &&
+                      ((reinterpret_cast<uintptr_t>(lo) | reinterpret_cast<uintptr_t>(hi)) & 7) == 0;
 
   // ---- 1 + 2a. windowed samples, 25-point DFTs over n2 for each n1 --------
   {
     float2 x[25];
     const float2* w2 = reinterpret_cast<const float2*>(tabs.window);
-    if (fast) {
-      const float2* src = reinterpret_cast<const float2*>(audio + base);
+    // sample pair m < 400 comes from lo, m >= 400 from hi (n2 = 12 straddles:
+    // lanes 0..15 read lo)
+    if (paired) {
+      const float2* l2 = reinterpret_cast<const float2*>(lo);
+      const float2* h2 = reinterpret_cast<const float2*>(hi);
 #pragma unroll
       for (int n2 = 0; n2 < 25; ++n2) {
         const int m = lane + 32 * n2;
-        const float2 a = src[m];
+        float2 a;
+        if (n2 < 12) a = l2[m];
+        else if (n2 > 12) a = h2[m - kHop / 2];
+        else a = lane < 16 ? l2[m] : h2[m - kHop / 2];
+        const float2 w = w2[m];
+        x[n2] = make_float2(a.x * w.x, a.y * w.y);
+      }
+    } else if (inside) {
+      // no carry (zeros) or unaligned sources: 4-byte reads
+#pragma unroll
+      for (int n2 = 0; n2 < 25; ++n2) {
+        const int m = lane + 32 * n2;
+        const bool from_lo = n2 < 12 || (n2 == 12 && lane < 16);
+        float2 a = make_float2(0.0f, 0.0f);
+        if (!from_lo) {
+          a = make_float2(hi[2 * m - kHop], hi[2 * m - kHop + 1]);
+        } else if (lo != nullptr) {
+          a = make_float2(lo[2 * m], lo[2 * m + 1]);
+        }
         const float2 w = w2[m];
         x[n2] = make_float2(a.x * w.x, a.y * w.y);
       }
