@@ -206,6 +206,31 @@ constexpr int kScaleTok = 2;                            // tokens per thread
 constexpr int kScaleBlock = kScaleThreads * kScaleTok;  // tokens per workgroup
 constexpr int kGPitch = kRows + 17;  // staged row pitch (floats): spreads the 16 rows over the banks
 
+// Stages rows c0 .. c0 + 15 of G, columns c0 .. 1279, at g_s[r * kGPitch +
+// c - c0]: a workgroup of 1024 threads gives each row 64 threads, which read
+// 4 columns per step (one 16-byte read when G is 16-byte aligned), with no
+// index division.
+__device__ __forceinline__ void stage_gram_rows(float* g_s, const float* __restrict__ gram, int c0, int tid) {
+  const int r = tid >> 6;  // 0..15
+  const int q = tid & 63;
+  const float* src = gram + static_cast<int64_t>(c0 + r) * kRows + c0;
+  float* dst = g_s + r * kGPitch;
+  const int width = kRows - c0;  // a multiple of 16
+  const bool vec = (reinterpret_cast<uintptr_t>(gram) & 15) == 0;
+  for (int c = 4 * q; c < width; c += 256) {
+    float4 v;
+    if (vec) {
+      v = *reinterpret_cast<const float4*>(src + c);
+    } else {
+      v = make_float4(src[c], src[c + 1], src[c + 2], src[c + 3]);
+    }
+    dst[c] = v.x;
+    dst[c + 1] = v.y;
+    dst[c + 2] = v.z;
+    dst[c + 3] = v.w;
+  }
+}
+
 // Off-diagonal terms q = 1..qlim of one staged row block (q = bin offset from
 // the block's bin).  QMAX bounds qlim for the range of bins the caller is in,
 // so the loop is fully unrolled with static register indices; terms past
@@ -255,13 +280,8 @@ rms_scale_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bin
   }
   for (int j = 0; j < kMels; ++j) {
     const int c0 = kLevels * j;
-    const int width = kRows - c0;
     __syncthreads();
-    for (int i = tid; i < 16 * width; i += kScaleThreads) {
-      const int r = i / width;
-      const int c = i - r * width;
-      g_s[r * kGPitch + c] = gram[static_cast<int64_t>(c0 + r) * kRows + c0 + c];
-    }
+    stage_gram_rows(g_s, gram, c0, tid);
     __syncthreads();
     // rot byte q = level of bin j + q; staged column of bin j + q, level L: 16 q + L
     const float* row[kScaleTok];
@@ -378,6 +398,7 @@ rms_scale_direct_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, in
 // real term: a sum that starts at +0.0 never becomes -0.0), so every byte
 // index is static and all lookups are independent.
 constexpr int kBinTok = 1024;
+static_assert(kBinTok == 1024 && kScaleThreads == 1024, "stage_gram_rows gives each of 16 rows 64 threads");
 
 template <bool kAny>
 __global__ void __launch_bounds__(kBinTok)
@@ -389,12 +410,7 @@ rms_bin_partials_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, in
   const int64_t t = static_cast<int64_t>(blockIdx.x % static_cast<unsigned>(n_chunks)) * kBinTok + tid;
   const bool active = t < n_tokens;
   const int c0 = kLevels * j;
-  const int width = kRows - c0;
-  for (int i = tid; i < 16 * width; i += kBinTok) {
-    const int r = i / width;
-    const int c = i - r * width;
-    g_s[r * kGPitch + c] = gram[static_cast<int64_t>(c0 + r) * kRows + c0 + c];
-  }
+  stage_gram_rows(g_s, gram, c0, tid);
   uint32_t lw[20];
   if (active && kAny) {
     load_levels_any(lw, levels, t, n_bins, static_cast<uint32_t>(n_levels - 1));
