@@ -417,32 +417,34 @@ __global__ void __launch_bounds__(256)
 rms_ds_stream_kernel(const float* __restrict__ s, const void* __restrict__ dy, const float* __restrict__ rms_weight,
                      const float* __restrict__ rms_scale, const float* __restrict__ coef, int64_t n_tokens,
                      int d_model, float* __restrict__ ds) {
+  // a workgroup takes whole tokens (their scale and coefficient are uniform
+  // loads), its threads 4 columns each
   const int q4 = d_model / 4;
-  const int64_t total = n_tokens * q4;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t t = i / q4;
-    const int c = static_cast<int>(i - t * q4) * 4;
+  for (int64_t t = blockIdx.x; t < n_tokens; t += gridDim.x) {
     const float r = rms_scale[t], cf = coef[t];
-    const float4 sv = reinterpret_cast<const float4*>(s)[i];
-    float gr[4];
-    if (kDyBf16) {
-      const uint2 h = reinterpret_cast<const uint2*>(dy)[i];
-      gr[0] = bf16_to_f32(h.x & 0xFFFFu);
-      gr[1] = bf16_to_f32(h.x >> 16);
-      gr[2] = bf16_to_f32(h.y & 0xFFFFu);
-      gr[3] = bf16_to_f32(h.y >> 16);
-    } else {
-      const float4 g = reinterpret_cast<const float4*>(dy)[i];
-      gr[0] = g.x;
-      gr[1] = g.y;
-      gr[2] = g.z;
-      gr[3] = g.w;
+    const int64_t row = t * q4;
+    for (int c4 = threadIdx.x; c4 < q4; c4 += 256) {
+      const int64_t i = row + c4;
+      const float4 sv = reinterpret_cast<const float4*>(s)[i];
+      float gr[4];
+      if (kDyBf16) {
+        const uint2 h = reinterpret_cast<const uint2*>(dy)[i];
+        gr[0] = bf16_to_f32(h.x & 0xFFFFu);
+        gr[1] = bf16_to_f32(h.x >> 16);
+        gr[2] = bf16_to_f32(h.y & 0xFFFFu);
+        gr[3] = bf16_to_f32(h.y >> 16);
+      } else {
+        const float4 g = reinterpret_cast<const float4*>(dy)[i];
+        gr[0] = g.x;
+        gr[1] = g.y;
+        gr[2] = g.z;
+        gr[3] = g.w;
+      }
+      const float4 w = reinterpret_cast<const float4*>(rms_weight)[c4];
+      reinterpret_cast<float4*>(ds)[i] =
+          make_float4(fmaf(-cf, sv.x, r * (w.x * gr[0])), fmaf(-cf, sv.y, r * (w.y * gr[1])),
+                      fmaf(-cf, sv.z, r * (w.z * gr[2])), fmaf(-cf, sv.w, r * (w.w * gr[3])));
     }
-    const float4 w = *reinterpret_cast<const float4*>(rms_weight + c);
-    reinterpret_cast<float4*>(ds)[i] =
-        make_float4(fmaf(-cf, sv.x, r * (w.x * gr[0])), fmaf(-cf, sv.y, r * (w.y * gr[1])),
-                    fmaf(-cf, sv.z, r * (w.z * gr[2])), fmaf(-cf, sv.w, r * (w.w * gr[3])));
   }
 }
 
@@ -594,8 +596,7 @@ hipError_t launch_rms_backward(const uint8_t* levels, int64_t n_tokens, int n_bi
     hipLaunchKernelGGL(rms_coef_kernel, dim3(static_cast<unsigned>((n_tokens + 255) / 256)), dim3(256), 0, stream,
                        dot_part, rms_scale, n_tokens, n_groups, d_model, coef);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t items = n_tokens * (d_model / 4);
-    const unsigned sb = static_cast<unsigned>(std::min<int64_t>((items + 255) / 256, 256 * 64));
+    const unsigned sb = static_cast<unsigned>(std::min<int64_t>(n_tokens, 256 * 64));
     if (dy_bf16) {
       hipLaunchKernelGGL(rms_ds_stream_kernel<true>, dim3(sb), dim3(256), 0, stream, s_store, dy, rms_weight,
                          rms_scale, coef, n_tokens, d_model, ds);
