@@ -292,10 +292,32 @@ __device__ __forceinline__ void load_dy(float (&gr)[kStrip], const void* dy, int
   }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+// Sums each of 16 values over the wavefront's 64 lanes with a transposing
+// butterfly: every exchange halves the number of values a lane carries, so 17
+// exchanges do the work of 96.  Afterwards lane L holds the total of value
+// (L >> 2) & 15 (and so do L ^ 1, L ^ 2, L ^ 3).
+__device__ __forceinline__ float wave_sum16(const float (&q)[16], int lane) {
+  float a[8], b[4], c[2];
+  const bool h5 = (lane & 32) != 0, h4 = (lane & 16) != 0, h3 = (lane & 8) != 0, h2 = (lane & 4) != 0;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  for (int i = 0; i < 8; ++i) {
+    const float send = h5 ? q[i] : q[8 + i];
+    a[i] = (h5 ? q[8 + i] : q[i]) + __shfl_xor(send, 32, 64);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float send = h4 ? a[i] : a[4 + i];
+    b[i] = (h4 ? a[4 + i] : a[i]) + __shfl_xor(send, 16, 64);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float send = h3 ? b[i] : b[2 + i];
+    c[i] = (h3 ? b[2 + i] : b[i]) + __shfl_xor(send, 8, 64);
+  }
+  float d = (h2 ? c[1] : c[0]) + __shfl_xor(h2 ? c[0] : c[1], 4, 64);
+  d += __shfl_xor(d, 2, 64);
+  d += __shfl_xor(d, 1, 64);
+  return d;
 }
 
 // Pass 1: per token, sum_c w_c dy_c s_c over the workgroup's strips (dot_part
@@ -340,12 +362,8 @@ rms_dot_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins,
                        dot = fmaf(rms_weight[col0 + c] * gr[c], acc[c], dot);
                        q[c] = (gr[c] * acc[c]) * r;
                      }
-#pragma unroll
-                     for (int c = 0; c < kStrip; ++c) q[c] = wave_sum(q[c]);
-                     if ((tid & 63) == 0) {
-#pragma unroll
-                       for (int c = 0; c < kStrip; ++c) red[tid >> 6][c] = q[c];
-                     }
+                     const float qs = wave_sum16(q, tid & 63);
+                     if ((tid & 3) == 0) red[tid >> 6][(tid >> 2) & 15] = qs;
                      __syncthreads();
                      if (tid < kStrip) {
                        float v = 0.0f;
