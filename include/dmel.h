@@ -32,8 +32,10 @@
  *    frame_off[0] = 0 and frame_off[c+1] - frame_off[c] =
  *    (sample_off[c+1] - sample_off[c]) / 800.  Both arrays are device int64
  *    [n_clips + 1] and must be non-decreasing.  Offsets that break these rules
- *    give unspecified values but never an out-of-bounds access: every sample
- *    read is bounds-checked against n_samples_total.
+ *    never cause an out-of-bounds access: a frame that does not lie inside
+ *    [0, n_samples_total) has every sample bounds-checked, and samples outside
+ *    the audio read as zeros (a clip reaching past either end gives the
+ *    log-mel of its zero-extended copy).
  *  - bf16 values travel as their uint16 bit patterns.  bf16 outputs are
  *    rounded to nearest-even.
  */

@@ -171,6 +171,45 @@ def test_ragged_clips_with_carry(env, table):
         P.check_levels(lv, ora_lm, o.quantize(ora_lm), gpu_lm=lm)
 
 
+@pytest.mark.parametrize("so", [[-1000, -200, 7600], [600, 1400, 8800]])
+def test_offsets_outside_the_audio(env, so):
+    # Offsets that do not describe the audio (clips starting before sample 0,
+    # a clip ending past the last sample; 10 frames over 8000 samples, as many
+    # as the host accepts): the kernels bounds-check every sample of such
+    # frames and read samples outside the audio as zeros, so each clip gives
+    # the log-mel of its zero-extended copy.
+    dm, ctx = env
+    rng = np.random.default_rng(41)
+    n_total = 8000
+    audio = (rng.standard_normal(n_total) * 0.1).astype(np.float32)
+    fo = [0, (so[1] - so[0]) // 800, (so[1] - so[0]) // 800 + (so[2] - so[1]) // 800]
+    T = fo[-1]
+
+    def extended(a, b):
+        out = np.zeros(b - a, np.float32)
+        lo, hi = max(a, 0), min(b, n_total)
+        if hi > lo:
+            out[lo - a:hi - a] = audio[lo:hi]
+        return out
+
+    clips = [extended(so[0], so[1]), extended(so[1], so[2])]
+    carry = (rng.standard_normal((2, 800)) * 0.1).astype(np.float32)
+    so_d = torch.tensor(so, dtype=torch.int64, device="cuda")
+    fo_d = torch.tensor(fo, dtype=torch.int64, device="cuda")
+    for use_carry in (False, True):
+        print(f"case: offsets {so} around {n_total} samples, carry={use_carry}", flush=True)
+        lm = torch.empty((T, 80), dtype=torch.float32, device="cuda")
+        lv = torch.empty((T, 80), dtype=torch.uint8, device="cuda")
+        c = P.to_dev(carry) if use_carry else None
+        dm.dmel_frames(ctx, P.to_dev(audio), n_total, so_d, fo_d, 2, T, c, lm)
+        dm.dmel_levels(ctx, P.to_dev(audio), n_total, so_d, fo_d, 2, T, c, lv)
+        torch.cuda.synchronize()
+        ora_lm = np.concatenate([o.log_mel(clips[k], carry[k] if use_carry else None) for k in range(2)])
+        lm_np, lv_np = lm.cpu().numpy(), lv.cpu().numpy()
+        P.check_logmel(lm_np, ora_lm)
+        P.check_levels(lv_np, ora_lm, o.quantize(ora_lm), gpu_lm=lm_np)
+
+
 def test_streaming_equals_batch(env, table):
     dm, ctx = env
     S, K = 37, 12
