@@ -109,8 +109,17 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Clip of global frame g: the largest c with frame_off[c] <= g.
-__device__ __forceinline__ int clip_of(const int64_t* frame_off, int n_clips, int64_t g) {
+// Clip of global frame g: the largest c with frame_off[c] <= g.  The first
+// guess, (g + 0.5) * n_clips / n_frames, is the clip when every clip has the
+// same number of frames F (the guess then lies at least 0.5 / F from an
+// integer): one round of reads instead of log2(n_clips) dependent ones for
+// uniform batches and streaming steps.  A clip c with frame_off[c] <= g <
+// frame_off[c + 1] is the answer because the offsets do not decrease; any
+// other guess falls back to binary search.
+__device__ __forceinline__ int clip_of(const int64_t* frame_off, int n_clips, double clip_rate, int64_t g) {
+  int c = static_cast<int>((static_cast<double>(g) + 0.5) * clip_rate);
+  c = c < 0 ? 0 : (c < n_clips - 1 ? c : n_clips - 1);
+  if (frame_off[c] <= g && g < frame_off[c + 1]) return c;
   int lo = 0, hi = n_clips;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -137,7 +146,7 @@ __device__ __forceinline__ int quantize(float l, const FrontTables& t) {
 __global__ void __launch_bounds__(kThreads)
 frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_samples_total,
                 const int64_t* __restrict__ sample_off, const int64_t* __restrict__ frame_off,
-                int n_clips, int64_t n_frames, const float* __restrict__ carry,
+                int n_clips, int64_t n_frames, double clip_rate, const float* __restrict__ carry,
                 float* __restrict__ logmel, uint8_t* __restrict__ levels) {
   // Only the frames' working buffer lives in LDS (52.8 KB: three workgroups
   // per CU); the constant tables are read from global memory (uniform indices
@@ -158,7 +167,7 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
   int64_t base = 0;
   bool first = false;
   if (valid) {
-    clip = clip_of(frame_off, n_clips, g);
+    clip = clip_of(frame_off, n_clips, clip_rate, g);
     const int64_t t = g - frame_off[clip];
     base = sample_off[clip] + kHop * t - kHop;
     first = (t == 0);
@@ -430,8 +439,8 @@ hipError_t launch_frontend(const FrontTables& tabs, const float* audio, int64_t 
   const int64_t blocks = (n_frames + kFramesPerBlock - 1) / kFramesPerBlock;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(frontend_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                     tabs, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames, carry,
-                     logmel, levels);
+                     tabs, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames,
+                     static_cast<double>(n_clips) / static_cast<double>(n_frames), carry, logmel, levels);
   return hipGetLastError();
 }
 
