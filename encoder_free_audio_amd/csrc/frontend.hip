@@ -109,23 +109,30 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Clip of global frame g: the largest c with frame_off[c] <= g.  The first
-// guess, (g + 0.5) * n_clips / n_frames, is the clip when every clip has the
-// same number of frames F (the guess then lies at least 0.5 / F from an
-// integer): one round of reads instead of log2(n_clips) dependent ones for
-// uniform batches and streaming steps.  A clip c with frame_off[c] <= g <
-// frame_off[c + 1] is the answer because the offsets do not decrease; any
-// other guess falls back to binary search.
-__device__ __forceinline__ int clip_of(const int64_t* frame_off, int n_clips, double clip_rate, int64_t g) {
+// Clip of global frame g (the largest c with frame_off[c] <= g), with
+// frame_off[c] and sample_off[c].  The first guess, (g + 0.5) * n_clips /
+// n_frames, is the clip when every clip has the same number of frames F (the
+// guess then lies at least 0.5 / F from an integer), and its three offsets
+// are read together: one round of reads instead of log2(n_clips) + 1
+// dependent ones for uniform batches and streaming steps.  A clip c with
+// frame_off[c] <= g < frame_off[c + 1] is the answer because the offsets do
+// not decrease; any other guess falls back to binary search.
+struct ClipPos {
+  int clip;
+  int64_t frame0, sample0;
+};
+__device__ __forceinline__ ClipPos clip_of(const int64_t* frame_off, const int64_t* sample_off, int n_clips,
+                                           double clip_rate, int64_t g) {
   int c = static_cast<int>((static_cast<double>(g) + 0.5) * clip_rate);
   c = c < 0 ? 0 : (c < n_clips - 1 ? c : n_clips - 1);
-  if (frame_off[c] <= g && g < frame_off[c + 1]) return c;
+  const int64_t f0 = frame_off[c], f1 = frame_off[c + 1], s0 = sample_off[c];
+  if (f0 <= g && g < f1) return {c, f0, s0};
   int lo = 0, hi = n_clips;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (frame_off[mid] <= g) lo = mid; else hi = mid;
   }
-  return lo;
+  return {lo, frame_off[lo], sample_off[lo]};
 }
 
 // Exact level of a log-mel value: the number of quantizer edges k = 1 .. V-1
@@ -167,9 +174,10 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
   int64_t base = 0;
   bool first = false;
   if (valid) {
-    clip = clip_of(frame_off, n_clips, clip_rate, g);
-    const int64_t t = g - frame_off[clip];
-    base = sample_off[clip] + kHop * t - kHop;
+    const ClipPos cp = clip_of(frame_off, sample_off, n_clips, clip_rate, g);
+    clip = cp.clip;
+    const int64_t t = g - cp.frame0;
+    base = cp.sample0 + kHop * t - kHop;
     first = (t == 0);
   }
   // Samples [0, 800) of the frame come from `lo` (the audio, or for a clip's
