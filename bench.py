@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--clips", type=int, default=64)
     ap.add_argument("--minutes", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-frames", type=int, default=10000, help="oracle sample: frames per worker")
+    ap.add_argument("--cpu-frames", type=int, default=20000, help="oracle sample: frames per worker")
     ap.add_argument("--workload", choices=("batch", "stream", "interleave", "copy", "shortconv", "shortconv_decode",
                                            "backward", "hmlp", "dft_gemm"),
                     default="batch",
