@@ -31,6 +31,11 @@ from encoder_free_audio_amd import synth  # noqa: E402
 HBM_BYTES_PER_TOKEN = 800 * 4 + 6144 * 2    # 3,200 B audio read (800 new samples) + 12,288 B bf16 token write
 PEAK_ADD_TFLOPS = 256 * 64 * 2.4e9 / 1e12   # v_add_f32: 256 CUs x 64 lanes x 2.4 GHz = 39.32 T adds/s
 PEAK_HBM_GBPS = 8000.0
+PEAK_ADD_PACKED_TFLOPS = 78.6   # the chip's fp32 vector figure, which counts packed (two-wide) adds
+PEAK_FP32_TFLOPS = 157.3        # fp32 vector peak with FMA counted as two flops
+# algorithmic flops per frame of the front end: FFT 2.5 N log2 N (N = 1600) 42,575,
+# mel 3,142, power 2,403, window 1,600
+FRONT_FLOPS_PER_FRAME = 42575 + 3142 + 2403 + 1600
 METRIC = "audio tokens/sec (dMel frames→6144-d embeds) + achieved HBM GB/s vs peak"
 COUNTERS_MD = os.path.join(ROOT, "profiles", "embed_kernel_64x20min_counters.md")
 EMBED_SRCS = [os.path.join(ROOT, "encoder_free_audio_amd", "csrc", f) for f in ("embed.hip", "embed_core.h")]
@@ -731,6 +736,21 @@ def bench_batch(args):
     print(f"[bench] per step: levels {k_front:.3f} ms, rms_scale {k_scale:.3f} ms, embed {k_embed:.3f} ms; "
           f"wall {ms_step:.3f} ms", file=sys.stderr, flush=True)
 
+    # a plain 1 GiB device copy, timed after the steps: the HBM rate this box
+    # reaches, to set the step's algorithmic rate against
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * 4 * (1 << 28) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+    front_tflops = FRONT_FLOPS_PER_FRAME * n_tok / (k_front * 1e-3) / 1e12
+
     cpu = None
     if not args.no_cpu_baseline:
         try:
@@ -758,6 +778,11 @@ def bench_batch(args):
                    "global_batch": n_clips, "seq_len": T_clip, "parallelism": "single GPU"},
         "hbm_achieved_GBps": hbm,
         "hbm_frac": hbm / PEAK_HBM_GBPS,
+        "copy_GBps": copy_gbps,
+        "hbm_frac_of_copy": hbm / copy_gbps,
+        "alu_frac_of_packed_peak": achieved / PEAK_ADD_PACKED_TFLOPS,
+        "frontend_TFLOPs": front_tflops,
+        "frontend_frac_of_fp32_peak": front_tflops / PEAK_FP32_TFLOPS,
         "kernel_ms": {"frontend_levels": k_front, "rms_scale": k_scale, "embed": k_embed},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_ADD_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_ADD_TFLOPS,
