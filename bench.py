@@ -118,7 +118,19 @@ def cpu_baseline(audio_dev, clip_len, table_bits, n_clips, frames_per_worker, co
     tokens = sum(res)
     return {"value": tokens / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
             "sample": f"first {frames_per_worker} frames of each of {workers} clips ({tokens} tokens, "
-                      f"RMSNorm on, bf16 out), one oracle process per core, {dt:.1f} s wall"}
+                      f"RMSNorm on, bf16 out), one oracle process per core, {dt:.1f} s wall",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _oracle_job(seg, tb, config=None):
