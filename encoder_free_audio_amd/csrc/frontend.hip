@@ -14,8 +14,12 @@
 // level = min(15, floor((clamp(l, -7, 2) + 7) * 16 / 9)) decided exactly.
 //
 // Work decomposition (one workgroup = 256 threads = 8 frames, fp32, LDS):
+//  0. a frame's 32 threads sit in one wavefront and find its clip and first
+//     sample themselves (steps 1-3 touch only the frame's own LDS rows, so
+//     the four wavefronts run them without workgroup barriers);
 //  1. the 1600 windowed samples of a frame are read as 800 complex values
-//     z[m] = x[2m] + i x[2m+1] straight into the registers of pass A;
+//     z[m] = x[2m] + i x[2m+1] straight into the registers of pass A (from
+//     the clip's carry or zeros, then the audio, for a clip's first frame);
 //  2. 800-point complex FFT, 800 = 32 x 25:
 //     pass A - one thread per (frame, n1 < 32): a 25-point DFT (5 x 5) over
 //              z[n1 + 32 n2] (coalesced 8-byte reads across n1) in registers,
@@ -25,10 +29,11 @@
 //     the exchange between the passes goes through LDS rows padded to 33
 //     complex values so that neither pass has bank conflicts;
 //  3. split Z into the 801-bin spectrum of the real frame and take |X|^2;
-//  4. mel: each bin lies between two triangle edges and feeds exactly two
-//     filters (the rising side of one, the falling side of the previous), so
-//     one pass over the 81 segments gives per-segment sums A_s (rising) and
-//     C_s (falling) and filter j is A_j + C_{j+1}; then log, clamp, quantize.
+//  4. mel (work items across the block's frames, after a barrier): each bin
+//     lies between two triangle edges and feeds exactly two filters (the
+//     rising side of one, the falling side of the previous), so one pass
+//     over the 81 segments gives per-segment sums A_s (rising) and C_s
+//     (falling) and filter j is A_j + C_{j+1}; then log, clamp, quantize.
 #include "internal.h"
 
 namespace dmel {
