@@ -351,14 +351,14 @@ def forward(x: np.ndarray, table_bits: np.ndarray, rms_weight=None, eps: float =
 # (evaluated in fp64 from the fp32 sum s).
 #
 # Embedding bag: dE[row] = sum of ds_t over the (t, j) with row r_tj = row.
-# Reading of the summation order (the pages give none; a fixed order makes the
-# result reproducible and checkable bit for bit): tokens are taken in
-# segments of SEGMENT consecutive tokens; within a segment each row sums its
-# tokens' gradients in increasing token order in fp32 starting from +0; the
-# result is then (start + partial_0) + partial_1 + ... in segment order in
-# fp32, where start is +0 or, when accumulating, the existing gradient.
+# Reading of the summation order (the pages give none): the plain definition,
+# each row's gradients added in increasing token order, one fp32 add per
+# selecting token, starting from +0 (the table gradient is a zero tensor that
+# every token adds its gradient into, token by token).  When accumulating
+# into an existing gradient G, the result is fl32(G + S) with S that sum (an
+# existing gradient plus a freshly computed one, as an optimizer's gradient
+# buffer receives it).
 # ---------------------------------------------------------------------------
-SEGMENT = 65536
 
 
 def rms_backward(lv: np.ndarray, table_bits: np.ndarray, weight, dy, eps: float = RMS_EPS,
@@ -382,23 +382,31 @@ def rms_backward_from_sum(s, weight, dy, eps: float = RMS_EPS):
     return ds, dw, r
 
 
-def embed_backward(lv: np.ndarray, dsum, n_levels: int = N_LEVELS, dtable=None, segment: int = SEGMENT):
-    """fp32 [n_bins * n_levels, d] gradient of the table in the fixed order above.
+def embed_backward(lv: np.ndarray, dsum, n_levels: int = N_LEVELS, dtable=None, cols=None):
+    """fp32 [n_bins * n_levels, d] gradient of the table, each row summed in
+    token order from +0 (see above).
 
     dsum: [n, d] gradient with respect to the fp32 sum (fp32 values, or bf16
-    values given as fp32).  dtable: existing gradient to accumulate into."""
+    values given as fp32).  dtable: existing gradient to accumulate into.
+    cols: optional column indices; only those columns are computed (the
+    result is then [rows, len(cols)]) - columns are independent sums, so this
+    changes nothing but the cost."""
     g = np.asarray(dsum, dtype=np.float32)
+    if cols is not None:
+        g = g[:, np.asarray(cols)]
     rows = table_rows(np.minimum(np.asarray(lv), n_levels - 1), n_levels)
     n, n_bins = rows.shape
     d = g.shape[1]
-    total = np.zeros((n_bins * n_levels, d), dtype=np.float32) if dtable is None else \
-        np.array(dtable, dtype=np.float32, copy=True)
-    for s0 in range(0, n, segment):
-        part = np.zeros_like(total)
-        for t in range(s0, min(n, s0 + segment)):
-            # the token's rows are distinct (one per bin): one fp32 add each
-            part[rows[t]] = part[rows[t]] + g[t][None, :]
-        total = total + part
+    total = np.zeros((n_bins * n_levels, d), dtype=np.float32)
+    for t in range(n):
+        # the token's rows are distinct (one per bin): one fp32 add each, and
+        # the tokens arrive in order
+        total[rows[t]] = total[rows[t]] + g[t][None, :]
+    if dtable is not None:
+        base = np.asarray(dtable, dtype=np.float32)
+        if cols is not None:
+            base = base[:, np.asarray(cols)]
+        total = base + total
     return total
 
 

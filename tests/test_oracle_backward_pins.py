@@ -1,6 +1,7 @@
 """Pins for the oracle's backward: finite differences of the RMSNorm, its
 closed forms, exact integer sums and the adjoint identity for the
-embedding-bag gradient, and a hand-worked case of the summation order."""
+embedding-bag gradient, and hand-worked cases of the summation order (token
+order from +0; the existing gradient added to the finished sum)."""
 
 import json
 import os
@@ -73,7 +74,7 @@ def test_embed_backward_integer_sums(n_bins, n_levels):
     n, d = 300, 8
     lv = rng.integers(0, n_levels, (n, n_bins)).astype(np.uint8)
     g = rng.integers(-50, 50, (n, d)).astype(np.float32)
-    got = o.embed_backward(lv, g, n_levels, segment=64)
+    got = o.embed_backward(lv, g, n_levels)
     want = np.zeros((n_bins * n_levels, d), dtype=np.int64)
     for t in range(n):
         for b in range(n_bins):
@@ -81,7 +82,7 @@ def test_embed_backward_integer_sums(n_bins, n_levels):
     assert np.array_equal(got.astype(np.int64), want)
     # and accumulating into an existing gradient adds it
     base = rng.integers(-5, 5, want.shape).astype(np.float32)
-    got2 = o.embed_backward(lv, g, n_levels, dtable=base, segment=64)
+    got2 = o.embed_backward(lv, g, n_levels, dtable=base)
     assert np.array_equal(got2.astype(np.int64), want + base.astype(np.int64))
 
 
@@ -99,14 +100,49 @@ def test_embed_backward_adjoint_identity():
     assert abs(lhs - rhs) < 1e-4 * np.sum(np.abs(g)) * 10
 
 
+def _one_row(terms):
+    # one bin of one level: every token selects row 0
+    g = np.array(terms, dtype=np.float32)[:, None]
+    return np.zeros((len(terms), 1), dtype=np.uint8), g
+
+
 def test_embed_backward_order_golden(golden_dir):
     with open(os.path.join(golden_dir, "embed_backward_order.json")) as f:
         c = json.load(f)
-    terms = np.array(c["terms"], dtype=np.float32)
-    lv = np.zeros((4, 1), dtype=np.uint8)          # one bin, level 0: row 0 for every token
-    g = terms[:, None]
-    assert o.embed_backward(lv, g, 1, segment=4)[0, 0] == c["one_segment"]
-    assert o.embed_backward(lv, g, 1, segment=2)[0, 0] == c["segments_of_two"]
+    lv, g = _one_row(c["order"]["terms"])
+    assert o.embed_backward(lv, g, 1)[0, 0] == c["order"]["token_order"]
+    # the hand-worked alternatives really are different numbers, so the pin
+    # separates token order from reverse order and from adding halves first
+    assert len({c["order"]["token_order"], c["order"]["reverse_order"], c["order"]["halves_first"]}) == 3
+    lv, g = _one_row(c["accumulate"]["terms"])
+    base = np.array([[c["accumulate"]["existing"]]], dtype=np.float32)
+    assert o.embed_backward(lv, g, 1, dtable=base)[0, 0] == c["accumulate"]["result"]
+    assert c["accumulate"]["result"] != c["accumulate"]["chained_from_existing"]
+    lv, g = _one_row(c["signed_zero"]["terms"])
+    got = o.embed_backward(lv, g, 1)[0, 0]
+    assert got == 0.0 and int(np.signbit(got)) == c["signed_zero"]["result_sign_bit"]
+
+
+def test_embed_backward_token_order_by_rows():
+    # the same sums formed the other way round: for each row, its tokens
+    # collected first, then added one by one as fp32 scalars; inputs drawn so
+    # that order matters (large and small magnitudes mixed)
+    rng = np.random.default_rng(7)
+    n, d, n_bins, n_levels = 150, 3, 4, 3
+    lv = rng.integers(0, n_levels, (n, n_bins)).astype(np.uint8)
+    g = (rng.standard_normal((n, d)) * np.where(rng.random((n, d)) < 0.2, 1e7, 1.0)).astype(np.float32)
+    got = o.embed_backward(lv, g, n_levels)
+    for b in range(n_bins):
+        for lev in range(n_levels):
+            toks = [t for t in range(n) if lv[t, b] == lev]
+            for c in range(d):
+                acc = np.float32(0.0)
+                for t in toks:
+                    acc = np.float32(acc + g[t, c])
+                assert got[n_levels * b + lev, c] == acc
+    # a column subset is the same computation on those columns
+    sub = o.embed_backward(lv, g, n_levels, cols=[2, 0])
+    assert np.array_equal(sub, got[:, [2, 0]])
 
 
 def test_embed_backward_untouched_rows_are_zero():
