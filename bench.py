@@ -177,8 +177,8 @@ def bench_backward(args):
     """Backward of the front end's trainable parts on the 64 x 20 min batch:
     the RMSNorm backward (dmel_rms_backward with the larger workspace: a first
     pass that recomputes the forward sum and keeps it, a second that streams
-    it) and the table gradient (dmel_embed_backward: level sort,
-    fixed-order scatter, segment combine), from a bf16 upstream gradient
+    it) and the table gradient (dmel_embed_backward: level sort, then the
+    token-order scatter), from a bf16 upstream gradient
     ~ N(0, 1e-3).  One step = both calls; the levels come from the front end
     before the timed region."""
     dev = "cuda"
@@ -253,7 +253,7 @@ def bench_backward(args):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"dMel backward: {n_clips} clips x {args.minutes:g} min ({T} tokens), table "
-                               f"1280x6144, bf16 upstream gradient, RMSNorm backward + fixed-order table gradient",
+                               f"1280x6144, bf16 upstream gradient, RMSNorm backward + token-order table gradient",
                    "global_batch": n_clips, "seq_len": T // n_clips, "parallelism": "single GPU"},
         "kernel_ms": {"rms_backward": float(k_rms), "table_gradient": float(k_tab)},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_ADD_TFLOPS, "unit": "TFLOP/s",

@@ -8,11 +8,11 @@
 //   dw = sum_t dy_t * s_t * r_t
 //   dE[row] = sum of ds_t over the (t, j) whose selected row r_tj is row.
 //
-// Table gradient order (fixed, so that the result is reproducible and equal
-// bit for bit to the sequential definition): tokens in segments of 65536;
-// inside a segment every row sums its tokens' gradients in increasing token
-// order in fp32 from +0; the segment partials are then added in order to +0
-// (or to the existing gradient when accumulating).
+// Table gradient order: the plain definition - every row adds the gradients
+// of the tokens that selected it in increasing token order, one fp32 add per
+// token, starting from +0; accumulating gives dtable + that sum.  The kernels
+// reproduce this order exactly, so results repeat bit for bit and equal the
+// sequential definition.
 //
 // Kernels:
 //  * bucket_kernel - for each chunk of 128 tokens and each bin, a stable
@@ -21,14 +21,15 @@
 //    rows, grouped by level, each group padded to a multiple of four entries
 //    with the address of a row of -0.0, and the 17 group starts (32-bit
 //    words, so that the scatter reads them with scalar loads).
-//  * scatter_kernel - a workgroup owns one segment, 16 bins (one wave each)
-//    and 256 columns (4 per lane); per chunk it stages the 128 x 256 gradient
-//    tile in LDS, then each wave walks its bin's level groups in token order
-//    and adds the tile rows into 16 x 4 accumulators in registers (one
-//    ds_read_b128 and four v_add_f32 per token); the group lists are uniform,
-//    so they come through scalar loads.  Workgroups that share a tile (the
-//    bin groups of one segment and strip) are placed on the same XCD.
-//  * combine_kernel - the segment partials, in order.
+//  * scatter_kernel - a workgroup owns 8 bins (one wave each) and 256
+//    columns (4 per lane) and walks every chunk of the batch in order; per
+//    chunk it stages the 128 x 256 gradient tile in LDS, then each wave walks
+//    its bin's level groups in token order and adds the tile rows into
+//    16 x 4 accumulators in registers (one ds_read_b128 and four v_add_f32
+//    per token); the group lists are uniform, so they come through scalar
+//    loads.  Every row's sum is thus one chain in token order across the
+//    whole batch.  Workgroups that share a tile (the bin groups of one
+//    strip) are placed on the same XCD.
 //  * rms_dot_kernel / rms_ds_kernel - the RMSNorm backward: the forward sum
 //    is recomputed exactly as embed_kernel computes it (embed_core.h); the
 //    first pass forms sum_c w_c dy_c s_c per token and per-workgroup partial
@@ -42,11 +43,10 @@ namespace {
 
 constexpr int kChunk = 128;                  // tokens per staged tile
 constexpr int kRounds = kChunk / 64;         // waves of 64 tokens per chunk in the level sort
-constexpr int kSegChunks = kBwdSegment / kChunk;
 constexpr int kBwdCols = 256;                // columns per workgroup (4 per lane)
-constexpr int kBwdBins = 16;                 // bins per workgroup (one per wave)
-constexpr int kBwdThreads = 64 * kBwdBins;   // 1024
-constexpr int kTileItems = kChunk * kBwdCols / 4 / kBwdThreads;  // float4 per thread per tile (8)
+constexpr int kBwdBins = 8;                  // bins per workgroup (one per wave)
+constexpr int kBwdThreads = 64 * kBwdBins;   // 512
+constexpr int kTileItems = kChunk * kBwdCols / 4 / kBwdThreads;  // float4 per thread per tile (16)
 constexpr int kListPitch = kChunk + 3 * 16;  // entries per (chunk, bin): groups padded to multiples of 4
 constexpr int kOffPitch = 17;                // group starts per (chunk, bin): 16 levels + end
 // LDS byte address of the tile row that holds -0.0 (after the kChunk token
@@ -165,24 +165,23 @@ __device__ __forceinline__ void add_chunk(float4 (&acc)[16], const char* tile_la
   }
 }
 
-// Workgroup (segment, bin group, strip); see the file comment.  Writes the
-// segment's partial sums to part (or, with a single segment, the final
-// gradient to out: out = (accumulate ? out : 0) + partial).
+// Workgroup (bin group, strip); see the file comment.  Writes
+// out = acc (or fl32(out + acc) when accumulating), acc being each row's
+// token-order sum over the whole batch.
 template <bool kBf16>
 __global__ void __launch_bounds__(kBwdThreads)
 scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_levels, int d_model,
                const uint32_t* __restrict__ lists, const uint32_t* __restrict__ starts, int64_t n_chunks,
-               int n_groups, int n_strips, int64_t n_outer, float* __restrict__ part, float* __restrict__ out,
-               int single, int accumulate) {
+               int n_groups, int n_strips, float* __restrict__ out, int accumulate) {
   __shared__ float4 tile[(kChunk + 1) * kBwdCols / 4];  // 128 KB of token rows + the -0.0 row
-  // blockIdx -> (outer = segment * n_strips + strip, bin group); the bin
-  // groups of one outer index are 8 apart, so they land on the same XCD
-  const int64_t bid = blockIdx.x;
-  const int grp = static_cast<int>((bid >> 3) % n_groups);
-  const int64_t outer = ((bid >> 3) / n_groups) * 8 + (bid & 7);
-  if (outer >= n_outer) return;  // before any barrier: the whole workgroup leaves
-  const int strip = static_cast<int>(outer % n_strips);
-  const int64_t seg = outer / n_strips;
+  // blockIdx -> (strip, bin group): workgroup b runs on XCD b % 8, and the
+  // bin groups of one strip are 8 apart, so they share the strip's tiles in
+  // that XCD's L2
+  const int bid = static_cast<int>(blockIdx.x);
+  const int local = bid >> 3;
+  const int grp = local % n_groups;
+  const int strip = (local / n_groups) * 8 + (bid & 7);
+  if (strip >= n_strips) return;  // before any barrier: the whole workgroup leaves
 
   const int tid = threadIdx.x;
   // the wave index, made explicitly uniform so that the group lists come
@@ -192,8 +191,6 @@ scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_l
   const bool bin_ok = j < n_bins;
   const int c_strip = strip * kBwdCols;
   const int c0 = c_strip + 4 * lane;
-  const int64_t ch0 = seg * kSegChunks;
-  const int64_t ch1 = min(ch0 + kSegChunks, n_chunks);
 
   float4 acc[16];
 #pragma unroll
@@ -201,12 +198,12 @@ scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_l
 
   if (tid < kBwdCols / 4) tile[kChunk * kBwdCols / 4 + tid] = make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
   float4 r[kTileItems];
-  tile_load<kBf16>(r, g, n_tokens, d_model, ch0 * kChunk, c_strip, tid);
+  tile_load<kBf16>(r, g, n_tokens, d_model, 0, c_strip, tid);
   const char* tile_lane = reinterpret_cast<const char*>(tile) + lane * 16;
-  for (int64_t ch = ch0; ch < ch1; ++ch) {
+  for (int64_t ch = 0; ch < n_chunks; ++ch) {
     tile_store(tile, r, tid);
     __syncthreads();
-    if (ch + 1 < ch1) tile_load<kBf16>(r, g, n_tokens, d_model, (ch + 1) * kChunk, c_strip, tid);
+    if (ch + 1 < n_chunks) tile_load<kBf16>(r, g, n_tokens, d_model, (ch + 1) * kChunk, c_strip, tid);
     if (bin_ok) {
       const int64_t pair = ch * n_bins + j;
       add_chunk(acc, tile_lane, lists + pair * kListPitch, starts + pair * kOffPitch);
@@ -219,15 +216,13 @@ scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_l
   for (int l = 0; l < 16; ++l) {
     if (l < n_levels) {
       const int64_t row = static_cast<int64_t>(j) * n_levels + l;
-      if (single) {
-        float4* o = reinterpret_cast<float4*>(out + row * d_model + c0);
-        float4 v = accumulate ? *o : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      float4* o = reinterpret_cast<float4*>(out + row * d_model + c0);
+      float4 v = acc[l];
+      if (accumulate) {
+        v = *o;
         add4(v, acc[l]);
-        *o = v;
-      } else {
-        const int64_t rows = static_cast<int64_t>(n_bins) * n_levels;
-        *reinterpret_cast<float4*>(part + (seg * rows + row) * d_model + c0) = acc[l];
       }
+      *o = v;
     }
   }
 }
@@ -245,17 +240,6 @@ hipError_t zero_fill(float* p, int64_t n, hipStream_t stream) {
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p, n);
   return hipGetLastError();
-}
-
-// out[i] = (accumulate ? out[i] : 0) + part[0][i] + part[1][i] + ... in order.
-__global__ void __launch_bounds__(256)
-combine_kernel(const float* __restrict__ part, int64_t n_seg, int64_t n4, float* __restrict__ out, int accumulate) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
-       i += static_cast<int64_t>(gridDim.x) * 256) {
-    float4 v = accumulate ? reinterpret_cast<const float4*>(out)[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int64_t s = 0; s < n_seg; ++s) add4(v, reinterpret_cast<const float4*>(part)[s * n4 + i]);
-    reinterpret_cast<float4*>(out)[i] = v;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -495,17 +479,14 @@ int strips_per_group(int64_t tblocks, int n_strips) {
 
 }  // namespace
 
-size_t bwd_layout(int64_t n_tokens, int n_bins, int n_levels, int d_model, size_t* off_starts, size_t* off_part) {
+size_t bwd_layout(int64_t n_tokens, int n_bins, size_t* off_starts) {
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
   const size_t n_chunks = static_cast<size_t>((n_tokens + kChunk - 1) / kChunk);
   const size_t pairs = n_chunks * static_cast<size_t>(n_bins);
-  const size_t n_seg = (n_chunks + kSegChunks - 1) / kSegChunks;
   const size_t b_lists = up(pairs * kListPitch * sizeof(uint32_t));
   const size_t b_starts = up(pairs * kOffPitch * sizeof(uint32_t));
-  const size_t b_part = n_seg > 1 ? up(n_seg * static_cast<size_t>(n_bins) * n_levels * d_model * sizeof(float)) : 0;
   if (off_starts) *off_starts = b_lists;
-  if (off_part) *off_part = b_lists + b_starts;
-  return b_lists + b_starts + b_part;
+  return b_lists + b_starts;
 }
 
 hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels, const void* dsum,
@@ -516,14 +497,12 @@ hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_
     if (accumulate) return hipSuccess;
     return zero_fill(dtable, rows * d_model, stream);
   }
-  size_t off_starts = 0, off_part = 0;
-  bwd_layout(n_tokens, n_bins, n_levels, d_model, &off_starts, &off_part);
+  size_t off_starts = 0;
+  bwd_layout(n_tokens, n_bins, &off_starts);
   auto* lists = static_cast<uint32_t*>(workspace);
   auto* starts = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + off_starts);
-  auto* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_part);
   const int64_t n_chunks = (n_tokens + kChunk - 1) / kChunk;
   const int64_t n_pairs = n_chunks * n_bins;
-  const int64_t n_seg = (n_chunks + kSegChunks - 1) / kSegChunks;
   const int64_t bblocks = (n_pairs + 3) / 4;
   if (bblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bucket_kernel, dim3(static_cast<unsigned>(bblocks)), dim3(256), 0, stream, levels, n_tokens,
@@ -532,26 +511,17 @@ hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_
   if (e != hipSuccess) return e;
   const int n_groups = (n_bins + kBwdBins - 1) / kBwdBins;
   const int n_strips = (d_model + kBwdCols - 1) / kBwdCols;
-  const int64_t n_outer = n_seg * n_strips;
-  const int64_t blocks = ((n_outer + 7) / 8) * 8 * n_groups;
+  const int64_t blocks = static_cast<int64_t>((n_strips + 7) / 8) * 8 * n_groups;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const int single = n_seg == 1;
   if (dsum_bf16) {
     hipLaunchKernelGGL(scatter_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kBwdThreads), 0, stream, dsum,
-                       n_tokens, n_bins, n_levels, d_model, lists, starts, n_chunks, n_groups, n_strips, n_outer,
-                       part, dtable, single, accumulate ? 1 : 0);
+                       n_tokens, n_bins, n_levels, d_model, lists, starts, n_chunks, n_groups, n_strips, dtable,
+                       accumulate ? 1 : 0);
   } else {
     hipLaunchKernelGGL(scatter_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kBwdThreads), 0, stream,
                        dsum, n_tokens, n_bins, n_levels, d_model, lists, starts, n_chunks, n_groups, n_strips,
-                       n_outer, part, dtable, single, accumulate ? 1 : 0);
+                       dtable, accumulate ? 1 : 0);
   }
-  e = hipGetLastError();
-  if (e != hipSuccess || single) return e;
-  const int64_t n4 = rows * d_model / 4;
-  int64_t cblocks = (n4 + 255) / 256;
-  if (cblocks > 65536) cblocks = 65536;
-  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(cblocks)), dim3(256), 0, stream, part, n_seg, n4,
-                     dtable, accumulate ? 1 : 0);
   return hipGetLastError();
 }
 

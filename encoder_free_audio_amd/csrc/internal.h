@@ -106,11 +106,9 @@ hipError_t launch_shortconv(const uint16_t* x, int64_t n_tokens, int channels, c
                             const float* weight, const uint16_t* state_in, uint16_t* state_out, void* y,
                             bool y_f32, hipStream_t stream);
 
-// Backward of the embedding (table gradient in a fixed order: token order
-// within segments of kBwdSegment tokens, then the segment partials in order)
-// and of its RMSNorm.
-constexpr int64_t kBwdSegment = 65536;
-size_t bwd_layout(int64_t n_tokens, int n_bins, int n_levels, int d_model, size_t* off_starts, size_t* off_part);
+// Backward of the embedding (table gradient: every row sums its tokens'
+// gradients in token order from +0, exactly) and of its RMSNorm.
+size_t bwd_layout(int64_t n_tokens, int n_bins, size_t* off_starts);
 hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels, const void* dsum,
                                  bool dsum_bf16, int d_model, float* dtable, bool accumulate, void* workspace,
                                  hipStream_t stream);

@@ -297,12 +297,13 @@ size_t dmel_embed_backward_workspace_bytes(int64_t n_tokens, int32_t n_bins, int
  *  dtable     fp32 [n_bins * n_levels, d_model] out (row n_levels * bin + level),
  *             16-byte aligned; overwritten, or added to when accumulate != 0
  *  workspace  device memory, 256-byte aligned, >= the size above
- * Summation order (fixed, so results repeat bit for bit): tokens are taken in
- * segments of 65536 consecutive tokens; inside a segment each row sums its
- * tokens' gradients in increasing token order in fp32 starting from +0; the
- * segment partials are then added in segment order in fp32 to +0 (or to the
- * existing dtable when accumulating).  d_model % 16 == 0; n_bins <= 80,
- * n_levels <= 16.  dtable and workspace must not overlap other arguments. */
+ * Summation order: the plain definition - each row adds the gradients of the
+ * tokens that selected it in increasing token order, one fp32 add per token,
+ * starting from +0 (so an unselected row is +0); with accumulate != 0 the row
+ * becomes fl32(dtable + that sum).  Results are bit-identical to that
+ * sequential definition and repeat bit for bit.  d_model % 16 == 0;
+ * n_bins <= 80, n_levels <= 16.  dtable and workspace must not overlap other
+ * arguments. */
 int dmel_embed_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels,
                         const void* dsum, int32_t dsum_dtype, int32_t d_model, float* dtable,
                         int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream);

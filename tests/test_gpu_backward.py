@@ -2,9 +2,10 @@
 the RMSNorm backward) through the C ABI against the oracle.
 
 Bars:
-* table gradient: bit-exact against the oracle's fixed-order definition
-  (fp32, token order inside segments of 65536 tokens, segments in order),
-  for fp32 and bf16 token gradients, every layout, accumulate on and off;
+* table gradient: bit-exact against the oracle's plain definition (each
+  row's gradients added in token order in fp32 from +0; accumulating adds the
+  finished sum to the existing gradient), for fp32 and bf16 token gradients,
+  every layout, accumulate on and off, batches of up to 1,536,000 tokens;
   repeated runs give identical bits.
 * RMSNorm backward, fp32 arithmetic against the oracle's fp64:
   |ds - ds_exact| <= 1e-5 * (|r w dy| + (r^3 / D) * sum_c |w_c dy_c s_c| * |s|)
@@ -95,26 +96,37 @@ def test_table_gradient_empty_batch(dm):
     assert bool((dt == 0.0).all())
 
 
-def test_segment_order_golden(dm, golden_dir):
-    # the hand-worked case across the 65536-token segment boundary: one row
+def test_order_golden(dm, golden_dir):
+    # the hand-worked cases, placed across chunk boundaries and far apart in
+    # a batch of more than 131,072 tokens; every other token adds +0.0
     with open(os.path.join(golden_dir, "embed_backward_order.json")) as f:
         c = json.load(f)
-    n, d = o.SEGMENT + 2, 16
-    print(f"case: segment boundary n={n}", flush=True)
+    n, d = 140_003, 16
+    print(f"case: order golden n={n}", flush=True)
     lv = np.zeros((n, 1), dtype=np.uint8)
     g = np.zeros((n, d), dtype=np.float32)
-    g[o.SEGMENT - 2: o.SEGMENT + 2, 0] = np.array(c["terms"], dtype=np.float32)
+    g[126:130, 0] = c["order"]["terms"]                  # spans the first chunk boundary
+    g[[5, 65_600, 131_100, n - 1], 1] = c["order"]["terms"]
+    g[[3, n - 2], 2] = c["accumulate"]["terms"]
+    g[77_777, 3] = c["signed_zero"]["terms"][0]
+    base = np.zeros((1, d), dtype=np.float32)
+    base[0, 2] = c["accumulate"]["existing"]
     got = gpu_embed_backward(dm, lv, g, 1)
-    assert got[0, 0] == c["segments_of_two"]          # 2 tokens each side of the boundary
-    assert np.array_equal(got, o.embed_backward(lv, g, 1))
+    assert got[0, 0] == c["order"]["token_order"] and got[0, 1] == c["order"]["token_order"]
+    assert got[0, 3] == 0.0 and not np.signbit(got[0, 3])
+    assert np.array_equal(got.view(np.uint32), o.embed_backward(lv, g, 1).view(np.uint32))
+    got = gpu_embed_backward(dm, lv, g, 1, dtable_in=base)
+    assert got[0, 2] == c["accumulate"]["result"]
+    assert np.array_equal(got.view(np.uint32), o.embed_backward(lv, g, 1, dtable=base).view(np.uint32))
 
 
-def test_multi_segment_and_determinism(dm):
+def test_long_batch_and_determinism(dm):
     rng = np.random.default_rng(8)
-    n, d = 2 * o.SEGMENT + 777, 32
-    print(f"case: three segments n={n}", flush=True)
+    n, d = 2 * 65_536 + 777, 32
+    print(f"case: long batch n={n}", flush=True)
     lv = rng.integers(0, 16, (n, 80)).astype(np.uint8)
-    g = rng.standard_normal((n, d)).astype(np.float32)
+    # magnitudes mixed over 2^20, so that the order of the adds shows in the bits
+    g = (rng.standard_normal((n, d)) * np.exp2(rng.integers(0, 20, (n, d)))).astype(np.float32)
     got = gpu_embed_backward(dm, lv, g, 16)
     again = gpu_embed_backward(dm, lv, g, 16)
     assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
@@ -188,7 +200,7 @@ def test_rms_backward(dm, n_bins, n_levels, dy_bf16):
 
 def test_rms_then_table_gradient_chain(dm):
     # the gradient flows through both calls; the table gradient of the GPU's
-    # ds equals the oracle's fixed-order sum of that ds bit for bit
+    # ds equals the oracle's token-order sum of that ds bit for bit
     rng = np.random.default_rng(12)
     n, d = 1500, 128
     lv = rng.integers(0, 16, (n, 80)).astype(np.uint8)
@@ -245,20 +257,10 @@ def test_full_size_backward_sampled(dm):
     tol = 1e-5 * (np.abs(r[:, None] * dys) + (r ** 3 / d * dot_abs)[:, None] * np.abs(s64)) + 1e-30
     got = ds[torch.from_numpy(picks).cuda()].cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - ds_want) <= tol)
-    # sampled rows and columns of the table gradient: the fixed-order sum of
-    # the GPU's ds over the tokens that selected the row
-    lv_np = lv.cpu().numpy()
-    cols = np.array([0, 1, 777, 6143])
-    for row in (16 * 0 + 15, 16 * 40 + 12, 16 * 79 + 9, 16 * 7 + 0):
-        j, l = divmod(row, 16)
-        toks = np.nonzero(np.minimum(lv_np[:, j], 15) == l)[0]
-        vals = ds[torch.from_numpy(toks).cuda()][:, torch.from_numpy(cols).cuda()].cpu().numpy() \
-            if toks.size else np.zeros((0, cols.size), np.float32)
-        total = np.zeros(cols.size, np.float32)
-        for s0 in range(0, T, o.SEGMENT):
-            seg = vals[(toks >= s0) & (toks < s0 + o.SEGMENT)]
-            part = np.cumsum(np.concatenate([np.zeros((1, cols.size), np.float32), seg]), axis=0,
-                             dtype=np.float32)[-1]
-            total = (total + part).astype(np.float32)
-        got = dt[row, torch.from_numpy(cols).cuda()].cpu().numpy()
-        assert np.array_equal(got.view(np.uint32), total.view(np.uint32)), (row, toks.size)
+    # every row of the table gradient in sampled columns: the oracle's
+    # token-order sum of the GPU's ds over all 1,536,000 tokens
+    cols = np.array([0, 1, 777, 4099, 6143])
+    cols_d = torch.from_numpy(cols).cuda()
+    want = o.embed_backward(lv.cpu().numpy(), ds[:, cols_d].cpu().numpy(), 16)
+    got = dt[:, cols_d].cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
