@@ -15,21 +15,20 @@
 // sequential definition.
 //
 // Kernels:
-//  * bucket_kernel - for each chunk of 128 tokens and each bin, a stable
-//    counting sort of the chunk's tokens by level (one wave per (chunk, bin),
-//    64 tokens per ballot): the LDS byte addresses of the tokens' gradient
-//    rows, grouped by level, each group padded to a multiple of four entries
-//    with the address of a row of -0.0, and the 17 group starts (32-bit
-//    words, so that the scatter reads them with scalar loads).
+//  * levels_t_kernel - the levels by bin ([bin][token], clamped), so that a
+//    chunk's 64 levels of one bin are 64 contiguous bytes.
 //  * scatter_kernel - a workgroup owns 8 bins (one wave each) and 256
-//    columns (4 per lane) and walks every chunk of the batch in order; per
-//    chunk it stages the 128 x 256 gradient tile in LDS, then each wave walks
-//    its bin's level groups in token order and adds the tile rows into
-//    16 x 4 accumulators in registers (one ds_read_b128 and four v_add_f32
-//    per token); the group lists are uniform, so they come through scalar
-//    loads.  Every row's sum is thus one chain in token order across the
-//    whole batch.  Workgroups that share a tile (the bin groups of one
-//    strip) are placed on the same XCD.
+//    columns (4 per lane) and walks every 64-token chunk of the batch in
+//    order; the chunk's 64 x 256 gradient tile and its levels are copied
+//    straight into LDS (double-buffered), and each wave takes the 64 tokens
+//    in order: one ds_read_b128 of the token's row (static offset) and four
+//    v_add_f32 into the accumulators of the token's level, which the wave
+//    selects with the GPR index mode (the level is the same in every lane,
+//    and the 16 x 4 accumulators sit in 64 consecutive registers).  Every
+//    row's sum is thus one chain in token order across the whole batch.  The
+//    workgroups that share a tile (the bin groups of one strip) run on the
+//    same XCD and are paced to stay close in the batch, so the L2 serves
+//    their re-reads.
 //  * rms_dot_kernel / rms_ds_kernel - the RMSNorm backward: the forward sum
 //    is recomputed exactly as embed_kernel computes it (embed_core.h); the
 //    first pass forms sum_c w_c dy_c s_c per token and per-workgroup partial
@@ -41,88 +40,104 @@
 namespace dmel {
 namespace {
 
-constexpr int kChunk = 128;                  // tokens per staged tile
-constexpr int kRounds = kChunk / 64;         // waves of 64 tokens per chunk in the level sort
+constexpr int kChunk = 64;                   // tokens per staged tile
 constexpr int kBwdCols = 256;                // columns per workgroup (4 per lane)
 constexpr int kBwdBins = 8;                  // bins per workgroup (one per wave)
 constexpr int kBwdThreads = 64 * kBwdBins;   // 512
-constexpr int kTileItems = kChunk * kBwdCols / 4 / kBwdThreads;  // float4 per thread per tile (16)
-constexpr int kListPitch = kChunk + 3 * 16;  // entries per (chunk, bin): groups padded to multiples of 4
-constexpr int kOffPitch = 17;                // group starts per (chunk, bin): 16 levels + end
-// LDS byte address of the tile row that holds -0.0 (after the kChunk token
-// rows): adding it is an exact no-op, so level groups are padded with it to
-// whole groups of four and the scatter needs no remainder loop.
-constexpr uint32_t kNegZeroRow = kChunk * kBwdCols * 4;
+constexpr int kRowBytes = kBwdCols * 4;      // one token's 256 fp32 gradients
+constexpr int kTileBytes = kChunk * kRowBytes;           // 64 KB
+constexpr int kLvBytes = kBwdBins * kChunk;              // the chunk's levels of the 8 bins
+static_assert(kChunk / kBwdBins * kBwdBins == kChunk, "tile copy: whole rows per wave");
+static_assert(kLvBytes == 32 * 16, "level copy: one 16-byte piece per lane of half a wave");
 
 // ---------------------------------------------------------------------------
+// Levels by bin: lvt[j][t] = min(levels[t][j], n_levels - 1) for t < n_tokens
+// and 0 up to the end of the last chunk (those tokens add a row of -0.0, see
+// tile_dma).  A workgroup transposes 64 tokens through LDS.  Also fills the
+// row of -0.0 that stands in for tokens past the batch.
 __global__ void __launch_bounds__(256)
-bucket_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels, int64_t n_pairs,
-              uint32_t* __restrict__ lists, uint32_t* __restrict__ starts) {
-  const int lane = threadIdx.x & 63;
-  const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (pair >= n_pairs) return;  // whole wave; no barriers in this kernel
-  const int64_t chunk = pair / n_bins;
-  const int j = static_cast<int>(pair - chunk * n_bins);
-  uint32_t L[kRounds];
-#pragma unroll
-  for (int r = 0; r < kRounds; ++r) {
-    const int64_t t = chunk * kChunk + r * 64 + lane;
-    L[r] = 0xFFu;  // no group
+levels_t_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels, int64_t t_pad,
+                uint8_t* __restrict__ lvt, float* __restrict__ neg_zero) {
+  __shared__ uint8_t tile[kChunk * kEmbMaxBins];
+  const int tid = threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kChunk;
+  const uint32_t vmax = static_cast<uint32_t>(n_levels - 1);
+  for (int i = tid; i < kChunk * n_bins; i += 256) {
+    const int64_t t = t0 + i / n_bins;
+    uint32_t v = 0;
     if (t < n_tokens) {
-      const uint32_t v = levels[t * n_bins + j];
-      L[r] = v < static_cast<uint32_t>(n_levels - 1) ? v : static_cast<uint32_t>(n_levels - 1);
+      v = levels[t0 * n_bins + i];
+      v = v < vmax ? v : vmax;
     }
+    tile[i] = static_cast<uint8_t>(v);
   }
-  uint32_t* lst = lists + pair * kListPitch;
-  uint32_t* st = starts + pair * kOffPitch;
-  uint32_t base = 0;
-  for (int l = 0; l < n_levels; ++l) {
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const uint64_t m = __ballot(L[r] == static_cast<uint32_t>(l));
-      const uint32_t rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-      if (L[r] == static_cast<uint32_t>(l)) lst[base + cnt + rank] = static_cast<uint32_t>((r * 64 + lane) * kBwdCols * 4);
-      cnt += static_cast<uint32_t>(__popcll(m));
-    }
-    const uint32_t padded = (cnt + 3u) & ~3u;
-    if (static_cast<uint32_t>(lane) < padded - cnt) lst[base + cnt + lane] = kNegZeroRow;
-    if (lane == 0) st[l] = base;
-    base += padded;
+  __syncthreads();
+  for (int i = tid; i < kChunk * n_bins; i += 256) {
+    const int j = i / kChunk, q = i - j * kChunk;
+    lvt[static_cast<int64_t>(j) * t_pad + t0 + q] = tile[q * n_bins + j];
   }
-  if (lane == 0) {
-    for (int l = n_levels; l <= 16; ++l) st[l] = base;
+  if (blockIdx.x == 0) {
+    for (int i = tid; i < kBwdCols; i += 256) neg_zero[i] = -0.0f;
   }
 }
 
 // ---------------------------------------------------------------------------
-template <bool kBf16>
-__device__ __forceinline__ void tile_load(float4 (&r)[kTileItems], const void* g, int64_t n_tokens, int d_model,
-                                          int64_t t0, int c_strip, int tid) {
-  // kChunk rows x 256 columns; item i = row * 64 + (4-column group)
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// fp32 gradients: chunk `ch`'s 64 x 256 tile straight from global memory into
+// tile buffer `tb` (wave w copies rows 8w .. 8w + 7, one 1 KB row per load:
+// lane i takes columns 4i .. 4i + 3).  Rows past the batch copy the row of
+// -0.0 (their tokens then add exact no-ops); columns past d_model read an
+// in-range address (no lane past d_model writes a result).
+__device__ __forceinline__ void tile_dma(char* tb, const float* g, const float* neg_zero, int64_t n_tokens,
+                                         int d_model, int64_t t0, int c_strip, int wave, int lane) {
+  const int c = min(c_strip + 4 * lane, d_model - 4);
 #pragma unroll
-  for (int k = 0; k < kTileItems; ++k) {
-    const int i = tid + k * kBwdThreads;
-    const int row = i >> 6, cg = i & 63;
-    const int64_t t = t0 + row;
-    const int c = c_strip + 4 * cg;
-    r[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (t < n_tokens && c < d_model) {
-      if (kBf16) {
-        const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g) + t * d_model + c);
-        r[k] = make_float4(bf16_to_f32(q.x & 0xFFFFu), bf16_to_f32(q.x >> 16), bf16_to_f32(q.y & 0xFFFFu),
-                           bf16_to_f32(q.y >> 16));
-      } else {
-        r[k] = *reinterpret_cast<const float4*>(static_cast<const float*>(g) + t * d_model + c);
-      }
-    }
+  for (int i = 0; i < kChunk / kBwdBins; ++i) {
+    const int r = wave * (kChunk / kBwdBins) + i;
+    const int64_t t = t0 + r;
+    const float* src = t < n_tokens ? g + t * d_model + c : neg_zero + 4 * lane;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(tb + r * kRowBytes), 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ void tile_store(float4* tile, const float4 (&r)[kTileItems], int tid) {
+// bf16 gradients: read through registers (converted to fp32 on the way), so
+// a tile is loaded into registers during the previous chunk and stored at the
+// top of its own; rows past the batch hold -0.0.
+constexpr int kBf16Items = kChunk * kBwdCols / 8 / kBwdThreads;   // 8 bf16 per item: 4
+__device__ __forceinline__ void tile_load_bf16(uint4 (&r)[kBf16Items], const uint16_t* g, int64_t n_tokens,
+                                               int d_model, int64_t t0, int c_strip, int tid) {
 #pragma unroll
-  for (int k = 0; k < kTileItems; ++k) tile[tid + k * kBwdThreads] = r[k];
+  for (int k = 0; k < kBf16Items; ++k) {
+    const int i = tid + k * kBwdThreads;   // row i / 32, 8-column group i % 32
+    const int64_t t = t0 + (i >> 5);
+    const int c = min(c_strip + 8 * (i & 31), d_model - 8);
+    r[k] = t < n_tokens ? *reinterpret_cast<const uint4*>(g + t * d_model + c)
+                        : make_uint4(0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u);
+  }
+}
+__device__ __forceinline__ void tile_store_bf16(char* tb, const uint4 (&r)[kBf16Items], int tid) {
+#pragma unroll
+  for (int k = 0; k < kBf16Items; ++k) {
+    const int i = tid + k * kBwdThreads;
+    float4* d = reinterpret_cast<float4*>(tb + (i >> 5) * kRowBytes + (i & 31) * 32);
+    const uint4 v = r[k];
+    d[0] = make_float4(bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
+                       bf16_to_f32(v.y >> 16));
+    d[1] = make_float4(bf16_to_f32(v.z & 0xFFFFu), bf16_to_f32(v.z >> 16), bf16_to_f32(v.w & 0xFFFFu),
+                       bf16_to_f32(v.w >> 16));
+  }
+}
+
+// The chunk's levels of the workgroup's 8 bins (64 bytes each, from the
+// by-bin copy) into level buffer `lb`: lanes 0..31 of wave 0 copy 16 bytes
+// each.  Bins past n_bins read the last bin's levels (unused).
+__device__ __forceinline__ void levels_dma(char* lb, const uint8_t* lvt, int64_t t_pad, int bin0, int n_bins,
+                                           int64_t t0, int wave, int lane) {
+  if (wave == 0 && lane < 32) {
+    const int j = min(bin0 + (lane >> 2), n_bins - 1);
+    __builtin_amdgcn_global_load_lds(lvt + j * t_pad + t0 + 16 * (lane & 3), (lds_void_t*)lb, 16, 0, 0);
+  }
 }
 
 __device__ __forceinline__ void add4(float4& a, const float4& v) {
@@ -132,100 +147,195 @@ __device__ __forceinline__ void add4(float4& a, const float4& v) {
   a.w += v.w;
 }
 
-// Adds one chunk of this wave's bin: the list's groups of four entries in
-// order (level l's groups, in token order, before level l + 1's), each into
-// acc[l].  The scalar read of a group's entries is issued one group ahead, so
-// that it is answered while the previous group's tile rows are read and each
-// group waits once, for its own rows.
-__device__ __forceinline__ void add_chunk(float4 (&acc)[16], const char* tile_lane, const uint32_t* __restrict__ lst,
-                                          const uint32_t* __restrict__ st) {
-  uint32_t bound[17];
+// The 16 level accumulators of a lane's 4 columns, one 16-wide vector per
+// column, pinned to v64..v127 so that a wave-uniform level can select the
+// accumulator through the GPR index mode.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// acc[L] += row, with L = the token's level: in the GPR index mode (index L,
+// relative source 0 and destination) one v_add_f32 per column adds the row
+// into register 64 + L (+ 16, 32, 48 for the other columns).  The mode keeps
+// its index in M0, which the asm declares as an output, so the compiler sets
+// M0 again wherever it needs it.
+#define DMEL_ADD_LEVEL(L, R)                                                                         \
+  do {                                                                                               \
+    uint32_t m0_out_;                                                                                \
+    asm volatile(                                                                                    \
+        "s_set_gpr_idx_on %5, gpr_idx(SRC0,DST)\n\t"                                                 \
+        "v_add_f32 v64, v64, %6\n\t"                                                                 \
+        "v_add_f32 v80, v80, %7\n\t"                                                                 \
+        "v_add_f32 v96, v96, %8\n\t"                                                                 \
+        "v_add_f32 v112, v112, %9\n\t"                                                               \
+        "s_set_gpr_idx_off"                                                                          \
+        : "+{v[64:79]}"(ax), "+{v[80:95]}"(ay), "+{v[96:111]}"(az), "+{v[112:127]}"(aw), "={m0}"(m0_out_) \
+        : "s"(L), "v"((R).x), "v"((R).y), "v"((R).z), "v"((R).w));                                  \
+  } while (0)
+
+// Pacing of the bin groups of one strip.  They read the same gradient tiles,
+// which the XCD's L2 serves to all of them only while they are close to each
+// other in the batch; left alone they drift apart and each re-reads the
+// tiles from HBM.  Every second chunk one thread of a workgroup publishes the
+// chunk it is at and reads where the other groups of its strip are; the reads
+// are used at the next check, so they cost no wait.  Only a group found more
+// than kPaceLead chunks ahead of the slowest waits, by a bounded poll.
+// Pacing affects speed only: results do not depend on it, and a workgroup
+// whose wait runs out of polls (a group not resident yet) stops pacing for the
+// rest of the call, so the wait is bounded.
+constexpr int kPaceLead = 4;
+constexpr int kPacePolls = 20000;
+constexpr int kMaxGroups = (kEmbMaxBins + kBwdBins - 1) / kBwdBins;   // 10
+struct Pace {
+  int seen[kMaxGroups];   // the groups' chunks as read at the previous check
+  bool on;
+};
+__device__ __forceinline__ void keep_pace(Pace& p, int* strip_prog, int grp, int n_groups, int64_t ch) {
+  const int c = static_cast<int>(ch);
+  int slowest = c;
 #pragma unroll
-  for (int l = 0; l <= 16; ++l) bound[l] = st[l];
-  const int end = static_cast<int>(bound[16]);  // >= 4: a chunk holds at least one token
-  uint4 an = *reinterpret_cast<const uint4*>(lst);
-  int k = 0;
+  for (int q = 0; q < kMaxGroups; ++q)
+    if (q < n_groups) slowest = min(slowest, p.seen[q]);
+  if (c - slowest > kPaceLead) {
+    __hip_atomic_store(strip_prog + grp, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int it = 0;
+    for (; it < kPacePolls; ++it) {
+      slowest = c;
+      for (int q = 0; q < n_groups; ++q)
+        slowest = min(slowest, __hip_atomic_load(strip_prog + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (c - slowest <= kPaceLead) break;
+      __builtin_amdgcn_s_sleep(4);
+    }
+    if (it == kPacePolls) p.on = false;
+  }
+  __hip_atomic_store(strip_prog + grp, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-  for (int l = 0; l < 16; ++l) {
-    const int e = static_cast<int>(bound[l + 1]);
-    for (; k < e; k += 4) {
-      const uint4 a = an;
-      // the next group's entries (the last group's again at the end: always
-      // inside the list)
-      an = *reinterpret_cast<const uint4*>(lst + (k + 4 < end ? k + 4 : end - 4));
-      const float4 v0 = *reinterpret_cast<const float4*>(tile_lane + a.x);
-      const float4 v1 = *reinterpret_cast<const float4*>(tile_lane + a.y);
-      const float4 v2 = *reinterpret_cast<const float4*>(tile_lane + a.z);
-      const float4 v3 = *reinterpret_cast<const float4*>(tile_lane + a.w);
-      add4(acc[l], v0);
-      add4(acc[l], v1);
-      add4(acc[l], v2);
-      add4(acc[l], v3);
+  for (int q = 0; q < kMaxGroups; ++q)
+    if (q < n_groups) p.seen[q] = __hip_atomic_load(strip_prog + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One chunk of the scatter: `cur` holds chunk ch (tile + levels), the copy of
+// chunk ch + 1 goes to `nxt`.  The two buffers are distinct LDS arrays so
+// that the compiler can see that the reads of one do not wait for the copies
+// into the other.
+template <bool kBf16>
+__device__ __forceinline__ void scatter_chunk(char* cur_tile, char* cur_lv, char* nxt_tile, char* nxt_lv,
+                                              int64_t ch, const void* g, int64_t n_tokens, int n_bins, int d_model,
+                                              const uint8_t* lvt, int64_t t_pad, const float* neg_zero,
+                                              int64_t n_chunks, int c_strip, int bin0, bool bin_ok, int wave,
+                                              int lane, int tid, uint4 (&rb)[kBf16 ? kBf16Items : 1],
+                                              f32x16_t& ax, f32x16_t& ay, f32x16_t& az, f32x16_t& aw) {
+  if (kBf16) tile_store_bf16(cur_tile, reinterpret_cast<uint4(&)[kBf16Items]>(rb), tid);
+  // this wave's copies of chunk ch have landed; after the barrier every
+  // wave's have, and every wave is done with chunk ch - 1
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (ch + 1 < n_chunks) {
+    if (kBf16) {
+      tile_load_bf16(reinterpret_cast<uint4(&)[kBf16Items]>(rb), static_cast<const uint16_t*>(g), n_tokens, d_model,
+                     (ch + 1) * kChunk, c_strip, tid);
+    } else {
+      tile_dma(nxt_tile, static_cast<const float*>(g), neg_zero, n_tokens, d_model, (ch + 1) * kChunk, c_strip, wave,
+               lane);
+    }
+    levels_dma(nxt_lv, lvt, t_pad, bin0, n_bins, (ch + 1) * kChunk, wave, lane);
+  }
+  if (bin_ok) {
+    // the wave's 64 levels (the same in every lane) into scalar registers
+    const auto* lw = reinterpret_cast<const uint32_t*>(cur_lv + wave * kChunk);
+    uint32_t w[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) w[q] = __builtin_amdgcn_readfirstlane(lw[q]);
+    const float4* row = reinterpret_cast<const float4*>(cur_tile) + lane;   // token t at row[64 t]
+    float4 r[kChunk];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = row[t * (kRowBytes / 16)];
+#pragma unroll
+    for (int t = 0; t < kChunk; ++t) {
+      if (t + 8 < kChunk) r[t + 8] = row[(t + 8) * (kRowBytes / 16)];
+      const uint32_t L = (w[t >> 2] >> (8 * (t & 3))) & 15u;
+      DMEL_ADD_LEVEL(L, r[t]);
     }
   }
 }
 
-// Workgroup (bin group, strip); see the file comment.  Writes
-// out = acc (or fl32(out + acc) when accumulating), acc being each row's
-// token-order sum over the whole batch.
+// Workgroup (bin group, strip): 8 bins (one wave each) and 256 columns (4
+// per lane), walking every chunk of the batch in order.  Per chunk each wave
+// takes the 64 tokens in order: the token's row from the LDS tile (static
+// offsets, read 8 tokens ahead) is added into the accumulator of the token's
+// level, so every row's gradient is one chain in token order across the
+// whole batch.  Writes out = acc (or fl32(out + acc) when accumulating).
+// Chunk ch is staged in buffer ch % 2: its copy is issued right after the
+// barrier that starts chunk ch - 1 (all waves have then finished chunk ch - 2,
+// the buffer's previous contents), so it lands while chunk ch - 1 is added;
+// one barrier per chunk.
 template <bool kBf16>
 __global__ void __launch_bounds__(kBwdThreads)
 scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_levels, int d_model,
-               const uint32_t* __restrict__ lists, const uint32_t* __restrict__ starts, int64_t n_chunks,
-               int n_groups, int n_strips, float* __restrict__ out, int accumulate) {
-  __shared__ float4 tile[(kChunk + 1) * kBwdCols / 4];  // 128 KB of token rows + the -0.0 row
-  // blockIdx -> (strip, bin group): workgroup b runs on XCD b % 8, and the
-  // bin groups of one strip are 8 apart, so they share the strip's tiles in
-  // that XCD's L2
+               const uint8_t* __restrict__ lvt, int64_t t_pad, const float* __restrict__ neg_zero, int64_t n_chunks,
+               int n_groups, int n_strips, int per_xcd, int* __restrict__ prog, float* __restrict__ out,
+               int accumulate) {
+  __shared__ __attribute__((aligned(1024))) char tile_a[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char tile_b[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char lv_a[kLvBytes];
+  __shared__ __attribute__((aligned(16))) char lv_b[kLvBytes];
+  // blockIdx -> (strip, bin group): workgroup b runs on XCD b % 8; XCD x
+  // takes strips x * per_xcd .. x * per_xcd + per_xcd - 1 with all their bin
+  // groups, so the bin groups of a strip share its tiles in that XCD's L2
   const int bid = static_cast<int>(blockIdx.x);
   const int local = bid >> 3;
   const int grp = local % n_groups;
-  const int strip = (local / n_groups) * 8 + (bid & 7);
-  if (strip >= n_strips) return;  // before any barrier: the whole workgroup leaves
+  const int strip = (bid & 7) * per_xcd + local / n_groups;
+  if (local / n_groups >= per_xcd || strip >= n_strips) return;  // before any barrier: the whole workgroup leaves
+  int* my_prog = prog + strip * n_groups;
+  Pace pace;
+  pace.on = n_groups > 1;
+#pragma unroll
+  for (int q = 0; q < kMaxGroups; ++q) pace.seen[q] = 0;
 
   const int tid = threadIdx.x;
-  // the wave index, made explicitly uniform so that the group lists come
-  // through scalar loads
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int j = grp * kBwdBins + wave;
+  const int bin0 = grp * kBwdBins;
+  const int j = bin0 + wave;
   const bool bin_ok = j < n_bins;
   const int c_strip = strip * kBwdCols;
   const int c0 = c_strip + 4 * lane;
 
-  float4 acc[16];
-#pragma unroll
-  for (int l = 0; l < 16; ++l) acc[l] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  f32x16_t ax = 0.0f, ay = 0.0f, az = 0.0f, aw = 0.0f;
 
-  if (tid < kBwdCols / 4) tile[kChunk * kBwdCols / 4 + tid] = make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
-  float4 r[kTileItems];
-  tile_load<kBf16>(r, g, n_tokens, d_model, 0, c_strip, tid);
-  const char* tile_lane = reinterpret_cast<const char*>(tile) + lane * 16;
-  for (int64_t ch = 0; ch < n_chunks; ++ch) {
-    tile_store(tile, r, tid);
-    __syncthreads();
-    if (ch + 1 < n_chunks) tile_load<kBf16>(r, g, n_tokens, d_model, (ch + 1) * kChunk, c_strip, tid);
-    if (bin_ok) {
-      const int64_t pair = ch * n_bins + j;
-      add_chunk(acc, tile_lane, lists + pair * kListPitch, starts + pair * kOffPitch);
+  uint4 rb[kBf16 ? kBf16Items : 1];
+  if (kBf16) {
+    tile_load_bf16(reinterpret_cast<uint4(&)[kBf16Items]>(rb), static_cast<const uint16_t*>(g), n_tokens, d_model,
+                   0, c_strip, tid);
+  } else {
+    tile_dma(tile_a, static_cast<const float*>(g), neg_zero, n_tokens, d_model, 0, c_strip, wave, lane);
+  }
+  levels_dma(lv_a, lvt, t_pad, bin0, n_bins, 0, wave, lane);
+  for (int64_t ch = 0; ch < n_chunks; ch += 2) {
+    if (pace.on && tid == 0) keep_pace(pace, my_prog, grp, n_groups, ch);
+    scatter_chunk<kBf16>(tile_a, lv_a, tile_b, lv_b, ch, g, n_tokens, n_bins, d_model, lvt, t_pad, neg_zero,
+                         n_chunks, c_strip, bin0, bin_ok, wave, lane, tid, rb, ax, ay, az, aw);
+    if (ch + 1 < n_chunks) {
+      scatter_chunk<kBf16>(tile_b, lv_b, tile_a, lv_a, ch + 1, g, n_tokens, n_bins, d_model, lvt, t_pad, neg_zero,
+                           n_chunks, c_strip, bin0, bin_ok, wave, lane, tid, rb, ax, ay, az, aw);
     }
-    __syncthreads();  // the tile is overwritten next
   }
 
   if (!bin_ok || c0 >= d_model) return;
 #pragma unroll
   for (int l = 0; l < 16; ++l) {
     if (l < n_levels) {
-      const int64_t row = static_cast<int64_t>(j) * n_levels + l;
-      float4* o = reinterpret_cast<float4*>(out + row * d_model + c0);
-      float4 v = acc[l];
+      const int64_t rw = static_cast<int64_t>(j) * n_levels + l;
+      float4* o = reinterpret_cast<float4*>(out + rw * d_model + c0);
+      const float4 a = make_float4(ax[l], ay[l], az[l], aw[l]);
+      float4 v = a;
       if (accumulate) {
         v = *o;
-        add4(v, acc[l]);
+        add4(v, a);
       }
       *o = v;
     }
   }
 }
+#undef DMEL_ADD_LEVEL
 
 // Zero fill (kept out of hipMemsetAsync so that a caller may capture the
 // calls in a graph).
@@ -479,14 +589,22 @@ int strips_per_group(int64_t tblocks, int n_strips) {
 
 }  // namespace
 
-size_t bwd_layout(int64_t n_tokens, int n_bins, size_t* off_starts) {
+size_t bwd_layout(int64_t n_tokens, int n_bins, int d_model, size_t* offs) {
+  // levels by bin [n_bins][t_pad] (t_pad = whole chunks), the row of -0.0,
+  // the pacing counters of every (strip, bin group); nothing for an empty batch
+  if (offs) offs[0] = offs[1] = 0;
+  if (n_tokens <= 0) return 0;
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-  const size_t n_chunks = static_cast<size_t>((n_tokens + kChunk - 1) / kChunk);
-  const size_t pairs = n_chunks * static_cast<size_t>(n_bins);
-  const size_t b_lists = up(pairs * kListPitch * sizeof(uint32_t));
-  const size_t b_starts = up(pairs * kOffPitch * sizeof(uint32_t));
-  if (off_starts) *off_starts = b_lists;
-  return b_lists + b_starts;
+  const size_t t_pad = static_cast<size_t>((n_tokens + kChunk - 1) / kChunk) * kChunk;
+  const size_t b_lvt = up(static_cast<size_t>(n_bins) * t_pad);
+  const size_t b_nz = up(kBwdCols * sizeof(float));
+  const size_t n_groups = static_cast<size_t>((n_bins + kBwdBins - 1) / kBwdBins);
+  const size_t n_strips = static_cast<size_t>((d_model + kBwdCols - 1) / kBwdCols);
+  if (offs) {
+    offs[0] = b_lvt;
+    offs[1] = b_lvt + b_nz;
+  }
+  return b_lvt + b_nz + up(n_groups * n_strips * sizeof(int));
 }
 
 hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels, const void* dsum,
@@ -497,30 +615,35 @@ hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_
     if (accumulate) return hipSuccess;
     return zero_fill(dtable, rows * d_model, stream);
   }
-  size_t off_starts = 0;
-  bwd_layout(n_tokens, n_bins, &off_starts);
-  auto* lists = static_cast<uint32_t*>(workspace);
-  auto* starts = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + off_starts);
+  size_t offs[2];
+  bwd_layout(n_tokens, n_bins, d_model, offs);
+  auto* lvt = static_cast<uint8_t*>(workspace);
+  auto* neg_zero = reinterpret_cast<float*>(static_cast<char*>(workspace) + offs[0]);
+  auto* prog = reinterpret_cast<int*>(static_cast<char*>(workspace) + offs[1]);
   const int64_t n_chunks = (n_tokens + kChunk - 1) / kChunk;
-  const int64_t n_pairs = n_chunks * n_bins;
-  const int64_t bblocks = (n_pairs + 3) / 4;
-  if (bblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bucket_kernel, dim3(static_cast<unsigned>(bblocks)), dim3(256), 0, stream, levels, n_tokens,
-                     n_bins, n_levels, n_pairs, lists, starts);
+  const int64_t t_pad = n_chunks * kChunk;
+  if (n_chunks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(levels_t_kernel, dim3(static_cast<unsigned>(n_chunks)), dim3(256), 0, stream, levels, n_tokens,
+                     n_bins, n_levels, t_pad, lvt, neg_zero);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_groups = (n_bins + kBwdBins - 1) / kBwdBins;
   const int n_strips = (d_model + kBwdCols - 1) / kBwdCols;
-  const int64_t blocks = static_cast<int64_t>((n_strips + 7) / 8) * 8 * n_groups;
+  const int per_xcd = (n_strips + 7) / 8;
+  const int64_t blocks = static_cast<int64_t>(per_xcd) * 8 * n_groups;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // pacing counters start at 0 (a fill kernel, so that the calls can be
+  // captured in a graph)
+  e = zero_fill(reinterpret_cast<float*>(prog), static_cast<int64_t>(n_groups) * n_strips, stream);
+  if (e != hipSuccess) return e;
   if (dsum_bf16) {
     hipLaunchKernelGGL(scatter_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kBwdThreads), 0, stream, dsum,
-                       n_tokens, n_bins, n_levels, d_model, lists, starts, n_chunks, n_groups, n_strips, dtable,
-                       accumulate ? 1 : 0);
+                       n_tokens, n_bins, n_levels, d_model, lvt, t_pad, neg_zero, n_chunks, n_groups, n_strips,
+                       per_xcd, prog, dtable, accumulate ? 1 : 0);
   } else {
     hipLaunchKernelGGL(scatter_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kBwdThreads), 0, stream,
-                       dsum, n_tokens, n_bins, n_levels, d_model, lists, starts, n_chunks, n_groups, n_strips,
-                       dtable, accumulate ? 1 : 0);
+                       dsum, n_tokens, n_bins, n_levels, d_model, lvt, t_pad, neg_zero, n_chunks, n_groups, n_strips,
+                       per_xcd, prog, dtable, accumulate ? 1 : 0);
   }
   return hipGetLastError();
 }

@@ -485,7 +485,7 @@ size_t dmel_embed_backward_workspace_bytes(int64_t n_tokens, int32_t n_bins, int
   if (n_tokens < 0 || n_bins < 1 || n_bins > dmel::kEmbMaxBins || n_levels < 1 || n_levels > dmel::kEmbMaxLevels ||
       d_model < 16)
     return 0;
-  return dmel::bwd_layout(n_tokens, n_bins, nullptr);
+  return dmel::bwd_layout(n_tokens, n_bins, d_model, nullptr);
 }
 
 int dmel_embed_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels, const void* dsum,

@@ -108,7 +108,7 @@ hipError_t launch_shortconv(const uint16_t* x, int64_t n_tokens, int channels, c
 
 // Backward of the embedding (table gradient: every row sums its tokens'
 // gradients in token order from +0, exactly) and of its RMSNorm.
-size_t bwd_layout(int64_t n_tokens, int n_bins, size_t* off_starts);
+size_t bwd_layout(int64_t n_tokens, int n_bins, int d_model, size_t* offs);
 hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels, const void* dsum,
                                  bool dsum_bf16, int d_model, float* dtable, bool accumulate, void* workspace,
                                  hipStream_t stream);
