@@ -15,3 +15,11 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_terminal_summary(terminalreporter):
+    import json
+
+    from tests import _record
+    for case, counts in _record.RECORDS:
+        terminalreporter.write_line(f"parity {case}: {json.dumps(counts, sort_keys=True)}")

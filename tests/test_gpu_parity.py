@@ -100,6 +100,52 @@ def test_c2_bursts_rmsnorm(env, table):
     print(f"RMSNorm max rel err {rel:.2e}; bf16 midpoint differences {nd}")
 
 
+def test_rmsnorm_weight_released_layout(env, table):
+    # a non-unit RMSNorm weight on the released 80 x 16 layout, fp32 and bf16
+    # out, against the oracle: the levels of the 8 x 30 s bursts workload
+    dm, ctx = env
+    x = synth.bursts_clips(seed=1, n_clips=8, n_samples=480000).numpy()
+    print("case: 8 x 30 s bursts, RMSNorm weight U(0.5, 1.5)", flush=True)
+    ora_lv = np.concatenate([o.levels(x[c]) for c in range(8)])
+    w = np.random.default_rng(31).uniform(0.5, 1.5, 6144).astype(np.float32)
+    tb = _tbits(table)
+    _, exact = o.embed(ora_lv, tb, rms_weight=w)
+    rel = P.check_rms_f32(P.gpu_embed(ora_lv, table, 6144, out_dtype="f32", rms_weight=w), exact)
+    nd = P.check_rms_bf16(P.gpu_embed(ora_lv, table, 6144, out_dtype="bf16", rms_weight=w), exact)
+    _record_rms("rmsnorm_weight_bursts", rel, nd, ora_lv.shape[0])
+
+
+def _cancelling_table(sigma, seed=5):
+    # rows of bin j = (-1)^j mu + N(0, sigma): the 80 rows a token selects
+    # cancel, so |s|^2 is far smaller than the sum of the Gram terms
+    rng = np.random.default_rng(seed)
+    mu = rng.standard_normal(6144)
+    mu *= np.sqrt(10.0) / np.linalg.norm(mu)
+    sign = np.where(np.arange(80) % 2 == 0, 1.0, -1.0)
+    e = np.repeat(sign, 16)[:, None] * mu[None, :] + sigma * rng.standard_normal((1280, 6144))
+    return torch.from_numpy(o.f32_to_bf16(e.astype(np.float32)).view(np.int16).copy())
+
+
+@pytest.mark.parametrize("sigma", [0.02, 0.002])
+def test_rmsnorm_cancelling_table(env, sigma):
+    dm, ctx = env
+    print(f"case: cancelling table |mu|^2 = 10, sigma {sigma}, random weight", flush=True)
+    t = _cancelling_table(sigma)
+    rng = np.random.default_rng(32)
+    lv = rng.integers(0, 16, (2 * 1024 + 37, 80)).astype(np.uint8)
+    w = rng.uniform(0.5, 1.5, 6144).astype(np.float32)
+    _, exact = o.embed(lv, _tbits(t), rms_weight=w)
+    rel = P.check_rms_f32(P.gpu_embed(lv, t, 6144, out_dtype="f32", rms_weight=w), exact)
+    nd = P.check_rms_bf16(P.gpu_embed(lv, t, 6144, out_dtype="bf16", rms_weight=w), exact)
+    _record_rms(f"rmsnorm_cancelling_sigma{sigma}", rel, nd, lv.shape[0])
+
+
+def _record_rms(case, rel, nd, n):
+    from tests import _record
+    _record.record(case, tokens=int(n), max_rel_err_f32=rel, bf16_midpoint_ulps=nd)
+    print(f"{case}: max rel err {rel:.2e}; bf16 midpoint differences {nd}")
+
+
 def test_embed_tiles_and_ragged_tail(env):
     dm, ctx = env
     rng = np.random.default_rng(21)
