@@ -194,7 +194,7 @@ def bench_backward(args):
     del audio
     table = synth.table_bf16(seed=1234).to(dev)
     w = torch.ones(d, dtype=torch.float32, device=dev)
-    gram = torch.empty((1280, 1280), dtype=torch.float32, device=dev)
+    gram = torch.empty((1280, 1280), dtype=torch.float64, device=dev)
     dm.dmel_rms_gram(table, d, gram)
     scale = torch.empty(T, dtype=torch.float32, device=dev)
     dm.dmel_rms_scale(lv, T, gram, d, 1e-6, scale)
@@ -588,7 +588,7 @@ def bench_stream(args):
     hops = synth.streaming_hops(seed=3, n_streams=S, n_steps=K + args.warmup, device=dev)
     table = synth.table_bf16(seed=1234).to(dev)
     rms_w = torch.ones(6144, dtype=torch.float32, device=dev)
-    gram = torch.empty((1280, 1280), dtype=torch.float32, device=dev)
+    gram = torch.empty((1280, 1280), dtype=torch.float64, device=dev)
     ctx = dm.dmel_create(0)
     dm.dmel_rms_gram(table, 6144, gram)
     so, fo, _ = dm.clip_offsets([800] * S, dev)
@@ -709,7 +709,7 @@ def bench_batch(args):
     so, fo, T = dm.clip_offsets([clip_len] * n_clips, dev)
     assert T == n_tok
     out = torch.empty((n_tok, d), dtype=torch.int16, device=dev)
-    gram = torch.empty((1280, 1280), dtype=torch.float32, device=dev)
+    gram = torch.empty((1280, 1280), dtype=torch.float64, device=dev)
     levels = torch.empty((n_tok, n_bins), dtype=torch.uint8, device=dev)
     scale = torch.empty(n_tok, dtype=torch.float32, device=dev)
     dm.dmel_rms_gram(table, d, gram, **lay)   # once per table (weight preparation), outside the step

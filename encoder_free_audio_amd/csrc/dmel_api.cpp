@@ -331,19 +331,19 @@ int dmel_levels(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "frontend launch");
 }
 
-int dmel_rms_gram(const uint16_t* table, int32_t n_bins, int32_t n_levels, int32_t d_model, float* gram,
+int dmel_rms_gram(const uint16_t* table, int32_t n_bins, int32_t n_levels, int32_t d_model, double* gram,
                   void* stream) {
   int rc = check_layout(n_bins, n_levels);
   if (rc != DMEL_OK) return rc;
   rc = check_table(table, d_model);
   if (rc != DMEL_OK) return rc;
   if (gram == nullptr) return fail(DMEL_EINVAL, "gram is NULL");
-  if (!aligned(gram, 4)) return fail(DMEL_EALIGN, "gram is not 4-byte aligned");
+  if (!aligned(gram, 16)) return fail(DMEL_EALIGN, "gram is not 16-byte aligned");
   hipError_t e = dmel::launch_gram(table, n_bins, n_levels, d_model, gram, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "gram launch");
 }
 
-int dmel_rms_scale(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels, const float* gram,
+int dmel_rms_scale(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels, const double* gram,
                    int32_t d_model, float eps, float* scale, void* stream) {
   if (n_tokens < 0) return fail(DMEL_EINVAL, "n_tokens is negative");
   int rc = check_layout(n_bins, n_levels);
@@ -354,7 +354,8 @@ int dmel_rms_scale(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int3
   if (levels == nullptr || gram == nullptr || scale == nullptr) return fail(DMEL_EINVAL, "NULL pointer argument");
   if (released_layout(n_bins, n_levels) && !aligned(levels, 16))
     return fail(DMEL_EALIGN, "levels is not 16-byte aligned");
-  if (!aligned(gram, 4) || !aligned(scale, 4)) return fail(DMEL_EALIGN, "gram / scale not 4-byte aligned");
+  if (!aligned(gram, 16)) return fail(DMEL_EALIGN, "gram is not 16-byte aligned");
+  if (!aligned(scale, 4)) return fail(DMEL_EALIGN, "scale is not 4-byte aligned");
   hipError_t e = dmel::launch_rms_scale(levels, n_tokens, n_bins, n_levels, gram, d_model, eps, scale, nullptr,
                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "rms_scale launch");
@@ -391,7 +392,7 @@ size_t dmel_forward_workspace_bytes(int64_t n_frames_total) {
 
 int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total, const int64_t* sample_off,
                  const int64_t* frame_off, int32_t n_clips, int64_t n_frames_total, const float* carry,
-                 const uint16_t* table, int32_t d_model, const float* rms_weight, const float* gram, float eps,
+                 const uint16_t* table, int32_t d_model, const float* rms_weight, const double* gram, float eps,
                  void* out, int32_t out_dtype, int64_t out_row_stride, const int64_t* out_rows, void* workspace,
                  size_t workspace_bytes, void* stream) {
   int rc = check_audio(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, out, "out");
@@ -407,7 +408,8 @@ int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_tota
   if (rms_weight != nullptr) {
     if (gram == nullptr) return fail(DMEL_EINVAL, "rms_weight given without gram");
     if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(DMEL_EINVAL, "eps must be finite and >= 0");
-    if (!aligned(rms_weight, 4) || !aligned(gram, 4)) return fail(DMEL_EALIGN, "rms_weight / gram not 4-byte aligned");
+    if (!aligned(rms_weight, 4)) return fail(DMEL_EALIGN, "rms_weight is not 4-byte aligned");
+    if (!aligned(gram, 16)) return fail(DMEL_EALIGN, "gram is not 16-byte aligned");
   }
   const size_t need = dmel_forward_workspace_bytes(n_frames_total);
   if (workspace_bytes < need)

@@ -147,15 +147,15 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, i
 }
 
 // ---------------------------------------------------------------------------
-// Gram matrix G = E E^T (fp64 accumulation of exact bf16 products, stored
-// fp32).  One workgroup per 16 x 16 block (bin j rows x bin j' rows), j <= j'.
-// G is indexed in the 80 x 16 row space (16 * bin + level) for every layout;
-// rows outside the n_bins x n_levels layout are zero.
+// Gram matrix G = E E^T, fp64 (accumulation of exact bf16 products over the
+// columns, stored as fp64).  One workgroup per 16 x 16 block (bin j rows x
+// bin j' rows), j <= j'.  G is indexed in the 80 x 16 row space (16 * bin +
+// level) for every layout; rows outside the n_bins x n_levels layout are 0.
 // ---------------------------------------------------------------------------
 constexpr int kGramChunk = 256;
 
 __global__ void __launch_bounds__(256)
-gram_kernel(const uint16_t* __restrict__ table, int n_bins, int n_levels, int d_model, float* __restrict__ gram) {
+gram_kernel(const uint16_t* __restrict__ table, int n_bins, int n_levels, int d_model, double* __restrict__ gram) {
   __shared__ float a_s[16][kGramChunk + 1];
   __shared__ float b_s[16][kGramChunk + 1];
   // blockIdx.x enumerates the upper-triangle pairs (j, j')
@@ -186,127 +186,155 @@ gram_kernel(const uint16_t* __restrict__ table, int n_bins, int n_levels, int d_
     for (int c = 0; c < width; ++c) acc = fma(static_cast<double>(a_s[ri][c]), static_cast<double>(b_s[rj][c]), acc);
   }
   const int r = kLevels * j + ri, rp = kLevels * jp + rj;
-  gram[static_cast<int64_t>(r) * kRows + rp] = static_cast<float>(acc);
-  gram[static_cast<int64_t>(rp) * kRows + r] = static_cast<float>(acc);
+  gram[static_cast<int64_t>(r) * kRows + rp] = acc;
+  gram[static_cast<int64_t>(rp) * kRows + r] = acc;
 }
 
 // ---------------------------------------------------------------------------
-// RMSNorm scale from the Gram matrix: |s|^2 = sum_j G[r_j][r_j]
-// + 2 sum_{j < j'} G[r_j][r_j'].  A workgroup owns 512 tokens (one per
-// thread).  For each bin j the 16 rows 16j..16j+15 of the upper triangle
-// (columns 16j..1279) are staged in LDS; the thread then adds the diagonal
-// term and the 79 - j terms of its token.  The token's 80 levels live in
-// registers as a byte string that is shifted by one byte per bin, so that the
-// level of bin j + q is always byte q: every index in the unrolled inner loop
-// is static, and the 79 - j lookups of a bin are independent loads.  Partial
-// sums per bin are fp32, the total fp64.
+// RMSNorm scale from the Gram matrix.  For a token with rows r_0 .. r_79
+// (r_j = 16 j + L_j), |s|^2 = sum_j (d_j + 2 o_j) with d_j = G[r_j][r_j] and
+// o_j = sum_{j' > j} G[r_j][r_j'].  Every kernel below evaluates it in fp64
+// in the same order: o_j from +0 in increasing j', the total from +0 adding
+// d_j then 2 o_j for j = 0 .. 79; then r = 1 / sqrt(total / d_model + eps)
+// in fp64, rounded to fp32.  A masked term adds +0.0, which leaves a sum that
+// started at +0.0 unchanged (such a sum is never -0.0), so the kernels give a
+// token the same bits whichever of them runs.
+//
+// The levels of a token are kept in registers as 80 bytes (bin j in byte
+// j % 4 of word j / 4), indexed statically.
 // ---------------------------------------------------------------------------
-constexpr int kScaleThreads = 1024;
-constexpr int kScaleTok = 2;                            // tokens per thread
-constexpr int kScaleBlock = kScaleThreads * kScaleTok;  // tokens per workgroup
-constexpr int kGPitch = kRows + 17;  // staged row pitch (floats): spreads the 16 rows over the banks
+__device__ __forceinline__ uint32_t level_byte(const uint32_t (&lw)[20], int j) {
+  return (lw[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+}
 
-// Stages rows c0 .. c0 + 15 of G, columns c0 .. 1279, at g_s[r * kGPitch +
-// c - c0]: a workgroup of 1024 threads gives each row 64 threads, which read
-// 4 columns per step (one 16-byte read when G is 16-byte aligned), with no
-// index division.
-__device__ __forceinline__ void stage_gram_rows(float* g_s, const float* __restrict__ gram, int c0, int tid) {
+__device__ __forceinline__ void load_token_levels(uint32_t (&lw)[20], const uint8_t* levels, int64_t t, bool active,
+                                                  bool any_layout, int n_bins, int n_levels) {
+  if (active && any_layout) {
+    load_levels_any(lw, levels, t, n_bins, static_cast<uint32_t>(n_levels - 1));
+  } else if (active) {
+    const uint4* p = reinterpret_cast<const uint4*>(levels + t * kMels);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const uint4 q = p[i];
+      lw[4 * i + 0] = clamp_levels(q.x);
+      lw[4 * i + 1] = clamp_levels(q.y);
+      lw[4 * i + 2] = clamp_levels(q.z);
+      lw[4 * i + 3] = clamp_levels(q.w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 20; ++i) lw[i] = 0;
+  }
+}
+
+// Rows 16 j .. 16 j + 15 of G, columns c0 .. c0 + width - 1, staged in LDS as
+// g_s[r * kGPitch + c - c0] (fp64): the 16 rows of bin j over a part of the
+// upper triangle.  A part spans at most kGCols columns (64 bins); bins
+// 0 .. 15 take two parts.  1024 threads: 64 per row, 16-byte reads.
+constexpr int kGCols = 1024;
+constexpr int kGPitch = kGCols + 1;           // doubles per staged row (odd: the 16 rows start in different banks)
+constexpr int kGStageBytes = 16 * kGPitch * 8;  // 131,200
+constexpr int kScaleThreads = 1024;
+__device__ __forceinline__ void stage_gram_part(double* g_s, const double* __restrict__ gram, int j, int c0, int width,
+                                                int tid) {
   const int r = tid >> 6;  // 0..15
   const int q = tid & 63;
-  const float* src = gram + static_cast<int64_t>(c0 + r) * kRows + c0;
-  float* dst = g_s + r * kGPitch;
-  const int width = kRows - c0;  // a multiple of 16
-  const bool vec = (reinterpret_cast<uintptr_t>(gram) & 15) == 0;
-  for (int c = 4 * q; c < width; c += 256) {
-    float4 v;
-    if (vec) {
-      v = *reinterpret_cast<const float4*>(src + c);
-    } else {
-      v = make_float4(src[c], src[c + 1], src[c + 2], src[c + 3]);
-    }
+  const double* src = gram + static_cast<int64_t>(kLevels * j + r) * kRows + c0;
+  double* dst = g_s + r * kGPitch;
+  for (int c = 2 * q; c < width; c += 128) {
+    const double2 v = *reinterpret_cast<const double2*>(src + c);
     dst[c] = v.x;
     dst[c + 1] = v.y;
-    dst[c + 2] = v.z;
-    dst[c + 3] = v.w;
   }
 }
 
-// Off-diagonal terms q = 1..qlim of one staged row block (q = bin offset from
-// the block's bin).  QMAX bounds qlim for the range of bins the caller is in,
-// so the loop is fully unrolled with static register indices; terms past
-// qlim are read (inside the staged row pitch) but replaced by 0 in a select.
-template <int QMAX>
-__device__ __forceinline__ void row_terms(float (&off)[kScaleTok], const float* const (&row)[kScaleTok],
-                                          const uint32_t (&rot)[kScaleTok][20], int qlim) {
+// Adds the terms of bins j' = j + q, q = Q0 .. Q1 (static), q <= qlim, of one
+// token to o: row[16 q + L_j' - base] with the row of level L_j staged from
+// column 16 j + base.  The bytes of bins j, j + 1, ... are bytes 0, 1, ... of
+// rot.  Masked terms read column 0 of the row and add +0.0.
+template <int Q0, int Q1>
+__device__ __forceinline__ void gram_terms(double& o, const double* row, const uint32_t (&rot)[20], int qlim,
+                                           int base) {
 #pragma unroll
-  for (int q = 1; q <= QMAX; ++q) {
+  for (int q = Q0; q <= Q1; ++q) {
     const bool use = q <= qlim;
-#pragma unroll
-    for (int k = 0; k < kScaleTok; ++k) {
-      const float v = row[k][kLevels * q + ((rot[k][q >> 2] >> (8 * (q & 3))) & 0xFFu)];
-      off[k] += use ? v : 0.0f;
-    }
+    const int idx = use ? kLevels * q + static_cast<int>(level_byte(rot, q)) - base : 0;
+    const double v = row[idx];
+    o += use ? v : 0.0;
   }
 }
+
+// The off-diagonal sum o_j of one token for bin j from the staged part
+// starting at column 16 j + base (part 1: base 0, bins j .. j + 63; part 2:
+// base 1024, bins j + 64 .. 79).  QMAX bounds 79 - j for the caller's range of
+// bins, so the loop is unrolled with static register indices.
+template <int QMAX>
+__device__ __forceinline__ void part1_terms(double& o, const double* row, const uint32_t (&rot)[20], int qlim) {
+  gram_terms<1, (QMAX < 63 ? QMAX : 63)>(o, row, rot, qlim, 0);
+}
+
+// Large batches: a workgroup owns 2048 tokens (two per thread); for each bin
+// the bin's 16 rows of G are staged part by part and every token adds its
+// terms.  The token's levels are a byte string shifted down by one byte per
+// bin (v_alignbyte), so that the level of bin j + q is always byte q.
+constexpr int kScaleTok = 2;                            // tokens per thread
+constexpr int kScaleBlock = kScaleThreads * kScaleTok;  // tokens per workgroup
 
 __global__ void __launch_bounds__(kScaleThreads)
 rms_scale_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels,
-                 const float* __restrict__ gram, int d_model, float eps, float* __restrict__ scale) {
-  __shared__ float g_s[16 * kGPitch];  // 83 KB
+                 const double* __restrict__ gram, int d_model, float eps, float* __restrict__ scale) {
+  __shared__ double g_s[16 * kGPitch];  // 131 KB
   const int tid = threadIdx.x;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kScaleBlock + tid;
+  const bool any = n_bins != kMels || n_levels != kLevels;
   uint32_t rot[kScaleTok][20];
   double total[kScaleTok];
 #pragma unroll
   for (int k = 0; k < kScaleTok; ++k) {
     const int64_t t = t0 + static_cast<int64_t>(k) * kScaleThreads;
     total[k] = 0.0;
-    if (t < n_tokens && (n_bins != kMels || n_levels != kLevels)) {
-      load_levels_any(rot[k], levels, t, n_bins, static_cast<uint32_t>(n_levels - 1));
-    } else if (t < n_tokens) {
-      const uint4* p = reinterpret_cast<const uint4*>(levels + t * kMels);
-#pragma unroll
-      for (int i = 0; i < 5; ++i) {
-        const uint4 q = p[i];
-        rot[k][4 * i + 0] = clamp_levels(q.x);
-        rot[k][4 * i + 1] = clamp_levels(q.y);
-        rot[k][4 * i + 2] = clamp_levels(q.z);
-        rot[k][4 * i + 3] = clamp_levels(q.w);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 20; ++i) rot[k][i] = 0;
-    }
+    load_token_levels(rot[k], levels, t, t < n_tokens, any, n_bins, n_levels);
   }
   for (int j = 0; j < kMels; ++j) {
     const int c0 = kLevels * j;
+    const int qlim = kMels - 1 - j;
     __syncthreads();
-    stage_gram_rows(g_s, gram, c0, tid);
+    stage_gram_part(g_s, gram, j, c0, min(kRows - c0, kGCols), tid);
     __syncthreads();
-    // rot byte q = level of bin j + q; staged column of bin j + q, level L: 16 q + L
-    const float* row[kScaleTok];
-    float off[kScaleTok];
+    double off[kScaleTok], diag[kScaleTok];
+    const double* row[kScaleTok];
 #pragma unroll
     for (int k = 0; k < kScaleTok; ++k) {
       const uint32_t lj = rot[k][0] & 0xFFu;
       row[k] = g_s + lj * kGPitch;
-      off[k] = 0.0f;
-      total[k] += static_cast<double>(row[k][lj]);  // diagonal term
-    }
-    const int qlim = kMels - 1 - j;
-    switch (j / 10) {
-      case 0: row_terms<79>(off, row, rot, qlim); break;
-      case 1: row_terms<69>(off, row, rot, qlim); break;
-      case 2: row_terms<59>(off, row, rot, qlim); break;
-      case 3: row_terms<49>(off, row, rot, qlim); break;
-      case 4: row_terms<39>(off, row, rot, qlim); break;
-      case 5: row_terms<29>(off, row, rot, qlim); break;
-      case 6: row_terms<19>(off, row, rot, qlim); break;
-      default: row_terms<9>(off, row, rot, qlim); break;
+      diag[k] = row[k][lj];
+      off[k] = 0.0;
     }
 #pragma unroll
     for (int k = 0; k < kScaleTok; ++k) {
-      total[k] += 2.0 * static_cast<double>(off[k]);
+      switch (j / 10) {
+        case 0: part1_terms<79>(off[k], row[k], rot[k], qlim); break;
+        case 1: part1_terms<69>(off[k], row[k], rot[k], qlim); break;
+        case 2: part1_terms<59>(off[k], row[k], rot[k], qlim); break;
+        case 3: part1_terms<49>(off[k], row[k], rot[k], qlim); break;
+        case 4: part1_terms<39>(off[k], row[k], rot[k], qlim); break;
+        case 5: part1_terms<29>(off[k], row[k], rot[k], qlim); break;
+        case 6: part1_terms<19>(off[k], row[k], rot[k], qlim); break;
+        default: part1_terms<9>(off[k], row[k], rot[k], qlim); break;
+      }
+    }
+    if (qlim >= 64) {
+      // bins j + 64 .. 79 (j <= 15)
+      __syncthreads();
+      stage_gram_part(g_s, gram, j, c0 + kGCols, kRows - c0 - kGCols, tid);
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kScaleTok; ++k) gram_terms<64, 79>(off[k], row[k], rot[k], qlim, kGCols);
+    }
+#pragma unroll
+    for (int k = 0; k < kScaleTok; ++k) {
+      total[k] += diag[k];
+      total[k] += 2.0 * off[k];
       // shift the byte string down by one byte
 #pragma unroll
       for (int i = 0; i < 19; ++i) rot[k][i] = __builtin_amdgcn_alignbyte(rot[k][i + 1], rot[k][i], 1);
@@ -323,21 +351,18 @@ rms_scale_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bin
   }
 }
 
-// Same scale for small batches, without staging: one thread per (token, bin j)
-// reads row r_j of G straight from memory (L2-resident) and forms the bin's
-// fp32 diagonal and off-diagonal sums exactly as rms_scale_kernel does (same
-// terms, same order); the token's total is then summed in bin order in fp64 by
-// one thread.  The arithmetic is identical to rms_scale_kernel's, so a token
-// gets the same scale whichever kernel runs, whatever the batch size.
+// Small batches without a workspace: one thread per (token, bin j) reads row
+// r_j of G straight from memory and forms d_j and o_j (same terms, same
+// order); the token's total is then summed in bin order by one thread.
 constexpr int kDirTok = 4;                  // tokens per workgroup
 constexpr int kDirThreads = kDirTok * kMels;  // 320
 
 __global__ void __launch_bounds__(kDirThreads)
 rms_scale_direct_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels,
-                        const float* __restrict__ gram, int d_model, float eps, float* __restrict__ scale) {
+                        const double* __restrict__ gram, int d_model, float eps, float* __restrict__ scale) {
   __shared__ __attribute__((aligned(16))) uint8_t lv_s[kDirTok][kMels];
-  __shared__ float d_s[kDirTok][kMels];
-  __shared__ float o_s[kDirTok][kMels];
+  __shared__ double d_s[kDirTok][kMels];
+  __shared__ double o_s[kDirTok][kMels];
   const int tid = threadIdx.x;
   const int tok = tid / kMels;
   const int j = tid - tok * kMels;
@@ -352,112 +377,107 @@ rms_scale_direct_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, in
   __syncthreads();
   if (active) {
     const int rj = kLevels * j + lv_s[tok][j];
-    const float* row = gram + static_cast<int64_t>(rj) * kRows;
-    const float diag = row[rj];
-    // all lookups are issued at once (their addresses are independent) and
-    // added in bin order; the terms of bins jp <= j are +0.0, which leave the
-    // sum at +0.0 until its first real term (a sum that starts at +0.0 never
-    // becomes -0.0), exactly as the staged kernel's masked terms
+    const double* row = gram + static_cast<int64_t>(rj) * kRows;
     uint32_t lw[20];
 #pragma unroll
     for (int i = 0; i < 20; ++i) lw[i] = reinterpret_cast<const uint32_t*>(lv_s[tok])[i];
-    float v[kMels];
+    // terms of bins jp <= j are +0.0; sixteen lookups are issued together
+    double off = 0.0;
 #pragma unroll
-    for (int jp = 0; jp < kMels; ++jp) {
-      const uint32_t L = (lw[jp >> 2] >> (8 * (jp & 3))) & 0xFFu;
-      v[jp] = jp > j ? row[kLevels * jp + L] : 0.0f;
+    for (int jb = 0; jb < kMels; jb += 16) {
+      double v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = row[kLevels * (jb + i) + level_byte(lw, jb + i)];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) off += jb + i > j ? v[i] : 0.0;
     }
-    float off = 0.0f;
-#pragma unroll
-    for (int jp = 0; jp < kMels; ++jp) off += v[jp];
-    d_s[tok][j] = diag;
+    d_s[tok][j] = row[rj];
     o_s[tok][j] = off;
   }
   __syncthreads();
   if (active && j == 0) {
     double total = 0.0;
-#pragma unroll 16
     for (int jj = 0; jj < kMels; ++jj) {
-      total += static_cast<double>(d_s[tok][jj]);
-      total += 2.0 * static_cast<double>(o_s[tok][jj]);
+      total += d_s[tok][jj];
+      total += 2.0 * o_s[tok][jj];
     }
     const double ms = total / static_cast<double>(d_model);
     scale[t] = static_cast<float>(1.0 / sqrt(ms + static_cast<double>(eps)));
   }
 }
 
-// Same scale for small batches with a workspace, bin-parallel: a workgroup
-// takes one bin j and 1024 tokens (one per thread), stages the 16 rows of bin
-// j of the upper triangle of G in LDS (as rms_scale_kernel does) and writes
-// each token's diagonal term and fp32 off-diagonal sum of bin j (same terms,
-// same order) to part[j][token]; rms_total_kernel then adds the 80 bins of
-// each token in bin order in fp64.  Identical arithmetic again, so the scale
-// does not depend on the kernel that computed it.  The token's levels stay in
-// registers as 80 bytes; the lookups run over a static bin index jp = 0..79
-// (terms of bins jp <= j are +0.0, which leave the sum at +0.0 until its first
-// real term: a sum that starts at +0.0 never becomes -0.0), so every byte
-// index is static and all lookups are independent.
+// Small batches with a workspace, bin-parallel: a workgroup takes one bin j
+// and 1024 tokens (one per thread), stages bin j's rows of G part by part and
+// writes each token's (d_j, o_j) to part[j][token]; rms_total_kernel then adds
+// the 80 bins of each token in order.  The lookups run over a static bin
+// index (terms of bins jp <= j are +0.0), so every byte index is static.
 constexpr int kBinTok = 1024;
-static_assert(kBinTok == 1024 && kScaleThreads == 1024, "stage_gram_rows gives each of 16 rows 64 threads");
+static_assert(kBinTok == kScaleThreads, "stage_gram_part gives each of 16 rows 64 threads");
 
 template <bool kAny>
 __global__ void __launch_bounds__(kBinTok)
 rms_bin_partials_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels,
-                        const float* __restrict__ gram, int n_chunks, float2* __restrict__ part) {
-  __shared__ float g_s[16 * kGPitch];              // 83 KB
+                        const double* __restrict__ gram, int n_chunks, double2* __restrict__ part) {
+  __shared__ double g_s[16 * kGPitch];   // 131 KB
   const int tid = threadIdx.x;
   const int j = static_cast<int>(blockIdx.x / static_cast<unsigned>(n_chunks));  // heavy (small) bins first
   const int64_t t = static_cast<int64_t>(blockIdx.x % static_cast<unsigned>(n_chunks)) * kBinTok + tid;
   const bool active = t < n_tokens;
   const int c0 = kLevels * j;
-  stage_gram_rows(g_s, gram, c0, tid);
+  stage_gram_part(g_s, gram, j, c0, min(kRows - c0, kGCols), tid);
   uint32_t lw[20];
-  if (active && kAny) {
-    load_levels_any(lw, levels, t, n_bins, static_cast<uint32_t>(n_levels - 1));
-  } else if (active) {
-    const uint4* p = reinterpret_cast<const uint4*>(levels + t * kMels);
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const uint4 q = p[i];
-      lw[4 * i + 0] = clamp_levels(q.x);
-      lw[4 * i + 1] = clamp_levels(q.y);
-      lw[4 * i + 2] = clamp_levels(q.z);
-      lw[4 * i + 3] = clamp_levels(q.w);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 20; ++i) lw[i] = 0;
-  }
+  load_token_levels(lw, levels, t, active, kAny, n_bins, n_levels);
   __syncthreads();
-  if (!active) return;
   uint32_t lj = 0;
 #pragma unroll
-  for (int jp = 0; jp < kMels; ++jp) lj = jp == j ? (lw[jp >> 2] >> (8 * (jp & 3))) & 0xFFu : lj;
-  const float* row = g_s + lj * kGPitch - c0;   // row[16 jp + L] = G[16 j + lj][16 jp + L]
-  float v[kMels];
+  for (int jp = 0; jp < kMels; ++jp) lj = jp == j ? level_byte(lw, jp) : lj;
+  const double* row = g_s + lj * kGPitch;   // row[16 (jp - j) + L] = G[16 j + lj][16 jp + L]
+  const double diag = row[lj];
+  // part 1: bins jp < j + 64 (inside the staged columns), in order, sixteen
+  // lookups issued together
+  double off = 0.0;
 #pragma unroll
-  for (int jp = 0; jp < kMels; ++jp) {
-    const uint32_t L = (lw[jp >> 2] >> (8 * (jp & 3))) & 0xFFu;
-    // (the address stays inside the staged rows for every jp)
-    const float g = row[jp > j ? kLevels * jp + static_cast<int>(L) : c0];
-    v[jp] = jp > j ? g : 0.0f;
+  for (int jb = 0; jb < kMels; jb += 16) {
+    double v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int jp = jb + i;
+      const bool use = jp > j && jp - j < 64;
+      v[i] = row[use ? kLevels * (jp - j) + static_cast<int>(level_byte(lw, jp)) : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int jp = jb + i;
+      off += (jp > j && jp - j < 64) ? v[i] : 0.0;
+    }
+    // keep the next group's lookups after this group's adds (registers)
+    asm volatile("" : "+v"(off)::"memory");
   }
-  float off = 0.0f;
+  if (j < kMels - 64) {
+    // part 2: bins j + 64 .. 79 (j <= 15; uniform over the workgroup)
+    __syncthreads();
+    stage_gram_part(g_s, gram, j, c0 + kGCols, kRows - c0 - kGCols, tid);
+    __syncthreads();
 #pragma unroll
-  for (int jp = 0; jp < kMels; ++jp) off += v[jp];
-  part[static_cast<int64_t>(j) * n_tokens + t] = make_float2(row[c0 + lj], off);
+    for (int jp = 64; jp < kMels; ++jp) {
+      const bool use = jp - j >= 64;
+      const int idx = use ? kLevels * (jp - j) + static_cast<int>(level_byte(lw, jp)) - kGCols : 0;
+      const double v = row[idx];
+      off += use ? v : 0.0;
+    }
+  }
+  if (active) part[static_cast<int64_t>(j) * n_tokens + t] = make_double2(diag, off);
 }
 
 __global__ void __launch_bounds__(256)
-rms_total_kernel(const float2* __restrict__ part, int64_t n_tokens, int d_model, float eps, float* __restrict__ scale) {
+rms_total_kernel(const double2* __restrict__ part, int64_t n_tokens, int d_model, float eps, float* __restrict__ scale) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (t >= n_tokens) return;
   double total = 0.0;
-#pragma unroll 16
   for (int j = 0; j < kMels; ++j) {
-    const float2 v = part[static_cast<int64_t>(j) * n_tokens + t];
-    total += static_cast<double>(v.x);
-    total += 2.0 * static_cast<double>(v.y);
+    const double2 v = part[static_cast<int64_t>(j) * n_tokens + t];
+    total += v.x;
+    total += 2.0 * v.y;
   }
   const double ms = total / static_cast<double>(d_model);
   scale[t] = static_cast<float>(1.0 / sqrt(ms + static_cast<double>(eps)));
@@ -531,7 +551,7 @@ hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, int n_bins, int
   return hipGetLastError();
 }
 
-hipError_t launch_gram(const uint16_t* table, int n_bins, int n_levels, int d_model, float* gram,
+hipError_t launch_gram(const uint16_t* table, int n_bins, int n_levels, int d_model, double* gram,
                        hipStream_t stream) {
   const int pairs = kMels * (kMels + 1) / 2;
   hipLaunchKernelGGL(gram_kernel, dim3(pairs), dim3(256), 0, stream, table, n_bins, n_levels, d_model, gram);
@@ -539,16 +559,16 @@ hipError_t launch_gram(const uint16_t* table, int n_bins, int n_levels, int d_mo
 }
 
 size_t rms_partials_bytes(int64_t n_tokens) {
-  return n_tokens > 0 && n_tokens <= kRmsDirectMax ? static_cast<size_t>(n_tokens) * kMels * sizeof(float2) : 0;
+  return n_tokens > 0 && n_tokens <= kRmsDirectMax ? static_cast<size_t>(n_tokens) * kMels * sizeof(double2) : 0;
 }
 
 hipError_t launch_rms_scale(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
-                            const float* gram, int d_model, float eps, float* scale, void* partials,
+                            const double* gram, int d_model, float eps, float* scale, void* partials,
                             hipStream_t stream) {
   if (n_tokens <= 0) return hipSuccess;
   if (n_tokens <= kRmsDirectMax && partials != nullptr) {
     const int n_chunks = static_cast<int>((n_tokens + kBinTok - 1) / kBinTok);
-    auto* part = static_cast<float2*>(partials);
+    auto* part = static_cast<double2*>(partials);
     const dim3 grid(static_cast<unsigned>(n_chunks * kMels));
     if (n_bins == kMels && n_levels == kLevels) {
       hipLaunchKernelGGL(rms_bin_partials_kernel<false>, grid, dim3(kBinTok), 0, stream, levels, n_tokens, n_bins,

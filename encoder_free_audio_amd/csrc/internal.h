@@ -85,7 +85,7 @@ hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, int n_bins, int
                         void* out, bool out_f32, int64_t out_row_stride, const int64_t* out_rows,
                         hipStream_t stream);
 
-hipError_t launch_gram(const uint16_t* table, int n_bins, int n_levels, int d_model, float* gram,
+hipError_t launch_gram(const uint16_t* table, int n_bins, int n_levels, int d_model, double* gram,
                        hipStream_t stream);
 
 // Batches up to this many tokens take a small-batch RMSNorm-scale path: with
@@ -97,7 +97,7 @@ constexpr int64_t kRmsDirectMax = 131072;
 
 size_t rms_partials_bytes(int64_t n_tokens);  // 0 above kRmsDirectMax
 hipError_t launch_rms_scale(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
-                            const float* gram, int d_model, float eps, float* scale, void* partials,
+                            const double* gram, int d_model, float eps, float* scale, void* partials,
                             hipStream_t stream);
 
 // Short convolution (width 4, residual) over ragged requests with per-request

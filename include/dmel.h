@@ -166,26 +166,30 @@ int dmel_levels(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total
  * give DMEL_ESHAPE. */
 
 /* Gram matrix of the table, G[r][r'] = sum_c E[r][c] * E[r'][c], accumulated
- * in fp64 and stored as fp32, for the RMSNorm of dmel_embed / dmel_forward.
+ * and stored in fp64, for the RMSNorm of dmel_embed / dmel_forward.
  *  table      bf16 [n_bins * n_levels, d_model], 16-byte aligned, row-major
- *  gram       fp32 [1280, 1280] out (both triangles are written), indexed by
- *             16 * bin + level whatever the layout; entries of (bin, level)
- *             pairs outside the layout are 0
+ *  gram       fp64 [1280, 1280] out, 16-byte aligned (both triangles are
+ *             written), indexed by 16 * bin + level whatever the layout;
+ *             entries of (bin, level) pairs outside the layout are 0
  * Recompute whenever the table's contents change.  d_model % 16 == 0. */
-int dmel_rms_gram(const uint16_t* table, int32_t n_bins, int32_t n_levels, int32_t d_model, float* gram,
+int dmel_rms_gram(const uint16_t* table, int32_t n_bins, int32_t n_levels, int32_t d_model, double* gram,
                   void* stream);
 
 /* Per-token RMSNorm scale r_t = 1 / sqrt(|s_t|^2 / d_model + eps), where
  * |s_t|^2 = sum_{j,j'} G[16 j + L_tj][16 j' + L_tj'] is the squared norm of
- * the exact sum of the token's n_bins rows (the "optional RMSNorm" of Part 1).
- * It differs from the norm of the fp32-rounded sum by about 1e-7 relative.
+ * the exact sum of the token's n_bins rows (the "optional RMSNorm" of Part 1),
+ * evaluated in fp64 in a fixed order (every batch size gives a token the same
+ * bits).  It differs from the norm of the fp32-rounded sum by the rounding of
+ * that sum (about 1e-7 relative for tables whose selected rows do not cancel
+ * almost completely) plus about 1e-16 times the sum of the absolute Gram terms
+ * over |s|^2.
  *  levels     uint8 [n_tokens, n_bins] (16-byte aligned for the released
  *             layout); values >= n_levels read as n_levels - 1
- *  gram       fp32 [1280, 1280] from dmel_rms_gram with the same layout
+ *  gram       fp64 [1280, 1280] from dmel_rms_gram with the same layout
  *  scale      fp32 [n_tokens] out
  * Errors: DMEL_EINVAL (eps < 0 or not finite), DMEL_EALIGN, DMEL_ESHAPE. */
 int dmel_rms_scale(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels,
-                   const float* gram, int32_t d_model, float eps, float* scale, void* stream);
+                   const double* gram, int32_t d_model, float eps, float* scale, void* stream);
 
 /* Bag-of-bins embedding ("A frame's 80 rows are summed into one 6144-dimensional
  * vector, with an optional RMSNorm", Part 1; "each mel bin owns its own block of
@@ -213,7 +217,7 @@ int dmel_embed(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t 
 
 /* Bytes of device workspace dmel_forward needs for n_frames_total frames
  * (levels plus per-token scales, and for batches of at most 131,072 frames
- * 640 bytes per frame of RMSNorm partial sums; each part 256-byte aligned).
+ * 1280 bytes per frame of RMSNorm partial sums; each part 256-byte aligned).
  * 0 for a negative count. */
 size_t dmel_forward_workspace_bytes(int64_t n_frames_total);
 
@@ -229,7 +233,7 @@ size_t dmel_forward_workspace_bytes(int64_t n_frames_total);
 int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total,
                  const int64_t* sample_off, const int64_t* frame_off, int32_t n_clips,
                  int64_t n_frames_total, const float* carry, const uint16_t* table,
-                 int32_t d_model, const float* rms_weight, const float* gram, float eps,
+                 int32_t d_model, const float* rms_weight, const double* gram, float eps,
                  void* out, int32_t out_dtype, int64_t out_row_stride, const int64_t* out_rows,
                  void* workspace, size_t workspace_bytes, void* stream);
 

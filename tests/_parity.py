@@ -65,7 +65,7 @@ def gpu_embed(levels_np, table_bits: torch.Tensor, d_model, out_dtype="bf16", rm
     if rms_weight is not None:
         w = to_dev(np.asarray(rms_weight, dtype=np.float32))
         if gram is None:
-            gram = torch.empty((1280, 1280), dtype=torch.float32, device=DEV)
+            gram = torch.empty((1280, 1280), dtype=torch.float64, device=DEV)
             dm.dmel_rms_gram(table, d_model, gram, **lay)
         scale = torch.empty(max(n, 1), dtype=torch.float32, device=DEV)
         dm.dmel_rms_scale(lv, n, gram, d_model, eps, scale, **lay)

@@ -152,7 +152,7 @@ def _rms_case(dm, lv, n_levels, d, dy_bf16, seed, accumulate=False):
     lvd = torch.from_numpy(np.ascontiguousarray(lv)).cuda()
     td = table.cuda()
     wd = torch.from_numpy(w).cuda()
-    gram = torch.empty((1280, 1280), dtype=torch.float32, device="cuda")
+    gram = torch.empty((1280, 1280), dtype=torch.float64, device="cuda")
     dm.dmel_rms_gram(td, d, gram, **lay)
     scale = torch.empty(n, dtype=torch.float32, device="cuda")
     dm.dmel_rms_scale(lvd, n, gram, d, 1e-6, scale, **lay)
@@ -227,7 +227,7 @@ def test_full_size_backward_sampled(dm):
     del audio
     table = synth.table_bf16(seed=1234).cuda()
     w = torch.ones(d, dtype=torch.float32, device="cuda")
-    gram = torch.empty((1280, 1280), dtype=torch.float32, device="cuda")
+    gram = torch.empty((1280, 1280), dtype=torch.float64, device="cuda")
     dm.dmel_rms_gram(table, d, gram)
     scale = torch.empty(T, dtype=torch.float32, device="cuda")
     dm.dmel_rms_scale(lv, T, gram, d, 1e-6, scale)

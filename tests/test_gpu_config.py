@@ -171,7 +171,7 @@ def test_layout_scale_same_for_both_kernels(dm, P):
     rng = np.random.default_rng(12)
     print("case: layout 41 x 12, scale kernels, n=133121", flush=True)
     t = synth.table_bf16(seed=13, rows=n_bins * n_levels, d_model=d).cuda()
-    gram = torch.empty((1280, 1280), dtype=torch.float32, device="cuda")
+    gram = torch.empty((1280, 1280), dtype=torch.float64, device="cuda")
     dm.dmel_rms_gram(t, d, gram, n_bins=n_bins, n_levels=n_levels)
     lv = torch.from_numpy(rng.integers(0, n_levels, size=(n_big, n_bins)).astype(np.uint8)).cuda()
     big = torch.empty(n_big, dtype=torch.float32, device="cuda")
@@ -190,7 +190,7 @@ def test_layout_scale_same_for_both_kernels(dm, P):
     sub = g[np.ix_(idx[:50], idx[:50])]
     src = (n_levels * (idx[:50] // 16) + idx[:50] % 16)
     ref = e[src] @ e[src].T
-    assert np.max(np.abs(sub - ref) / np.maximum(np.abs(ref), 1e-3)) < 1e-6
+    assert np.max(np.abs(sub - ref) / np.maximum(np.abs(ref), 1e-3)) < 1e-11
     # and the sampled scales against the oracle's norm
     lvn = lv[:64].cpu().numpy()
     s = o.embed_sum(lvn, t.cpu().numpy().view(np.uint16), n_levels=n_levels).astype(np.float64)

@@ -47,7 +47,7 @@ def test_batch_64x20min_full(env):
     so, fo, T = dm.clip_offsets([clip_len] * n_clips, "cuda")
     assert T == 1_536_000
     w = torch.ones(6144, dtype=torch.float32, device="cuda")
-    gram = torch.empty((1280, 1280), dtype=torch.float32, device="cuda")
+    gram = torch.empty((1280, 1280), dtype=torch.float64, device="cuda")
     dm.dmel_rms_gram(table, 6144, gram)
     out = torch.empty((T, 6144), dtype=torch.int16, device="cuda")
     ws = torch.empty(dm.dmel_forward_workspace_bytes(T), dtype=torch.uint8, device="cuda")
@@ -95,7 +95,7 @@ def test_streaming_4096x1000_equals_batch(env):
     hops = synth.streaming_hops(seed=3, n_streams=S, n_steps=K, device="cuda")   # [K, S, 800]
     table = synth.table_bf16(1234).cuda()
     w = torch.ones(6144, dtype=torch.float32, device="cuda")
-    gram = torch.empty((1280, 1280), dtype=torch.float32, device="cuda")
+    gram = torch.empty((1280, 1280), dtype=torch.float64, device="cuda")
     dm.dmel_rms_gram(table, 6144, gram)
     # batch reference: each stream as one clip of 800 000 samples
     streams = hops.permute(1, 0, 2).contiguous().view(-1)
