@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libdmel.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["dmel_api.cpp", "tables.cpp", "frontend.hip", "embed.hip", "shortconv.hip", "backward.hip", "hmlp.hip", "dft_gemm.hip"]
+SOURCES = ["dmel_api.cpp", "tables.cpp", "frontend.hip", "embed.hip", "shortconv.hip", "backward.hip", "hmlp.hip", "dft_gemm.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are switched off (they are never needed for

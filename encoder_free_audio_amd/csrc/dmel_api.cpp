@@ -179,6 +179,12 @@ int dmel_create_config(dmel_ctx** out, int device, const dmel_config* config) {
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   e = hipSetDevice(device);
   if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  // the device address of the allocation-free forward's scratch (once per device)
+  e = dmel::noalloc_init(device);
+  if (e != hipSuccess) {
+    (void)hipSetDevice(prev);
+    return hip_fail(e, "scratch symbol lookup");
+  }
 
   dmel::HostTables* h = new (std::nothrow) dmel::HostTables;
   dmel_ctx* ctx = new (std::nothrow) dmel_ctx;
@@ -390,16 +396,20 @@ size_t dmel_forward_workspace_bytes(int64_t n_frames_total) {
          round_up(dmel::rms_partials_bytes(n_frames_total), 256);
 }
 
-int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total, const int64_t* sample_off,
-                 const int64_t* frame_off, int32_t n_clips, int64_t n_frames_total, const float* carry,
-                 const uint16_t* table, int32_t d_model, const float* rms_weight, const double* gram, float eps,
-                 void* out, int32_t out_dtype, int64_t out_row_stride, const int64_t* out_rows, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by dmel_forward and dmel_forward_noalloc (everything but
+// the intermediates' memory).
+int check_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total, const int64_t* sample_off,
+                  const int64_t* frame_off, int32_t n_clips, int64_t n_frames_total, const float* carry,
+                  const uint16_t* table, int32_t d_model, const float* rms_weight, const double* gram, float eps,
+                  void* out, int32_t out_dtype, int64_t out_row_stride, const int64_t* out_rows) {
   int rc = check_audio(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, out, "out");
   if (rc != DMEL_OK) return rc;
   if (carry != nullptr && !aligned(carry, 4)) return fail(DMEL_EALIGN, "carry is not 4-byte aligned");
-  const int32_t n_bins = ctx->cfg.n_mel_bins, n_levels = ctx->cfg.mel_vocab_size;
-  rc = check_layout(n_bins, n_levels);
+  rc = check_layout(ctx->cfg.n_mel_bins, ctx->cfg.mel_vocab_size);
   if (rc != DMEL_OK) return rc;
   rc = check_table(table, d_model);
   if (rc != DMEL_OK) return rc;
@@ -411,30 +421,82 @@ int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_tota
     if (!aligned(rms_weight, 4)) return fail(DMEL_EALIGN, "rms_weight is not 4-byte aligned");
     if (!aligned(gram, 16)) return fail(DMEL_EALIGN, "gram is not 16-byte aligned");
   }
+  return DMEL_OK;
+}
+
+// The forward's launches: levels -> (scales) -> tokens, with the
+// intermediates at `levels` / `scale` / `partials` (partials may be NULL).
+int forward_launch(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total, const int64_t* sample_off,
+                   const int64_t* frame_off, int32_t n_clips, int64_t n_frames_total, const float* carry,
+                   const uint16_t* table, int32_t d_model, const float* rms_weight, const double* gram, float eps,
+                   void* out, int32_t out_dtype, int64_t out_row_stride, const int64_t* out_rows, uint8_t* levels,
+                   float* scale, void* partials, hipStream_t s) {
+  const int32_t n_bins = ctx->cfg.n_mel_bins, n_levels = ctx->cfg.mel_vocab_size;
+  hipError_t e = dmel::launch_frontend(ctx->tabs, audio, n_samples_total, sample_off, frame_off, n_clips,
+                                       n_frames_total, carry, nullptr, levels, s);
+  if (e != hipSuccess) return hip_fail(e, "frontend launch");
+  if (rms_weight != nullptr) {
+    e = dmel::launch_rms_scale(levels, n_frames_total, n_bins, n_levels, gram, d_model, eps, scale, partials, s);
+    if (e != hipSuccess) return hip_fail(e, "rms_scale launch");
+  }
+  e = dmel::launch_embed(levels, n_frames_total, n_bins, n_levels, table, d_model, rms_weight,
+                         rms_weight ? scale : nullptr, out, out_dtype == DMEL_F32, out_row_stride, out_rows, s);
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "embed launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total, const int64_t* sample_off,
+                 const int64_t* frame_off, int32_t n_clips, int64_t n_frames_total, const float* carry,
+                 const uint16_t* table, int32_t d_model, const float* rms_weight, const double* gram, float eps,
+                 void* out, int32_t out_dtype, int64_t out_row_stride, const int64_t* out_rows, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  int rc = check_forward(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, carry, table,
+                         d_model, rms_weight, gram, eps, out, out_dtype, out_row_stride, out_rows);
+  if (rc != DMEL_OK) return rc;
   const size_t need = dmel_forward_workspace_bytes(n_frames_total);
   if (workspace_bytes < need)
     return fail(DMEL_ENOMEM, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
   if (n_frames_total == 0) return DMEL_OK;
   if (workspace == nullptr) return fail(DMEL_EINVAL, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(DMEL_EALIGN, "workspace is not 256-byte aligned");
-  auto* levels = static_cast<uint8_t*>(workspace);
-  // levels [n, n_bins] (n_bins <= 80), then the scales
-  auto* scale = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         round_up(static_cast<size_t>(n_frames_total) * dmel::kMels, 256));
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dmel::launch_frontend(ctx->tabs, audio, n_samples_total, sample_off, frame_off, n_clips,
-                                       n_frames_total, carry, nullptr, levels, s);
-  if (e != hipSuccess) return hip_fail(e, "frontend launch");
-  if (rms_weight != nullptr) {
-    void* partials = static_cast<char*>(workspace) + round_up(static_cast<size_t>(n_frames_total) * dmel::kMels, 256) +
-                     round_up(static_cast<size_t>(n_frames_total) * sizeof(float), 256);
-    e = dmel::launch_rms_scale(levels, n_frames_total, n_bins, n_levels, gram, d_model, eps, scale,
-                               dmel::rms_partials_bytes(n_frames_total) > 0 ? partials : nullptr, s);
-    if (e != hipSuccess) return hip_fail(e, "rms_scale launch");
-  }
-  e = dmel::launch_embed(levels, n_frames_total, n_bins, n_levels, table, d_model, rms_weight,
-                         rms_weight ? scale : nullptr, out, out_dtype == DMEL_F32, out_row_stride, out_rows, s);
-  return e == hipSuccess ? DMEL_OK : hip_fail(e, "embed launch");
+  // levels [n, n_bins] (n_bins <= 80), then the scales, then the partials
+  auto* base = static_cast<char*>(workspace);
+  const size_t off_scale = round_up(static_cast<size_t>(n_frames_total) * dmel::kMels, 256);
+  const size_t off_part = off_scale + round_up(static_cast<size_t>(n_frames_total) * sizeof(float), 256);
+  void* partials = dmel::rms_partials_bytes(n_frames_total) > 0 ? base + off_part : nullptr;
+  return forward_launch(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, carry, table,
+                        d_model, rms_weight, gram, eps, out, out_dtype, out_row_stride, out_rows,
+                        reinterpret_cast<uint8_t*>(base), reinterpret_cast<float*>(base + off_scale), partials,
+                        static_cast<hipStream_t>(stream));
+}
+
+int dmel_forward_noalloc(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total,
+                         const int64_t* sample_off, const int64_t* frame_off, int32_t n_clips,
+                         int64_t n_frames_total, const float* carry, const uint16_t* table, int32_t d_model,
+                         const float* rms_weight, const double* gram, float eps, void* out, int32_t out_dtype,
+                         int64_t out_row_stride, const int64_t* out_rows, void* stream) {
+  int rc = check_forward(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, carry, table,
+                         d_model, rms_weight, gram, eps, out, out_dtype, out_row_stride, out_rows);
+  if (rc != DMEL_OK) return rc;
+  if (n_frames_total > dmel::kNoAllocMaxFrames)
+    return fail(DMEL_ENOMEM, "%lld frames exceed the %lld frames the fixed scratch holds (call dmel_forward with a "
+                "workspace, or split the batch)", (long long)n_frames_total, (long long)dmel::kNoAllocMaxFrames);
+  if (n_frames_total == 0) return DMEL_OK;
+  auto* base = static_cast<char*>(dmel::noalloc_scratch(ctx->device));
+  if (base == nullptr) return fail(DMEL_ESTATE, "no scratch address for device %d", ctx->device);
+  // the scratch address belongs to ctx's device: the work must run there
+  int dev = -1;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "device of the stream");
+  if (dev != ctx->device) return fail(DMEL_ESTATE, "ctx belongs to device %d, the work would run on device %d", ctx->device, dev);
+  void* partials = n_frames_total <= dmel::kNoAllocPartialFrames ? base + dmel::kNoAllocPartOff : nullptr;
+  return forward_launch(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, carry, table,
+                        d_model, rms_weight, gram, eps, out, out_dtype, out_row_stride, out_rows,
+                        reinterpret_cast<uint8_t*>(base), reinterpret_cast<float*>(base + dmel::kNoAllocScaleOff),
+                        partials, static_cast<hipStream_t>(stream));
 }
 
 int dmel_gather_rows(const uint16_t* table, int64_t n_table_rows, int32_t d_model, const int32_t* ids, int64_t n,

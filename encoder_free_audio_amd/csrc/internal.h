@@ -138,6 +138,20 @@ hipError_t launch_dft_gemm_frames(const FrontTables& tabs, const float* audio, i
                                   const float* carry, const uint16_t* B, float* logmel, void* workspace,
                                   hipStream_t stream);
 
+// Scratch of the allocation-free forward (noalloc.hip): a static device array
+// of kNoAllocScratchBytes per GPU holding, for at most kNoAllocMaxFrames
+// frames, the levels [n, 80] at 0, the RMSNorm scales [n] at kNoAllocScaleOff
+// and, for at most kNoAllocPartialFrames frames, the RMSNorm partial sums at
+// kNoAllocPartOff.  noalloc_init looks its address up on `device` (which must
+// be current); noalloc_scratch returns it (nullptr before noalloc_init).
+constexpr int64_t kNoAllocMaxFrames = 262144;
+constexpr int64_t kNoAllocPartialFrames = 4096;
+constexpr size_t kNoAllocScaleOff = static_cast<size_t>(kNoAllocMaxFrames) * kMels;
+constexpr size_t kNoAllocPartOff = kNoAllocScaleOff + static_cast<size_t>(kNoAllocMaxFrames) * 4;
+constexpr size_t kNoAllocScratchBytes = kNoAllocPartOff + static_cast<size_t>(kNoAllocPartialFrames) * kMels * 16;
+hipError_t noalloc_init(int device);
+void* noalloc_scratch(int device);
+
 hipError_t launch_gather_rows(const uint16_t* table, int64_t n_table_rows, int d_model,
                               const int32_t* ids, int64_t n, uint16_t* out, int64_t out_row_stride,
                               const int64_t* out_rows, hipStream_t stream);

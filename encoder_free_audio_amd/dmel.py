@@ -27,7 +27,8 @@ _STATUS = {0: "DMEL_OK", -1: "DMEL_EINVAL", -2: "DMEL_ESHAPE", -3: "DMEL_EDTYPE"
 # Every symbol include/dmel.h declares.
 EXPORTS = ("dmel_get_params", "dmel_num_frames", "dmel_last_error", "dmel_default_config", "dmel_create",
            "dmel_create_config", "dmel_get_config", "dmel_destroy", "dmel_frames", "dmel_levels", "dmel_rms_gram",
-           "dmel_rms_scale", "dmel_embed", "dmel_forward_workspace_bytes", "dmel_forward", "dmel_gather_rows",
+           "dmel_rms_scale", "dmel_embed", "dmel_forward_workspace_bytes", "dmel_forward", "dmel_forward_noalloc",
+           "dmel_gather_rows",
            "dmel_shortconv", "dmel_embed_backward_workspace_bytes", "dmel_embed_backward",
            "dmel_rms_backward_workspace_bytes", "dmel_rms_backward_stored_workspace_bytes", "dmel_rms_backward",
            "dmel_hmlp_workspace_bytes",
@@ -93,6 +94,8 @@ def lib() -> ctypes.CDLL:
             "dmel_forward_workspace_bytes": (_SZ, [_I64]),
             "dmel_forward": (ctypes.c_int, [_P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _I32, _P, _P, _F,
                                             _P, _I32, _I64, _P, _P, _SZ, _P]),
+            "dmel_forward_noalloc": (ctypes.c_int, [_P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _I32, _P, _P, _F,
+                                                    _P, _I32, _I64, _P, _P]),
             "dmel_gather_rows": (ctypes.c_int, [_P, _I64, _I32, _P, _I64, _P, _I64, _P, _P]),
             "dmel_shortconv": (ctypes.c_int, [_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _I32, _P]),
             "dmel_embed_backward_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32]),
@@ -261,6 +264,20 @@ def dmel_forward(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_
                                               float(eps), _ptr(out), int(out_dtype), int(out_row_stride),
                                               _ptr(out_rows), _ptr(workspace), int(workspace_bytes),
                                               _stream(stream)))
+
+
+# Largest batch dmel_forward_noalloc accepts (DMEL_NOALLOC_MAX_FRAMES).
+NOALLOC_MAX_FRAMES = 262144
+
+
+def dmel_forward_noalloc(ctx, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames_total, carry, table,
+                         d_model, rms_weight, gram, eps, out, out_dtype, out_row_stride, out_rows,
+                         stream=None) -> None:
+    _check("dmel_forward_noalloc",
+           lib().dmel_forward_noalloc(ctx, _ptr(audio), int(n_samples_total), _ptr(sample_off), _ptr(frame_off),
+                                      int(n_clips), int(n_frames_total), _ptr(carry), _ptr(table), int(d_model),
+                                      _ptr(rms_weight), _ptr(gram), float(eps), _ptr(out), int(out_dtype),
+                                      int(out_row_stride), _ptr(out_rows), _stream(stream)))
 
 
 def dmel_gather_rows(table, n_table_rows, d_model, ids, n, out, out_row_stride, out_rows=None,

@@ -237,6 +237,29 @@ int dmel_forward(const dmel_ctx* ctx, const float* audio, int64_t n_samples_tota
                  void* out, int32_t out_dtype, int64_t out_row_stride, const int64_t* out_rows,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Largest batch dmel_forward_noalloc accepts, in frames (about 3.6 hours of
+ * audio). */
+#define DMEL_NOALLOC_MAX_FRAMES 262144
+
+/* dmel_forward without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  The intermediates (levels, RMSNorm scales, and for
+ * batches of at most 4096 frames the RMSNorm partial sums) live in a fixed
+ * array of the library, 26 MiB on each GPU, whose address dmel_create looks
+ * up on its device.  Arguments and results as dmel_forward, minus the
+ * workspace; the same kernels run, so the results are the same bits.
+ * Allocates nothing.  At most DMEL_NOALLOC_MAX_FRAMES frames per call
+ * (DMEL_ENOMEM beyond).  Every call on a GPU shares that GPU's array and
+ * leaves its last contents there: calls that overlap on one GPU (other
+ * streams, other threads) race, so the caller serialises them.  ctx must
+ * belong to the device the work runs on (the stream's device, or the current
+ * device for the NULL stream): DMEL_ESTATE otherwise. */
+int dmel_forward_noalloc(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total,
+                         const int64_t* sample_off, const int64_t* frame_off, int32_t n_clips,
+                         int64_t n_frames_total, const float* carry, const uint16_t* table, int32_t d_model,
+                         const float* rms_weight, const double* gram, float eps, void* out, int32_t out_dtype,
+                         int64_t out_row_stride, const int64_t* out_rows, void* stream);
+
 /* Row copy for the text positions of an interleaved sequence (one audio item
  * expands into its frame positions among text tokens; "Inside Inkling: Audio
  * Design", Part 3, "Where audio touches the serving path").
