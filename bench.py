@@ -71,7 +71,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=20000, help="oracle sample: frames per worker")
     ap.add_argument("--workload", choices=("batch", "stream", "interleave", "copy", "shortconv", "shortconv_decode",
-                                           "backward", "hmlp", "dft_gemm"),
+                                           "backward", "hmlp", "dft_gemm", "rounding"),
                     default="batch",
                     help="batch: 64 x 20 min clips (default); stream: 4096 streams, one hop per step; "
                          "interleave: 256 x 32768 audio/text positions; copy: a plain 1 GiB device copy "
@@ -155,7 +155,8 @@ def main():
         sys.exit(1)
     if args.steps is None:
         args.steps = {"batch": 20, "stream": 1000, "interleave": 5, "copy": 5, "shortconv": 20,
-                      "shortconv_decode": 1000, "backward": 5, "hmlp": 10, "dft_gemm": 3}[args.workload]
+                      "shortconv_decode": 1000, "backward": 5, "hmlp": 10, "dft_gemm": 3,
+                      "rounding": 1}[args.workload]
     if args.workload == "stream":
         return bench_stream(args)
     if args.workload == "interleave":
@@ -170,6 +171,8 @@ def main():
         return bench_hmlp(args)
     if args.workload == "dft_gemm":
         return bench_dft_gemm(args)
+    if args.workload == "rounding":
+        return bench_rounding(args)
     return bench_batch(args)
 
 
@@ -269,7 +272,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 def bench_dft_gemm(args):
     """The two ways to the log-mel of the 64 x 20 min batch (1,536,000 frames):
     the mixed-radix FFT staged in LDS (dmel_frames) and the DFT as one bf16x3
-    matrix-core product (dmel_frames_dft_gemm: split frames, GEMM over
+    matrix-core product (dmel_bench_frames_dft_gemm of the benchmark-only
+    library: split frames, GEMM over
     K = 4800 into 1792 fp32 columns, power + mel + log).  A step = one call of
     each, timed separately with HIP events.  `value` is the DFT-as-GEMM
     variant's frames/s; the FFT's is beside it."""
@@ -281,11 +285,12 @@ def bench_dft_gemm(args):
     so, fo, T = dm.clip_offsets([clip_len] * n_clips, dev)
     lm_fft = torch.empty((T, 80), dtype=torch.float32, device=dev)
     lm_mm = torch.empty((T, 80), dtype=torch.float32, device=dev)
-    mat = torch.empty(dm.dmel_dft_matrix_bytes(), dtype=torch.uint8, device=dev)
-    wsb = dm.dmel_frames_dft_gemm_workspace_bytes(T)
+    from encoder_free_audio_amd import bench_ext as be
+    mat = torch.empty(be.dmel_bench_dft_matrix_bytes(), dtype=torch.uint8, device=dev)
+    wsb = be.dmel_bench_dft_gemm_workspace_bytes(T)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    dm.dmel_dft_matrix(mat, stream)
+    be.dmel_bench_dft_matrix(mat, stream)
 
     def step(ev=None):
         if ev is not None:
@@ -293,7 +298,8 @@ def bench_dft_gemm(args):
         dm.dmel_frames(ctx, audio, audio.numel(), so, fo, n_clips, T, None, lm_fft, stream)
         if ev is not None:
             ev[1].record(stream)
-        dm.dmel_frames_dft_gemm(ctx, audio, audio.numel(), so, fo, n_clips, T, None, mat, lm_mm, ws, wsb, stream)
+        be.dmel_bench_frames_dft_gemm(ctx, audio, audio.numel(), so, fo, n_clips, T, None, mat, lm_mm, ws, wsb,
+                                      stream)
         if ev is not None:
             ev[2].record(stream)
 
@@ -338,6 +344,67 @@ def bench_dft_gemm(args):
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_rounding(args):
+    """In-bounds probe of how one add c + e (c fp32, e a bf16 value) rounds on
+    this chip: by v_add_f32, by a matrix-core product with c as accumulator
+    and a one-hot row selecting e, by the same product with a zero
+    accumulator (e passed through), and by the bf16 dot instruction; each
+    against the round-to-nearest-even sum numpy computes on the host.  The
+    bag-of-bins embedding needs exactly that rounding for every add.  Cases:
+    random pairs whose sum is inexact, exact midpoints (ties), and signed
+    zeros.  Prints one JSON line of counts."""
+    from encoder_free_audio_amd import bench_ext as be
+    rng = np.random.default_rng(77)
+    n = 1 << 24
+    # c: sign, exponent in [-20, 20], random 23-bit mantissa
+    c = (rng.choice([-1.0, 1.0], n) * np.ldexp(1.0 + rng.integers(0, 1 << 23, n) / float(1 << 23),
+                                               rng.integers(-20, 21, n))).astype(np.float32)
+    kind = np.zeros(n, np.int8)   # 0 random, 1 tie, 2 signed zero
+    # random e: c scaled by 2^U[-12, 2], rounded to bf16 (varied alignment)
+    e = (c.astype(np.float64) * np.ldexp(rng.uniform(0.5, 1.0, n), rng.integers(-12, 3, n))
+         * rng.choice([-1.0, 1.0], n)).astype(np.float32)
+    # ties: e = (2k + 1) 2^(E - 24) lands c + e exactly between two fp32
+    # values of c's binade (k < 64, so e has at most 7 significant bits)
+    t = rng.random(n) < 0.25
+    ex = np.frexp(c)[1] - 1
+    k = rng.integers(0, 64, n)
+    e_tie = (rng.choice([-1.0, 1.0], n) * np.ldexp(2.0 * k + 1.0, ex - 24)).astype(np.float32)
+    e = np.where(t, e_tie, e)
+    kind[t] = 1
+    z = rng.random(n) < 0.01
+    c = np.where(z, np.where(rng.random(n) < 0.5, np.float32(0.0), np.float32(-0.0)), c).astype(np.float32)
+    e = np.where(z, np.where(rng.random(n) < 0.5, np.float32(0.0), np.float32(-0.0)), e).astype(np.float32)
+    kind[z] = 2
+    e_bits = (e.view(np.uint32) >> 16).astype(np.uint16)          # bf16 by truncation: exact for ties and zeros
+    ef = (e_bits.astype(np.uint32) << 16).view(np.float32)
+    want = (c + ef).astype(np.float32)                                # numpy: IEEE fp32 add, nearest even
+    exact = c.astype(np.float64) + ef.astype(np.float64)              # exact: both fit in fp64's 53 bits
+    inexact = exact != want.astype(np.float64)
+    # a tie: the exact sum lies halfway between the nearest-even result and its other neighbour
+    other = np.nextafter(want, np.where(exact > want, np.float32(np.inf), np.float32(-np.inf))).astype(np.float64)
+    kind[(kind == 1) & ~(inexact & (np.abs(exact - want) == np.abs(exact - other)))] = 0
+    cd = torch.from_numpy(c).cuda()
+    ed = torch.from_numpy(e_bits.view(np.int16)).cuda()
+    out = torch.empty((4, n), dtype=torch.float32, device="cuda")
+    be.dmel_bench_rounding_probe(cd, ed, n, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    wb = want.view(np.uint32)
+    res = {"workload": "rounding_probe", "cases": n, "random_cases": int((kind == 0).sum()),
+           "tie_cases": int((kind == 1).sum()), "zero_cases": int((kind == 2).sum()),
+           "inexact_cases": int(inexact.sum())}
+    for i, name in ((0, "v_add_f32"), (1, "mfma_accumulate"), (3, "dot2_bf16")):
+        bad = got[i].view(np.uint32) != wb
+        res[name] = {"mismatches": int(bad.sum()), "mismatches_inexact": int((bad & inexact).sum()),
+                     "mismatches_ties": int((bad & (kind == 1)).sum()), "mismatches_zeros": int((bad & (kind == 2)).sum()),
+                     "below_nearest_even": int((bad & (got[i].astype(np.float64) < want)).sum())}
+    bad = got[2].view(np.uint32) != ef.view(np.uint32)
+    res["mfma_zero_accumulator_vs_e"] = {"mismatches": int(bad.sum()),
+                                         "mismatches_nonzero_e": int((bad & (ef != 0)).sum()),
+                                         "mismatches_negative_zero_e": int((bad & (e_bits == 0x8000)).sum())}
+    print(json.dumps(res), flush=True)
 
 
 def bench_hmlp(args):

@@ -16,7 +16,7 @@
 // Work per frame: 2 * 1792 * 4800 = 17.2 MFLOP of matrix-core products (the
 // FFT needs ~43 kFLOP), 9.6 KB of A written and read, 7.2 KB of spectrum
 // written and read.
-#include "internal.h"
+#include "bench_internal.h"
 
 namespace dmel {
 namespace {

@@ -6,6 +6,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "dmel.h"
+
 namespace dmel {
 
 // Front-end constants ("Inside Inkling: Audio Design", Part 1 and "Why this is
@@ -129,15 +131,6 @@ hipError_t launch_hmlp(const uint16_t* images, int n_images, int height, int wid
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, const float* bias, void* C, int64_t M, int N, int K,
                             bool gelu, bool out_f32, hipStream_t stream);
 
-// Log-mel through the DFT as a matrix-core product (dft_gemm.hip).
-size_t dft_matrix_bytes();
-size_t dft_gemm_workspace_bytes(int64_t n_frames);
-hipError_t launch_dft_matrix(uint16_t* B, hipStream_t stream);
-hipError_t launch_dft_gemm_frames(const FrontTables& tabs, const float* audio, int64_t n_samples_total,
-                                  const int64_t* sample_off, const int64_t* frame_off, int n_clips, int64_t n_frames,
-                                  const float* carry, const uint16_t* B, float* logmel, void* workspace,
-                                  hipStream_t stream);
-
 // Scratch of the allocation-free forward (noalloc.hip): a static device array
 // of kNoAllocScratchBytes per GPU holding, for at most kNoAllocMaxFrames
 // frames, the levels [n, 80] at 0, the RMSNorm scales [n] at kNoAllocScaleOff
@@ -157,3 +150,12 @@ hipError_t launch_gather_rows(const uint16_t* table, int64_t n_table_rows, int d
                               const int64_t* out_rows, hipStream_t stream);
 
 }  // namespace dmel
+
+// A context (include/dmel.h): its device and the constant tables of its
+// front-end configuration in one device allocation.
+struct dmel_ctx {
+  int device = -1;
+  void* dev_mem = nullptr;  // one allocation holding every constant table
+  dmel_config cfg{};
+  dmel::FrontTables tabs{};
+};

@@ -405,39 +405,6 @@ int dmel_hmlp_stage(const uint16_t* x, int64_t n_rows, int32_t k, const uint16_t
                     const float* bias, int32_t n, int32_t gelu, void* y, int32_t y_dtype,
                     void* stream);
 
-/* ---- Measured alternative: the DFT as a matrix-core product -------------
- * The same log-mel as dmel_frames ("an 80-channel log-mel spectrogram",
- * "Inside Inkling: Audio Design", Part 1), with the 1600-point DFT of each
- * windowed frame computed as one bf16 matrix product instead of the LDS FFT:
- * frame and DFT matrix are split into bf16 high and low parts and
- * X = Fh Dh + Fh Dl + Fl Dh is accumulated in fp32 (K = 4800, 1792 output
- * columns: 801 real, 801 imaginary, zero padding), then power, mel filters
- * and log as in dmel_frames.  Kept as the benchmark the FFT is chosen
- * against; it is ~400 times the FFT's arithmetic. */
-
-/* Bytes of the split DFT matrix buffer (bf16 [1792, 4800] + 1792 fp32 zeros). */
-size_t dmel_dft_matrix_bytes(void);
-
-/* Fills `matrix` (device, 256-byte aligned, dmel_dft_matrix_bytes() bytes)
- * with the split DFT matrix; enqueued on `stream`.  Errors: DMEL_EINVAL
- * (NULL), DMEL_EALIGN, DMEL_EHIP. */
-int dmel_dft_matrix(void* matrix, void* stream);
-
-/* Workspace of dmel_frames_dft_gemm: 9,600 bytes of split frames and 7,168
- * bytes of spectrum per frame (0 for a negative count). */
-size_t dmel_frames_dft_gemm_workspace_bytes(int64_t n_frames_total);
-
-/* dmel_frames through the matrix product.  Arguments as dmel_frames, plus
- *  matrix     the buffer dmel_dft_matrix filled (caller-owned, read only)
- *  workspace  device memory, 256-byte aligned, at least
- *             dmel_frames_dft_gemm_workspace_bytes(n_frames_total) bytes
- * Frames and spectrum pass through the workspace (HBM).  Errors: as
- * dmel_frames, DMEL_ENOMEM (workspace too small). */
-int dmel_frames_dft_gemm(const dmel_ctx* ctx, const float* audio, int64_t n_samples_total,
-                         const int64_t* sample_off, const int64_t* frame_off, int32_t n_clips,
-                         int64_t n_frames_total, const float* carry, const void* matrix, float* logmel,
-                         void* workspace, size_t workspace_bytes, void* stream);
-
 #ifdef __cplusplus
 }
 #endif

@@ -280,21 +280,48 @@ def test_product_path_does_not_touch_the_oracle():
                 assert "dmel_oracle" not in text, fn
 
 
+def _bench_header_symbols():
+    with open(os.path.join(ROOT, "encoder_free_audio_amd", "csrc", "bench", "dmel_bench.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dmel_bench_[a-z_]+)\s*\(", text)))
+
+
+def test_bench_library_exports(dm):
+    # the benchmark-only library loads (after the product library it links
+    # against) and exports what its header declares; the product library
+    # exports none of it
+    from encoder_free_audio_amd import bench_ext as be
+    be.lib()
+    syms = _bench_header_symbols()
+    assert sorted(be.EXPORTS) == syms
+    out = subprocess.run(["nm", "-D", "--defined-only", be.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    assert not [s for s in syms if s not in set(re.findall(r"\bT (dmel_\w+)", out))]
+    prod = subprocess.run(["nm", "-D", "--defined-only", dm.LIB_PATH], capture_output=True, text=True,
+                          check=True).stdout
+    assert "dft" not in " ".join(re.findall(r"\bT (dmel_\w+)", prod))
+
+
 def test_dft_gemm_validation(dm):
-    # sizes and rejections of the DFT-as-GEMM front end, in host code
-    assert dm.dmel_dft_matrix_bytes() == 1792 * 4800 * 2 + 1792 * 4
-    assert dm.dmel_frames_dft_gemm_workspace_bytes(0) == 0
-    assert dm.dmel_frames_dft_gemm_workspace_bytes(1) == 9728 + 7168
-    assert dm.dmel_frames_dft_gemm_workspace_bytes(1000) == 9_600_000 + 7_168_000
-    assert dm.dmel_frames_dft_gemm_workspace_bytes(-1) == 0
+    # sizes and rejections of the DFT-as-GEMM front end (bench library), in host code
+    from encoder_free_audio_amd import bench_ext as be
+    assert be.dmel_bench_dft_matrix_bytes() == 1792 * 4800 * 2 + 1792 * 4
+    assert be.dmel_bench_dft_gemm_workspace_bytes(0) == 0
+    assert be.dmel_bench_dft_gemm_workspace_bytes(1) == 9728 + 7168
+    assert be.dmel_bench_dft_gemm_workspace_bytes(1000) == 9_600_000 + 7_168_000
+    assert be.dmel_bench_dft_gemm_workspace_bytes(-1) == 0
     E = dm.DmelError
-    lib = dm.lib()
+    lib = be.lib()
     with pytest.raises(E) as e:
-        dm._check("dmel_dft_matrix", lib.dmel_dft_matrix(None, None))
+        be._check("dmel_bench_dft_matrix", lib.dmel_bench_dft_matrix(None, None))
     assert _code(e) == -1
     with pytest.raises(E) as e:
-        dm._check("dmel_dft_matrix", lib.dmel_dft_matrix(8, None))
+        be._check("dmel_bench_dft_matrix", lib.dmel_bench_dft_matrix(8, None))
     assert _code(e) == -4
+    with pytest.raises(E) as e:
+        be._check("dmel_bench_rounding_probe", lib.dmel_bench_rounding_probe(256, 512, 1000, 1024, None))
+    assert _code(e) == -2
     # (fake, aligned device addresses: every check fails before any HIP call)
     args = dict(audio=256, n=1600, so=512, fo=768, clips=1, frames=2, carry=None, mat=1024, lm=2048, ws=4096,
                 wsb=10 ** 6)
@@ -302,13 +329,13 @@ def test_dft_gemm_validation(dm):
     def call(ctx=None, **kw):
         a = dict(args)
         a.update(kw)
-        return lib.dmel_frames_dft_gemm(ctx, a["audio"], a["n"], a["so"], a["fo"], a["clips"], a["frames"],
-                                        a["carry"], a["mat"], a["lm"], a["ws"], a["wsb"], None)
+        return lib.dmel_bench_frames_dft_gemm(ctx, a["audio"], a["n"], a["so"], a["fo"], a["clips"], a["frames"],
+                                              a["carry"], a["mat"], a["lm"], a["ws"], a["wsb"], None)
     assert call() == -1                                   # NULL context
+    assert call(frames=3) == -2                           # more frames than the audio holds
     ctx = dm.dmel_create(0) if dm_has_gpu() else None
     if ctx is not None:
         try:
-            assert call(ctx, frames=3) == -2              # more frames than the audio holds
             assert call(ctx, wsb=100) == -6               # workspace too small
             assert call(ctx, mat=None) == -1
             assert call(ctx, mat=1030) == -4

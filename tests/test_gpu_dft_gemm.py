@@ -1,4 +1,5 @@
-"""GPU parity of the DFT-as-GEMM front end (dmel_frames_dft_gemm): its log-mel
+"""GPU parity of the DFT-as-GEMM front end of the benchmark-only library
+(dmel_bench_frames_dft_gemm, the measured alternative to the FFT): its log-mel
 against the CPU oracle, to the same bar as dmel_frames (|dl| <= 1e-3 on values
 clamped to [-7, 2]; values below the clamp only need to stay below it)."""
 
@@ -20,22 +21,23 @@ def env():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from tests import _parity
-    from encoder_free_audio_amd import dmel as dm
+    from encoder_free_audio_amd import bench_ext as be
+    from encoder_free_audio_amd import dmel
     P = _parity
-    ctx = dm.dmel_create(0)
-    mat = torch.empty(dm.dmel_dft_matrix_bytes(), dtype=torch.uint8, device="cuda")
-    dm.dmel_dft_matrix(mat)
-    yield dm, ctx, mat
+    ctx = dmel.dmel_create(0)
+    mat = torch.empty(be.dmel_bench_dft_matrix_bytes(), dtype=torch.uint8, device="cuda")
+    be.dmel_bench_dft_matrix(mat)
+    yield be, ctx, mat
     torch.cuda.synchronize()
-    dm.dmel_destroy(ctx)
+    dmel.dmel_destroy(ctx)
 
 
 def gemm_frames(dm, ctx, mat, flat, lengths, carry=None):
     so, fo, T = P.offsets(lengths)
     lm = torch.empty((max(T, 1), 80), dtype=torch.float32, device="cuda")
-    wsb = dm.dmel_frames_dft_gemm_workspace_bytes(T)
+    wsb = dm.dmel_bench_dft_gemm_workspace_bytes(T)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
-    dm.dmel_frames_dft_gemm(ctx, flat, flat.numel(), so, fo, len(lengths), T, carry, mat, lm, ws, wsb)
+    dm.dmel_bench_frames_dft_gemm(ctx, flat, flat.numel(), so, fo, len(lengths), T, carry, mat, lm, ws, wsb)
     torch.cuda.synchronize()
     return lm[:T].cpu().numpy()
 
