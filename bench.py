@@ -1,11 +1,13 @@
 """Benchmark of the dMel front end on one MI355X.
 
-One step = one pass of the whole hot path over one batch: framing + FFT +
-log-mel + quantizer (dmel_levels), the RMSNorm scales (dmel_rms_scale) and the
-bag-of-bins embedding with RMSNorm and bf16 output (dmel_embed) - the three
-launches dmel_forward enqueues - for 64 clips of 20 minutes of speech-like
-16 kHz audio (1,536,000 tokens of width 6144).  Inputs are generated on the
-device before the timed region.
+One step = one dmel_forward call, the whole hot path over one batch: framing
++ FFT + log-mel + quantizer, the RMSNorm scales and the bag-of-bins embedding
+with RMSNorm and bf16 output, for 64 clips of 20 minutes of speech-like 16 kHz
+audio (1,536,000 tokens of width 6144).  Inputs are generated on the device
+before the timed region; the table's Gram matrix is computed once per table,
+outside it.  After the timed region the same three launches are called one by
+one with events between them for the per-kernel split, and the oracle runs on
+a sample of the batch, compared with the GPU's results for it.
 
 Prints one JSON line (see the fields below).  ``--gpus N`` with N > 1 exits:
 this front end runs on one GPU here.
@@ -95,31 +97,55 @@ def parse():
     return args
 
 
-def cpu_baseline(audio_dev, clip_len, table_bits, n_clips, frames_per_worker, config=None):
+# Host data of the oracle leg, set before the pool forks (the workers read it
+# without copies): per sampled clip its audio, and the GPU's log-mel, levels
+# and tokens of the same frames.
+_ORACLE_DATA: dict = {}
+
+
+def _host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(audio_dev, clip_len, table_bits, n_clips, frames_per_worker, gpu_sample, config=None):
     """Time the CPU oracle on a bounded sample of the same workload: the first
-    frames of several clips (causal framing makes them the clip's first frames)."""
+    frames of several clips (causal framing makes them the clip's first
+    frames), one oracle process per core, and compare its results with the
+    GPU's for the same frames (gpu_sample(clip, n_frames) -> (log-mel, levels,
+    tokens) on the host).  The time is the slowest worker's oracle forward
+    alone (not the comparison)."""
     import multiprocessing as mp
 
     from oracle import dmel_oracle  # noqa: F401  (imported here: test infrastructure)
 
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    workers = max(1, min(cores, 16, n_clips))
+    host = _host_cores()
+    # at most 16 processes: the GPU box's share of host cores
+    workers = max(1, min(host, 16, n_clips))
     n = frames_per_worker * 800
-    segs = [audio_dev[c * clip_len: c * clip_len + n].cpu().numpy() for c in range(workers)]
-    tb = table_bits.cpu().numpy().view(np.uint16)
+    _ORACLE_DATA.clear()
+    _ORACLE_DATA["clips"] = [(audio_dev[c * clip_len: c * clip_len + n].cpu().numpy(),) + gpu_sample(c, frames_per_worker)
+                             for c in range(workers)]
+    _ORACLE_DATA["table"] = table_bits.cpu().numpy().view(np.uint16)
+    _ORACLE_DATA["config"] = config
     ctx = mp.get_context("fork")
-    with ctx.Pool(workers) as pool:
-        t0 = time.perf_counter()
-        res = pool.starmap(_oracle_job, [(s, tb, config) for s in segs])
-        dt = time.perf_counter() - t0
-    tokens = sum(res)
+    try:
+        with ctx.Pool(workers) as pool:
+            res = pool.map(_oracle_job, range(workers), chunksize=1)
+    finally:
+        _ORACLE_DATA.clear()
+    tokens = sum(r["tokens"] for r in res)
+    dt = max(r["seconds"] for r in res)
+    parity = {}
+    for r in res:
+        for k, v in r["parity"].items():
+            parity[k] = max(parity.get(k, 0.0), v) if k.startswith("max_") else parity.get(k, 0) + v
     return {"value": tokens / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
             "sample": f"first {frames_per_worker} frames of each of {workers} clips ({tokens} tokens, "
-                      f"RMSNorm on, bf16 out), one oracle process per core, {dt:.1f} s wall",
-            "cpu_model": _cpu_model()}
+                      f"RMSNorm on, bf16 out), one oracle process per core; the slowest process took {dt:.1f} s",
+            "host_cores": host, "cores_used": workers, "cpu_model": _cpu_model()}, parity
 
 
 def _cpu_model() -> str:
@@ -133,14 +159,65 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def _oracle_job(seg, tb, config=None):
+def _oracle_job(i):
+    """One worker: the oracle forward of one clip's sample (timed), then its
+    comparison with the GPU's log-mel, levels and tokens of the same frames
+    to the parity bars (counted, not asserted)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import dmel_oracle as o
+    seg, lm_g, lv_g, tok_g = _ORACLE_DATA["clips"][i]
+    tb = _ORACLE_DATA["table"]
+    config = _ORACLE_DATA["config"]
     cfg = o.Config(**config) if config is not None else None
+    w = np.ones(tb.shape[1], dtype=np.float32)
     with threadpool_limits(1):
-        _, _, out, _ = o.forward(seg, tb, rms_weight=np.ones(tb.shape[1], dtype=np.float32), cfg=cfg)
-    return int(out.shape[0])
+        t0 = time.perf_counter()
+        lm, lv, out, exact = o.forward(seg, tb, rms_weight=w, cfg=cfg)
+        dt = time.perf_counter() - t0
+        cfg = cfg or o.Config()
+        lo, hi = cfg.min_value, cfg.max_value
+        err = np.abs(np.clip(lm_g.astype(np.float64), lo, hi) - np.clip(lm, lo, hi))
+        edges = o.level_edges(lo, hi, cfg.mel_vocab_size)
+        band = (np.min(np.abs(lm[..., None] - edges), axis=-1) <= 1e-3) if edges.size else np.zeros(lm.shape, bool)
+        mism = lv_g != lv
+        same = ~mism.any(axis=1)
+        exact_tok = np.all(tok_g == out, axis=1)
+        d = (tok_g != out) & same[:, None]
+        # a bf16 difference is within the bar if it is one ulp next to a rounding midpoint
+        gv = o.bf16_to_f32(tok_g).astype(np.float64)
+        wv = o.bf16_to_f32(out).astype(np.float64)
+        mid_ok = (np.abs(exact - 0.5 * (gv + wv)) <= 1e-5 * np.abs(exact)) & \
+                 (np.abs(tok_g.astype(np.int64) - out.astype(np.int64)) == 1)
+    return {"tokens": int(out.shape[0]), "seconds": dt,
+            "parity": {"frames": int(lm.shape[0]), "max_err_clamped_logmel": float(err.max(initial=0.0)),
+                       "edge_band": int(band.sum()), "forgiven": int((mism & band).sum()),
+                       "level_mismatches_outside_band": int((mism & ~band).sum()),
+                       "frames_affected": int(mism.any(axis=1).sum()),
+                       "tokens_compared": int(same.sum()), "tokens_bit_exact": int((exact_tok & same).sum()),
+                       "bf16_midpoint_ulps": int((d & mid_ok).sum()),
+                       "bf16_outside_bar": int((d & ~mid_ok).sum())}}
+
+
+def one_core_baseline():
+    """The oracle on one core for the 1 s three-tone clip (20 tokens, no
+    RMSNorm) and the 8 x 30 s bursts batch (4800 tokens, RMSNorm on)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import dmel_oracle as o
+    tb = synth.table_bf16(seed=1234).numpy().view(np.uint16)
+    res = {}
+    with threadpool_limits(1):
+        x = synth.tones_clip(seed=0)
+        t0 = time.perf_counter()
+        _, _, out, _ = o.forward(x, tb)
+        res["tones_1s_tokens_per_s"] = out.shape[0] / (time.perf_counter() - t0)
+        xs = synth.bursts_clips(seed=1, n_clips=8, n_samples=480000).numpy()
+        w = np.ones(6144, np.float32)
+        t0 = time.perf_counter()
+        n = sum(o.forward(xs[c], tb, rms_weight=w)[2].shape[0] for c in range(8))
+        res["bursts_8x30s_tokens_per_s"] = n / (time.perf_counter() - t0)
+    return res
 
 
 def main():
@@ -777,43 +854,67 @@ def bench_batch(args):
     assert T == n_tok
     out = torch.empty((n_tok, d), dtype=torch.int16, device=dev)
     gram = torch.empty((1280, 1280), dtype=torch.float64, device=dev)
-    levels = torch.empty((n_tok, n_bins), dtype=torch.uint8, device=dev)
-    scale = torch.empty(n_tok, dtype=torch.float32, device=dev)
-    dm.dmel_rms_gram(table, d, gram, **lay)   # once per table (weight preparation), outside the step
     stream = torch.cuda.current_stream()
+    # the Gram matrix of the table: once per table (weight preparation), outside the step
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    dm.dmel_rms_gram(table, d, gram, stream, **lay)
+    g1.record(stream)
+    ws = torch.empty(dm.dmel_forward_workspace_bytes(n_tok), dtype=torch.uint8, device=dev)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        dm.dmel_levels(ctx, audio, audio.numel(), so, fo, n_clips, n_tok, None, levels, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        dm.dmel_rms_scale(levels, n_tok, gram, d, 1e-6, scale, stream, **lay)
-        if ev is not None:
-            ev[2].record(stream)
-        dm.dmel_embed(levels, n_tok, table, d, rms_w, scale, out, dm.DMEL_BF16, d, None, stream, **lay)
-        if ev is not None:
-            ev[3].record(stream)
+    def step():
+        dm.dmel_forward(ctx, audio, audio.numel(), so, fo, n_clips, n_tok, None, table, d, rms_w, gram, 1e-6, out,
+                        dm.DMEL_BF16, d, None, ws, ws.numel(), stream)
 
+    # timed region: the product call, one dmel_forward per step
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    ev[0].record(stream)
     for k in range(args.steps):
-        step(events[k])
+        step()
+        ev[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in events])  # ms
-    k_front, k_scale, k_embed = per.mean(axis=0)
+    step_ms = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)])
     ms_step = wall * 1e3 / args.steps
     tok_s = n_tok / (ms_step * 1e-3)
+    gram_ms = g0.elapsed_time(g1)
+
+    # per-kernel split: the same three launches dmel_forward enqueues, called
+    # one by one with events between them (same kernels, same sizes)
+    levels = ws[: n_tok * n_bins].view(n_tok, n_bins)
+    scale = torch.empty(n_tok, dtype=torch.float32, device=dev)
+
+    def split(e=None):
+        if e is not None:
+            e[0].record(stream)
+        dm.dmel_levels(ctx, audio, audio.numel(), so, fo, n_clips, n_tok, None, levels, stream)
+        if e is not None:
+            e[1].record(stream)
+        dm.dmel_rms_scale(levels, n_tok, gram, d, 1e-6, scale, stream, **lay)
+        if e is not None:
+            e[2].record(stream)
+        dm.dmel_embed(levels, n_tok, table, d, rms_w, scale, out, dm.DMEL_BF16, d, None, stream, **lay)
+        if e is not None:
+            e[3].record(stream)
+
+    split()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        split(events[k])
+    torch.cuda.synchronize()
+    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in events])  # ms
+    k_front, k_scale, k_embed = per.mean(axis=0)
     embed_adds = (n_bins - 1) * d * n_tok   # 79 x 6144 per token for the released 80 bins
     achieved = embed_adds / (k_embed * 1e-3) / 1e12
     hbm = HBM_BYTES_PER_TOKEN * n_tok / (ms_step * 1e-3) / 1e9
-    print(f"[bench] per step: levels {k_front:.3f} ms, rms_scale {k_scale:.3f} ms, embed {k_embed:.3f} ms; "
-          f"wall {ms_step:.3f} ms", file=sys.stderr, flush=True)
+    print(f"[bench] dmel_forward {ms_step:.3f} ms per step (events: p50 {np.median(step_ms):.3f}, max "
+          f"{step_ms.max():.3f}); split: levels {k_front:.3f} ms, rms_scale {k_scale:.3f} ms, embed {k_embed:.3f} ms; "
+          f"Gram (once per table) {gram_ms:.3f} ms", file=sys.stderr, flush=True)
 
     # a plain 1 GiB device copy, timed after the steps: the HBM rate this box
     # reaches, to set the step's algorithmic rate against
@@ -830,10 +931,24 @@ def bench_batch(args):
     del src, dst
     front_tflops = FRONT_FLOPS_PER_FRAME * n_tok / (k_front * 1e-3) / 1e12
 
-    cpu = None
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
+        # the GPU's results for the oracle's sample: the product call's tokens,
+        # its levels, and the log-mel of the same frames (dmel_frames)
+        step()
+        lm = torch.empty((n_tok, n_bins), dtype=torch.float32, device=dev)
+        dm.dmel_frames(ctx, audio, audio.numel(), so, fo, n_clips, n_tok, None, lm, stream)
+        torch.cuda.synchronize()
+
+        def gpu_sample(c, f):
+            r = slice(c * T_clip, c * T_clip + f)
+            return (lm[r].cpu().numpy(), ws[: n_tok * n_bins].view(n_tok, n_bins)[r].cpu().numpy(),
+                    out[r].cpu().numpy().view(np.uint16))
         try:
-            cpu = cpu_baseline(audio, clip_len, table, n_clips, args.cpu_frames, None if released else cfg)
+            cpu, parity = cpu_baseline(audio, clip_len, table, n_clips, args.cpu_frames, gpu_sample,
+                                       None if released else cfg)
+            if released:
+                cpu["one_core"] = one_core_baseline()
         except Exception as e:  # report, never hide the GPU line
             cpu = {"value": None, "unit": "tokens/s", "cores": 0, "kind": "oracle", "sample": f"failed: {e}"}
     dm.dmel_destroy(ctx)
@@ -850,10 +965,11 @@ def bench_batch(args):
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"dMel forward: {n_clips} clips x {args.minutes:g} min of 16 kHz speech-like audio "
-                               f"({n_tok} tokens), {n_bins} mel bins x {n_lv} levels over "
+        "config": {"workload": f"dMel forward (dmel_forward per step): {n_clips} clips x {args.minutes:g} min of "
+                               f"16 kHz speech-like audio ({n_tok} tokens), {n_bins} mel bins x {n_lv} levels over "
                                f"[{cfg['min_value']:g}, {cfg['max_value']:g}], table {n_bins * n_lv}x6144 bf16, "
-                               f"fp32 sum, RMSNorm on, bf16 out",
+                               f"fp32 sum, RMSNorm on, bf16 out; the table's Gram matrix is computed once per table "
+                               f"({gram_ms:.2f} ms), outside the step",
                    "global_batch": n_clips, "seq_len": T_clip, "parallelism": "single GPU"},
         "hbm_achieved_GBps": hbm,
         "hbm_frac": hbm / PEAK_HBM_GBPS,
@@ -862,10 +978,12 @@ def bench_batch(args):
         "alu_frac_of_packed_peak": achieved / PEAK_ADD_PACKED_TFLOPS,
         "frontend_TFLOPs": front_tflops,
         "frontend_frac_of_fp32_peak": front_tflops / PEAK_FP32_TFLOPS,
-        "kernel_ms": {"frontend_levels": k_front, "rms_scale": k_scale, "embed": k_embed},
+        "step_ms_p50": float(np.median(step_ms)),
+        "kernel_ms": {"frontend_levels": k_front, "rms_scale": k_scale, "embed": k_embed, "gram_once": gram_ms},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_ADD_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_ADD_TFLOPS,
                      "traffic": embed_traffic() if (n_clips, clip_len) == (64, 19_200_000) and released else None},
+        "parity": parity,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
