@@ -187,8 +187,14 @@ int dmel_create_config(dmel_ctx** out, int device, const dmel_config* config) {
     (void)hipSetDevice(prev);
     return fail(DMEL_ENOMEM, "host allocation failed");
   }
-  dmel::build_host_tables(h, cfg.n_mel_bins, cfg.mel_vocab_size, cfg.min_value, cfg.max_value);
-  // layout: window | tw800 | tw1600 | twa | seg_start | seg_lo | seg_hi | seg_inv | q_edge
+  if (!dmel::build_host_tables(h, cfg.n_mel_bins, cfg.mel_vocab_size, cfg.min_value, cfg.max_value)) {
+    delete h;
+    delete ctx;
+    (void)hipSetDevice(prev);
+    return fail(DMEL_EINVAL, "filter schedule for %d filters exceeds its table", cfg.n_mel_bins);
+  }
+  // layout: window | tw800 | tw1600 | twa | seg_start | seg_lo | seg_hi | seg_inv | q_edge |
+  //         lds_image | mel_w | mel_first | mel_filt | mel_round
   size_t off_window = 0;
   size_t off_tw800 = round_up(off_window + sizeof(h->window), 256);
   size_t off_tw1600 = round_up(off_tw800 + sizeof(h->tw800), 256);
@@ -198,7 +204,12 @@ int dmel_create_config(dmel_ctx** out, int device, const dmel_config* config) {
   size_t off_hi = round_up(off_lo + sizeof(h->seg_lo), 256);
   size_t off_inv = round_up(off_hi + sizeof(h->seg_hi), 256);
   size_t off_qe = round_up(off_inv + sizeof(h->seg_inv), 256);
-  size_t total = round_up(off_qe + sizeof(h->q_edge), 256);
+  size_t off_img = round_up(off_qe + sizeof(h->q_edge), 256);
+  size_t off_mw = round_up(off_img + sizeof(h->lds_image), 256);
+  size_t off_mb = round_up(off_mw + sizeof(h->mel_w), 256);
+  size_t off_mf = round_up(off_mb + sizeof(h->mel_first), 256);
+  size_t off_mr = round_up(off_mf + sizeof(h->mel_filt), 256);
+  size_t total = round_up(off_mr + sizeof(h->mel_round), 256);
   char* staging = new (std::nothrow) char[total];
   if (staging == nullptr) {
     delete h;
@@ -216,6 +227,11 @@ int dmel_create_config(dmel_ctx** out, int device, const dmel_config* config) {
   std::memcpy(staging + off_hi, h->seg_hi, sizeof(h->seg_hi));
   std::memcpy(staging + off_inv, h->seg_inv, sizeof(h->seg_inv));
   std::memcpy(staging + off_qe, h->q_edge, sizeof(h->q_edge));
+  std::memcpy(staging + off_img, h->lds_image, sizeof(h->lds_image));
+  std::memcpy(staging + off_mw, h->mel_w, sizeof(h->mel_w));
+  std::memcpy(staging + off_mb, h->mel_first, sizeof(h->mel_first));
+  std::memcpy(staging + off_mf, h->mel_filt, sizeof(h->mel_filt));
+  std::memcpy(staging + off_mr, h->mel_round, sizeof(h->mel_round));
   int rc = DMEL_OK;
   char* dev = nullptr;
   e = hipMalloc(reinterpret_cast<void**>(&dev), total);
@@ -241,6 +257,12 @@ int dmel_create_config(dmel_ctx** out, int device, const dmel_config* config) {
     ctx->tabs.seg_hi = reinterpret_cast<const float*>(dev + off_hi);
     ctx->tabs.seg_inv = reinterpret_cast<const float*>(dev + off_inv);
     ctx->tabs.q_edge = reinterpret_cast<const float*>(dev + off_qe);
+    ctx->tabs.lds_image = reinterpret_cast<const float*>(dev + off_img);
+    ctx->tabs.mel_in_lds = h->mel_in_lds;
+    ctx->tabs.mel_w = reinterpret_cast<const float4*>(dev + off_mw);
+    ctx->tabs.mel_first = reinterpret_cast<const int*>(dev + off_mb);
+    ctx->tabs.mel_filt = reinterpret_cast<const int*>(dev + off_mf);
+    ctx->tabs.mel_round = reinterpret_cast<const int*>(dev + off_mr);
     ctx->tabs.n_mels = cfg.n_mel_bins;
     ctx->tabs.n_levels = cfg.mel_vocab_size;
     ctx->tabs.q_lo = cfg.min_value;

@@ -15,25 +15,32 @@
 //
 // Work decomposition (one workgroup = 256 threads = 8 frames, fp32, LDS):
 //  0. a frame's 32 threads sit in one wavefront and find its clip and first
-//     sample themselves (steps 1-3 touch only the frame's own LDS rows, so
+//     sample themselves (steps 1-3 touch only the frame's own LDS buffer, so
 //     the four wavefronts run them without workgroup barriers);
-//  1. the 1600 windowed samples of a frame are read as 800 complex values
-//     z[m] = x[2m] + i x[2m+1] straight into the registers of pass A (from
-//     the clip's carry or zeros, then the audio, for a clip's first frame);
+//  1. the frame's 1600 samples are read as 800 complex values z[m] = x[2m] +
+//     i x[2m+1] straight into registers (from the clip's carry or zeros, then
+//     the audio, for a clip's first frame), while the tables read per lane
+//     (window, pass-A twiddles, split twiddles, quantizer edges and the
+//     filter schedule) are copied once per workgroup into LDS: read from
+//     global memory by every frame, they were two thirds of the kernel's
+//     vector-memory traffic;
 //  2. 800-point complex FFT, 800 = 32 x 25:
-//     pass A - one thread per (frame, n1 < 32): a 25-point DFT (5 x 5) over
-//              z[n1 + 32 n2] (coalesced 8-byte reads across n1) in registers,
-//              then the twiddle W800^(n1 k2);
+//     pass A - one thread per (frame, n1 < 32): windowing, a 25-point DFT
+//              (5 x 5) over z[n1 + 32 n2] in registers, then the twiddle
+//              W800^(n1 k2);
 //     pass B - one thread per (frame, k2 < 25): a 32-point DFT (8 x 4) over
 //              n1 in registers, giving Z[k2 + 25 k1];
-//     the exchange between the passes goes through LDS rows padded to 33
-//     complex values so that neither pass has bank conflicts;
+//     the exchanges (A to B, B to the split) go through the frame's LDS
+//     buffer of rows padded to 33, real parts first, then imaginary parts:
+//     half the buffer of complex exchanges, which leaves room in LDS for the
+//     tables at three workgroups per CU;
 //  3. split Z into the 801-bin spectrum of the real frame and take |X|^2;
-//  4. mel (work items across the block's frames, after a barrier): each bin
-//     lies between two triangle edges and feeds exactly two filters (the
-//     rising side of one, the falling side of the previous), so one pass
-//     over the 81 segments gives per-segment sums A_s (rising) and C_s
-//     (falling) and filter j is A_j + C_{j+1}; then log, clamp, quantize.
+//  4. filters (after a barrier: lanes work across the block's frames): a
+//     fixed schedule built on the host (FrontTables::mel_w) gives each of the
+//     four wavefronts a balanced share of the filters; a lane computes one
+//     filter of one frame as a weighted sum over the filter's contiguous
+//     bins (weights from the schedule in LDS, 8 bins per step), then log,
+//     clamp and the exact quantizer.
 #include "internal.h"
 
 namespace dmel {
@@ -41,7 +48,20 @@ namespace {
 
 constexpr int kFramesPerBlock = 8;
 constexpr int kThreads = 256;
-constexpr int kSlots = 825;  // complex slots per frame in LDS: 25 rows x 33
+// Floats per frame in the exchange buffer: 825 used (25 rows x 33); the
+// stride is 24 mod 64 so that the two frames of a wavefront overlap in few
+// LDS banks during the FFT exchanges, and the filter step's reads (8 frames x
+// 8 slots whose bins differ mod 8) fall in 64 distinct banks.
+constexpr int kSlots = 856;
+constexpr int kXchg = kFramesPerBlock * kSlots;  // exchange floats of a workgroup
+// the filter step's powers: bin k at float kPOff + k of the frame's buffer,
+// bins [-8, 0) and [801, kMelReadEnd) zero
+constexpr int kPOff = 8;
+static_assert(kSlots % 64 == 24, "bank spread of the exchange buffers");
+static_assert(kPOff + kMelReadEnd <= kSlots, "the filter step reads inside the frame's buffer");
+static_assert(kPOff + kMelReadEnd - kBins <= 32, "the zero pads are written by one lane each");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
   return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
@@ -142,34 +162,48 @@ __device__ __forceinline__ ClipPos clip_of(const int64_t* frame_off, const int64
 
 // Exact level of a log-mel value: the number of quantizer edges k = 1 .. V-1
 // that the clamped value reaches, i.e. floor((c - lo) * V / (hi - lo)) capped
-// at V - 1, decided by exact comparisons (the released edges -7 + 9k/16 are
-// exact in fp32; other edges are stored rounded up, see FrontTables).
-__device__ __forceinline__ int quantize(float l, const FrontTables& t) {
+// at V - 1, decided by exact comparisons with the edges qe[0..V] (the released
+// edges -7 + 9k/16 are exact in fp32; other edges are stored rounded up, see
+// FrontTables), which the kernel keeps in LDS.
+__device__ __forceinline__ int quantize(float l, const FrontTables& t, const float* qe) {
   const float c = fminf(fmaxf(l, t.q_lo), t.q_hi);
   const int vmax = t.n_levels - 1;
   int q = static_cast<int>((c - t.q_lo) * t.q_scale);
   q = q < 0 ? 0 : (q > vmax ? vmax : q);
-  // the estimate is within one or two of the exact level
-  while (q > 0 && c < t.q_edge[q]) --q;
-  while (q < vmax && c >= t.q_edge[q + 1]) ++q;
+  // The estimate is within one of the exact level: with t = (c - lo) V /
+  // (hi - lo), the level is min(floor(t), V - 1), and the three fp32 roundings
+  // (the difference, the stored V / (hi - lo), the product) move t by at most
+  // 3 * 2^-24 * t <= 5e-5.  So one comparison each way decides it.
+  const float e_lo = qe[q], e_hi = qe[q + 1];
+  if (q > 0 && c < e_lo) return q - 1;
+  if (q < vmax && c >= e_hi) return q + 1;
   return q;
 }
 
+// kMelLds: the filter schedule comes with the table image into LDS (it has
+// at most kMelLdsChunks chunks); otherwise its weights are read from global
+// memory.
+template <bool kMelLds>
 __global__ void __launch_bounds__(kThreads)
 frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_samples_total,
                 const int64_t* __restrict__ sample_off, const int64_t* __restrict__ frame_off,
                 int n_clips, int64_t n_frames, double clip_rate, const float* __restrict__ carry,
                 float* __restrict__ logmel, uint8_t* __restrict__ levels) {
-  // Only the frames' working buffer lives in LDS (52.8 KB: three workgroups
-  // per CU); the constant tables are read from global memory (uniform indices
-  // become scalar loads, the rest hit the L1).
-  __shared__ float2 zbuf[kFramesPerBlock * kSlots];
+  // LDS: the frames' exchange buffers (8 x 856 floats), then the table image
+  // (window, twa, tw1600, quantizer edges, with kMelLds the schedule): 52.3 KB
+  // (41.0 KB without the schedule), three workgroups per CU.
+  constexpr int kImg = kMelLds ? kImgFull : kImgFloats;
+  constexpr int kImgPieces = (kImg + 255) / 256;  // 1 KB pieces (the last one partial)
+  static_assert(kImg % 4 == 0, "16-byte copies");
+  __shared__ float smem[kXchg + kImg];
+  float* const img = smem + kXchg;
 
   const int tid = threadIdx.x;
+  const int wave = tid >> 6;
   const int f = tid >> 5;      // frame within the block
   const int lane = tid & 31;   // n1 in pass A, k2 in pass B
   const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kFramesPerBlock;
-  float2* zf = zbuf + f * kSlots;
+  float* const zf = smem + f * kSlots;
   const float2* __restrict__ tw = tabs.tw800;
 
   // the frame's clip and first sample (each of its 32 threads finds them)
@@ -188,77 +222,88 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
   // Samples [0, 800) of the frame come from `lo` (the audio, or for a clip's
   // first frame its carry, or zeros without one) and [800, 1600) from `hi`
   // (the audio), whenever the frame lies inside the audio, which offsets that
-  // describe the audio always give; other frames check every sample.
+  // describe the audio always give; `paired` marks the usual case of both
+  // sources present and 8-byte aligned.  Other frames read every sample with
+  // its own checks.
   const float* lo = nullptr;
   const float* hi = nullptr;
-  bool inside = false;
   if (valid && base + kHop >= 0 && base + kWindow <= n_samples_total && (first || base >= 0)) {
-    inside = true;
     hi = audio + (base + kHop);
     if (!first) lo = audio + base;
     else if (carry != nullptr) lo = carry + static_cast<int64_t>(clip) * kHop;
   }
-  // the usual case: both sources present and 8-byte aligned
-  const bool paired = inside && lo != nullptr &&
-                      ((reinterpret_cast<uintptr_t>(lo) | reinterpret_cast<uintptr_t>(hi)) & 7) == 0;
+  const bool paired = lo != nullptr && ((reinterpret_cast<uintptr_t>(lo) | reinterpret_cast<uintptr_t>(hi)) & 7) == 0;
 
-  // ---- 1 + 2a. windowed samples, 25-point DFTs over n2 for each n1 --------
-  {
-    float2 x[25];
-    const float2* w2 = reinterpret_cast<const float2*>(tabs.window);
-    // sample pair m < 400 comes from lo, m >= 400 from hi (n2 = 12 straddles:
-    // lanes 0..15 read lo)
-    if (paired) {
-      const float2* l2 = reinterpret_cast<const float2*>(lo);
-      const float2* h2 = reinterpret_cast<const float2*>(hi);
+  // ---- 1. the frame's samples as 800 pairs z[m] = x[2m] + i x[2m+1] -----
+  // (pair m = lane + 32 n2; m < 400 from lo, m >= 400 from hi: n2 = 12
+  // straddles, lanes 0..15 read lo), and the table image copied into LDS
+  // while they are in flight
+  float2 raw[25];
+  if (paired) {
+    const float2* l2 = reinterpret_cast<const float2*>(lo);
+    const float2* h2 = reinterpret_cast<const float2*>(hi);
 #pragma unroll
-      for (int n2 = 0; n2 < 25; ++n2) {
-        const int m = lane + 32 * n2;
-        float2 a;
-        if (n2 < 12) a = l2[m];
-        else if (n2 > 12) a = h2[m - kHop / 2];
-        else a = lane < 16 ? l2[m] : h2[m - kHop / 2];
-        const float2 w = w2[m];
-        x[n2] = make_float2(a.x * w.x, a.y * w.y);
-      }
-    } else if (inside) {
-      // no carry (zeros) or unaligned sources: 4-byte reads
+    for (int n2 = 0; n2 < 25; ++n2) {
+      const int m = lane + 32 * n2;
+      if (n2 < 12) raw[n2] = l2[m];
+      else if (n2 > 12) raw[n2] = h2[m - kHop / 2];
+      else raw[n2] = lane < 16 ? l2[m] : h2[m - kHop / 2];
+    }
+  } else {
+    const int64_t cbase = static_cast<int64_t>(clip) * kHop;
 #pragma unroll
-      for (int n2 = 0; n2 < 25; ++n2) {
-        const int m = lane + 32 * n2;
-        const bool from_lo = n2 < 12 || (n2 == 12 && lane < 16);
-        float2 a = make_float2(0.0f, 0.0f);
-        if (!from_lo) {
-          a = make_float2(hi[2 * m - kHop], hi[2 * m - kHop + 1]);
-        } else if (lo != nullptr) {
-          a = make_float2(lo[2 * m], lo[2 * m + 1]);
-        }
-        const float2 w = w2[m];
-        x[n2] = make_float2(a.x * w.x, a.y * w.y);
-      }
-    } else {
-      const int64_t cbase = static_cast<int64_t>(clip) * kHop;
+    for (int n2 = 0; n2 < 25; ++n2) {
+      const int m = lane + 32 * n2;
+      float v[2];
 #pragma unroll
-      for (int n2 = 0; n2 < 25; ++n2) {
-        const int m = lane + 32 * n2;
-        float v[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int n = 2 * m + h;
-          float val = 0.0f;
-          if (valid) {
-            if (first && n < kHop) {
-              if (carry != nullptr) val = carry[cbase + n];
-            } else {
-              const int64_t sidx = base + n;
-              if (sidx >= 0 && sidx < n_samples_total) val = audio[sidx];
-            }
+      for (int h = 0; h < 2; ++h) {
+        const int n = 2 * m + h;
+        float val = 0.0f;
+        if (valid) {
+          if (first && n < kHop) {
+            if (carry != nullptr) val = carry[cbase + n];
+          } else {
+            const int64_t sidx = base + n;
+            if (sidx >= 0 && sidx < n_samples_total) val = audio[sidx];
           }
-          v[h] = val;
         }
-        const float2 w = w2[m];
-        x[n2] = make_float2(v[0] * w.x, v[1] * w.y);
+        v[h] = val;
       }
+      raw[n2] = make_float2(v[0], v[1]);
+    }
+  }
+  for (int i = wave; i < kImgPieces; i += kThreads / 64) {
+    if (256 * i + 4 * (tid & 63) < kImg) {
+      __builtin_amdgcn_global_load_lds(tabs.lds_image + 256 * i + 4 * (tid & 63), (lds_void_t*)(img + 256 * i), 16, 0,
+                                       0);
+    }
+  }
+  // the copies into LDS are not tracked by the compiler: wait for every
+  // memory read of the wave, then for the other waves
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // ---- 2a. windowing, 25-point DFTs over n2 for each n1 ----------------
+  {
+    // window pair (w[2m], w[2m+1]) of pair m = lane + 32 n2: from the stored
+    // half for m < 400, else (w[1600 - 2m], w[1599 - 2m]) (n2 = 12 straddles)
+    const float* wh = img + kImgWindow;
+    float2 x[25];
+#pragma unroll
+    for (int n2 = 0; n2 < 25; ++n2) {
+      const int m = lane + 32 * n2;
+      float2 w;
+      if (n2 < 12) {
+        w = *reinterpret_cast<const float2*>(wh + 2 * m);
+      } else if (n2 > 12) {
+        w = make_float2(wh[kWindow - 2 * m], wh[kWindow - 1 - 2 * m]);
+      } else {
+        const bool low = lane < 16;
+        const int i0 = low ? 2 * m : kWindow - 1 - 2 * m;  // the lower of the two indices
+        const float a = wh[i0], b = wh[i0 + 1];
+        w = low ? make_float2(a, b) : make_float2(b, a);
+      }
+      x[n2] = make_float2(raw[n2].x * w.x, raw[n2].y * w.y);
     }
     // n2 = 5 a + b: 5-point DFTs over a for each b
 #pragma unroll
@@ -281,20 +326,29 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
       y[c + 15] = u3;
       y[c + 20] = u4;
     }
+    const float2* twa = reinterpret_cast<const float2*>(img + kImgTwa);
 #pragma unroll
-    for (int k2 = 1; k2 < 25; ++k2) y[k2] = cmul(y[k2], tabs.twa[(k2 - 1) * 32 + lane]);
-#pragma unroll
-    for (int k2 = 0; k2 < 25; ++k2) zf[lane + 33 * k2] = y[k2];
-  }
-  wave_sync();
+    for (int k2 = 1; k2 < 25; ++k2) y[k2] = cmul(y[k2], twa[(k2 - 1) * 32 + lane]);
 
-  // ---- 2b. 32-point DFTs over n1 for each k2 ---------------------------
-  {
-    float2 a[32];
+    // ---- exchange to pass B: real parts, then imaginary parts, through the
+    // frame's 825 floats (rows of 33: neither side has bank conflicts)
     const bool active = lane < 25;
     const int k2 = active ? lane : 0;
+    float2 a[32];
 #pragma unroll
-    for (int n1 = 0; n1 < 32; ++n1) a[n1] = zf[n1 + 33 * k2];
+    for (int i = 0; i < 25; ++i) zf[lane + 33 * i] = y[i].x;
+    wave_sync();
+#pragma unroll
+    for (int n1 = 0; n1 < 32; ++n1) a[n1].x = zf[n1 + 33 * k2];
+    wave_sync();
+#pragma unroll
+    for (int i = 0; i < 25; ++i) zf[lane + 33 * i] = y[i].y;
+    wave_sync();
+#pragma unroll
+    for (int n1 = 0; n1 < 32; ++n1) a[n1].y = zf[n1 + 33 * k2];
+    wave_sync();
+
+    // ---- 2b. 32-point DFTs over n1 for each k2 -------------------------
     // n1 = 4 p + q: 8-point DFTs over p for each q, output r
     float2 v[4][8];
 #pragma unroll
@@ -312,132 +366,114 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
     // 4-point DFTs over q for each r: output k1 = r + 8 s
 #pragma unroll
     for (int r = 0; r < 8; ++r) dft4(v[0][r], v[1][r], v[2][r], v[3][r]);
+
+    // ---- exchange to the split: Z[k2 + 25 k1], real parts then imaginary
+    // parts; the frame's thread `lane` then takes k = lane + 32 m and 800 - k
+    constexpr int kPairs = kHalf / 2 + 1;            // 401
+    constexpr int kPer = (kPairs + 31) / 32;         // 13
+    float2 zk[kPer], zm[kPer];
+    if (active) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) zf[k2 + 25 * (r + 8 * s)] = v[s][r].x;
+      }
+    }
+    wave_sync();
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int k = min(lane + 32 * m, kPairs - 1);
+      zk[m].x = zf[k];
+      zm[m].x = zf[k == 0 ? 0 : kHalf - k];
+    }
     wave_sync();
     if (active) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) zf[k2 + 25 * (r + 8 * s)] = v[s][r];
+        for (int s = 0; s < 4; ++s) zf[k2 + 25 * (r + 8 * s)] = v[s][r].y;
       }
     }
-  }
-  wave_sync();
-
-  // ---- 3. real-spectrum split and power ---------------------------------
-  // E[k] = (Z[k] + conj Z[800-k]) / 2, O[k] = (Z[k] - conj Z[800-k]) / 2i,
-  // X[k] = E + W1600^k O and X[800-k] = conj(E - W1600^k O), k = 0..400;
-  // the frame's thread `lane` takes k = lane + 32 m.
-  constexpr int kPairs = kHalf / 2 + 1;            // 401
-  constexpr int kPer = (kPairs + 31) / 32;         // 13
-  float p_lo[kPer], p_hi[kPer];
+    wave_sync();
 #pragma unroll
-  for (int m = 0; m < kPer; ++m) {
-    const int k = lane + 32 * m;
-    p_lo[m] = 0.0f;
-    p_hi[m] = 0.0f;
-    if (k < kPairs) {
-      const float2 zk = zf[k];
-      const float2 zm = zf[k == 0 ? 0 : kHalf - k];
-      const float2 e = make_float2(0.5f * (zk.x + zm.x), 0.5f * (zk.y - zm.y));
-      const float2 o = make_float2(0.5f * (zk.y + zm.y), -0.5f * (zk.x - zm.x));
-      const float2 wo = cmul(tabs.tw1600[k], o);  // L1-cached table
-      const float2 x1 = cadd(e, wo), x2 = csub(e, wo);
-      p_lo[m] = x1.x * x1.x + x1.y * x1.y;
-      p_hi[m] = x2.x * x2.x + x2.y * x2.y;
+    for (int m = 0; m < kPer; ++m) {
+      const int k = min(lane + 32 * m, kPairs - 1);
+      zk[m].y = zf[k];
+      zm[m].y = zf[k == 0 ? 0 : kHalf - k];
     }
-  }
-  wave_sync();
-  {
-    float* pw = reinterpret_cast<float*>(zf);  // the frame's 801 powers
+    wave_sync();
+
+    // ---- 3. real-spectrum split and power -------------------------------
+    // E[k] = (Z[k] + conj Z[800-k]) / 2, O[k] = (Z[k] - conj Z[800-k]) / 2i,
+    // X[k] = E + W1600^k O and X[800-k] = conj(E - W1600^k O), k = 0..400.
+    // The halves are left out (2E, 2O, so the powers are 4 |X|^2); the filter
+    // weights carry the 1/4.
+    const float2* t16 = reinterpret_cast<const float2*>(img + kImgTw1600);
 #pragma unroll
     for (int m = 0; m < kPer; ++m) {
       const int k = lane + 32 * m;
       if (k < kPairs) {
-        pw[k] = p_lo[m];
-        pw[kHalf - k] = p_hi[m];
+        const float2 e = make_float2(zk[m].x + zm[m].x, zk[m].y - zm[m].y);
+        const float2 o = make_float2(zk[m].y + zm[m].y, zm[m].x - zk[m].x);
+        const float2 wo = cmul(t16[k], o);
+        const float2 x1 = cadd(e, wo), x2 = csub(e, wo);
+        zf[kPOff + k] = x1.x * x1.x + x1.y * x1.y;
+        zf[kPOff + kHalf - k] = x2.x * x2.x + x2.y * x2.y;
       }
     }
+    // the filter step reads bins [-8, kMelReadEnd) with zero weights outside a
+    // filter's range; the powers it reads there must be finite: zero
+    if (lane < kPOff) zf[lane] = 0.0f;
+    else if (lane < kPOff + kMelReadEnd - kBins) zf[kBins + lane] = 0.0f;
   }
-  __syncthreads();  // the mel step works across the block's frames
-
-  // ---- 4. mel: segment sums, then filters, log, clamp, quantize ----------
+  // ---- 4. filters, log, clamp, quantize ----------------------------------
+  // Wavefront r runs round r of the schedule (FrontTables::mel_w): lane
+  // 8 * slot + ff computes, for frame ff and each side of the round, the
+  // filter of `slot` as the sum over the side's 8-bin chunks of the chunk's
+  // weights (the 8 lanes of a slot share each read) times the frame's powers,
+  // then writes its log-mel value and level.
+  __syncthreads();  // the powers of all 8 frames are in LDS
   {
-    float* pf = reinterpret_cast<float*>(zbuf);
+    const int r = __builtin_amdgcn_readfirstlane(wave);
+    const int slot = (tid >> 3) & 7;
+    const int ff = tid & 7;
+    const int* rd = tabs.mel_round + 8 * r;
+    const int base = rd[0], sides = rd[2];
+    const float4* mw = kMelLds ? reinterpret_cast<const float4*>(img + kImgMelW) : tabs.mel_w;
+    const int* mfirst = kMelLds ? reinterpret_cast<const int*>(img + kImgMelFirst) : tabs.mel_first;
+    const int* mfilt = kMelLds ? reinterpret_cast<const int*>(img + kImgMelFilt) : tabs.mel_filt;
     const int n_mels = tabs.n_mels;
-    const int n_seg = n_mels + 1;    // 81 segments for 80 filters
-    constexpr int kAOff = 1024;      // per-frame float offsets of A_s and C_s (past the 801 powers)
-    constexpr int kCOff = kAOff + kMaxMels + 8;
-    static_assert(kCOff + kMaxMels + 1 <= 2 * kSlots, "segment sums must fit the frame's buffer");
-    // segments s and n_seg - 1 - s are paired (a narrow low band with a wide
-    // high one) so that the threads' loops are of similar length
-    const int n_pairs = (n_seg + 1) / 2;  // 41: (0,80) .. (39,41), (40)
-    const int* __restrict__ seg = tabs.seg_start;
-    const float bin_hz = static_cast<float>(kSampleRate) / kNfft;
-    // pair-major order: the lanes of a wavefront take neighbouring pairs, whose
-    // segments have similar lengths, so their loops run about the same count
-    static_assert(kFramesPerBlock == 8, "pair-major order assumes 8 frames");
-    for (int it = tid; it < kFramesPerBlock * n_pairs; it += kThreads) {
-      const int pr = it >> 3;
-      const int ff = it & 7;
-      const float* p = pf + 2 * ff * kSlots;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int sg = h == 0 ? pr : n_seg - 1 - pr;
-        if (h == 1 && sg == pr) break;
-        // triangle weights of the segment's bins, from its edges
-        const float inv = tabs.seg_inv[sg];
-        const float lo = tabs.seg_lo[sg], hi = tabs.seg_hi[sg];
-        float a = 0.0f, c = 0.0f;
-        const int k0 = seg[sg], k1 = seg[sg + 1];
-        float fk = bin_hz * static_cast<float>(k0);  // 10 k Hz, exact
-        // four bins per step, their reads issued together, then one step over
-        // the last 0..3 bins whose reads past the segment (at most index 802,
-        // inside the frame's slots) are dropped
-        int k = k0;
-        for (; k + 4 <= k1; k += 4) {
-          float q[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) q[i] = p[k + i];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            a = fmaf(fk - lo, q[i], a);  // filter sg, rising side
-            c = fmaf(hi - fk, q[i], c);  // filter sg - 1, falling side
-            fk += bin_hz;
-          }
-        }
-        if (k < k1) {
-          float q[3];
-#pragma unroll
-          for (int i = 0; i < 3; ++i) q[i] = p[k + i];
-#pragma unroll
-          for (int i = 0; i < 3; ++i) {
-            const float pk = k + i < k1 ? q[i] : 0.0f;
-            a = fmaf(fk - lo, pk, a);
-            c = fmaf(hi - fk, pk, c);
-            fk += bin_hz;
-          }
-        }
-        pf[2 * ff * kSlots + kAOff + sg] = a * inv;
-        pf[2 * ff * kSlots + kCOff + sg] = c * inv;
-      }
-    }
-    __syncthreads();
-    // output it = ff * n_mels + j of the block; ff = floor((it + 0.5) / n_mels)
-    // in fp32 is exact: it < 1024 puts the product within 1.3e-4 of the
-    // quotient, whose distance to an integer is at least 0.5 / 128
     const int64_t n_valid = n_frames - g0 < kFramesPerBlock ? n_frames - g0 : kFramesPerBlock;
-    const int n_out = static_cast<int>(n_valid) * n_mels;
-    const float inv_n = 1.0f / static_cast<float>(n_mels);
-    float* lm_out = logmel != nullptr ? logmel + g0 * n_mels : nullptr;
-    uint8_t* lv_out = levels != nullptr ? levels + g0 * n_mels : nullptr;
-    for (int it = tid; it < n_out; it += kThreads) {
-      const int ff = static_cast<int>((static_cast<float>(it) + 0.5f) * inv_n);
-      const int j = it - ff * n_mels;
-      const float m = pf[2 * ff * kSlots + kAOff + j] + pf[2 * ff * kSlots + kCOff + j + 1];
-      // ln m = ln 2 * log2 m with the hardware log2 (about 1 ulp; m >= 1e-10 is normal)
-      const float l = 0.69314718055994531f * __builtin_amdgcn_logf(fmaxf(m, kLogFloor));
-      if (lm_out != nullptr) lm_out[it] = l;
-      if (lv_out != nullptr) lv_out[it] = static_cast<uint8_t>(quantize(l, tabs));
+    const float* p_frame = smem + ff * kSlots + kPOff;
+    const float* qe = img + kImgEdge;
+    const int64_t orow = (g0 + ff) * n_mels;
+    for (int h = 0; h < sides; ++h) {
+      const int i = 8 * (kMelMaxSides * r + h) + slot;
+      const int j = mfilt[i];
+      const int c_first = rd[3 + h], c_end = rd[4 + h];
+      const float* p = p_frame + mfirst[i] - 8 * c_first;
+      float a0 = 0.0f, a1 = 0.0f;
+      for (int c = c_first; c < c_end; ++c) {
+        const float4 u = mw[16 * (base + c) + slot];
+        const float4 v = mw[16 * (base + c) + 8 + slot];
+        float q[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) q[k] = p[8 * c + k];
+        a0 = fmaf(u.x, q[0], a0);
+        a1 = fmaf(u.y, q[1], a1);
+        a0 = fmaf(u.z, q[2], a0);
+        a1 = fmaf(u.w, q[3], a1);
+        a0 = fmaf(v.x, q[4], a0);
+        a1 = fmaf(v.y, q[5], a1);
+        a0 = fmaf(v.z, q[6], a0);
+        a1 = fmaf(v.w, q[7], a1);
+      }
+      if (j >= 0 && ff < n_valid) {
+        // ln m = ln 2 * log2 m with the hardware log2 (about 1 ulp; m >= 1e-10 is normal)
+        const float l = 0.69314718055994531f * __builtin_amdgcn_logf(fmaxf(a0 + a1, kLogFloor));
+        if (logmel != nullptr) logmel[orow + j] = l;
+        if (levels != nullptr) levels[orow + j] = static_cast<uint8_t>(quantize(l, tabs, qe));
+      }
     }
   }
 }
@@ -451,9 +487,16 @@ hipError_t launch_frontend(const FrontTables& tabs, const float* audio, int64_t 
   if (n_frames <= 0) return hipSuccess;
   const int64_t blocks = (n_frames + kFramesPerBlock - 1) / kFramesPerBlock;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(frontend_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                     tabs, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames,
-                     static_cast<double>(n_clips) / static_cast<double>(n_frames), carry, logmel, levels);
+  const double rate = static_cast<double>(n_clips) / static_cast<double>(n_frames);
+  if (tabs.mel_in_lds) {
+    hipLaunchKernelGGL(frontend_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                       tabs, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames, rate, carry, logmel,
+                       levels);
+  } else {
+    hipLaunchKernelGGL(frontend_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                       tabs, audio, n_samples_total, sample_off, frame_off, n_clips, n_frames, rate, carry, logmel,
+                       levels);
+  }
   return hipGetLastError();
 }
 

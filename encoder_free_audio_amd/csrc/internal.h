@@ -51,11 +51,57 @@ struct FrontTables {
   // lo + ((hi - lo) * k) / n_levels, so the fp32 test c >= q_edge[k] is the
   // exact comparison with the fp64 edge.
   const float* q_edge;    // [n_levels + 1]
+  // The tables the front end reads per lane, packed as the kernel stages them
+  // in LDS (kImg* float offsets): window, twa, tw1600, q_edge and, when the
+  // filter schedule has at most kMelLdsChunks chunks (mel_in_lds), its
+  // weights, first bins and filters.
+  const float* lds_image;  // [kImgFull]
+  int mel_in_lds;
+  // Filter step as a fixed schedule (tables.cpp).  Filter j is one weighted
+  // sum over its contiguous bins [seg_start[j], seg_start[j + 2]), taken in
+  // chunks of 8 bins.  The four wavefronts of a workgroup run one round each
+  // for the workgroup's 8 frames (lane = 8 * slot + frame).  Round r is the
+  // chunk list [base, base + chunks) with base, chunks, sides = mel_round[8r],
+  // [8r + 1], [8r + 2]; side h < sides is the chunk range [start_h,
+  // start_{h+1}) of the round (start_h = mel_round[8r + 3 + h], relative to
+  // base).  With i = 8 (kMelMaxSides r + h) + slot, side h gives the slot the
+  // filter mel_filt[i] (-1: none) and its first chunk starts at bin
+  // mel_first[i] (>= -8, = slot mod 8, so that the 8 slots' reads fall in
+  // distinct LDS banks; the bins before the filter's range have weight 0).
+  // Chunk c, slot s: weights mel_w[16c + s] (bins 0..3 of the chunk) and
+  // mel_w[16c + 8 + s] (bins 4..7), 0 outside the filter's range.  Weights are
+  // the triangle values times 1/4: the kernel's power spectrum is 4 |X|^2.
+  const float4* mel_w;
+  const int* mel_first;
+  const int* mel_filt;
+  const int* mel_round;
   int n_mels;             // filters, 1 .. 128
   int n_levels;           // 1 .. 256
   float q_lo, q_hi;       // clamp range
   float q_scale;          // n_levels / (hi - lo), for the first estimate
 };
+
+// Limits of the filter schedule: kMelMaxSides sides per round, kMelChunks
+// chunks in all (every filter count 1 .. 128 needs at most 101), and the
+// powers read, which lie in bins [-8, kMelReadEnd) (below 808 for every filter
+// count); the kernel keeps the powers outside [0, 801) there at zero.
+constexpr int kMelMaxSides = (kMaxMels + 31) / 32;
+constexpr int kMelChunks = 128;
+constexpr int kMelReadEnd = 808;
+
+// Float offsets of the front end's LDS table image (16-byte aligned parts).
+// The window is stored as w[0..800]: the periodic Hann window is symmetric,
+// w[n] = w[1600 - n].
+constexpr int kImgWindow = 0;                                // [801]
+constexpr int kImgTwa = 804;                                 // [24 * 32 * 2]
+constexpr int kImgTw1600 = kImgTwa + 2 * 24 * 32;            // [401 * 2]
+constexpr int kImgEdge = kImgTw1600 + 2 * (kHalf / 2 + 1) + 2;  // [kMaxLevels + 1]
+constexpr int kImgFloats = (kImgEdge + kMaxLevels + 1 + 3) / 4 * 4;  // without the schedule
+constexpr int kMelLdsChunks = 40;
+constexpr int kImgMelW = kImgFloats;                          // [kMelLdsChunks][16] float4
+constexpr int kImgMelFirst = kImgMelW + kMelLdsChunks * 64;    // [4 * kMelMaxSides * 8] int
+constexpr int kImgMelFilt = kImgMelFirst + 4 * kMelMaxSides * 8;  // [4 * kMelMaxSides * 8] int
+constexpr int kImgFull = kImgMelFilt + 4 * kMelMaxSides * 8;
 
 // Host-built tables, in the layout FrontTables points to (see tables.cpp).
 struct HostTables {
@@ -68,9 +114,17 @@ struct HostTables {
   float seg_hi[kMaxMels + 1];
   float seg_inv[kMaxMels + 1];
   float q_edge[kMaxLevels + 1];
+  alignas(16) float lds_image[kImgFull];
+  int mel_in_lds;
+  alignas(16) float mel_w[kMelChunks * 16 * 4];
+  int mel_first[4 * kMelMaxSides * 8];
+  int mel_filt[4 * kMelMaxSides * 8];
+  int mel_round[4 * 8];
 };
 // n_mels in [1, 128], n_levels in [1, 256], lo < hi (validated by the caller).
-void build_host_tables(HostTables* t, int n_mels, int n_levels, float lo, float hi);
+// Returns false only if the filter schedule exceeds kMelChunks or kMelReadEnd
+// (no filter count in range does).
+bool build_host_tables(HostTables* t, int n_mels, int n_levels, float lo, float hi);
 
 // Kernel launchers (all enqueue on `stream` and return the launch status).
 hipError_t launch_frontend(const FrontTables& tabs, const float* audio, int64_t n_samples_total,

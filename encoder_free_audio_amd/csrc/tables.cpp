@@ -13,7 +13,9 @@
 //    (n_mel_bins filters and n_mel_bins + 2 edges in general);
 //  * uniform quantizer over the clamp range [lo, hi] in n_levels steps, whose
 //    edges are lo + ((hi - lo) * k) / n_levels evaluated in fp64.
+#include <algorithm>
 #include <cmath>
+#include <cstring>
 
 #include "internal.h"
 
@@ -24,7 +26,7 @@ double hz_to_mel(double f) { return 2595.0 * std::log10(1.0 + f / 700.0); }
 double mel_to_hz(double m) { return 700.0 * (std::pow(10.0, m / 2595.0) - 1.0); }
 }  // namespace
 
-void build_host_tables(HostTables* t, int n_mels, int n_levels, float lo, float hi) {
+bool build_host_tables(HostTables* t, int n_mels, int n_levels, float lo, float hi) {
   const double two_pi = 2.0 * M_PI;
   for (int n = 0; n < kWindow; ++n) {
     t->window[n] = static_cast<float>(0.5 - 0.5 * std::cos(two_pi * n / kWindow));
@@ -82,6 +84,125 @@ void build_host_tables(HostTables* t, int n_mels, int n_levels, float lo, float 
     t->q_edge[k] = f;
   }
   t->q_edge[n_levels] = hi;
+
+  // the LDS image: window (its first half and middle), twa, tw1600 and the
+  // quantizer edges
+  std::memset(t->lds_image, 0, sizeof(t->lds_image));
+  std::memcpy(t->lds_image + kImgWindow, t->window, sizeof(float) * (kWindow / 2 + 1));
+  std::memcpy(t->lds_image + kImgTwa, t->twa, sizeof(t->twa));
+  std::memcpy(t->lds_image + kImgTw1600, t->tw1600, sizeof(t->tw1600));
+  std::memcpy(t->lds_image + kImgEdge, t->q_edge, sizeof(float) * (n_levels + 1));
+
+  // Filter schedule (FrontTables::mel_w).  Filter j is the weighted sum over
+  // its bins [seg_start[j], seg_start[j + 2]): rising (f - e_j) / (e_{j+1} - e_j)
+  // over segment j, falling (e_{j+2} - f) / (e_{j+2} - e_{j+1}) over segment
+  // j + 1, each weight times 1/4 (exact) for the kernel's 4 |X|^2 powers.
+  // Filters are taken longest first in sets of 8 (one side each).  Inside a
+  // set, longest first, each filter takes the free slot s that needs the
+  // fewest chunks once its reads start at the bin = s mod 8 at or below its
+  // range (never below bin -8).  A side costs the chunks of its costliest
+  // slot, and the sets go, costliest first, to the round with the least work
+  // so far that has a side free.
+  static_assert(kMelMaxSides + 4 <= 8, "a round's entries must fit 8 ints");
+  int order[kMaxMels], len[kMaxMels];
+  for (int j = 0; j < n_mels; ++j) {
+    order[j] = j;
+    len[j] = t->seg_start[j + 2] - t->seg_start[j];
+  }
+  std::stable_sort(order, order + n_mels, [&](int a, int b) { return len[a] > len[b]; });
+  const int n_sets = (n_mels + 7) / 8;
+  const int max_sides = (n_mels + 31) / 32;
+  constexpr int kSets = (kMaxMels + 7) / 8;
+  int set_filt[kSets][8], set_first[kSets][8], set_cost[kSets];
+  for (int s = 0; s < n_sets; ++s) {
+    bool used[8] = {false, false, false, false, false, false, false, false};
+    set_cost[s] = 0;
+    for (int slot = 0; slot < 8; ++slot) {
+      set_filt[s][slot] = -1;
+      set_first[s][slot] = slot - 8;
+    }
+    for (int i = 8 * s; i < 8 * s + 8 && i < n_mels; ++i) {
+      const int j = order[i];
+      const int first = t->seg_start[j];
+      int best = -1, best_chunks = 0, best_pad = 0;
+      for (int slot = 0; slot < 8; ++slot) {
+        if (used[slot]) continue;
+        const int pad = ((first - slot) % 8 + 8) % 8;
+        if (first - pad < -8) continue;
+        const int chunks = (len[j] + pad + 7) / 8;
+        if (best < 0 || chunks < best_chunks || (chunks == best_chunks && pad < best_pad)) {
+          best = slot;
+          best_chunks = chunks;
+          best_pad = pad;
+        }
+      }
+      used[best] = true;
+      set_filt[s][best] = j;
+      set_first[s][best] = first - best_pad;
+      if (best_chunks > set_cost[s]) set_cost[s] = best_chunks;
+    }
+  }
+  int set_order[kSets];
+  for (int s = 0; s < n_sets; ++s) set_order[s] = s;
+  std::stable_sort(set_order, set_order + n_sets, [&](int a, int b) { return set_cost[a] > set_cost[b]; });
+  int load[4] = {0, 0, 0, 0}, sides[4] = {0, 0, 0, 0};
+  int set_of[4][kMelMaxSides];
+  for (int i = 0; i < n_sets; ++i) {
+    const int s = set_order[i];
+    int best = -1;
+    for (int r = 0; r < 4; ++r) {
+      if (sides[r] < max_sides && (best < 0 || load[r] < load[best])) best = r;
+    }
+    set_of[best][sides[best]++] = s;
+    load[best] += set_cost[s];
+  }
+  std::memset(t->mel_w, 0, sizeof(t->mel_w));
+  std::memset(t->mel_round, 0, sizeof(t->mel_round));
+  for (int i = 0; i < 4 * kMelMaxSides * 8; ++i) {
+    t->mel_filt[i] = -1;
+    t->mel_first[i] = (i % 8) - 8;
+  }
+  int base = 0;  // chunks so far
+  for (int r = 0; r < 4; ++r) {
+    int* rd = t->mel_round + 8 * r;
+    rd[0] = base;
+    rd[2] = sides[r];
+    int c0 = 0;  // chunk of the round where the side starts
+    for (int h = 0; h < sides[r]; ++h) {
+      const int s = set_of[r][h];
+      const int chunks = set_cost[s];
+      if (base + c0 + chunks > kMelChunks) return false;
+      rd[3 + h] = c0;
+      for (int slot = 0; slot < 8; ++slot) {
+        const int j = set_filt[s][slot];
+        const int pb = set_first[s][slot];
+        t->mel_filt[8 * (kMelMaxSides * r + h) + slot] = j;
+        t->mel_first[8 * (kMelMaxSides * r + h) + slot] = pb;
+        if (pb + 8 * chunks > kMelReadEnd) return false;
+        if (j < 0) continue;
+        for (int k = t->seg_start[j]; k < t->seg_start[j + 2]; ++k) {
+          const double f = static_cast<double>(k) * kSampleRate / kNfft;
+          const double w = k < t->seg_start[j + 1] ? (f - edges[j]) / (edges[j + 1] - edges[j])
+                                                   : (edges[j + 2] - f) / (edges[j + 2] - edges[j + 1]);
+          const int i = k - pb;  // position in the slot's chunks
+          const int c = base + c0 + i / 8;
+          t->mel_w[4 * (16 * c + 8 * ((i % 8) / 4) + slot) + (i % 4)] = static_cast<float>(0.25 * w);
+        }
+      }
+      c0 += chunks;
+    }
+    rd[3 + sides[r]] = c0;
+    rd[1] = c0;
+    base += c0;
+  }
+  // the schedule in the LDS image, when it fits
+  t->mel_in_lds = base <= kMelLdsChunks ? 1 : 0;
+  if (t->mel_in_lds) {
+    std::memcpy(t->lds_image + kImgMelW, t->mel_w, sizeof(float) * 64 * base);
+    std::memcpy(t->lds_image + kImgMelFirst, t->mel_first, sizeof(t->mel_first));
+    std::memcpy(t->lds_image + kImgMelFilt, t->mel_filt, sizeof(t->mel_filt));
+  }
+  return true;
 }
 
 }  // namespace dmel
