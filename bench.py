@@ -31,9 +31,12 @@ from encoder_free_audio_amd import dmel as dm  # noqa: E402
 from encoder_free_audio_amd import synth  # noqa: E402
 
 HBM_BYTES_PER_TOKEN = 800 * 4 + 6144 * 2    # 3,200 B audio read (800 new samples) + 12,288 B bf16 token write
-PEAK_ADD_TFLOPS = 256 * 64 * 2.4e9 / 1e12   # v_add_f32: 256 CUs x 64 lanes x 2.4 GHz = 39.32 T adds/s
+# fp32 adds: the chip's fp32 vector figure (157.3 TFLOP/s) is 128 fused multiply-adds per clock per CU at
+# 2.4 GHz; an add is one flop, so 256 CUs x 128 x 2.4 GHz = 78.6 T adds/s.  Plain (non-packed) v_add_f32
+# with VGPR operands issues at 64.6 T/s (VOP2) to 70.2 T/s (VOP3) on this chip: bench.py --workload valu,
+# profiles/valu_rates_mi355x.md.
+PEAK_ADD_TFLOPS = 78.6
 PEAK_HBM_GBPS = 8000.0
-PEAK_ADD_PACKED_TFLOPS = 78.6   # the chip's fp32 vector figure, which counts packed (two-wide) adds
 PEAK_FP32_TFLOPS = 157.3        # fp32 vector peak with FMA counted as two flops
 # algorithmic flops per frame of the front end: FFT 2.5 N log2 N (N = 1600) 42,575,
 # mel 3,142, power 2,403, window 1,600
@@ -73,7 +76,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=20000, help="oracle sample: frames per worker")
     ap.add_argument("--workload", choices=("batch", "stream", "interleave", "copy", "shortconv", "shortconv_decode",
-                                           "backward", "hmlp", "dft_gemm", "rounding"),
+                                           "backward", "hmlp", "dft_gemm", "rounding", "valu"),
                     default="batch",
                     help="batch: 64 x 20 min clips (default); stream: 4096 streams, one hop per step; "
                          "interleave: 256 x 32768 audio/text positions; copy: a plain 1 GiB device copy "
@@ -81,7 +84,9 @@ def parse():
                          "short convolution over 64 requests x 24,000 tokens x 6144 channels (prefill); "
                          "shortconv_decode: 4096 requests, one token per step, state carried; backward: the "
                          "RMSNorm and table-gradient backward of the 64 x 20 min batch; hmlp: the four-stage "
-                         "image front end over 32 images of 1280 x 1280 (32768 patches of 40 x 40)")
+                         "image front end over 32 images of 1280 x 1280 (32768 patches of 40 x 40); valu: issue "
+                         "rates of single vector-ALU instruction forms (the ceiling the embedding's adds are "
+                         "priced against)")
     ap.add_argument("--streams", type=int, default=4096)
     ap.add_argument("--config", default=None,
                     help="batch workload with another front-end configuration, "
@@ -233,7 +238,7 @@ def main():
     if args.steps is None:
         args.steps = {"batch": 20, "stream": 1000, "interleave": 5, "copy": 5, "shortconv": 20,
                       "shortconv_decode": 1000, "backward": 5, "hmlp": 10, "dft_gemm": 3,
-                      "rounding": 1}[args.workload]
+                      "rounding": 1, "valu": 5}[args.workload]
     if args.workload == "stream":
         return bench_stream(args)
     if args.workload == "interleave":
@@ -250,6 +255,8 @@ def main():
         return bench_dft_gemm(args)
     if args.workload == "rounding":
         return bench_rounding(args)
+    if args.workload == "valu":
+        return bench_valu(args)
     return bench_batch(args)
 
 
@@ -711,6 +718,44 @@ def bench_copy(args):
                       "GBps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
+VALU_KINDS = ("v_add_f32 VOP2, VGPR operands", "v_add_f32 VOP3, VGPR operands", "v_add_f32 with an SGPR operand",
+              "v_fmac_f32 VOP2", "v_fma_f32 VOP3", "v_mul_f32 VOP2")
+
+
+def bench_valu(args):
+    """Issue rate of single vector-ALU instruction forms over the whole chip
+    (dmel_bench_valu_rate: 16 independent register chains per lane, no memory
+    in the loop).  8192 workgroups of 256 lanes (32 waves per CU) x 4096
+    rounds x 16 chains = 1.37e11 lane-operations per launch (about 2 ms);
+    the rate is lane-operations per second, timed with HIP events per
+    launch."""
+    from encoder_free_audio_amd import bench_ext as be
+    blocks, iters = 8192, 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ops = float(blocks) * 256 * iters * 16
+    rates = {}
+    for kind, name in enumerate(VALU_KINDS):
+        for _ in range(args.warmup):
+            be.dmel_bench_valu_rate(kind, blocks, iters, out, stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev[0].record(stream)
+        for k in range(args.steps):
+            be.dmel_bench_valu_rate(kind, blocks, iters, out, stream)
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+        ms_mean = float(np.mean(ms))
+        rates[name] = {"ms_per_launch": ms_mean, "T_ops_per_s": ops / (ms_mean * 1e-3) / 1e12}
+        print(f"[bench] {name}: {ms_mean:.3f} ms, {rates[name]['T_ops_per_s']:.1f} T lane-ops/s",
+              file=sys.stderr, flush=True)
+    assert bool(torch.isfinite(out).all())
+    print(json.dumps({"workload": "valu_issue_rates", "blocks": blocks, "threads": 256, "rounds": iters,
+                      "chains": 16, "lane_ops_per_launch": ops, "rates": rates,
+                      "clock_x_lanes_T": 256 * 64 * 2.4e9 / 1e12, "datasheet_fp32_vector_T": PEAK_FP32_TFLOPS}),
+          flush=True)
+
+
 def _base_line(args, value, ms_step, workload, extra):
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -975,7 +1020,6 @@ def bench_batch(args):
         "hbm_frac": hbm / PEAK_HBM_GBPS,
         "copy_GBps": copy_gbps,
         "hbm_frac_of_copy": hbm / copy_gbps,
-        "alu_frac_of_packed_peak": achieved / PEAK_ADD_PACKED_TFLOPS,
         "frontend_TFLOPs": front_tflops,
         "frontend_frac_of_fp32_peak": front_tflops / PEAK_FP32_TFLOPS,
         "step_ms_p50": float(np.median(step_ms)),

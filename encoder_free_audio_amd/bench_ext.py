@@ -1,6 +1,7 @@
 """ctypes binding of libdmel_bench (csrc/bench/dmel_bench.h), the
 benchmark-only companion of libdmel: the DFT-as-matrix-product log-mel that
-the FFT front end was measured against, and the rounding probe.  Argument
+the FFT front end was measured against, the rounding probe and the
+vector-ALU issue-rate calibration.  Argument
 marshalling only; only bench.py and the tests load it."""
 
 from __future__ import annotations
@@ -13,7 +14,8 @@ from encoder_free_audio_amd import dmel as _dm
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdmel_bench.so")
 EXPORTS = ("dmel_bench_last_error", "dmel_bench_dft_matrix_bytes", "dmel_bench_dft_matrix",
-           "dmel_bench_dft_gemm_workspace_bytes", "dmel_bench_frames_dft_gemm", "dmel_bench_rounding_probe")
+           "dmel_bench_dft_gemm_workspace_bytes", "dmel_bench_frames_dft_gemm", "dmel_bench_rounding_probe",
+           "dmel_bench_valu_rate")
 
 _handle = None
 _lock = threading.Lock()
@@ -38,6 +40,7 @@ def lib() -> ctypes.CDLL:
                 "dmel_bench_frames_dft_gemm": (ctypes.c_int, [_P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _P, _P,
                                                               _SZ, _P]),
                 "dmel_bench_rounding_probe": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
+                "dmel_bench_valu_rate": (ctypes.c_int, [_I32, _I32, _I32, _P, _P]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(h, name)
@@ -77,3 +80,8 @@ def dmel_bench_rounding_probe(c, e, n, out, stream=None) -> None:
     p = _dm._ptr
     _check("dmel_bench_rounding_probe", lib().dmel_bench_rounding_probe(p(c), p(e), int(n), p(out),
                                                                         _dm._stream(stream)))
+
+
+def dmel_bench_valu_rate(kind, blocks, iters, out, stream=None) -> None:
+    _check("dmel_bench_valu_rate", lib().dmel_bench_valu_rate(int(kind), int(blocks), int(iters), _dm._ptr(out),
+                                                              _dm._stream(stream)))

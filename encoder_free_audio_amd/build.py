@@ -20,7 +20,7 @@ BENCH_LIB_PATH = os.path.join(PKG_DIR, "libdmel_bench.so")
 
 SOURCES = ["dmel_api.cpp", "tables.cpp", "frontend.hip", "embed.hip", "shortconv.hip", "backward.hip", "hmlp.hip",
            "noalloc.hip"]
-BENCH_SOURCES = ["bench/bench_api.cpp", "bench/dft_gemm.hip", "bench/rounding_probe.hip"]
+BENCH_SOURCES = ["bench/bench_api.cpp", "bench/dft_gemm.hip", "bench/rounding_probe.hip", "bench/valu_rate.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are switched off (they are never needed for

@@ -17,4 +17,7 @@ hipError_t launch_dft_gemm_frames(const FrontTables& tabs, const float* audio, i
 // Rounding probe (rounding_probe.hip); n % 1024 == 0.
 hipError_t launch_rounding_probe(const float* c, const uint16_t* e, int64_t n, float* out, hipStream_t stream);
 
+// Vector-ALU issue-rate calibration (valu_rate.hip): kind 0..5.
+hipError_t launch_valu_rate(int kind, int blocks, int iters, float* out, hipStream_t stream);
+
 }  // namespace dmel

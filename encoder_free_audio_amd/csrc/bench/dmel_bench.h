@@ -68,6 +68,14 @@ int dmel_bench_frames_dft_gemm(const dmel_ctx* ctx, const float* audio, int64_t 
  * fp32 [4, n]. */
 int dmel_bench_rounding_probe(const float* c, const uint16_t* e, int64_t n, float* out, void* stream);
 
+/* Vector-ALU issue rate: `blocks` workgroups of 256 threads, each lane
+ * running 16 independent chains of one instruction form for `iters` rounds
+ * (16 * iters instructions per lane): kind 0 v_add_f32 (VOP2, VGPR operands),
+ * 1 v_add_f32 (VOP3), 2 v_add_f32 with an SGPR operand, 3 v_fmac_f32 (VOP2),
+ * 4 v_fma_f32 (VOP3), 5 v_mul_f32 (VOP2).  out: fp32 [blocks * 256], one
+ * value per lane (keeps the chains live).  The caller times the launch. */
+int dmel_bench_valu_rate(int32_t kind, int32_t blocks, int32_t iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
