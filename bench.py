@@ -37,6 +37,9 @@ HBM_BYTES_PER_TOKEN = 800 * 4 + 6144 * 2    # 3,200 B audio read (800 new sample
 # profiles/valu_rates_mi355x.md.
 PEAK_ADD_TFLOPS = 78.6
 PEAK_HBM_GBPS = 8000.0
+# LDS: ds_read_b128 of 16-float rows at the embedding's 80-byte pitch, measured on this chip (bench.py --workload
+# valu, profiles/valu_rates_mi355x.md): the ceiling of the embedding's gathers, which read 4 bytes per add
+LDS_GATHER_TBPS = 143.0
 PEAK_FP32_TFLOPS = 157.3        # fp32 vector peak with FMA counted as two flops
 # algorithmic flops per frame of the front end: FFT 2.5 N log2 N (N = 1600) 42,575,
 # mel 3,142, power 2,403, window 1,600
@@ -719,7 +722,11 @@ def bench_copy(args):
 
 
 VALU_KINDS = ("v_add_f32 VOP2, VGPR operands", "v_add_f32 VOP3, VGPR operands", "v_add_f32 with an SGPR operand",
-              "v_fmac_f32 VOP2", "v_fma_f32 VOP3", "v_mul_f32 VOP2")
+              "v_fmac_f32 VOP2", "v_fma_f32 VOP3", "v_mul_f32 VOP2", "v_lshlrev_b32 by 16",
+              "v_and_b32 with a VGPR mask", "v_and_b32 with a literal mask", "v_cvt_f32_bf16 SDWA high half",
+              "v_cvt_f32_bf16 VOP1", "v_mov_b32 SDWA low word to high word", "v_perm_b32",
+              "v_alignbit_b32 by 16", "v_mul_u32_u24 by 65536")
+LDS_MODES = ("linear", "one address", "16-float rows, 80 B pitch", "16-float rows, 64 B pitch")
 
 
 def bench_valu(args):
@@ -728,14 +735,17 @@ def bench_valu(args):
     in the loop).  8192 workgroups of 256 lanes (32 waves per CU) x 4096
     rounds x 16 chains = 1.37e11 lane-operations per launch (about 2 ms);
     the rate is lane-operations per second, timed with HIP events per
-    launch."""
+    launch.  Then v_add_f32 at 1, 2, 4 and 8 waves per SIMD (same lane-
+    operations), and the LDS read rate of dmel_bench_lds_rate for its four
+    access patterns (4096 workgroups of 256 lanes x 2048 rounds x 64 B)."""
     from encoder_free_audio_amd import bench_ext as be
     blocks, iters = 8192, 4096
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     ops = float(blocks) * 256 * iters * 16
     rates = {}
-    for kind, name in enumerate(VALU_KINDS):
+    kinds = list(enumerate(VALU_KINDS)) + [(15, "mfma_32x32x16_bf16 only"), (16, "mfma_32x32x16_bf16 + 16 v_add_f32")]
+    for kind, name in kinds:
         for _ in range(args.warmup):
             be.dmel_bench_valu_rate(kind, blocks, iters, out, stream)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -746,13 +756,58 @@ def bench_valu(args):
         torch.cuda.synchronize()
         ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
         ms_mean = float(np.mean(ms))
+        if kind >= 15:
+            # rounds per SIMD: 8192 x 4 waves over 1024 SIMDs, `iters` rounds each
+            clk = ms_mean * 1e-3 * 2.4e9 / (blocks * 4 / 1024 * iters)
+            rates[name] = {"ms_per_launch": ms_mean, "clk_per_round_per_SIMD_at_2.4GHz": clk}
+            print(f"[bench] {name}: {ms_mean:.3f} ms, {clk:.1f} clk per round per SIMD", file=sys.stderr, flush=True)
+            continue
         rates[name] = {"ms_per_launch": ms_mean, "T_ops_per_s": ops / (ms_mean * 1e-3) / 1e12}
         print(f"[bench] {name}: {ms_mean:.3f} ms, {rates[name]['T_ops_per_s']:.1f} T lane-ops/s",
               file=sys.stderr, flush=True)
-    assert bool(torch.isfinite(out).all())
+    # plain adds at lower occupancy: 256-lane workgroups are 4 waves, one per SIMD
+    occ = {}
+    for wps in (1, 2, 4, 8):
+        b = 256 * wps
+        it = iters * 32 // wps // 4
+        for _ in range(args.warmup):
+            be.dmel_bench_valu_rate(0, b, it, out, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            be.dmel_bench_valu_rate(0, b, it, out, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_mean = e0.elapsed_time(e1) / args.steps
+        occ[f"{wps} waves per SIMD"] = {"ms_per_launch": ms_mean,
+                                        "T_ops_per_s": float(b) * 256 * it * 16 / (ms_mean * 1e-3) / 1e12}
+        print(f"[bench] v_add_f32 VOP2 at {wps} waves per SIMD: {occ[f'{wps} waves per SIMD']['T_ops_per_s']:.1f} "
+              f"T lane-ops/s", file=sys.stderr, flush=True)
+    # LDS: 4096 workgroups (four resident per CU) x 256 lanes x 2048 rounds x 64 B
+    lblocks, liters = 4096, 2048
+    lout = torch.empty(lblocks * 256, dtype=torch.float32, device="cuda")
+    lbytes = float(lblocks) * 256 * liters * 64
+    lds = {}
+    for mode, name in enumerate(LDS_MODES):
+        for _ in range(args.warmup):
+            be.dmel_bench_lds_rate(mode, lblocks, liters, lout, stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev[0].record(stream)
+        for k in range(args.steps):
+            be.dmel_bench_lds_rate(mode, lblocks, liters, lout, stream)
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        ms_mean = float(np.mean([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]))
+        tbps = lbytes / (ms_mean * 1e-3) / 1e12
+        lds[name] = {"ms_per_launch": ms_mean, "TB_per_s": tbps, "B_per_clk_per_CU_at_2.4GHz": tbps * 1e12 / 256 / 2.4e9}
+        print(f"[bench] LDS ds_read_b128, {name}: {ms_mean:.3f} ms, {tbps:.1f} TB/s", file=sys.stderr, flush=True)
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lout).all())
     print(json.dumps({"workload": "valu_issue_rates", "blocks": blocks, "threads": 256, "rounds": iters,
                       "chains": 16, "lane_ops_per_launch": ops, "rates": rates,
-                      "clock_x_lanes_T": 256 * 64 * 2.4e9 / 1e12, "datasheet_fp32_vector_T": PEAK_FP32_TFLOPS}),
+                      "clock_x_lanes_T": 256 * 64 * 2.4e9 / 1e12, "datasheet_fp32_vector_T": PEAK_FP32_TFLOPS,
+                      "v_add_f32_by_occupancy": occ,
+                      "lds_read": {"blocks": lblocks, "threads": 256, "rounds": liters,
+                                   "bytes_per_launch": lbytes, "modes": lds}}),
           flush=True)
 
 
@@ -1020,6 +1075,8 @@ def bench_batch(args):
         "hbm_frac": hbm / PEAK_HBM_GBPS,
         "copy_GBps": copy_gbps,
         "hbm_frac_of_copy": hbm / copy_gbps,
+        "embed_lds_gather": {"bytes_per_add": 4, "achieved_TBps": achieved * 4, "ceiling_TBps": LDS_GATHER_TBPS,
+                             "frac": achieved * 4 / LDS_GATHER_TBPS},
         "frontend_TFLOPs": front_tflops,
         "frontend_frac_of_fp32_peak": front_tflops / PEAK_FP32_TFLOPS,
         "step_ms_p50": float(np.median(step_ms)),

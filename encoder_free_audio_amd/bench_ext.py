@@ -15,7 +15,7 @@ from encoder_free_audio_amd import dmel as _dm
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdmel_bench.so")
 EXPORTS = ("dmel_bench_last_error", "dmel_bench_dft_matrix_bytes", "dmel_bench_dft_matrix",
            "dmel_bench_dft_gemm_workspace_bytes", "dmel_bench_frames_dft_gemm", "dmel_bench_rounding_probe",
-           "dmel_bench_valu_rate")
+           "dmel_bench_valu_rate", "dmel_bench_lds_rate")
 
 _handle = None
 _lock = threading.Lock()
@@ -41,6 +41,7 @@ def lib() -> ctypes.CDLL:
                                                               _SZ, _P]),
                 "dmel_bench_rounding_probe": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
                 "dmel_bench_valu_rate": (ctypes.c_int, [_I32, _I32, _I32, _P, _P]),
+                "dmel_bench_lds_rate": (ctypes.c_int, [_I32, _I32, _I32, _P, _P]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(h, name)
@@ -85,3 +86,8 @@ def dmel_bench_rounding_probe(c, e, n, out, stream=None) -> None:
 def dmel_bench_valu_rate(kind, blocks, iters, out, stream=None) -> None:
     _check("dmel_bench_valu_rate", lib().dmel_bench_valu_rate(int(kind), int(blocks), int(iters), _dm._ptr(out),
                                                               _dm._stream(stream)))
+
+
+def dmel_bench_lds_rate(mode, blocks, iters, out, stream=None) -> None:
+    _check("dmel_bench_lds_rate", lib().dmel_bench_lds_rate(int(mode), int(blocks), int(iters), _dm._ptr(out),
+                                                            _dm._stream(stream)))

@@ -83,12 +83,21 @@ int dmel_bench_rounding_probe(const float* c, const uint16_t* e, int64_t n, floa
 }
 
 int dmel_bench_valu_rate(int32_t kind, int32_t blocks, int32_t iters, float* out, void* stream) {
-  if (kind < 0 || kind > 5) return fail(DMEL_EINVAL, "kind must be in [0, 5] (got %d)", kind);
+  if (kind < 0 || kind > 16) return fail(DMEL_EINVAL, "kind must be in [0, 16] (got %d)", kind);
   if (blocks < 1 || iters < 1) return fail(DMEL_EINVAL, "blocks and iters must be positive");
   if (out == nullptr) return fail(DMEL_EINVAL, "NULL pointer argument");
   if (!aligned(out, 4)) return fail(DMEL_EALIGN, "out must be 4-byte aligned");
   hipError_t err = dmel::launch_valu_rate(kind, blocks, iters, out, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? DMEL_OK : hip_fail(err, "valu rate launch");
+}
+
+int dmel_bench_lds_rate(int32_t mode, int32_t blocks, int32_t iters, float* out, void* stream) {
+  if (mode < 0 || mode > 3) return fail(DMEL_EINVAL, "mode must be in [0, 3] (got %d)", mode);
+  if (blocks < 1 || iters < 1) return fail(DMEL_EINVAL, "blocks and iters must be positive");
+  if (out == nullptr) return fail(DMEL_EINVAL, "NULL pointer argument");
+  if (!aligned(out, 4)) return fail(DMEL_EALIGN, "out must be 4-byte aligned");
+  hipError_t err = dmel::launch_lds_rate(mode, blocks, iters, out, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? DMEL_OK : hip_fail(err, "lds rate launch");
 }
 
 }  // extern "C"

@@ -17,7 +17,9 @@ hipError_t launch_dft_gemm_frames(const FrontTables& tabs, const float* audio, i
 // Rounding probe (rounding_probe.hip); n % 1024 == 0.
 hipError_t launch_rounding_probe(const float* c, const uint16_t* e, int64_t n, float* out, hipStream_t stream);
 
-// Vector-ALU issue-rate calibration (valu_rate.hip): kind 0..5.
+// Vector-ALU issue-rate calibration (valu_rate.hip): kind 0..16.
 hipError_t launch_valu_rate(int kind, int blocks, int iters, float* out, hipStream_t stream);
+// LDS ds_read_b128 rate (valu_rate.hip): mode 0..3.
+hipError_t launch_lds_rate(int mode, int blocks, int iters, float* out, hipStream_t stream);
 
 }  // namespace dmel

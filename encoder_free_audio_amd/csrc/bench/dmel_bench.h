@@ -72,9 +72,21 @@ int dmel_bench_rounding_probe(const float* c, const uint16_t* e, int64_t n, floa
  * running 16 independent chains of one instruction form for `iters` rounds
  * (16 * iters instructions per lane): kind 0 v_add_f32 (VOP2, VGPR operands),
  * 1 v_add_f32 (VOP3), 2 v_add_f32 with an SGPR operand, 3 v_fmac_f32 (VOP2),
- * 4 v_fma_f32 (VOP3), 5 v_mul_f32 (VOP2).  out: fp32 [blocks * 256], one
- * value per lane (keeps the chains live).  The caller times the launch. */
+ * 4 v_fma_f32 (VOP3), 5 v_mul_f32 (VOP2), 6 v_lshlrev_b32 by 16, 7 v_and_b32
+ * with a VGPR mask, 8 v_and_b32 with a literal mask, 9 v_cvt_f32_bf16 (SDWA,
+ * high half), 10 v_cvt_f32_bf16 (VOP1), 11 v_mov_b32 SDWA (low word to high
+ * word), 12 v_perm_b32, 13 v_alignbit_b32 by 16, 14 v_mul_u32_u24 by 65536,
+ * 15 one v_mfma_f32_32x32x16_bf16 per round and no adds, 16 that MFMA and
+ * the 16 adds of kind 0 per round.  out: fp32 [blocks * 256], one value per
+ * lane (keeps the chains live).  The caller times the launch. */
 int dmel_bench_valu_rate(int32_t kind, int32_t blocks, int32_t iters, float* out, void* stream);
+
+/* LDS read rate: `blocks` workgroups of 256 threads with 36 KB of LDS each;
+ * every lane issues four ds_read_b128 per round (64 B) for `iters` rounds:
+ * mode 0 linear pieces, 1 one address for all lanes, 2 and 3 the embedding's
+ * gather (the 16-float row a random level selects in a 16-row block, row
+ * pitch 80 B or 64 B).  out: fp32 [blocks * 256].  The caller times it. */
+int dmel_bench_lds_rate(int32_t mode, int32_t blocks, int32_t iters, float* out, void* stream);
 
 #ifdef __cplusplus
 }

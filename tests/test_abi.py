@@ -322,13 +322,14 @@ def test_dft_gemm_validation(dm):
     with pytest.raises(E) as e:
         be._check("dmel_bench_rounding_probe", lib.dmel_bench_rounding_probe(256, 512, 1000, 1024, None))
     assert _code(e) == -2
-    for bad in ((6, 1, 1, 256), (-1, 1, 1, 256), (0, 0, 1, 256), (0, 1, 0, 256), (0, 1, 1, None)):
+    for fn, top in (("dmel_bench_valu_rate", 16), ("dmel_bench_lds_rate", 3)):
+        for bad in ((top + 1, 1, 1, 256), (-1, 1, 1, 256), (0, 0, 1, 256), (0, 1, 0, 256), (0, 1, 1, None)):
+            with pytest.raises(E) as e:
+                be._check(fn, getattr(lib, fn)(*bad, None))
+            assert _code(e) == -1
         with pytest.raises(E) as e:
-            be._check("dmel_bench_valu_rate", lib.dmel_bench_valu_rate(*bad, None))
-        assert _code(e) == -1
-    with pytest.raises(E) as e:
-        be._check("dmel_bench_valu_rate", lib.dmel_bench_valu_rate(0, 1, 1, 2, None))
-    assert _code(e) == -4
+            be._check(fn, getattr(lib, fn)(0, 1, 1, 2, None))
+        assert _code(e) == -4
     # (fake, aligned device addresses: every check fails before any HIP call)
     args = dict(audio=256, n=1600, so=512, fo=768, clips=1, frames=2, carry=None, mat=1024, lm=2048, ws=4096,
                 wsb=10 ** 6)
