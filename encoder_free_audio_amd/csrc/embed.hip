@@ -235,49 +235,78 @@ constexpr int kGCols = 1024;
 constexpr int kGPitch = kGCols + 1;           // doubles per staged row (odd: the 16 rows start in different banks)
 constexpr int kGStageBytes = 16 * kGPitch * 8;  // 131,200
 constexpr int kScaleThreads = 1024;
+// Columns width .. zero_end - 1 of each staged row (both even) are set to
+// +0.0, for lookups that run past the end of the upper triangle.
 __device__ __forceinline__ void stage_gram_part(double* g_s, const double* __restrict__ gram, int j, int c0, int width,
-                                                int tid) {
+                                                int tid, int zero_end) {
   const int r = tid >> 6;  // 0..15
   const int q = tid & 63;
   const double* src = gram + static_cast<int64_t>(kLevels * j + r) * kRows + c0;
   double* dst = g_s + r * kGPitch;
-  for (int c = 2 * q; c < width; c += 128) {
-    const double2 v = *reinterpret_cast<const double2*>(src + c);
-    dst[c] = v.x;
-    dst[c + 1] = v.y;
-  }
-}
-
-// Adds the terms of bins j' = j + q, q = Q0 .. Q1 (static), q <= qlim, of one
-// token to o: row[16 q + L_j' - base] with the row of level L_j staged from
-// column 16 j + base.  The bytes of bins j, j + 1, ... are bytes 0, 1, ... of
-// rot.  Masked terms read column 0 of the row and add +0.0.
-template <int Q0, int Q1>
-__device__ __forceinline__ void gram_terms(double& o, const double* row, const uint32_t (&rot)[20], int qlim,
-                                           int base) {
+  // four reads in flight per thread, then their stores
+  for (int c = 2 * q; c < width; c += 4 * 128) {
+    double2 v[4];
 #pragma unroll
-  for (int q = Q0; q <= Q1; ++q) {
-    const bool use = q <= qlim;
-    const int idx = use ? kLevels * q + static_cast<int>(level_byte(rot, q)) - base : 0;
-    const double v = row[idx];
-    o += use ? v : 0.0;
+    for (int i = 0; i < 4; ++i)
+      if (c + 128 * i < width) v[i] = *reinterpret_cast<const double2*>(src + c + 128 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (c + 128 * i < width) {
+        dst[c + 128 * i] = v[i].x;
+        dst[c + 128 * i + 1] = v[i].y;
+      }
+    }
+  }
+  for (int c = width + 2 * q; c < zero_end; c += 128) {
+    dst[c] = 0.0;
+    dst[c + 1] = 0.0;
   }
 }
 
-// The off-diagonal sum o_j of one token for bin j from the staged part
-// starting at column 16 j + base (part 1: base 0, bins j .. j + 63; part 2:
-// base 1024, bins j + 64 .. 79).  QMAX bounds 79 - j for the caller's range of
-// bins, so the loop is unrolled with static register indices.
-template <int QMAX>
-__device__ __forceinline__ void part1_terms(double& o, const double* row, const uint32_t (&rot)[20], int qlim) {
-  gram_terms<1, (QMAX < 63 ? QMAX : 63)>(o, row, rot, qlim, 0);
+// Adds the terms of bins j' = j + q, q = Q0 .. Q1 (static), of one token to
+// o: the value at column 16 q + L_j' - base of the token's staged row (the
+// row of level L_j, staged from column 16 j + base).  rot8 holds the levels
+// times 8 (byte offsets of a double), bins j, j + 1, ... in bytes 0, 1, ...;
+// so a lookup is one add of a byte to the row's LDS address, with 8 (16 q -
+// base) in the read's immediate offset.  Bins past 79 (q > 79 - j) land in
+// the zeroed columns after the triangle and add +0.0, which leaves the sum
+// unchanged (it starts at +0.0, so it is never -0.0).  The lookups go out
+// kTermBatch at a time and are then added in order, so a wavefront has that
+// many LDS reads in flight.
+constexpr int kTermBatch = 8;
+template <int Q0, int Q1>
+__device__ __forceinline__ void gram_terms(double& o, const char* row, const uint32_t (&rot8)[20], int base) {
+#pragma unroll
+  for (int q0 = Q0; q0 <= Q1; q0 += kTermBatch) {
+    double v[kTermBatch];
+#pragma unroll
+    for (int i = 0; i < kTermBatch; ++i) {
+      const int q = q0 + i;
+      if (q <= Q1) v[i] = *reinterpret_cast<const double*>(row + level_byte(rot8, q) + 8 * (kLevels * q - base));
+    }
+#pragma unroll
+    for (int i = 0; i < kTermBatch; ++i) {
+      if (q0 + i <= Q1) o += v[i];
+    }
+    // keep the next batch's lookups after this batch's adds (registers)
+    asm volatile("" : "+v"(o)::"memory");
+  }
 }
 
-// Large batches: a workgroup owns 2048 tokens (two per thread); for each bin
+// The off-diagonal sum o_j of one token for bin j from part 1 (base 0, bins
+// j .. j + 63).  QMAX bounds 79 - j for the caller's range of bins, so the
+// loop is unrolled with static register indices; its terms past 79 - j read
+// zeros.
+template <int QMAX>
+__device__ __forceinline__ void part1_terms(double& o, const char* row, const uint32_t (&rot8)[20]) {
+  gram_terms<1, (QMAX < 63 ? QMAX : 63)>(o, row, rot8, 0);
+}
+
+// Large batches: a workgroup owns 3072 tokens (three per thread); for each bin
 // the bin's 16 rows of G are staged part by part and every token adds its
 // terms.  The token's levels are a byte string shifted down by one byte per
 // bin (v_alignbyte), so that the level of bin j + q is always byte q.
-constexpr int kScaleTok = 2;                            // tokens per thread
+constexpr int kScaleTok = 3;                            // tokens per thread
 constexpr int kScaleBlock = kScaleThreads * kScaleTok;  // tokens per workgroup
 
 __global__ void __launch_bounds__(kScaleThreads)
@@ -294,42 +323,48 @@ rms_scale_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bin
     const int64_t t = t0 + static_cast<int64_t>(k) * kScaleThreads;
     total[k] = 0.0;
     load_token_levels(rot[k], levels, t, t < n_tokens, any, n_bins, n_levels);
+    // levels (at most 15) times 8, byte by byte
+#pragma unroll
+    for (int i = 0; i < 20; ++i) rot[k][i] <<= 3;
   }
+  const char* g_b = reinterpret_cast<const char*>(g_s);
   for (int j = 0; j < kMels; ++j) {
     const int c0 = kLevels * j;
-    const int qlim = kMels - 1 - j;
+    const int width = min(kRows - c0, kGCols);
     __syncthreads();
-    stage_gram_part(g_s, gram, j, c0, min(kRows - c0, kGCols), tid);
+    // zeros for the lookups of up to 9 bins past bin 79 (the QMAX groups below)
+    stage_gram_part(g_s, gram, j, c0, width, tid, min(kGCols, width + 160));
     __syncthreads();
     double off[kScaleTok], diag[kScaleTok];
-    const double* row[kScaleTok];
+    const char* row[kScaleTok];
 #pragma unroll
     for (int k = 0; k < kScaleTok; ++k) {
-      const uint32_t lj = rot[k][0] & 0xFFu;
-      row[k] = g_s + lj * kGPitch;
-      diag[k] = row[k][lj];
+      const uint32_t lj8 = rot[k][0] & 0xFFu;   // 8 L_j
+      row[k] = g_b + lj8 * kGPitch;
+      diag[k] = *reinterpret_cast<const double*>(row[k] + lj8);
       off[k] = 0.0;
     }
 #pragma unroll
     for (int k = 0; k < kScaleTok; ++k) {
       switch (j / 10) {
-        case 0: part1_terms<79>(off[k], row[k], rot[k], qlim); break;
-        case 1: part1_terms<69>(off[k], row[k], rot[k], qlim); break;
-        case 2: part1_terms<59>(off[k], row[k], rot[k], qlim); break;
-        case 3: part1_terms<49>(off[k], row[k], rot[k], qlim); break;
-        case 4: part1_terms<39>(off[k], row[k], rot[k], qlim); break;
-        case 5: part1_terms<29>(off[k], row[k], rot[k], qlim); break;
-        case 6: part1_terms<19>(off[k], row[k], rot[k], qlim); break;
-        default: part1_terms<9>(off[k], row[k], rot[k], qlim); break;
+        case 0: part1_terms<79>(off[k], row[k], rot[k]); break;
+        case 1: part1_terms<69>(off[k], row[k], rot[k]); break;
+        case 2: part1_terms<59>(off[k], row[k], rot[k]); break;
+        case 3: part1_terms<49>(off[k], row[k], rot[k]); break;
+        case 4: part1_terms<39>(off[k], row[k], rot[k]); break;
+        case 5: part1_terms<29>(off[k], row[k], rot[k]); break;
+        case 6: part1_terms<19>(off[k], row[k], rot[k]); break;
+        default: part1_terms<9>(off[k], row[k], rot[k]); break;
       }
     }
-    if (qlim >= 64) {
-      // bins j + 64 .. 79 (j <= 15)
+    if (j < kMels - 64) {
+      // bins j + 64 .. 79 (j <= 15): columns 16 j + 1024 .. 1279, then zeros
+      // up to relative column 256 for the terms past bin 79
       __syncthreads();
-      stage_gram_part(g_s, gram, j, c0 + kGCols, kRows - c0 - kGCols, tid);
+      stage_gram_part(g_s, gram, j, c0 + kGCols, kRows - c0 - kGCols, tid, 256);
       __syncthreads();
 #pragma unroll
-      for (int k = 0; k < kScaleTok; ++k) gram_terms<64, 79>(off[k], row[k], rot[k], qlim, kGCols);
+      for (int k = 0; k < kScaleTok; ++k) gram_terms<64, 79>(off[k], row[k], rot[k], kGCols);
     }
 #pragma unroll
     for (int k = 0; k < kScaleTok; ++k) {
@@ -424,7 +459,7 @@ rms_bin_partials_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, in
   const int64_t t = static_cast<int64_t>(blockIdx.x % static_cast<unsigned>(n_chunks)) * kBinTok + tid;
   const bool active = t < n_tokens;
   const int c0 = kLevels * j;
-  stage_gram_part(g_s, gram, j, c0, min(kRows - c0, kGCols), tid);
+  stage_gram_part(g_s, gram, j, c0, min(kRows - c0, kGCols), tid, min(kRows - c0, kGCols));
   uint32_t lw[20];
   load_token_levels(lw, levels, t, active, kAny, n_bins, n_levels);
   __syncthreads();
@@ -456,7 +491,7 @@ rms_bin_partials_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, in
   if (j < kMels - 64) {
     // part 2: bins j + 64 .. 79 (j <= 15; uniform over the workgroup)
     __syncthreads();
-    stage_gram_part(g_s, gram, j, c0 + kGCols, kRows - c0 - kGCols, tid);
+    stage_gram_part(g_s, gram, j, c0 + kGCols, kRows - c0 - kGCols, tid, kRows - c0 - kGCols);
     __syncthreads();
 #pragma unroll
     for (int jp = 64; jp < kMels; ++jp) {

@@ -403,8 +403,12 @@ def test_scale_and_embed_independent_of_batch_size(env, table):
     s_small = torch.empty(n_small, dtype=torch.float32, device="cuda")
     dm.dmel_rms_scale(lv, n_big, gram, 6144, 1e-6, s_big)
     dm.dmel_rms_scale(lv, n_small, gram, 6144, 1e-6, s_small)
+    # the ragged last workgroups of the staged kernel against the direct one
+    s_tail = torch.empty(n_small, dtype=torch.float32, device="cuda")
+    dm.dmel_rms_scale(lv[n_big - n_small:], n_small, gram, 6144, 1e-6, s_tail)
     torch.cuda.synchronize()
     assert torch.equal(s_small, s_big[:n_small])
+    assert torch.equal(s_tail, s_big[n_big - n_small:])
     s = o.embed_sum(lv[:300].cpu().numpy(), _tbits(table)).astype(np.float64)
     want = 1.0 / np.sqrt(np.mean(s * s, axis=1) + 1e-6)
     assert np.max(np.abs(s_big[:300].cpu().numpy() - want) / want) < 1e-6
