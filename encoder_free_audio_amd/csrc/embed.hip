@@ -444,8 +444,9 @@ rms_scale_direct_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, in
 // Small batches with a workspace, bin-parallel: a workgroup takes one bin j
 // and 1024 tokens (one per thread), stages bin j's rows of G part by part and
 // writes each token's (d_j, o_j) to part[j][token]; rms_total_kernel then adds
-// the 80 bins of each token in order.  The lookups run over a static bin
-// index (terms of bins jp <= j are +0.0), so every byte index is static.
+// the 80 bins of each token in order.  The lookups are those of
+// rms_scale_kernel (gram_terms), on the token's level string shifted by j
+// bytes, so every byte index is static.
 constexpr int kBinTok = 1024;
 static_assert(kBinTok == kScaleThreads, "stage_gram_part gives each of 16 rows 64 threads");
 
@@ -459,47 +460,57 @@ rms_bin_partials_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, in
   const int64_t t = static_cast<int64_t>(blockIdx.x % static_cast<unsigned>(n_chunks)) * kBinTok + tid;
   const bool active = t < n_tokens;
   const int c0 = kLevels * j;
-  stage_gram_part(g_s, gram, j, c0, min(kRows - c0, kGCols), tid, min(kRows - c0, kGCols));
+  const int width = min(kRows - c0, kGCols);
   uint32_t lw[20];
   load_token_levels(lw, levels, t, active, kAny, n_bins, n_levels);
+  // The token's levels from bin j on, times 8 (byte offsets of a double), as
+  // a byte string whose byte q is bin j + q (zeros past bin 79): each thread
+  // writes its 80 bytes (+ a zero word) to LDS and reads them back shifted by
+  // j bytes (j is the same for the whole workgroup).  Only the thread itself
+  // reads its words.
+  uint32_t* lv_s = reinterpret_cast<uint32_t*>(g_s) + tid * 21;   // 84 KB of the 131 KB
+#pragma unroll
+  for (int i = 0; i < 20; ++i) lv_s[i] = lw[i] << 3;
+  lv_s[20] = 0u;
+  const int jw = j >> 2, jb = j & 3;
+  uint32_t rot[20];
+  {
+    uint32_t lo = lv_s[jw];
+#pragma unroll
+    for (int i = 0; i < 20; ++i) {
+      // words past the thread's 21 read as zero (the read itself stays inside
+      // the 84 KB region)
+      const uint32_t hi = jw + i + 1 <= 20 ? lv_s[jw + i + 1] : 0u;
+      rot[i] = __builtin_amdgcn_alignbyte(hi, lo, static_cast<uint32_t>(jb));
+      lo = hi;
+    }
+  }
+  __syncthreads();   // every thread has its levels before G overwrites them
+  // zeros for the lookups of up to 9 bins past bin 79 (the QMAX groups below)
+  stage_gram_part(g_s, gram, j, c0, width, tid, min(kGCols, width + 160));
   __syncthreads();
-  uint32_t lj = 0;
-#pragma unroll
-  for (int jp = 0; jp < kMels; ++jp) lj = jp == j ? level_byte(lw, jp) : lj;
-  const double* row = g_s + lj * kGPitch;   // row[16 (jp - j) + L] = G[16 j + lj][16 jp + L]
-  const double diag = row[lj];
-  // part 1: bins jp < j + 64 (inside the staged columns), in order, sixteen
-  // lookups issued together
+  const char* g_b = reinterpret_cast<const char*>(g_s);
+  const uint32_t lj8 = rot[0] & 0xFFu;   // 8 L_j
+  const char* row = g_b + lj8 * kGPitch;
+  const double diag = *reinterpret_cast<const double*>(row + lj8);
   double off = 0.0;
-#pragma unroll
-  for (int jb = 0; jb < kMels; jb += 16) {
-    double v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int jp = jb + i;
-      const bool use = jp > j && jp - j < 64;
-      v[i] = row[use ? kLevels * (jp - j) + static_cast<int>(level_byte(lw, jp)) : 0];
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int jp = jb + i;
-      off += (jp > j && jp - j < 64) ? v[i] : 0.0;
-    }
-    // keep the next group's lookups after this group's adds (registers)
-    asm volatile("" : "+v"(off)::"memory");
+  switch (j / 10) {   // uniform over the workgroup
+    case 0: part1_terms<79>(off, row, rot); break;
+    case 1: part1_terms<69>(off, row, rot); break;
+    case 2: part1_terms<59>(off, row, rot); break;
+    case 3: part1_terms<49>(off, row, rot); break;
+    case 4: part1_terms<39>(off, row, rot); break;
+    case 5: part1_terms<29>(off, row, rot); break;
+    case 6: part1_terms<19>(off, row, rot); break;
+    default: part1_terms<9>(off, row, rot); break;
   }
   if (j < kMels - 64) {
-    // part 2: bins j + 64 .. 79 (j <= 15; uniform over the workgroup)
+    // bins j + 64 .. 79 (j <= 15): columns 16 j + 1024 .. 1279, then zeros up
+    // to relative column 256 for the terms past bin 79
     __syncthreads();
-    stage_gram_part(g_s, gram, j, c0 + kGCols, kRows - c0 - kGCols, tid, kRows - c0 - kGCols);
+    stage_gram_part(g_s, gram, j, c0 + kGCols, kRows - c0 - kGCols, tid, 256);
     __syncthreads();
-#pragma unroll
-    for (int jp = 64; jp < kMels; ++jp) {
-      const bool use = jp - j >= 64;
-      const int idx = use ? kLevels * (jp - j) + static_cast<int>(level_byte(lw, jp)) - kGCols : 0;
-      const double v = row[idx];
-      off += use ? v : 0.0;
-    }
+    gram_terms<64, 79>(off, row, rot, kGCols);
   }
   if (active) part[static_cast<int64_t>(j) * n_tokens + t] = make_double2(diag, off);
 }
