@@ -468,7 +468,8 @@ rms_bin_partials_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, in
   // writes its 80 bytes (+ a zero word) to LDS and reads them back shifted by
   // j bytes (j is the same for the whole workgroup).  Only the thread itself
   // reads its words.
-  uint32_t* lv_s = reinterpret_cast<uint32_t*>(g_s) + tid * 21;   // 84 KB of the 131 KB
+  typedef uint32_t __attribute__((may_alias)) lds_word_t;   // the words share the fp64 buffer
+  lds_word_t* lv_s = reinterpret_cast<lds_word_t*>(g_s) + tid * 21;   // 84 KB of the 131 KB
 #pragma unroll
   for (int i = 0; i < 20; ++i) lv_s[i] = lw[i] << 3;
   lv_s[20] = 0u;
