@@ -27,8 +27,7 @@
 //    and the 16 x 4 accumulators sit in 64 consecutive registers).  Every
 //    row's sum is thus one chain in token order across the whole batch.  The
 //    workgroups that share a tile (the bin groups of one strip) run on the
-//    same XCD and are paced to stay close in the batch, so the L2 serves
-//    their re-reads.
+//    same XCD and start together, so its L2 serves most of their re-reads.
 //  * rms_dot_kernel / rms_ds_kernel - the RMSNorm backward: the forward sum
 //    is recomputed exactly as embed_kernel computes it (embed_core.h); the
 //    first pass forms sum_c w_c dy_c s_c per token and per-workgroup partial
@@ -171,47 +170,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
         : "s"(L), "v"((R).x), "v"((R).y), "v"((R).z), "v"((R).w));                                  \
   } while (0)
 
-// Pacing of the bin groups of one strip.  They read the same gradient tiles,
-// which the XCD's L2 serves to all of them only while they are close to each
-// other in the batch; left alone they drift apart and each re-reads the
-// tiles from HBM.  Every second chunk one thread of a workgroup publishes the
-// chunk it is at and reads where the other groups of its strip are; the reads
-// are used at the next check, so they cost no wait.  Only a group found more
-// than kPaceLead chunks ahead of the slowest waits, by a bounded poll.
-// Pacing affects speed only: results do not depend on it, and a workgroup
-// whose wait runs out of polls (a group not resident yet) stops pacing for the
-// rest of the call, so the wait is bounded.
-constexpr int kPaceLead = 4;
-constexpr int kPacePolls = 20000;
-constexpr int kMaxGroups = (kEmbMaxBins + kBwdBins - 1) / kBwdBins;   // 10
-struct Pace {
-  int seen[kMaxGroups];   // the groups' chunks as read at the previous check
-  bool on;
-};
-__device__ __forceinline__ void keep_pace(Pace& p, int* strip_prog, int grp, int n_groups, int64_t ch) {
-  const int c = static_cast<int>(ch);
-  int slowest = c;
-#pragma unroll
-  for (int q = 0; q < kMaxGroups; ++q)
-    if (q < n_groups) slowest = min(slowest, p.seen[q]);
-  if (c - slowest > kPaceLead) {
-    __hip_atomic_store(strip_prog + grp, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int it = 0;
-    for (; it < kPacePolls; ++it) {
-      slowest = c;
-      for (int q = 0; q < n_groups; ++q)
-        slowest = min(slowest, __hip_atomic_load(strip_prog + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      if (c - slowest <= kPaceLead) break;
-      __builtin_amdgcn_s_sleep(4);
-    }
-    if (it == kPacePolls) p.on = false;
-  }
-  __hip_atomic_store(strip_prog + grp, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-  for (int q = 0; q < kMaxGroups; ++q)
-    if (q < n_groups) p.seen[q] = __hip_atomic_load(strip_prog + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // One chunk of the scatter: `cur` holds chunk ch (tile + levels), the copy of
 // chunk ch + 1 goes to `nxt`.  The two buffers are distinct LDS arrays so
 // that the compiler can see that the reads of one do not wait for the copies
@@ -271,7 +229,7 @@ template <bool kBf16>
 __global__ void __launch_bounds__(kBwdThreads)
 scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_levels, int d_model,
                const uint8_t* __restrict__ lvt, int64_t t_pad, const float* __restrict__ neg_zero, int64_t n_chunks,
-               int n_groups, int n_strips, int per_xcd, int* __restrict__ prog, float* __restrict__ out,
+               int n_groups, int n_strips, int per_xcd, float* __restrict__ out,
                int accumulate) {
   __shared__ __attribute__((aligned(1024))) char tile_a[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char tile_b[kTileBytes];
@@ -285,11 +243,6 @@ scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_l
   const int grp = local % n_groups;
   const int strip = (bid & 7) * per_xcd + local / n_groups;
   if (local / n_groups >= per_xcd || strip >= n_strips) return;  // before any barrier: the whole workgroup leaves
-  int* my_prog = prog + strip * n_groups;
-  Pace pace;
-  pace.on = n_groups > 1;
-#pragma unroll
-  for (int q = 0; q < kMaxGroups; ++q) pace.seen[q] = 0;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -310,7 +263,6 @@ scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_l
   }
   levels_dma(lv_a, lvt, t_pad, bin0, n_bins, 0, wave, lane);
   for (int64_t ch = 0; ch < n_chunks; ch += 2) {
-    if (pace.on && tid == 0) keep_pace(pace, my_prog, grp, n_groups, ch);
     scatter_chunk<kBf16>(tile_a, lv_a, tile_b, lv_b, ch, g, n_tokens, n_bins, d_model, lvt, t_pad, neg_zero,
                          n_chunks, c_strip, bin0, bin_ok, wave, lane, tid, rb, ax, ay, az, aw);
     if (ch + 1 < n_chunks) {
@@ -590,21 +542,17 @@ int strips_per_group(int64_t tblocks, int n_strips) {
 }  // namespace
 
 size_t bwd_layout(int64_t n_tokens, int n_bins, int d_model, size_t* offs) {
-  // levels by bin [n_bins][t_pad] (t_pad = whole chunks), the row of -0.0,
-  // the pacing counters of every (strip, bin group); nothing for an empty batch
-  if (offs) offs[0] = offs[1] = 0;
+  // levels by bin [n_bins][t_pad] (t_pad = whole chunks), then the row of
+  // -0.0; nothing for an empty batch
+  (void)d_model;
+  if (offs) offs[0] = 0;
   if (n_tokens <= 0) return 0;
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
   const size_t t_pad = static_cast<size_t>((n_tokens + kChunk - 1) / kChunk) * kChunk;
   const size_t b_lvt = up(static_cast<size_t>(n_bins) * t_pad);
   const size_t b_nz = up(kBwdCols * sizeof(float));
-  const size_t n_groups = static_cast<size_t>((n_bins + kBwdBins - 1) / kBwdBins);
-  const size_t n_strips = static_cast<size_t>((d_model + kBwdCols - 1) / kBwdCols);
-  if (offs) {
-    offs[0] = b_lvt;
-    offs[1] = b_lvt + b_nz;
-  }
-  return b_lvt + b_nz + up(n_groups * n_strips * sizeof(int));
+  if (offs) offs[0] = b_lvt;
+  return b_lvt + b_nz;
 }
 
 hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels, const void* dsum,
@@ -615,11 +563,10 @@ hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_
     if (accumulate) return hipSuccess;
     return zero_fill(dtable, rows * d_model, stream);
   }
-  size_t offs[2];
+  size_t offs[1];
   bwd_layout(n_tokens, n_bins, d_model, offs);
   auto* lvt = static_cast<uint8_t*>(workspace);
   auto* neg_zero = reinterpret_cast<float*>(static_cast<char*>(workspace) + offs[0]);
-  auto* prog = reinterpret_cast<int*>(static_cast<char*>(workspace) + offs[1]);
   const int64_t n_chunks = (n_tokens + kChunk - 1) / kChunk;
   const int64_t t_pad = n_chunks * kChunk;
   if (n_chunks > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -632,18 +579,14 @@ hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_
   const int per_xcd = (n_strips + 7) / 8;
   const int64_t blocks = static_cast<int64_t>(per_xcd) * 8 * n_groups;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  // pacing counters start at 0 (a fill kernel, so that the calls can be
-  // captured in a graph)
-  e = zero_fill(reinterpret_cast<float*>(prog), static_cast<int64_t>(n_groups) * n_strips, stream);
-  if (e != hipSuccess) return e;
   if (dsum_bf16) {
     hipLaunchKernelGGL(scatter_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kBwdThreads), 0, stream, dsum,
                        n_tokens, n_bins, n_levels, d_model, lvt, t_pad, neg_zero, n_chunks, n_groups, n_strips,
-                       per_xcd, prog, dtable, accumulate ? 1 : 0);
+                       per_xcd, dtable, accumulate ? 1 : 0);
   } else {
     hipLaunchKernelGGL(scatter_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kBwdThreads), 0, stream,
                        dsum, n_tokens, n_bins, n_levels, d_model, lvt, t_pad, neg_zero, n_chunks, n_groups, n_strips,
-                       per_xcd, prog, dtable, accumulate ? 1 : 0);
+                       per_xcd, dtable, accumulate ? 1 : 0);
   }
   return hipGetLastError();
 }
