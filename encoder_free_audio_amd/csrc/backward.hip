@@ -308,32 +308,41 @@ hipError_t zero_fill(float* p, int64_t n, hipStream_t stream) {
 // RMSNorm backward.  Workgroups as embed_kernel: 1024 tokens (one per lane)
 // and a group of 16-column strips.
 // ---------------------------------------------------------------------------
+// A strip's 16 upstream gradients of token t, read raw at the start of the
+// strip (bf16: two 16-byte pieces, fp32: four) and widened in its epilogue,
+// so the read is in flight during the strip's adds.
 template <bool kDyBf16>
-__device__ __forceinline__ void load_dy(float (&gr)[kStrip], const void* dy, int64_t t, int d_model, int col0,
-                                        bool active) {
+using DyRaw = uint4[kDyBf16 ? 2 : 4];
+template <bool kDyBf16>
+__device__ __forceinline__ void load_dy_raw(DyRaw<kDyBf16>& raw, const void* dy, int64_t t, int d_model, int col0,
+                                            bool active) {
+  constexpr int n = kDyBf16 ? 2 : 4;
   if (!active) {
 #pragma unroll
-    for (int c = 0; c < kStrip; ++c) gr[c] = 0.0f;
+    for (int i = 0; i < n; ++i) raw[i] = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
+  const uint4* p = kDyBf16 ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(dy) + t * d_model + col0)
+                           : reinterpret_cast<const uint4*>(static_cast<const float*>(dy) + t * d_model + col0);
+#pragma unroll
+  for (int i = 0; i < n; ++i) raw[i] = p[i];
+}
+template <bool kDyBf16>
+__device__ __forceinline__ void unpack_dy(float (&gr)[kStrip], const DyRaw<kDyBf16>& raw) {
   if (kDyBf16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(dy) + t * d_model + col0);
-    const uint4 a = p[0], b = p[1];
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       gr[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
       gr[2 * i + 1] = bf16_to_f32(w[i] >> 16);
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(dy) + t * d_model + col0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 v = p[q];
-      gr[4 * q] = v.x;
-      gr[4 * q + 1] = v.y;
-      gr[4 * q + 2] = v.z;
-      gr[4 * q + 3] = v.w;
+      gr[4 * q] = __uint_as_float(raw[q].x);
+      gr[4 * q + 1] = __uint_as_float(raw[q].y);
+      gr[4 * q + 2] = __uint_as_float(raw[q].z);
+      gr[4 * q + 3] = __uint_as_float(raw[q].w);
     }
   }
 }
@@ -391,7 +400,9 @@ rms_dot_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins,
   token_offsets<kAny>(offs, levels, t, active, n_bins, n_levels);
   const float r = active ? rms_scale[t] : 0.0f;
   float dot = 0.0f;
+  DyRaw<kDyBf16> dyr;
   sum_strips<kAny>(tab, table, d_model, s_first, s_end, tid, n_bins, n_levels, offs,
+                   [&](int col0) { load_dy_raw<kDyBf16>(dyr, dy, t, d_model, col0, active); },
                    [&](int col0, float (&acc)[kStrip]) {
                      if (s_out != nullptr && active) {
                        float4* so = reinterpret_cast<float4*>(s_out + t * d_model + col0);
@@ -401,7 +412,7 @@ rms_dot_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins,
                        so[3] = make_float4(acc[12], acc[13], acc[14], acc[15]);
                      }
                      float gr[kStrip];
-                     load_dy<kDyBf16>(gr, dy, t, d_model, col0, active);
+                     unpack_dy<kDyBf16>(gr, dyr);
                      float q[kStrip];
 #pragma unroll
                      for (int c = 0; c < kStrip; ++c) {
@@ -446,11 +457,13 @@ rms_ds_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, 
     for (int g = 0; g < n_groups; ++g) dot += dot_part[t * n_groups + g];
     coef = ((r * r) * r) / static_cast<float>(d_model) * dot;
   }
+  DyRaw<kDyBf16> dyr;
   sum_strips<kAny>(tab, table, d_model, s_first, s_end, tid, n_bins, n_levels, offs,
+                   [&](int col0) { load_dy_raw<kDyBf16>(dyr, dy, t, d_model, col0, active); },
                    [&](int col0, float (&acc)[kStrip]) {
                      if (!active) return;
                      float gr[kStrip];
-                     load_dy<kDyBf16>(gr, dy, t, d_model, col0, true);
+                     unpack_dy<kDyBf16>(gr, dyr);
                      float o[kStrip];
 #pragma unroll
                      for (int c = 0; c < kStrip; ++c) o[c] = fmaf(-coef, acc[c], r * (rms_weight[col0 + c] * gr[c]));

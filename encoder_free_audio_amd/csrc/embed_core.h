@@ -200,9 +200,12 @@ __device__ __forceinline__ void token_offsets(uint32_t (&offs)[40], const uint8_
 // the staging and bin order of embed_kernel: epi(col0, acc) receives the exact
 // fp32 sums of columns col0 .. col0 + 15 of this thread's token.  Contains
 // barriers: every thread of the workgroup calls it; epi may use barriers too.
-template <bool kAny, typename Epi>
+// pre(col0) runs at the start of each strip, before its adds (for reads the
+// epilogue of the strip will use).
+template <bool kAny, typename Pre, typename Epi>
 __device__ __forceinline__ void sum_strips(float* tab, const uint16_t* table, int d_model, int s_first, int s_end,
-                                           int tid, int n_bins, int n_levels, uint32_t (&offs)[40], Epi&& epi) {
+                                           int tid, int n_bins, int n_levels, uint32_t (&offs)[40], Pre&& pre,
+                                           Epi&& epi) {
   uint4 st[kStagePer];
   stage_load<kAny>(st, table, d_model, s_first * kStrip, 0, tid, n_bins, n_levels);
   stage_store(tab, st, 0, tid);
@@ -212,6 +215,7 @@ __device__ __forceinline__ void sum_strips(float* tab, const uint16_t* table, in
 #pragma unroll
     for (int i = 0; i < 40; ++i) asm volatile("" : "+v"(offs[i]));
     stage_load<kAny>(st, table, d_model, col0, 1, tid, n_bins, n_levels);
+    pre(col0);
     float acc[kStrip];
     add_bins<0, kMels / 2>(acc, tab, offs);
     stage_store(tab, st, 1, tid);
