@@ -147,47 +147,110 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, i
 }
 
 // ---------------------------------------------------------------------------
-// Gram matrix G = E E^T, fp64 (accumulation of exact bf16 products over the
-// columns, stored as fp64).  One workgroup per 16 x 16 block (bin j rows x
-// bin j' rows), j <= j'.  G is indexed in the 80 x 16 row space (16 * bin +
-// level) for every layout; rows outside the n_bins x n_levels layout are 0.
+// Gram matrix G = E E^T in fp64.  A product of two bf16 entries is exact in
+// fp64; the products are summed over the columns in fp64 on the matrix cores
+// (v_mfma_f64_16x16x4_f64).  G is indexed in the 80 x 16 row space (16 * bin
+// + level) for every layout; rows outside the n_bins x n_levels layout are 0.
+// One workgroup per 64 x 64 block of the upper triangle (20 x 20 blocks of
+// 4 bins each); each wavefront owns a 32 x 32 quarter as 2 x 2 MFMA tiles.
+// The columns pass through LDS in chunks of 64, converted to fp64 and stored
+// column by column; the next chunk is read into registers while the current
+// one is multiplied.
 // ---------------------------------------------------------------------------
-constexpr int kGramChunk = 256;
+constexpr int kGTile = 64;
+constexpr int kGTiles = kRows / kGTile;  // 20
+constexpr int kGK = 64;                  // columns per chunk
+constexpr int kGPitchD = kGTile + 2;     // doubles per staged column
+
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+// A block's 64 rows x 64 columns as 512 pieces of 8 bf16: piece p = tid +
+// 256 i is row p / 8, columns c0 + 8 (p % 8) .. + 7 (d_model is a multiple
+// of 16, so a piece lies wholly inside or wholly past the last column).
+__device__ __forceinline__ void gram_fetch(uint4 (&v)[2], const uint16_t* __restrict__ table, int d_model,
+                                           int n_bins, int n_levels, int blk, int c0, int tid) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = tid + 256 * i, row = p >> 3, col = c0 + 8 * (p & 7);
+    const int r = kGTile * blk + row, bin = r >> 4, lev = r & 15;
+    v[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (bin < n_bins && lev < n_levels && col < d_model)
+      v[i] = *reinterpret_cast<const uint4*>(table + static_cast<int64_t>(n_levels * bin + lev) * d_model + col);
+  }
+}
+
+__device__ __forceinline__ void gram_stage(double* s, const uint4 (&v)[2], int tid) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = tid + 256 * i, row = p >> 3, c = 8 * (p & 7);
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s[(c + 2 * q) * kGPitchD + row] = static_cast<double>(bf16_to_f32(w[q] & 0xFFFFu));
+      s[(c + 2 * q + 1) * kGPitchD + row] = static_cast<double>(bf16_to_f32(w[q] >> 16));
+    }
+  }
+}
 
 __global__ void __launch_bounds__(256)
 gram_kernel(const uint16_t* __restrict__ table, int n_bins, int n_levels, int d_model, double* __restrict__ gram) {
-  __shared__ float a_s[16][kGramChunk + 1];
-  __shared__ float b_s[16][kGramChunk + 1];
-  // blockIdx.x enumerates the upper-triangle pairs (j, j')
+  __shared__ double a_s[kGK * kGPitchD];
+  __shared__ double b_s[kGK * kGPitchD];
+  // blockIdx.x enumerates the upper-triangle block pairs (J, J')
   int idx = blockIdx.x;
-  int j = 0;
-  while (idx >= kMels - j) {
-    idx -= kMels - j;
-    ++j;
+  int bj = 0;
+  while (idx >= kGTiles - bj) {
+    idx -= kGTiles - bj;
+    ++bj;
   }
-  const int jp = j + idx;
-  const int tid = threadIdx.x;
-  const int ri = tid >> 4, rj = tid & 15;
-  double acc = 0.0;
-  for (int c0 = 0; c0 < d_model; c0 += kGramChunk) {
-    const int width = min(kGramChunk, d_model - c0);
+  const int bjp = bj + idx;
+  const bool diag = bj == bjp;
+  const double* bsrc = diag ? a_s : b_s;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wr = (wv >> 1) * 32, wc = (wv & 1) * 32;
+  f64x4_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  uint4 va[2], vb[2];
+  gram_fetch(va, table, d_model, n_bins, n_levels, bj, 0, tid);
+  if (!diag) gram_fetch(vb, table, d_model, n_bins, n_levels, bjp, 0, tid);
+  for (int c0 = 0; c0 < d_model; c0 += kGK) {
     __syncthreads();
-    for (int i = tid; i < 16 * kGramChunk; i += 256) {
-      const int r = i / kGramChunk, c = i - r * kGramChunk;
-      float va = 0.0f, vb = 0.0f;
-      if (c < width && r < n_levels) {
-        if (j < n_bins) va = bf16_to_f32(table[static_cast<int64_t>(n_levels * j + r) * d_model + c0 + c]);
-        if (jp < n_bins) vb = bf16_to_f32(table[static_cast<int64_t>(n_levels * jp + r) * d_model + c0 + c]);
-      }
-      a_s[r][c] = va;
-      b_s[r][c] = vb;
+    gram_stage(a_s, va, tid);
+    if (!diag) gram_stage(b_s, vb, tid);
+    __syncthreads();
+    if (c0 + kGK < d_model) {
+      gram_fetch(va, table, d_model, n_bins, n_levels, bj, c0 + kGK, tid);
+      if (!diag) gram_fetch(vb, table, d_model, n_bins, n_levels, bjp, c0 + kGK, tid);
     }
-    __syncthreads();
-    for (int c = 0; c < width; ++c) acc = fma(static_cast<double>(a_s[ri][c]), static_cast<double>(b_s[rj][c]), acc);
+    // MFMA operands: lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]
+#pragma unroll 4
+    for (int k = 0; k < kGK; k += 4) {
+      const int c = k + (lane >> 4);
+      const double a0 = a_s[c * kGPitchD + wr + (lane & 15)];
+      const double a1 = a_s[c * kGPitchD + wr + 16 + (lane & 15)];
+      const double b0 = bsrc[c * kGPitchD + wc + (lane & 15)];
+      const double b1 = bsrc[c * kGPitchD + wc + 16 + (lane & 15)];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+    }
   }
-  const int r = kLevels * j + ri, rp = kLevels * jp + rj;
-  gram[static_cast<int64_t>(r) * kRows + rp] = acc;
-  gram[static_cast<int64_t>(rp) * kRows + r] = acc;
+  // result: lane l, element e holds row l / 16 + 4 e, column l % 16 of a tile
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = kGTile * bj + wr + 16 * a + (lane >> 4) + 4 * e;
+        const int cc = kGTile * bjp + wc + 16 * b + (lane & 15);
+        gram[static_cast<int64_t>(r) * kRows + cc] = acc[a][b][e];
+        if (!diag) gram[static_cast<int64_t>(cc) * kRows + r] = acc[a][b][e];
+      }
 }
 
 // ---------------------------------------------------------------------------
@@ -233,7 +296,6 @@ __device__ __forceinline__ void load_token_levels(uint32_t (&lw)[20], const uint
 // 0 .. 15 take two parts.  1024 threads: 64 per row, 16-byte reads.
 constexpr int kGCols = 1024;
 constexpr int kGPitch = kGCols + 1;           // doubles per staged row (odd: the 16 rows start in different banks)
-constexpr int kGStageBytes = 16 * kGPitch * 8;  // 131,200
 constexpr int kScaleThreads = 1024;
 // Columns width .. zero_end - 1 of each staged row (both even) are set to
 // +0.0, for lookups that run past the end of the upper triangle.
@@ -600,7 +662,7 @@ hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, int n_bins, int
 
 hipError_t launch_gram(const uint16_t* table, int n_bins, int n_levels, int d_model, double* gram,
                        hipStream_t stream) {
-  const int pairs = kMels * (kMels + 1) / 2;
+  const int pairs = kGTiles * (kGTiles + 1) / 2;
   hipLaunchKernelGGL(gram_kernel, dim3(pairs), dim3(256), 0, stream, table, n_bins, n_levels, d_model, gram);
   return hipGetLastError();
 }
