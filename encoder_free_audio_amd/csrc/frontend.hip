@@ -13,10 +13,10 @@
 // spectrum, 80 HTK triangles over 0..8000 Hz, ln(max(M, 1e-10)), and
 // level = min(15, floor((clamp(l, -7, 2) + 7) * 16 / 9)) decided exactly.
 //
-// Work decomposition (one workgroup = 256 threads = 8 frames, fp32, LDS):
+// Work decomposition (one workgroup = 512 threads = 16 frames, fp32, LDS):
 //  0. a frame's 32 threads sit in one wavefront and find its clip and first
 //     sample themselves (steps 1-3 touch only the frame's own LDS buffer, so
-//     the four wavefronts run them without workgroup barriers);
+//     the eight wavefronts run them without workgroup barriers);
 //  1. the frame's 1600 samples are read as 800 complex values z[m] = x[2m] +
 //     i x[2m+1] straight into registers (from the clip's carry or zeros, then
 //     the audio, for a clip's first frame), while the tables read per lane
@@ -33,11 +33,12 @@
 //     the exchanges (A to B, B to the split) go through the frame's LDS
 //     buffer of rows padded to 33, real parts first, then imaginary parts:
 //     half the buffer of complex exchanges, which leaves room in LDS for the
-//     tables at three workgroups per CU;
+//     tables at two workgroups (16 wavefronts) per CU;
 //  3. split Z into the 801-bin spectrum of the real frame and take |X|^2;
-//  4. filters (after a barrier: lanes work across the block's frames): a
-//     fixed schedule built on the host (FrontTables::mel_w) gives each of the
-//     four wavefronts a balanced share of the filters; a lane computes one
+//  4. filters (after a barrier: lanes work across 8 of the block's frames):
+//     a fixed schedule built on the host (FrontTables::mel_w) gives each of
+//     four wavefronts a balanced share of the filters, once for frames 0..7
+//     and once for frames 8..15; a lane computes one
 //     filter of one frame as a weighted sum over the filter's contiguous
 //     bins (weights from the schedule in LDS, 8 bins per step), then log,
 //     clamp and the exact quantizer.
@@ -46,18 +47,20 @@
 namespace dmel {
 namespace {
 
-constexpr int kFramesPerBlock = 8;
-constexpr int kThreads = 256;
+// Two halves of 8 frames; each half runs the four-round filter schedule.
+constexpr int kFramesPerBlock = 16;
+constexpr int kThreads = 512;
 // Floats per frame in the exchange buffer: 825 used (25 rows x 33); the
-// stride is 24 mod 64 so that the two frames of a wavefront overlap in few
-// LDS banks during the FFT exchanges, and the filter step's reads (8 frames x
-// 8 slots whose bins differ mod 8) fall in 64 distinct banks.
-constexpr int kSlots = 856;
+// stride is 8 mod 64, so the filter step's reads (a wavefront's 8 frames x 8
+// slots whose bins differ mod 8) fall in 64 distinct banks, and the buffers
+// of 16 frames plus the tables fit two workgroups in a CU's LDS.
+constexpr int kSlots = 840;
 constexpr int kXchg = kFramesPerBlock * kSlots;  // exchange floats of a workgroup
 // the filter step's powers: bin k at float kPOff + k of the frame's buffer,
 // bins [-8, 0) and [801, kMelReadEnd) zero
 constexpr int kPOff = 8;
-static_assert(kSlots % 64 == 24, "bank spread of the exchange buffers");
+static_assert(kSlots % 64 == 8, "bank spread of the filter step's reads");
+static_assert(kSlots >= 25 * 33, "the FFT exchanges fit in the frame's buffer");
 static_assert(kPOff + kMelReadEnd <= kSlots, "the filter step reads inside the frame's buffer");
 static_assert(kPOff + kMelReadEnd - kBins <= 32, "the zero pads are written by one lane each");
 
@@ -126,7 +129,7 @@ __device__ __forceinline__ void dft8(float2 (&v)[8]) {
 // and read only by its own 32 threads, which lie in one wavefront, and a
 // wavefront's LDS operations complete in issue order; so between the FFT
 // passes it is enough to keep the compiler from moving memory operations
-// across this point, and the four wavefronts of a workgroup run those passes
+// across this point, and the wavefronts of a workgroup run those passes
 // without waiting for each other.
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -183,15 +186,18 @@ __device__ __forceinline__ int quantize(float l, const FrontTables& t, const flo
 // kMelLds: the filter schedule comes with the table image into LDS (it has
 // at most kMelLdsChunks chunks); otherwise its weights are read from global
 // memory.
+// Four wavefronts per SIMD (two workgroups per CU) need at most 128 VGPRs;
+// the compiler then spills a few values (12 bytes per lane) to scratch,
+// outside the loops.
 template <bool kMelLds>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_samples_total,
                 const int64_t* __restrict__ sample_off, const int64_t* __restrict__ frame_off,
                 int n_clips, int64_t n_frames, double clip_rate, const float* __restrict__ carry,
                 float* __restrict__ logmel, uint8_t* __restrict__ levels) {
-  // LDS: the frames' exchange buffers (8 x 856 floats), then the table image
-  // (window, twa, tw1600, quantizer edges, with kMelLds the schedule): 52.3 KB
-  // (41.0 KB without the schedule), three workgroups per CU.
+  // LDS: the frames' exchange buffers (16 x 840 floats), then the table
+  // image (window, twa, tw1600, quantizer edges, with kMelLds the schedule):
+  // 78.6 KB (67.4 KB without the schedule), two workgroups per CU.
   constexpr int kImg = kMelLds ? kImgFull : kImgFloats;
   constexpr int kImgPieces = (kImg + 255) / 256;  // 1 KB pieces (the last one partial)
   static_assert(kImg % 4 == 0, "16-byte copies");
@@ -427,16 +433,17 @@ frontend_kernel(FrontTables tabs, const float* __restrict__ audio, int64_t n_sam
     else if (lane < kPOff + kMelReadEnd - kBins) zf[kBins + lane] = 0.0f;
   }
   // ---- 4. filters, log, clamp, quantize ----------------------------------
-  // Wavefront r runs round r of the schedule (FrontTables::mel_w): lane
-  // 8 * slot + ff computes, for frame ff and each side of the round, the
+  // Wavefronts r and 4 + r run round r of the schedule (FrontTables::mel_w)
+  // for frames 0..7 and 8..15: lane 8 * slot + f8 computes, for frame
+  // ff = 8 * (wave / 4) + f8 and each side of the round, the
   // filter of `slot` as the sum over the side's 8-bin chunks of the chunk's
   // weights (the 8 lanes of a slot share each read) times the frame's powers,
   // then writes its log-mel value and level.
-  __syncthreads();  // the powers of all 8 frames are in LDS
+  __syncthreads();  // the powers of all 16 frames are in LDS
   {
-    const int r = __builtin_amdgcn_readfirstlane(wave);
+    const int r = __builtin_amdgcn_readfirstlane(wave & 3);
     const int slot = (tid >> 3) & 7;
-    const int ff = tid & 7;
+    const int ff = 8 * (wave >> 2) + (tid & 7);
     const int* rd = tabs.mel_round + 8 * r;
     const int base = rd[0], sides = rd[2];
     const float4* mw = kMelLds ? reinterpret_cast<const float4*>(img + kImgMelW) : tabs.mel_w;

@@ -59,8 +59,8 @@ struct FrontTables {
   int mel_in_lds;
   // Filter step as a fixed schedule (tables.cpp).  Filter j is one weighted
   // sum over its contiguous bins [seg_start[j], seg_start[j + 2]), taken in
-  // chunks of 8 bins.  The four wavefronts of a workgroup run one round each
-  // for the workgroup's 8 frames (lane = 8 * slot + frame).  Round r is the
+  // chunks of 8 bins.  Four wavefronts of a workgroup run one round each for
+  // 8 of its frames (lane = 8 * slot + frame).  Round r is the
   // chunk list [base, base + chunks) with base, chunks, sides = mel_round[8r],
   // [8r + 1], [8r + 2]; side h < sides is the chunk range [start_h,
   // start_{h+1}) of the round (start_h = mel_round[8r + 3 + h], relative to

@@ -288,17 +288,18 @@ def test_streaming_equals_batch(env, table):
 
 def test_frontend_position_invariance(env):
     """A frame's log-mel bits do not depend on where it falls in the kernel's
-    8-frame workgroups (its 32-thread group, its wavefront, the filter slots
-    that read it): the clip is run alone and behind a first clip of k = 1..9
-    frames, which moves every frame to another position.  An LDS race between
-    the frames or wavefronts of a workgroup would show up as a difference."""
+    16-frame workgroups (its 32-thread group, its wavefront, its 8-frame half
+    and the filter slots that read it): the clip is run alone and behind a
+    first clip of k = 1..17 frames, which moves every frame through every
+    position.  An LDS race between the frames or wavefronts of a workgroup
+    would show up as a difference."""
     dm, ctx = env
     x = synth.bursts_clips(seed=21, n_clips=1, n_samples=800 * 61).reshape(-1).cuda()
     so, fo, T = P.offsets([x.numel()])
     ref = torch.empty((T, 80), dtype=torch.float32, device="cuda")
     dm.dmel_frames(ctx, x, x.numel(), so, fo, 1, T, None, ref)
-    pre = synth.bursts_clips(seed=22, n_clips=1, n_samples=800 * 9).reshape(-1).cuda()
-    for k in range(1, 10):
+    pre = synth.bursts_clips(seed=22, n_clips=1, n_samples=800 * 17).reshape(-1).cuda()
+    for k in range(1, 18):
         a = torch.cat([pre[: 800 * k], x])
         so2, fo2, T2 = P.offsets([800 * k, x.numel()])
         lm = torch.empty((T2, 80), dtype=torch.float32, device="cuda")
