@@ -34,6 +34,26 @@
 namespace dmel {
 namespace {
 
+// The (strip group, token block) of this workgroup, for a grid of
+// n_groups x token blocks.  Workgroup b runs on XCD b % 8.  With a multiple
+// of 8 strip groups, XCD x takes group x for every token block, then group
+// x + 8, and so on, so its L2 holds one group's table slices at a time (655 KB
+// for 16 strips) while the output streams through it; otherwise consecutive
+// workgroups take the groups of one token block.  (The backward's recompute
+// passes keep the second order: they stream dy per token block, and measured
+// slower with the first.)
+__device__ __forceinline__ void block_tile(int n_groups, int& grp, int64_t& tb) {
+  if (n_groups % 8 == 0) {
+    const unsigned x = blockIdx.x & 7u, r = blockIdx.x >> 3;
+    const unsigned tblocks = gridDim.x / static_cast<unsigned>(n_groups);
+    grp = static_cast<int>(8u * (r / tblocks) + x);
+    tb = r % tblocks;
+  } else {
+    grp = static_cast<int>(blockIdx.x % static_cast<unsigned>(n_groups));
+    tb = blockIdx.x / static_cast<unsigned>(n_groups);
+  }
+}
+
 // kAny = false: the released layout (levels [n, 80], 16-byte aligned, table
 // [1280, d]); true: any n_bins <= 80, n_levels <= 16 (see the top of the file).
 template <bool kAny>
@@ -46,8 +66,9 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, i
   float* tab = reinterpret_cast<float*>(tab4);
 
   const int tid = threadIdx.x;
-  const int grp = static_cast<int>(blockIdx.x % static_cast<unsigned>(n_groups));
-  const int64_t tb = blockIdx.x / static_cast<unsigned>(n_groups);
+  int grp;
+  int64_t tb;
+  block_tile(n_groups, grp, tb);
   const int64_t t = tb * kEmbThreads + tid;
   const bool active = t < n_tokens;
   const int s_first = grp * strips_per_group;
