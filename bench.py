@@ -264,13 +264,18 @@ def main():
 
 
 def bench_backward(args):
-    """Backward of the front end's trainable parts on the 64 x 20 min batch:
-    the RMSNorm backward (dmel_rms_backward with the larger workspace: a first
-    pass that recomputes the forward sum and keeps it, a second that streams
-    it) and the table gradient (dmel_embed_backward: level sort, then the
-    token-order scatter), from a bf16 upstream gradient
-    ~ N(0, 1e-3).  One step = both calls; the levels come from the front end
-    before the timed region."""
+    """Backward of the front end's trainable parts on the 64 x 20 min batch,
+    from a bf16 upstream gradient ~ N(0, 1e-3); the levels come from the front
+    end before the timed region.  Two RMSNorm backwards are timed, then the
+    table gradient (dmel_embed_backward, the token-order scatter):
+    * from the sums the forward kept (dmel_embed_train writes them, then
+      dmel_rms_backward_sums streams them): the training path, and the
+      step the JSON line reports (rms from sums + table gradient);
+    * dmel_rms_backward with the larger workspace (a first pass that
+      recomputes the forward sum and keeps it, a second that streams it), for
+      callers that do not keep the sums.
+    The forward's extra cost of keeping the sums is timed as well
+    (dmel_embed_train against dmel_embed, RMSNorm on, bf16 out)."""
     dev = "cuda"
     n_clips = args.clips
     clip_len = int(round(args.minutes * 60 * 16000))
@@ -292,39 +297,48 @@ def bench_backward(args):
     ds = torch.empty((T, d), dtype=torch.float32, device=dev)
     dw = torch.empty(d, dtype=torch.float32, device=dev)
     dt = torch.empty((1280, d), dtype=torch.float32, device=dev)
+    sums = torch.empty((T, d), dtype=torch.float32, device=dev)
+    y = torch.empty((T, d), dtype=torch.int16, device=dev)
     wb1 = dm.dmel_rms_backward_stored_workspace_bytes(T, d)   # keeps the sums between the two passes
     wb2 = dm.dmel_embed_backward_workspace_bytes(T, 80, 16, d)
-    ws = torch.empty(max(wb1, wb2), dtype=torch.uint8, device=dev)
+    wb3 = dm.dmel_rms_backward_sums_workspace_bytes(T, d)
+    ws = torch.empty(max(wb1, wb2, wb3), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        dm.dmel_rms_backward(lv, T, 80, 16, table, d, w, scale, dy, dm.DMEL_BF16, ds, dw, 0, ws, wb1, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        dm.dmel_embed_backward(lv, T, 80, 16, ds, dm.DMEL_F32, d, dt, 0, ws, wb2, stream)
-        if ev is not None:
-            ev[2].record(stream)
+    def timed(calls, steps, warmup):
+        """Mean event time of each call over `steps` rounds, and the wall time per round."""
+        for _ in range(warmup):
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for k in range(steps):
+            events[k][0].record(stream)
+            for i, c in enumerate(calls):
+                c()
+                events[k][i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(calls))] for e in events]).mean(axis=0)
+        return per, wall
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t_start = time.perf_counter()
-    for k in range(args.steps):
-        step(events[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(2)] for e in events])
-    k_rms, k_tab = per.mean(axis=0)
-    ms_step = wall * 1e3 / args.steps
+    fwd = lambda: dm.dmel_embed(lv, T, table, d, w, scale, y, dm.DMEL_BF16, d, None, stream)
+    fwd_sums = lambda: dm.dmel_embed_train(lv, T, table, d, w, scale, y, dm.DMEL_BF16, d, None, sums, stream)
+    rms_sums = lambda: dm.dmel_rms_backward_sums(sums, T, d, w, scale, dy, dm.DMEL_BF16, ds, dw, 0, ws, wb3, stream)
+    rms_rec = lambda: dm.dmel_rms_backward(lv, T, 80, 16, table, d, w, scale, dy, dm.DMEL_BF16, ds, dw, 0, ws, wb1,
+                                           stream)
+    tab = lambda: dm.dmel_embed_backward(lv, T, 80, 16, ds, dm.DMEL_F32, d, dt, 0, ws, wb2, stream)
+    (k_fwd, k_fwd_sums), _ = timed([fwd, fwd_sums], 3, 1)   # leaves the sums in place
+    (k_rms_rec,), _ = timed([rms_rec], max(2, args.steps // 2), 1)
+    (k_rms, k_tab), ms_step = timed([rms_sums, tab], args.steps, args.warmup)
     # the table gradient adds every token's gradient into one row per bin:
     # 80 x 6144 fp32 adds per token
     adds = 80 * d * T
     achieved = adds / (k_tab * 1e-3) / 1e12
-    print(f"[bench] backward per step: rms {k_rms:.3f} ms, table gradient {k_tab:.3f} ms; wall {ms_step:.3f} ms",
-          file=sys.stderr, flush=True)
+    print(f"[bench] backward per step: rms from kept sums {k_rms:.3f} ms, table gradient {k_tab:.3f} ms; wall "
+          f"{ms_step:.3f} ms; rms recomputing the sums {k_rms_rec:.3f} ms; forward embed {k_fwd:.3f} ms, "
+          f"keeping the sums {k_fwd_sums:.3f} ms", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_backward(lv, table, dy, d)
@@ -343,9 +357,13 @@ def bench_backward(args):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"dMel backward: {n_clips} clips x {args.minutes:g} min ({T} tokens), table "
-                               f"1280x6144, bf16 upstream gradient, RMSNorm backward + token-order table gradient",
+                               f"1280x6144, bf16 upstream gradient, RMSNorm backward from the sums the forward "
+                               f"kept (dmel_embed_train: {k_fwd_sums - k_fwd:.2f} ms more than dmel_embed) + "
+                               f"token-order table gradient",
                    "global_batch": n_clips, "seq_len": T // n_clips, "parallelism": "single GPU"},
-        "kernel_ms": {"rms_backward": float(k_rms), "table_gradient": float(k_tab)},
+        "kernel_ms": {"rms_backward_from_sums": float(k_rms), "table_gradient": float(k_tab),
+                      "rms_backward_recomputing_sums": float(k_rms_rec), "embed_forward": float(k_fwd),
+                      "embed_forward_keeping_sums": float(k_fwd_sums)},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_ADD_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_ADD_TFLOPS, "traffic": None},
         "cpu_baseline": cpu,

@@ -375,6 +375,46 @@ __device__ __forceinline__ float wave_sum16(const float (&q)[16], int lane) {
   return d;
 }
 
+// The first pass's work on one strip, given the exact fp32 sums acc of
+// columns col0 .. col0 + 15 of this thread's token: the token's dot chain
+// (one fma per column, in column order), and the strip's 16 column sums of
+// dy * s * r over the workgroup's tokens (a transposing butterfly per
+// wavefront, then the 16 wavefronts in order) into dw_part.  Contains a
+// barrier; the caller keeps `red` unwritten until the first 16 threads have
+// read it (another barrier).
+// (dot_strip_q: the dot chain and the wavefront's butterfly, whose result
+// lane L holds for column (L >> 2) & 15; red_sum: the sum over the 16
+// wavefronts in order.)
+template <bool kDyBf16>
+__device__ __forceinline__ float dot_strip_q(int col0, const float (&acc)[kStrip], const DyRaw<kDyBf16>& dyr,
+                                             const float* __restrict__ rms_weight, float r, float& dot, int tid) {
+  float gr[kStrip];
+  unpack_dy<kDyBf16>(gr, dyr);
+  float q[kStrip];
+#pragma unroll
+  for (int c = 0; c < kStrip; ++c) {
+    dot = fmaf(rms_weight[col0 + c] * gr[c], acc[c], dot);
+    q[c] = (gr[c] * acc[c]) * r;
+  }
+  return wave_sum16(q, tid & 63);
+}
+__device__ __forceinline__ float red_sum(const float (*red)[kStrip], int c) {
+  float v = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kEmbThreads / 64; ++w) v += red[w][c];
+  return v;
+}
+template <bool kDyBf16>
+__device__ __forceinline__ void dot_strip(int col0, const float (&acc)[kStrip], const DyRaw<kDyBf16>& dyr,
+                                          const float* __restrict__ rms_weight, float r, float& dot,
+                                          float (*red)[kStrip], int tid, float* __restrict__ dw_part, int64_t tb,
+                                          int d_model) {
+  const float qs = dot_strip_q<kDyBf16>(col0, acc, dyr, rms_weight, r, dot, tid);
+  if ((tid & 3) == 0) red[tid >> 6][(tid >> 2) & 15] = qs;
+  __syncthreads();
+  if (tid < kStrip) dw_part[tb * d_model + col0 + tid] = red_sum(red, tid);
+}
+
 // Pass 1: per token, sum_c w_c dy_c s_c over the workgroup's strips (dot_part
 // [n_tokens, n_groups]); per column, sum over the workgroup's tokens of
 // dy * s * r (dw_part [token blocks, d_model]); with s_out, the sums s
@@ -411,24 +451,69 @@ rms_dot_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins,
                        so[2] = make_float4(acc[8], acc[9], acc[10], acc[11]);
                        so[3] = make_float4(acc[12], acc[13], acc[14], acc[15]);
                      }
-                     float gr[kStrip];
-                     unpack_dy<kDyBf16>(gr, dyr);
-                     float q[kStrip];
-#pragma unroll
-                     for (int c = 0; c < kStrip; ++c) {
-                       dot = fmaf(rms_weight[col0 + c] * gr[c], acc[c], dot);
-                       q[c] = (gr[c] * acc[c]) * r;
-                     }
-                     const float qs = wave_sum16(q, tid & 63);
-                     if ((tid & 3) == 0) red[tid >> 6][(tid >> 2) & 15] = qs;
-                     __syncthreads();
-                     if (tid < kStrip) {
-                       float v = 0.0f;
-#pragma unroll
-                       for (int w = 0; w < kEmbThreads / 64; ++w) v += red[w][tid];
-                       dw_part[tb * d_model + col0 + tid] = v;
-                     }
+                     dot_strip<kDyBf16>(col0, acc, dyr, rms_weight, r, dot, red, tid, dw_part, tb, d_model);
                    });
+  if (active) dot_part[t * n_groups + grp] = dot;
+}
+
+// Pass 1 from sums the forward kept (sums [n_tokens, d_model] fp32): the same
+// workgroups, strips and per-strip arithmetic as rms_dot_kernel, with the
+// sums read instead of recomputed.  Strips go in pairs: a lane reads a whole
+// 128-byte line of its token's sums, the two strips' butterflies are
+// independent, and one pair of barriers serves both.  (A thread past the batch adds +0 where
+// rms_dot_kernel adds a zero of either sign; the column sums are then equal,
+// and dw_reduce_kernel starts from +0, so the results are the same bits.)
+template <bool kDyBf16>
+__global__ void __launch_bounds__(kEmbThreads)
+rms_dot_sums_kernel(const float* __restrict__ sums, int64_t n_tokens, int d_model, const float* __restrict__ rms_weight,
+                    const float* __restrict__ rms_scale, const void* __restrict__ dy, float* __restrict__ dot_part,
+                    float* __restrict__ dw_part, int n_groups, int n_strips, int strips_per_group) {
+  __shared__ float red[2][kEmbThreads / 64][kStrip];
+  const int tid = threadIdx.x;
+  const int grp = static_cast<int>(blockIdx.x % static_cast<unsigned>(n_groups));
+  const int64_t tb = blockIdx.x / static_cast<unsigned>(n_groups);
+  const int64_t t = tb * kEmbThreads + tid;
+  const bool active = t < n_tokens;
+  const int s_first = grp * strips_per_group;
+  const int s_end = min(n_strips, s_first + strips_per_group);
+  const float r = active ? rms_scale[t] : 0.0f;
+  float dot = 0.0f;
+  auto load = [&](int col0, DyRaw<kDyBf16>& dyr, float (&acc)[kStrip]) {
+    load_dy_raw<kDyBf16>(dyr, dy, t, d_model, col0, active);
+    if (active) {
+      const float4* sp = reinterpret_cast<const float4*>(sums + t * d_model + col0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = sp[q];
+        acc[4 * q] = v.x;
+        acc[4 * q + 1] = v.y;
+        acc[4 * q + 2] = v.z;
+        acc[4 * q + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < kStrip; ++c) acc[c] = 0.0f;
+    }
+  };
+  for (int strip = s_first; strip < s_end; strip += 2) {
+    const int col0 = strip * kStrip;
+    const bool two = strip + 1 < s_end;  // the same in every thread
+    DyRaw<kDyBf16> dyr0, dyr1;
+    float acc0[kStrip], acc1[kStrip];
+    load(col0, dyr0, acc0);
+    if (two) load(col0 + kStrip, dyr1, acc1);
+    const float qs0 = dot_strip_q<kDyBf16>(col0, acc0, dyr0, rms_weight, r, dot, tid);
+    float qs1 = 0.0f;
+    if (two) qs1 = dot_strip_q<kDyBf16>(col0 + kStrip, acc1, dyr1, rms_weight, r, dot, tid);
+    if ((tid & 3) == 0) {
+      red[0][tid >> 6][(tid >> 2) & 15] = qs0;
+      red[1][tid >> 6][(tid >> 2) & 15] = qs1;
+    }
+    __syncthreads();
+    if (tid < kStrip) dw_part[tb * d_model + col0 + tid] = red_sum(red[0], tid);
+    else if (two && tid < 2 * kStrip) dw_part[tb * d_model + col0 + tid] = red_sum(red[1], tid - kStrip);
+    __syncthreads();  // red is read before the next pair writes it
+  }
   if (active) dot_part[t * n_groups + grp] = dot;
 }
 
@@ -678,6 +763,56 @@ hipError_t launch_rms_backward(const uint8_t* levels, int64_t n_tokens, int n_bi
 #undef DMEL_RMS_PASS
   e = hipGetLastError();
   if (e != hipSuccess || dweight == nullptr) return e;
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((d_model + 255) / 256), dim3(256), 0, stream, dw_part, tblocks, d_model,
+                     dweight, accumulate_dweight ? 1 : 0);
+  return hipGetLastError();
+}
+
+size_t rms_bwd_sums_bytes(int64_t n_tokens, int d_model) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  return rms_bwd_layout(n_tokens, d_model, nullptr) + up(static_cast<size_t>(n_tokens) * sizeof(float));
+}
+
+hipError_t launch_rms_backward_sums(const float* sums, int64_t n_tokens, int d_model, const float* rms_weight,
+                                    const float* rms_scale, const void* dy, bool dy_bf16, float* ds, float* dweight,
+                                    bool accumulate_dweight, void* workspace, hipStream_t stream) {
+  if (n_tokens <= 0) {
+    if (dweight == nullptr || accumulate_dweight) return hipSuccess;
+    return zero_fill(dweight, d_model, stream);
+  }
+  size_t off_dw = 0;
+  const size_t base = rms_bwd_layout(n_tokens, d_model, &off_dw);
+  auto* dot_part = static_cast<float*>(workspace);
+  auto* dw_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_dw);
+  auto* coef = reinterpret_cast<float*>(static_cast<char*>(workspace) + base);
+  const int n_strips = d_model / kStrip;
+  const int64_t tblocks = (n_tokens + kEmbThreads - 1) / kEmbThreads;
+  const int g = strips_per_group(tblocks, n_strips);
+  const int n_groups = (n_strips + g - 1) / g;
+  const int64_t blocks = tblocks * n_groups;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kEmbThreads);
+  if (dy_bf16) {
+    hipLaunchKernelGGL(rms_dot_sums_kernel<true>, grid, block, 0, stream, sums, n_tokens, d_model, rms_weight,
+                       rms_scale, dy, dot_part, dw_part, n_groups, n_strips, g);
+  } else {
+    hipLaunchKernelGGL(rms_dot_sums_kernel<false>, grid, block, 0, stream, sums, n_tokens, d_model, rms_weight,
+                       rms_scale, dy, dot_part, dw_part, n_groups, n_strips, g);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rms_coef_kernel, dim3(static_cast<unsigned>((n_tokens + 255) / 256)), dim3(256), 0, stream,
+                     dot_part, rms_scale, n_tokens, n_groups, d_model, coef);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned sb = static_cast<unsigned>(std::min<int64_t>(n_tokens, 256 * 64));
+  if (dy_bf16) {
+    hipLaunchKernelGGL(rms_ds_stream_kernel<true>, dim3(sb), dim3(256), 0, stream, sums, dy, rms_weight, rms_scale,
+                       coef, n_tokens, d_model, ds);
+  } else {
+    hipLaunchKernelGGL(rms_ds_stream_kernel<false>, dim3(sb), dim3(256), 0, stream, sums, dy, rms_weight, rms_scale,
+                       coef, n_tokens, d_model, ds);
+  }
+  if ((e = hipGetLastError()) != hipSuccess || dweight == nullptr) return e;
   hipLaunchKernelGGL(dw_reduce_kernel, dim3((d_model + 255) / 256), dim3(256), 0, stream, dw_part, tblocks, d_model,
                      dweight, accumulate_dweight ? 1 : 0);
   return hipGetLastError();

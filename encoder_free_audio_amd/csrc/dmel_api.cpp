@@ -371,6 +371,40 @@ int dmel_embed(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t 
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "embed launch");
 }
 
+int dmel_embed_train(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels, const uint16_t* table,
+                     int32_t d_model, const float* rms_weight, const float* rms_scale, void* out, int32_t out_dtype,
+                     int64_t out_row_stride, const int64_t* out_rows, float* sums, void* stream) {
+  if (n_tokens < 0) return fail(DMEL_EINVAL, "n_tokens is negative");
+  int rc = check_layout(n_bins, n_levels);
+  if (rc != DMEL_OK) return rc;
+  rc = check_table(table, d_model);
+  if (rc != DMEL_OK) return rc;
+  rc = check_out(out, out_dtype, out_row_stride, d_model, out_rows);
+  if (rc != DMEL_OK) return rc;
+  if (rms_weight != nullptr && rms_scale == nullptr) return fail(DMEL_EINVAL, "rms_weight given without rms_scale");
+  if (rms_weight != nullptr && (!aligned(rms_weight, 4) || !aligned(rms_scale, 4)))
+    return fail(DMEL_EALIGN, "rms_weight / rms_scale not 4-byte aligned");
+  if (n_tokens == 0) return DMEL_OK;
+  if (levels == nullptr) return fail(DMEL_EINVAL, "levels is NULL");
+  if (sums == nullptr) return fail(DMEL_EINVAL, "sums is NULL");
+  if (released_layout(n_bins, n_levels) && !aligned(levels, 16))
+    return fail(DMEL_EALIGN, "levels is not 16-byte aligned");
+  if (!aligned(sums, 16)) return fail(DMEL_EALIGN, "sums is not 16-byte aligned");
+  const size_t T = static_cast<size_t>(n_tokens), D = static_cast<size_t>(d_model);
+  const size_t b_sums = T * D * 4;
+  // the output's extent: rows up to the largest index a token may use
+  const size_t esz = out_dtype == DMEL_F32 ? 4 : 2;
+  const size_t b_out = out_rows == nullptr ? ((T - 1) * static_cast<size_t>(out_row_stride) + D) * esz : 0;
+  if (overlaps(sums, b_sums, levels, T * n_bins) ||
+      overlaps(sums, b_sums, table, static_cast<size_t>(n_bins) * n_levels * D * 2) ||
+      (out_rows == nullptr && overlaps(sums, b_sums, out, b_out)) || (out_rows != nullptr && sums == out))
+    return fail(DMEL_EINVAL, "sums overlaps another argument");
+  hipError_t e = dmel::launch_embed(levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, out,
+                                    out_dtype == DMEL_F32, out_row_stride, out_rows, static_cast<hipStream_t>(stream),
+                                    sums);
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "embed launch");
+}
+
 size_t dmel_forward_workspace_bytes(int64_t n_frames_total) {
   if (n_frames_total < 0) return 0;
   const size_t n = static_cast<size_t>(n_frames_total);
@@ -614,6 +648,44 @@ int dmel_rms_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, i
   hipError_t e = dmel::launch_rms_backward(levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, dy,
                                            dy_dtype == DMEL_BF16, dsum, dweight, accumulate_dweight != 0, workspace,
                                            stored, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DMEL_OK : hip_fail(e, "rms backward launch");
+}
+
+size_t dmel_rms_backward_sums_workspace_bytes(int64_t n_tokens, int32_t d_model) {
+  if (n_tokens < 0 || d_model < 16 || d_model % 16 != 0) return 0;
+  return dmel::rms_bwd_sums_bytes(n_tokens, d_model);
+}
+
+int dmel_rms_backward_sums(const float* sums, int64_t n_tokens, int32_t d_model, const float* rms_weight,
+                           const float* rms_scale, const void* dy, int32_t dy_dtype, float* dsum, float* dweight,
+                           int32_t accumulate_dweight, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_tokens < 0) return fail(DMEL_EINVAL, "n_tokens is negative");
+  if (d_model < 16 || d_model > 65536 || d_model % 16 != 0)
+    return fail(DMEL_ESHAPE, "d_model must be a multiple of 16 in [16, 65536] (got %d)", d_model);
+  if (dy_dtype != DMEL_BF16 && dy_dtype != DMEL_F32) return fail(DMEL_EDTYPE, "unsupported dy_dtype %d", dy_dtype);
+  if (rms_weight == nullptr) return fail(DMEL_EINVAL, "rms_weight is NULL");
+  if (!aligned(rms_weight, 4)) return fail(DMEL_EALIGN, "rms_weight is not 4-byte aligned");
+  if (dweight != nullptr && !aligned(dweight, 4)) return fail(DMEL_EALIGN, "dweight is not 4-byte aligned");
+  const size_t need = dmel_rms_backward_sums_workspace_bytes(n_tokens, d_model);
+  if (workspace_bytes < need)
+    return fail(DMEL_ENOMEM, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  if (n_tokens > 0) {
+    if (sums == nullptr || rms_scale == nullptr || dy == nullptr || dsum == nullptr || workspace == nullptr)
+      return fail(DMEL_EINVAL, "sums / rms_scale / dy / dsum / workspace is NULL");
+    if (!aligned(sums, 16) || !aligned(dy, 16) || !aligned(dsum, 16) || !aligned(rms_scale, 4))
+      return fail(DMEL_EALIGN, "sums / dy / dsum must be 16-byte aligned, rms_scale 4-byte aligned");
+    if (!aligned(workspace, 256)) return fail(DMEL_EALIGN, "workspace is not 256-byte aligned");
+    const size_t T = static_cast<size_t>(n_tokens), D = static_cast<size_t>(d_model);
+    const size_t b_ds = T * D * 4, b_dy = T * D * (dy_dtype == DMEL_F32 ? 4 : 2);
+    if (overlaps(dsum, b_ds, dy, b_dy) || overlaps(dsum, b_ds, workspace, need) || overlaps(dsum, b_ds, sums, b_ds) ||
+        overlaps(dsum, b_ds, rms_scale, T * 4) || overlaps(dsum, b_ds, dweight, D * 4) ||
+        overlaps(workspace, need, dy, b_dy) || overlaps(workspace, need, sums, b_ds) ||
+        overlaps(dweight, D * 4, workspace, need) || overlaps(dweight, D * 4, sums, b_ds))
+      return fail(DMEL_EINVAL, "dsum / dweight / workspace overlap another argument");
+  }
+  hipError_t e = dmel::launch_rms_backward_sums(sums, n_tokens, d_model, rms_weight, rms_scale, dy,
+                                                dy_dtype == DMEL_BF16, dsum, dweight, accumulate_dweight != 0,
+                                                workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DMEL_OK : hip_fail(e, "rms backward launch");
 }
 

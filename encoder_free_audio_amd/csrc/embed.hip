@@ -56,12 +56,14 @@ __device__ __forceinline__ void block_tile(int n_groups, int& grp, int64_t& tb) 
 
 // kAny = false: the released layout (levels [n, 80], 16-byte aligned, table
 // [1280, d]); true: any n_bins <= 80, n_levels <= 16 (see the top of the file).
-template <bool kAny>
+// kSums: also write each token's fp32 sums (before the RMSNorm) to sums_out.
+template <bool kAny, bool kSums>
 __global__ void __launch_bounds__(kEmbThreads)
 embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, int n_levels,
              const uint16_t* __restrict__ table, int d_model, const float* __restrict__ rms_weight,
              const float* __restrict__ rms_scale, void* __restrict__ out, int out_f32, int64_t out_row_stride,
-             const int64_t* __restrict__ out_rows, int n_groups, int n_strips, int strips_per_group) {
+             const int64_t* __restrict__ out_rows, int n_groups, int n_strips, int strips_per_group,
+             float* __restrict__ sums_out) {
   __shared__ float4 tab4[kRows * kPitch / 4];
   float* tab = reinterpret_cast<float*>(tab4);
 
@@ -137,6 +139,14 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, i
     if (!kAny || n_bins > kMels / 2) add_bins<kMels / 2, kMels>(acc, tab, offs);
 
     if (active) {
+      if (kSums) {
+        // the fp32 sums themselves, for a backward that does not recompute them
+        float4* so = reinterpret_cast<float4*>(sums_out + t * d_model + col0);
+        so[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        so[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        so[2] = make_float4(acc[8], acc[9], acc[10], acc[11]);
+        so[3] = make_float4(acc[12], acc[13], acc[14], acc[15]);
+      }
       if (rms_weight != nullptr) {
 #pragma unroll
         for (int c = 0; c < kStrip; ++c) acc[c] = (acc[c] * scale) * rms_weight[col0 + c];
@@ -640,7 +650,7 @@ gather_rows_kernel(const uint16_t* __restrict__ table, int64_t n_table_rows, int
 hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
                         const uint16_t* table, int d_model, const float* rms_weight, const float* rms_scale,
                         void* out, bool out_f32, int64_t out_row_stride, const int64_t* out_rows,
-                        hipStream_t stream) {
+                        hipStream_t stream, float* sums_out) {
   if (n_tokens <= 0) return hipSuccess;
   const int n_strips = d_model / kStrip;
   const int64_t tblocks = (n_tokens + kEmbThreads - 1) / kEmbThreads;
@@ -669,15 +679,16 @@ hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, int n_bins, int
   const int n_groups = (n_strips + best - 1) / best;
   const int64_t blocks = tblocks * n_groups;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (n_bins == kMels && n_levels == kLevels) {
-    hipLaunchKernelGGL(embed_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kEmbThreads), 0, stream,
-                       levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, out,
-                       out_f32 ? 1 : 0, out_row_stride, out_rows, n_groups, n_strips, best);
-  } else {
-    hipLaunchKernelGGL(embed_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kEmbThreads), 0, stream,
-                       levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, out,
-                       out_f32 ? 1 : 0, out_row_stride, out_rows, n_groups, n_strips, best);
-  }
+#define DMEL_EMBED_LAUNCH(ANY, SUMS)                                                                          \
+  hipLaunchKernelGGL((embed_kernel<ANY, SUMS>), dim3(static_cast<unsigned>(blocks)), dim3(kEmbThreads), 0, stream, \
+                     levels, n_tokens, n_bins, n_levels, table, d_model, rms_weight, rms_scale, out,              \
+                     out_f32 ? 1 : 0, out_row_stride, out_rows, n_groups, n_strips, best, sums_out)
+  const bool released = n_bins == kMels && n_levels == kLevels;
+  if (released && sums_out == nullptr) DMEL_EMBED_LAUNCH(false, false);
+  else if (released) DMEL_EMBED_LAUNCH(false, true);
+  else if (sums_out == nullptr) DMEL_EMBED_LAUNCH(true, false);
+  else DMEL_EMBED_LAUNCH(true, true);
+#undef DMEL_EMBED_LAUNCH
   return hipGetLastError();
 }
 

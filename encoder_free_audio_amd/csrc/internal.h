@@ -136,10 +136,11 @@ hipError_t launch_frontend(const FrontTables& tabs, const float* audio, int64_t 
 // n_levels * bin + level (1 <= n_levels <= 16).  Internally every kernel works
 // in the released 80 x 16 row space (row 16 * bin + level): missing bins read
 // a row of -0.0 (an exact no-op in the fp32 sum, and 0 in the Gram matrix).
+// sums_out (may be NULL): each token's fp32 sum before the RMSNorm, [n, d].
 hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, int n_bins, int n_levels,
                         const uint16_t* table, int d_model, const float* rms_weight, const float* rms_scale,
                         void* out, bool out_f32, int64_t out_row_stride, const int64_t* out_rows,
-                        hipStream_t stream);
+                        hipStream_t stream, float* sums_out = nullptr);
 
 hipError_t launch_gram(const uint16_t* table, int n_bins, int n_levels, int d_model, double* gram,
                        hipStream_t stream);
@@ -176,6 +177,14 @@ hipError_t launch_rms_backward(const uint8_t* levels, int64_t n_tokens, int n_bi
                                const uint16_t* table, int d_model, const float* rms_weight, const float* rms_scale,
                                const void* dy, bool dy_bf16, float* ds, float* dweight, bool accumulate_dweight,
                                void* workspace, bool stored, hipStream_t stream);
+// The same from sums the forward kept (launch_embed's sums_out): both passes
+// stream them, with the first pass's arithmetic and order unchanged, so the
+// results equal launch_rms_backward's bit for bit.  Workspace:
+// rms_bwd_sums_bytes.
+size_t rms_bwd_sums_bytes(int64_t n_tokens, int d_model);
+hipError_t launch_rms_backward_sums(const float* sums, int64_t n_tokens, int d_model, const float* rms_weight,
+                                    const float* rms_scale, const void* dy, bool dy_bf16, float* ds, float* dweight,
+                                    bool accumulate_dweight, void* workspace, hipStream_t stream);
 
 // hMLP image front end (four stages over 40 x 40 patches) and its stage GEMM.
 size_t hmlp_layout(int64_t n_patches, int hidden, size_t* off);

@@ -27,10 +27,12 @@ _STATUS = {0: "DMEL_OK", -1: "DMEL_EINVAL", -2: "DMEL_ESHAPE", -3: "DMEL_EDTYPE"
 # Every symbol include/dmel.h declares.
 EXPORTS = ("dmel_get_params", "dmel_num_frames", "dmel_last_error", "dmel_default_config", "dmel_create",
            "dmel_create_config", "dmel_get_config", "dmel_destroy", "dmel_frames", "dmel_levels", "dmel_rms_gram",
-           "dmel_rms_scale", "dmel_embed", "dmel_forward_workspace_bytes", "dmel_forward", "dmel_forward_noalloc",
+           "dmel_rms_scale", "dmel_embed", "dmel_embed_train", "dmel_forward_workspace_bytes", "dmel_forward",
+           "dmel_forward_noalloc",
            "dmel_gather_rows",
            "dmel_shortconv", "dmel_embed_backward_workspace_bytes", "dmel_embed_backward",
            "dmel_rms_backward_workspace_bytes", "dmel_rms_backward_stored_workspace_bytes", "dmel_rms_backward",
+           "dmel_rms_backward_sums_workspace_bytes", "dmel_rms_backward_sums",
            "dmel_hmlp_workspace_bytes",
            "dmel_hmlp_forward", "dmel_hmlp_stage")
 
@@ -90,6 +92,7 @@ def lib() -> ctypes.CDLL:
             "dmel_rms_gram": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P]),
             "dmel_rms_scale": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _F, _P, _P]),
             "dmel_embed": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _I64, _P, _P]),
+            "dmel_embed_train": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _I64, _P, _P, _P]),
             "dmel_forward_workspace_bytes": (_SZ, [_I64]),
             "dmel_forward": (ctypes.c_int, [_P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _I32, _P, _P, _F,
                                             _P, _I32, _I64, _P, _P, _SZ, _P]),
@@ -107,6 +110,8 @@ def lib() -> ctypes.CDLL:
             "dmel_hmlp_stage": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _I32, _I32, _P, _I32, _P]),
             "dmel_rms_backward": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _P, _P, _I32, _P,
                                                  _SZ, _P]),
+            "dmel_rms_backward_sums_workspace_bytes": (_SZ, [_I64, _I32]),
+            "dmel_rms_backward_sums": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _I32, _P, _P, _I32, _P, _SZ, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(h, name)
@@ -226,6 +231,14 @@ def dmel_embed(levels, n_tokens, table, d_model, rms_weight, rms_scale, out, out
                                           int(out_dtype), int(out_row_stride), _ptr(out_rows), _stream(stream)))
 
 
+def dmel_embed_train(levels, n_tokens, table, d_model, rms_weight, rms_scale, out, out_dtype, out_row_stride,
+                     out_rows, sums, stream=None, *, n_bins=80, n_levels=16) -> None:
+    _check("dmel_embed_train", lib().dmel_embed_train(_ptr(levels), int(n_tokens), int(n_bins), int(n_levels),
+                                                      _ptr(table), int(d_model), _ptr(rms_weight), _ptr(rms_scale),
+                                                      _ptr(out), int(out_dtype), int(out_row_stride),
+                                                      _ptr(out_rows), _ptr(sums), _stream(stream)))
+
+
 def dmel_forward_workspace_bytes(n_frames_total: int) -> int:
     return int(lib().dmel_forward_workspace_bytes(int(n_frames_total)))
 
@@ -296,6 +309,18 @@ def dmel_rms_backward(levels, n_tokens, n_bins, n_levels, table, d_model, rms_we
                                                         _ptr(dy), int(dy_dtype), _ptr(dsum), _ptr(dweight),
                                                         int(accumulate_dweight), _ptr(workspace),
                                                         int(workspace_bytes), _stream(stream)))
+
+
+def dmel_rms_backward_sums_workspace_bytes(n_tokens, d_model) -> int:
+    return int(lib().dmel_rms_backward_sums_workspace_bytes(int(n_tokens), int(d_model)))
+
+
+def dmel_rms_backward_sums(sums, n_tokens, d_model, rms_weight, rms_scale, dy, dy_dtype, dsum, dweight,
+                           accumulate_dweight, workspace, workspace_bytes, stream=None) -> None:
+    _check("dmel_rms_backward_sums",
+           lib().dmel_rms_backward_sums(_ptr(sums), int(n_tokens), int(d_model), _ptr(rms_weight), _ptr(rms_scale),
+                                        _ptr(dy), int(dy_dtype), _ptr(dsum), _ptr(dweight), int(accumulate_dweight),
+                                        _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def dmel_hmlp_workspace_bytes(n_images, height, width, hidden) -> int:

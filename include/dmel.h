@@ -215,6 +215,19 @@ int dmel_embed(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t 
                void* out, int32_t out_dtype, int64_t out_row_stride, const int64_t* out_rows,
                void* stream);
 
+/* dmel_embed for training: the same output, and each token's fp32 sum s
+ * (before the RMSNorm) kept for the backward (the sums the derivative of the
+ * RMSNorm needs, see dmel_rms_backward_sums; training the front end is the
+ * Coda's experimental case, "Inside Inkling: Audio Design").
+ *  sums       fp32 [n_tokens, d_model] out, 16-byte aligned, token i at row i
+ *             (not out_rows[i]); bit-identical to dmel_embed's fp32 output
+ *             without RMSNorm; must not overlap out, levels or table
+ * Other arguments and errors as dmel_embed. */
+int dmel_embed_train(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, int32_t n_levels,
+                     const uint16_t* table, int32_t d_model, const float* rms_weight, const float* rms_scale,
+                     void* out, int32_t out_dtype, int64_t out_row_stride, const int64_t* out_rows,
+                     float* sums, void* stream);
+
 /* Bytes of device workspace dmel_forward needs for n_frames_total frames
  * (levels plus per-token scales, and for batches of at most 131,072 frames
  * 1280 bytes per frame of RMSNorm partial sums; each part 256-byte aligned).
@@ -363,6 +376,26 @@ int dmel_rms_backward(const uint8_t* levels, int64_t n_tokens, int32_t n_bins, i
                       const float* rms_scale, const void* dy, int32_t dy_dtype, float* dsum,
                       float* dweight, int32_t accumulate_dweight, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace dmel_rms_backward_sums needs (dmel_rms_backward_workspace_bytes
+ * + n_tokens * 4, 256-byte aligned; 0 for invalid sizes). */
+size_t dmel_rms_backward_sums_workspace_bytes(int64_t n_tokens, int32_t d_model);
+
+/* dmel_rms_backward from the sums dmel_embed_train kept, instead of the
+ * levels and the table: both passes stream the sums (no recomputation), with
+ * the same arithmetic in the same order, so dsum and dweight are the same bits
+ * as dmel_rms_backward's.
+ *  sums       fp32 [n_tokens, d_model], 16-byte aligned, from dmel_embed_train
+ *  rms_weight, rms_scale, dy, dsum, dweight, accumulate_dweight   as
+ *             dmel_rms_backward
+ *  workspace  device memory, 256-byte aligned, >= the size above
+ * Errors: DMEL_EINVAL (NULL where data is needed, overlapping buffers),
+ * DMEL_ESHAPE (d_model), DMEL_EDTYPE, DMEL_EALIGN, DMEL_ENOMEM (workspace too
+ * small), DMEL_EHIP. */
+int dmel_rms_backward_sums(const float* sums, int64_t n_tokens, int32_t d_model, const float* rms_weight,
+                           const float* rms_scale, const void* dy, int32_t dy_dtype, float* dsum,
+                           float* dweight, int32_t accumulate_dweight, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* hMLP image front end: one d_model-wide embedding per 40 x 40 pixel patch
  * ("Inside Inkling: Audio Design", Part 1, "Why this is a reasonable bet": a

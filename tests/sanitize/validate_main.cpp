@@ -100,6 +100,18 @@ int main() {
                              nullptr) == DMEL_EDTYPE);
   EXPECT(dmel_rms_backward(lv, 4, 80, 16, tb, 6144, a, a, FAKE, DMEL_BF16, static_cast<float*>(FAKE), nullptr, 0,
                            FAKE, 0, nullptr) == DMEL_ENOMEM);
+  float* const fs = static_cast<float*>(FAKE);
+  EXPECT(dmel_rms_backward_sums_workspace_bytes(1000, 6144) >= dmel_rms_backward_workspace_bytes(1000, 6144) + 4000);
+  EXPECT(dmel_rms_backward_sums_workspace_bytes(-1, 6144) == 0 && dmel_rms_backward_sums_workspace_bytes(9, 100) == 0);
+  EXPECT(dmel_rms_backward_sums(fs, 4, 6144, a, a, FAKE, DMEL_BF16, fs, nullptr, 0, FAKE, 0, nullptr) == DMEL_ENOMEM);
+  EXPECT(dmel_rms_backward_sums(fs, 4, 6008, a, a, FAKE, DMEL_BF16, fs, nullptr, 0, FAKE, size_t{1} << 30,
+                                nullptr) == DMEL_ESHAPE);
+  EXPECT(dmel_rms_backward_sums(nullptr, 4, 6144, a, a, FAKE, DMEL_F32, fs + (1 << 20), nullptr, 0, FAKE,
+                                size_t{1} << 30, nullptr) == DMEL_EINVAL);
+  EXPECT(dmel_embed_train(lv, 4, 80, 16, tb, 6144, nullptr, nullptr, FAKE, DMEL_BF16, 6144, nullptr, nullptr,
+                          nullptr) == DMEL_EINVAL);
+  EXPECT(dmel_embed_train(lv, 4, 80, 16, tb, 6144, nullptr, nullptr, FAKE, DMEL_BF16, 6144, nullptr, fs + 1,
+                          nullptr) == DMEL_EALIGN);
 
   // host tables of many configurations
   auto* t = new dmel::HostTables;

@@ -215,6 +215,59 @@ def test_validation_other_entry_points(dm):
     assert _code(e) in (-1, -5)
 
 
+def test_validation_training_entry_points(dm):
+    """dmel_embed_train and dmel_rms_backward_sums validate before any launch."""
+    E = dm.DmelError
+    d = 6144
+    # embed_train: the dmel_embed checks, then the sums buffer
+    with pytest.raises(E) as e:
+        dm.dmel_embed_train(FAKE, 5, FAKE, d, None, None, FAKE, dm.DMEL_BF16, d, None, None)
+    assert _code(e) == -1 and "sums" in str(e.value)
+    with pytest.raises(E) as e:
+        dm.dmel_embed_train(FAKE, 5, FAKE, d, None, None, FAKE, dm.DMEL_BF16, d, None, FAKE + 4)
+    assert _code(e) == -4
+    with pytest.raises(E) as e:
+        dm.dmel_embed_train(FAKE, 5, FAKE, 6008, None, None, FAKE, dm.DMEL_BF16, 6008, None, FAKE << 4)
+    assert _code(e) == -2
+    with pytest.raises(E) as e:  # sums on top of the output
+        dm.dmel_embed_train(FAKE, 5, FAKE, d, None, None, FAKE << 8, dm.DMEL_BF16, d, None, (FAKE << 8) + 4096)
+    assert _code(e) == -1 and "overlap" in str(e.value)
+    dm.dmel_embed_train(None, 0, FAKE, d, None, None, FAKE, dm.DMEL_BF16, d, None, None)  # empty: no-op
+    # rms_backward_sums: sizes, dtype, workspace, alignment, overlap
+    need = dm.dmel_rms_backward_sums_workspace_bytes(1000, d)
+    assert need >= dm.dmel_rms_backward_workspace_bytes(1000, d) + 1000 * 4 and need % 256 == 0
+    assert dm.dmel_rms_backward_sums_workspace_bytes(-1, d) == 0
+    assert dm.dmel_rms_backward_sums_workspace_bytes(10, 100) == 0
+    args = [FAKE << 4, 1000, d, FAKE, FAKE, FAKE << 5, dm.DMEL_BF16, FAKE << 6, None, 0]
+    with pytest.raises(E) as e:
+        dm.dmel_rms_backward_sums(*args, FAKE << 7, need - 1)
+    assert _code(e) == -6
+    a = list(args); a[2] = 6008
+    with pytest.raises(E) as e:
+        dm.dmel_rms_backward_sums(*a, FAKE << 7, need)
+    assert _code(e) == -2
+    a = list(args); a[6] = 7
+    with pytest.raises(E) as e:
+        dm.dmel_rms_backward_sums(*a, FAKE << 7, need)
+    assert _code(e) == -3
+    a = list(args); a[0] = None
+    with pytest.raises(E) as e:
+        dm.dmel_rms_backward_sums(*a, FAKE << 7, need)
+    assert _code(e) == -1
+    a = list(args); a[3] = None
+    with pytest.raises(E) as e:
+        dm.dmel_rms_backward_sums(*a, FAKE << 7, need)
+    assert _code(e) == -1
+    a = list(args); a[0] = (FAKE << 4) + 8
+    with pytest.raises(E) as e:
+        dm.dmel_rms_backward_sums(*a, FAKE << 7, need)
+    assert _code(e) == -4
+    a = list(args); a[7] = FAKE << 4  # dsum on top of the sums
+    with pytest.raises(E) as e:
+        dm.dmel_rms_backward_sums(*a, FAKE << 7, need)
+    assert _code(e) == -1 and "overlap" in str(e.value)
+
+
 def test_validation_shortconv(dm):
     E = dm.DmelError
     C, T, S = 64, 10, 2

@@ -185,6 +185,26 @@ def _rms_case(dm, lv, n_levels, d, dy_bf16, seed, accumulate=False):
     torch.cuda.synchronize()
     assert torch.equal(ds2.view(torch.int32), ds.view(torch.int32))
     assert torch.equal(dw2.view(torch.int32), dw.view(torch.int32))
+    # the training path: the forward keeps the sums (the oracle's sequential
+    # fp32 sums, bit for bit, beside the unchanged output) and the backward
+    # streams them: the same bits again
+    out_t = torch.empty((n, d), dtype=torch.int16, device="cuda")
+    out_r = torch.empty((n, d), dtype=torch.int16, device="cuda")
+    sums = torch.full((n, d), float("nan"), dtype=torch.float32, device="cuda")
+    dm.dmel_embed_train(lvd, n, td, d, wd, scale, out_t, dm.DMEL_BF16, d, None, sums, **lay)
+    dm.dmel_embed(lvd, n, td, d, wd, scale, out_r, dm.DMEL_BF16, d, **lay)
+    torch.cuda.synchronize()
+    assert torch.equal(out_t, out_r)
+    assert np.array_equal(sums.cpu().numpy().view(np.uint32), np.ascontiguousarray(s, dtype=np.float32).view(np.uint32))
+    wsb3 = dm.dmel_rms_backward_sums_workspace_bytes(n, d)
+    ws3 = torch.empty(wsb3, dtype=torch.uint8, device="cuda")
+    ds3 = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    dw3 = torch.from_numpy(dw0.copy()).cuda()
+    dm.dmel_rms_backward_sums(sums, n, d, wd, scale, dyd, dm.DMEL_BF16 if dy_bf16 else dm.DMEL_F32, ds3, dw3,
+                              1 if accumulate else 0, ws3, wsb3)
+    torch.cuda.synchronize()
+    assert torch.equal(ds3.view(torch.int32), ds.view(torch.int32))
+    assert torch.equal(dw3.view(torch.int32), dw.view(torch.int32))
     return ds
 
 
@@ -196,6 +216,32 @@ def test_rms_backward(dm, n_bins, n_levels, dy_bf16):
         print(f"case: rms backward {n_bins}x{n_levels} dy_bf16={dy_bf16} n={n} d={d}", flush=True)
         lv = rng.integers(0, n_levels, (n, n_bins)).astype(np.uint8)
         _rms_case(dm, lv, n_levels, d, dy_bf16, seed=n + d, accumulate=(n == 300))
+
+
+def test_embed_train_scattered_rows_and_fp32(dm):
+    # dmel_embed_train with out_rows and fp32 output: the output rows are
+    # dmel_embed's, the sums stay in token order; a batch of 3 x 1024 + 5
+    # tokens (a ragged last token block)
+    rng = np.random.default_rng(31)
+    n, d = 3 * 1024 + 5, 512
+    lv = rng.integers(0, 16, (n, 80)).astype(np.uint8)
+    table = synth.table_bf16(seed=32, rows=1280, d_model=d)
+    lvd = torch.from_numpy(lv).cuda()
+    td = table.cuda()
+    rows = torch.from_numpy(rng.permutation(2 * n)[:n].astype(np.int64)).cuda()
+    a = torch.full((2 * n, d), float("nan"), dtype=torch.float32, device="cuda")
+    b = torch.full((2 * n, d), float("nan"), dtype=torch.float32, device="cuda")
+    sums = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    dm.dmel_embed_train(lvd, n, td, d, None, None, a, dm.DMEL_F32, d, rows, sums)
+    dm.dmel_embed(lvd, n, td, d, None, None, b, dm.DMEL_F32, d, rows)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    # without RMSNorm the output row of token i is its sum
+    assert torch.equal(a[rows].view(torch.int32), sums.view(torch.int32))
+    want = o.embed_sum(lv, table.numpy().view(np.uint16))
+    assert np.array_equal(sums.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    # an empty batch writes nothing
+    dm.dmel_embed_train(lvd, 0, td, d, None, None, a, dm.DMEL_F32, d, None, sums)
 
 
 def test_rms_then_table_gradient_chain(dm):
@@ -234,10 +280,26 @@ def test_full_size_backward_sampled(dm):
     dy = synth.activations_bf16(seed=21, n_tokens=T, channels=d, std=1e-3, device="cuda")
     ds = torch.empty((T, d), dtype=torch.float32, device="cuda")
     dw = torch.empty(d, dtype=torch.float32, device="cuda")
-    wsb = dm.dmel_rms_backward_stored_workspace_bytes(T, d)   # the path bench.py times
+    # the path bench.py times: the forward keeps the sums, the backward streams them
+    y = torch.empty((T, d), dtype=torch.int16, device="cuda")
+    sums = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    dm.dmel_embed_train(lv, T, table, d, w, scale, y, dm.DMEL_BF16, d, None, sums)
+    del y
+    wsb = dm.dmel_rms_backward_sums_workspace_bytes(T, d)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    dm.dmel_rms_backward(lv, T, 80, 16, table, d, w, scale, dy, dm.DMEL_BF16, ds, dw, 0, ws, wsb)
+    dm.dmel_rms_backward_sums(sums, T, d, w, scale, dy, dm.DMEL_BF16, ds, dw, 0, ws, wsb)
+    del ws, sums
+    # the same bits as recomputing the sums (with the workspace that keeps them between the passes)
+    wsb = dm.dmel_rms_backward_stored_workspace_bytes(T, d)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    ds_r = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    dw_r = torch.empty(d, dtype=torch.float32, device="cuda")
+    dm.dmel_rms_backward(lv, T, 80, 16, table, d, w, scale, dy, dm.DMEL_BF16, ds_r, dw_r, 0, ws, wsb)
+    torch.cuda.synchronize()
     del ws
+    assert torch.equal(ds_r.view(torch.int32), ds.view(torch.int32))
+    assert torch.equal(dw_r.view(torch.int32), dw.view(torch.int32))
+    del ds_r
     wsb2 = dm.dmel_embed_backward_workspace_bytes(T, 80, 16, d)
     ws2 = torch.empty(wsb2, dtype=torch.uint8, device="cuda")
     dt = torch.empty((1280, d), dtype=torch.float32, device="cuda")
