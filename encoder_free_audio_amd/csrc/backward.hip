@@ -459,8 +459,9 @@ rms_dot_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins,
 // Pass 1 from sums the forward kept (sums [n_tokens, d_model] fp32): the same
 // workgroups, strips and per-strip arithmetic as rms_dot_kernel, with the
 // sums read instead of recomputed.  Strips go in pairs: a lane reads a whole
-// 128-byte line of its token's sums, the two strips' butterflies are
-// independent, and one pair of barriers serves both.  (A thread past the batch adds +0 where
+// 128-byte line of its token's sums (and of dy: four strips of bf16 at a
+// time), the two strips' butterflies are independent, and one pair of
+// barriers serves both.  (A thread past the batch adds +0 where
 // rms_dot_kernel adds a zero of either sign; the column sums are then equal,
 // and dw_reduce_kernel starts from +0, so the results are the same bits.)
 template <bool kDyBf16>
@@ -478,8 +479,7 @@ rms_dot_sums_kernel(const float* __restrict__ sums, int64_t n_tokens, int d_mode
   const int s_end = min(n_strips, s_first + strips_per_group);
   const float r = active ? rms_scale[t] : 0.0f;
   float dot = 0.0f;
-  auto load = [&](int col0, DyRaw<kDyBf16>& dyr, float (&acc)[kStrip]) {
-    load_dy_raw<kDyBf16>(dyr, dy, t, d_model, col0, active);
+  auto load_sums = [&](int col0, float (&acc)[kStrip]) {
     if (active) {
       const float4* sp = reinterpret_cast<const float4*>(sums + t * d_model + col0);
 #pragma unroll
@@ -495,24 +495,35 @@ rms_dot_sums_kernel(const float* __restrict__ sums, int64_t n_tokens, int d_mode
       for (int c = 0; c < kStrip; ++c) acc[c] = 0.0f;
     }
   };
-  for (int strip = s_first; strip < s_end; strip += 2) {
-    const int col0 = strip * kStrip;
-    const bool two = strip + 1 < s_end;  // the same in every thread
-    DyRaw<kDyBf16> dyr0, dyr1;
-    float acc0[kStrip], acc1[kStrip];
-    load(col0, dyr0, acc0);
-    if (two) load(col0 + kStrip, dyr1, acc1);
-    const float qs0 = dot_strip_q<kDyBf16>(col0, acc0, dyr0, rms_weight, r, dot, tid);
-    float qs1 = 0.0f;
-    if (two) qs1 = dot_strip_q<kDyBf16>(col0 + kStrip, acc1, dyr1, rms_weight, r, dot, tid);
-    if ((tid & 3) == 0) {
-      red[0][tid >> 6][(tid >> 2) & 15] = qs0;
-      red[1][tid >> 6][(tid >> 2) & 15] = qs1;
+  // dy is read a whole 128-byte line per lane at a time: 4 strips of bf16, 2 of fp32
+  constexpr int kDyStrips = kDyBf16 ? 4 : 2;
+  for (int s0 = s_first; s0 < s_end; s0 += kDyStrips) {
+    DyRaw<kDyBf16> dyq[kDyStrips];
+#pragma unroll
+    for (int i = 0; i < kDyStrips; ++i) {
+      if (s0 + i < s_end) load_dy_raw<kDyBf16>(dyq[i], dy, t, d_model, (s0 + i) * kStrip, active);
     }
-    __syncthreads();
-    if (tid < kStrip) dw_part[tb * d_model + col0 + tid] = red_sum(red[0], tid);
-    else if (two && tid < 2 * kStrip) dw_part[tb * d_model + col0 + tid] = red_sum(red[1], tid - kStrip);
-    __syncthreads();  // red is read before the next pair writes it
+#pragma unroll
+    for (int p = 0; p < kDyStrips; p += 2) {
+      const int strip = s0 + p;
+      if (strip >= s_end) break;  // the same in every thread
+      const int col0 = strip * kStrip;
+      const bool two = strip + 1 < s_end;
+      float acc0[kStrip], acc1[kStrip];
+      load_sums(col0, acc0);
+      if (two) load_sums(col0 + kStrip, acc1);
+      const float qs0 = dot_strip_q<kDyBf16>(col0, acc0, dyq[p], rms_weight, r, dot, tid);
+      float qs1 = 0.0f;
+      if (two) qs1 = dot_strip_q<kDyBf16>(col0 + kStrip, acc1, dyq[p + 1], rms_weight, r, dot, tid);
+      if ((tid & 3) == 0) {
+        red[0][tid >> 6][(tid >> 2) & 15] = qs0;
+        red[1][tid >> 6][(tid >> 2) & 15] = qs1;
+      }
+      __syncthreads();
+      if (tid < kStrip) dw_part[tb * d_model + col0 + tid] = red_sum(red[0], tid);
+      else if (two && tid < 2 * kStrip) dw_part[tb * d_model + col0 + tid] = red_sum(red[1], tid - kStrip);
+      __syncthreads();  // red is read before the next pair writes it
+    }
   }
   if (active) dot_part[t * n_groups + grp] = dot;
 }
