@@ -37,8 +37,8 @@ namespace {
 // The (strip group, token block) of this workgroup, for a grid of
 // n_groups x token blocks.  Workgroup b runs on XCD b % 8.  With a multiple
 // of 8 strip groups, XCD x takes group x for every token block, then group
-// x + 8, and so on, so its L2 holds one group's table slices at a time (655 KB
-// for 16 strips) while the output streams through it; otherwise consecutive
+// x + 8, and so on, so its L2 holds one group's table slices at a time (983 KB
+// for 24 strips) while the output streams through it; otherwise consecutive
 // workgroups take the groups of one token block.  (The backward's recompute
 // passes keep the second order: they stream dy per token block, and measured
 // slower with the first.)
@@ -151,7 +151,7 @@ embed_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins, i
 #pragma unroll
         for (int c = 0; c < kStrip; ++c) acc[c] = (acc[c] * scale) * rms_weight[col0 + c];
       }
-      // Plain stores: the 16 strips of a workgroup complete each token's
+      // Plain stores: the strips of a workgroup complete each token's
       // 128-byte lines in L2 before they are written back.  (Non-temporal
       // stores, which would keep the output from evicting the table slices,
       // send the 32-byte pieces to memory one by one and nearly double the
@@ -654,12 +654,13 @@ hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, int n_bins, int
   if (n_tokens <= 0) return hipSuccess;
   const int n_strips = d_model / kStrip;
   const int64_t tblocks = (n_tokens + kEmbThreads - 1) / kEmbThreads;
-  // Strips per workgroup: more strips amortise the per-workgroup set-up (16 was
-  // the fastest count measured on a 1.5M-token batch), but a small batch then
-  // launches too few workgroups to fill the chip.  One workgroup fits per CU
-  // (LDS), so the cost of a count g is about rounds-of-256-workgroups x g; take
-  // the largest g within 5% of the cheapest.
-  static const int kCounts[] = {16, 12, 8, 6, 4, 3, 2, 1};
+  // Strips per workgroup: more strips amortise the per-workgroup set-up (24,
+  // then 16, were the fastest counts measured on a 1.5M-token batch with the
+  // XCD-ordered groups), but a small batch then launches too few workgroups to
+  // fill the chip.  One workgroup fits per CU (LDS), so the cost of a count g
+  // is about rounds-of-256-workgroups x g; take the largest g within 5% of the
+  // cheapest.
+  static const int kCounts[] = {24, 16, 12, 8, 6, 4, 3, 2, 1};
   constexpr int kNCounts = sizeof(kCounts) / sizeof(kCounts[0]);
   int64_t cost[kNCounts];
   int64_t min_cost = -1;
