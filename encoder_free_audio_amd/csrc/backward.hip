@@ -17,9 +17,10 @@
 // Kernels:
 //  * levels_t_kernel - the levels by bin ([bin][token], clamped), so that a
 //    chunk's 64 levels of one bin are 64 contiguous bytes.
-//  * scatter_kernel - a workgroup owns 8 bins (one wave each) and 256
-//    columns (4 per lane) and walks every 64-token chunk of the batch in
-//    order; the chunk's 64 x 256 gradient tile and its levels are copied
+//  * scatter_kernel (bf16 gradients) / scatter16_kernel (fp32 gradients) - a
+//    workgroup owns 8 bins (one wave each) and 256 columns (4 per lane), or
+//    16 bins and 128 columns (2 per lane), and walks every 64-token chunk of
+//    the batch in order; the chunk's 64 x 256 gradient tile and its levels are copied
 //    straight into LDS (double-buffered), and each wave takes the 64 tokens
 //    in order: one ds_read_b128 of the token's row (static offset) and four
 //    v_add_f32 into the accumulators of the token's level, which the wave
@@ -288,6 +289,141 @@ scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_l
   }
 }
 #undef DMEL_ADD_LEVEL
+
+// fp32 gradients: 16 bins x 128 columns per workgroup (two columns per lane),
+// so that each copied tile serves twice the bins of scatter_kernel while the
+// launch still has 240 workgroups (5 bin groups x 48 strips).  The same chunk
+// walk, buffers and token order; per token a wave reads 512 bytes of the row
+// (ds_read_b64) and adds two columns into the accumulators of the token's
+// level (16 levels x 2 columns pinned to v64..v95).
+constexpr int kS16Bins = 16;
+constexpr int kS16Cols = 128;
+constexpr int kS16Threads = 64 * kS16Bins;             // 1024
+constexpr int kS16RowBytes = kS16Cols * 4;             // 512
+constexpr int kS16TileBytes = kChunk * kS16RowBytes;   // 32 KB
+static_assert(kChunk / kS16Bins == 4, "tile copy: four rows per wave, two per load");
+static_assert(kS16Bins * kChunk == 64 * 16, "level copy: one 16-byte piece per lane of a wave");
+static_assert(kS16Cols <= kBwdCols, "rows past the batch read the row of -0.0");
+
+// Chunk rows into tile buffer `tb`: wave w copies rows 4w .. 4w + 3, two per
+// load (lanes 0..31 the first row, 32..63 the second; lane i takes columns
+// 4 (i & 31) .. + 3).  Rows past the batch copy the row of -0.0.
+__device__ __forceinline__ void tile_dma16(char* tb, const float* g, const float* neg_zero, int64_t n_tokens,
+                                           int d_model, int64_t t0, int c_strip, int wave, int lane) {
+  const int c = min(c_strip + 4 * (lane & 31), d_model - 4);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r0 = wave * 4 + 2 * i;
+    const int64_t t = t0 + r0 + (lane >> 5);
+    const float* src = t < n_tokens ? g + t * d_model + c : neg_zero + 4 * (lane & 31);
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(tb + r0 * kS16RowBytes), 16, 0, 0);
+  }
+}
+
+// The chunk's levels of the workgroup's 16 bins: the 64 lanes of wave 0 copy
+// 16 bytes each.  Bins past n_bins read the last bin's levels (unused).
+__device__ __forceinline__ void levels_dma16(char* lb, const uint8_t* lvt, int64_t t_pad, int bin0, int n_bins,
+                                             int64_t t0, int wave, int lane) {
+  if (wave == 0) {
+    const int j = min(bin0 + (lane >> 2), n_bins - 1);
+    __builtin_amdgcn_global_load_lds(lvt + j * t_pad + t0 + 16 * (lane & 3), (lds_void_t*)lb, 16, 0, 0);
+  }
+}
+
+#define DMEL_ADD_LEVEL2(L, R)                                                                        \
+  do {                                                                                               \
+    uint32_t m0_out_;                                                                                \
+    asm volatile(                                                                                    \
+        "s_set_gpr_idx_on %3, gpr_idx(SRC0,DST)\n\t"                                                 \
+        "v_add_f32 v64, v64, %4\n\t"                                                                 \
+        "v_add_f32 v80, v80, %5\n\t"                                                                 \
+        "s_set_gpr_idx_off"                                                                          \
+        : "+{v[64:79]}"(ax), "+{v[80:95]}"(ay), "={m0}"(m0_out_)                                       \
+        : "s"(L), "v"((R).x), "v"((R).y));                                                           \
+  } while (0)
+
+__device__ __forceinline__ void scatter16_chunk(char* cur_tile, char* cur_lv, char* nxt_tile, char* nxt_lv,
+                                                int64_t ch, const float* g, int64_t n_tokens, int n_bins,
+                                                int d_model, const uint8_t* lvt, int64_t t_pad,
+                                                const float* neg_zero, int64_t n_chunks, int c_strip, int bin0,
+                                                bool bin_ok, int wave, int lane, f32x16_t& ax, f32x16_t& ay) {
+  // this wave's copies of chunk ch have landed; after the barrier every
+  // wave's have, and every wave is done with chunk ch - 1
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (ch + 1 < n_chunks) {
+    tile_dma16(nxt_tile, g, neg_zero, n_tokens, d_model, (ch + 1) * kChunk, c_strip, wave, lane);
+    levels_dma16(nxt_lv, lvt, t_pad, bin0, n_bins, (ch + 1) * kChunk, wave, lane);
+  }
+  if (bin_ok) {
+    const auto* lw = reinterpret_cast<const uint32_t*>(cur_lv + wave * kChunk);
+    uint32_t w[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) w[q] = __builtin_amdgcn_readfirstlane(lw[q]);
+    const float2* row = reinterpret_cast<const float2*>(cur_tile) + lane;   // token t at row[64 t]
+    float2 r[kChunk];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = row[t * (kS16RowBytes / 8)];
+#pragma unroll
+    for (int t = 0; t < kChunk; ++t) {
+      if (t + 8 < kChunk) r[t + 8] = row[(t + 8) * (kS16RowBytes / 8)];
+      const uint32_t L = (w[t >> 2] >> (8 * (t & 3))) & 15u;
+      DMEL_ADD_LEVEL2(L, r[t]);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kS16Threads)
+scatter16_kernel(const float* __restrict__ g, int64_t n_tokens, int n_bins, int n_levels, int d_model,
+                 const uint8_t* __restrict__ lvt, int64_t t_pad, const float* __restrict__ neg_zero,
+                 int64_t n_chunks, int n_groups, int n_strips, int per_xcd, float* __restrict__ out, int accumulate) {
+  __shared__ __attribute__((aligned(1024))) char tile_a[kS16TileBytes];
+  __shared__ __attribute__((aligned(1024))) char tile_b[kS16TileBytes];
+  __shared__ __attribute__((aligned(16))) char lv_a[kS16Bins * kChunk];
+  __shared__ __attribute__((aligned(16))) char lv_b[kS16Bins * kChunk];
+  // blockIdx -> (strip, bin group) as in scatter_kernel
+  const int bid = static_cast<int>(blockIdx.x);
+  const int local = bid >> 3;
+  const int grp = local % n_groups;
+  const int strip = (bid & 7) * per_xcd + local / n_groups;
+  if (local / n_groups >= per_xcd || strip >= n_strips) return;  // before any barrier: the whole workgroup leaves
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int bin0 = grp * kS16Bins;
+  const int j = bin0 + wave;
+  const bool bin_ok = j < n_bins;
+  const int c_strip = strip * kS16Cols;
+  const int c0 = c_strip + 2 * lane;
+
+  f32x16_t ax = 0.0f, ay = 0.0f;
+  tile_dma16(tile_a, g, neg_zero, n_tokens, d_model, 0, c_strip, wave, lane);
+  levels_dma16(lv_a, lvt, t_pad, bin0, n_bins, 0, wave, lane);
+  for (int64_t ch = 0; ch < n_chunks; ch += 2) {
+    scatter16_chunk(tile_a, lv_a, tile_b, lv_b, ch, g, n_tokens, n_bins, d_model, lvt, t_pad, neg_zero, n_chunks,
+                    c_strip, bin0, bin_ok, wave, lane, ax, ay);
+    if (ch + 1 < n_chunks) {
+      scatter16_chunk(tile_b, lv_b, tile_a, lv_a, ch + 1, g, n_tokens, n_bins, d_model, lvt, t_pad, neg_zero,
+                      n_chunks, c_strip, bin0, bin_ok, wave, lane, ax, ay);
+    }
+  }
+
+  if (!bin_ok || c0 >= d_model) return;
+#pragma unroll
+  for (int l = 0; l < 16; ++l) {
+    if (l < n_levels) {
+      const int64_t rw = static_cast<int64_t>(j) * n_levels + l;
+      float2* o = reinterpret_cast<float2*>(out + rw * d_model + c0);
+      float2 v = make_float2(ax[l], ay[l]);
+      if (accumulate) {
+        const float2 p = *o;
+        v = make_float2(p.x + v.x, p.y + v.y);
+      }
+      *o = v;
+    }
+  }
+}
+#undef DMEL_ADD_LEVEL2
 
 // Zero fill (kept out of hipMemsetAsync so that a caller may capture the
 // calls in a graph).
@@ -693,9 +829,13 @@ hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_
                        n_tokens, n_bins, n_levels, d_model, lvt, t_pad, neg_zero, n_chunks, n_groups, n_strips,
                        per_xcd, dtable, accumulate ? 1 : 0);
   } else {
-    hipLaunchKernelGGL(scatter_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kBwdThreads), 0, stream,
-                       dsum, n_tokens, n_bins, n_levels, d_model, lvt, t_pad, neg_zero, n_chunks, n_groups, n_strips,
-                       per_xcd, dtable, accumulate ? 1 : 0);
+    const int groups16 = (n_bins + kS16Bins - 1) / kS16Bins;
+    const int strips16 = (d_model + kS16Cols - 1) / kS16Cols;
+    const int per_xcd16 = (strips16 + 7) / 8;
+    const int64_t blocks16 = static_cast<int64_t>(per_xcd16) * 8 * groups16;
+    hipLaunchKernelGGL(scatter16_kernel, dim3(static_cast<unsigned>(blocks16)), dim3(kS16Threads), 0, stream,
+                       static_cast<const float*>(dsum), n_tokens, n_bins, n_levels, d_model, lvt, t_pad, neg_zero,
+                       n_chunks, groups16, strips16, per_xcd16, dtable, accumulate ? 1 : 0);
   }
   return hipGetLastError();
 }
