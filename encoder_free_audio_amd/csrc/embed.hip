@@ -37,8 +37,8 @@ namespace {
 // The (strip group, token block) of this workgroup, for a grid of
 // n_groups x token blocks.  Workgroup b runs on XCD b % 8.  With a multiple
 // of 8 strip groups, XCD x takes group x for every token block, then group
-// x + 8, and so on, so its L2 holds one group's table slices at a time (983 KB
-// for 24 strips) while the output streams through it; otherwise consecutive
+// x + 8, and so on, so its L2 holds one group's table slices at a time (1.97 MB
+// for 48 strips) while the output streams through it; otherwise consecutive
 // workgroups take the groups of one token block.  (The backward's recompute
 // passes keep the second order: they stream dy per token block, and measured
 // slower with the first.)
@@ -654,13 +654,14 @@ hipError_t launch_embed(const uint8_t* levels, int64_t n_tokens, int n_bins, int
   if (n_tokens <= 0) return hipSuccess;
   const int n_strips = d_model / kStrip;
   const int64_t tblocks = (n_tokens + kEmbThreads - 1) / kEmbThreads;
-  // Strips per workgroup: more strips amortise the per-workgroup set-up (24,
-  // then 16, were the fastest counts measured on a 1.5M-token batch with the
-  // XCD-ordered groups), but a small batch then launches too few workgroups to
-  // fill the chip.  One workgroup fits per CU (LDS), so the cost of a count g
-  // is about rounds-of-256-workgroups x g; take the largest g within 5% of the
+  // Strips per workgroup: more strips amortise the per-workgroup set-up (48 -
+  // eight groups of 6144 columns, one per XCD - then 24 and 16 were the
+  // fastest counts measured on a 1.5M-token batch with the XCD-ordered
+  // groups), but a small batch then launches too few workgroups to fill the
+  // chip.  One workgroup fits per CU (LDS), so the cost of a count g is about
+  // rounds-of-256-workgroups x g; take the largest g within 5% of the
   // cheapest.
-  static const int kCounts[] = {24, 16, 12, 8, 6, 4, 3, 2, 1};
+  static const int kCounts[] = {48, 24, 16, 12, 8, 6, 4, 3, 2, 1};
   constexpr int kNCounts = sizeof(kCounts) / sizeof(kCounts[0]);
   int64_t cost[kNCounts];
   int64_t min_cost = -1;
