@@ -84,23 +84,6 @@ levels_t_kernel(const uint8_t* __restrict__ levels, int64_t n_tokens, int n_bins
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// fp32 gradients: chunk `ch`'s 64 x 256 tile straight from global memory into
-// tile buffer `tb` (wave w copies rows 8w .. 8w + 7, one 1 KB row per load:
-// lane i takes columns 4i .. 4i + 3).  Rows past the batch copy the row of
-// -0.0 (their tokens then add exact no-ops); columns past d_model read an
-// in-range address (no lane past d_model writes a result).
-__device__ __forceinline__ void tile_dma(char* tb, const float* g, const float* neg_zero, int64_t n_tokens,
-                                         int d_model, int64_t t0, int c_strip, int wave, int lane) {
-  const int c = min(c_strip + 4 * lane, d_model - 4);
-#pragma unroll
-  for (int i = 0; i < kChunk / kBwdBins; ++i) {
-    const int r = wave * (kChunk / kBwdBins) + i;
-    const int64_t t = t0 + r;
-    const float* src = t < n_tokens ? g + t * d_model + c : neg_zero + 4 * lane;
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(tb + r * kRowBytes), 16, 0, 0);
-  }
-}
-
 // bf16 gradients: read through registers (converted to fp32 on the way), so
 // a tile is loaded into registers during the previous chunk and stored at the
 // top of its own; rows past the batch hold -0.0.
@@ -175,26 +158,20 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // chunk ch + 1 goes to `nxt`.  The two buffers are distinct LDS arrays so
 // that the compiler can see that the reads of one do not wait for the copies
 // into the other.
-template <bool kBf16>
 __device__ __forceinline__ void scatter_chunk(char* cur_tile, char* cur_lv, char* nxt_tile, char* nxt_lv,
-                                              int64_t ch, const void* g, int64_t n_tokens, int n_bins, int d_model,
-                                              const uint8_t* lvt, int64_t t_pad, const float* neg_zero,
-                                              int64_t n_chunks, int c_strip, int bin0, bool bin_ok, int wave,
-                                              int lane, int tid, uint4 (&rb)[kBf16 ? kBf16Items : 1],
-                                              f32x16_t& ax, f32x16_t& ay, f32x16_t& az, f32x16_t& aw) {
-  if (kBf16) tile_store_bf16(cur_tile, reinterpret_cast<uint4(&)[kBf16Items]>(rb), tid);
+                                              int64_t ch, const uint16_t* g, int64_t n_tokens, int n_bins,
+                                              int d_model, const uint8_t* lvt, int64_t t_pad, int64_t n_chunks,
+                                              int c_strip, int bin0, bool bin_ok, int wave, int lane, int tid,
+                                              uint4 (&rb)[kBf16Items], f32x16_t& ax, f32x16_t& ay, f32x16_t& az,
+                                              f32x16_t& aw) {
+  (void)nxt_tile;  // the next tile waits in registers (rb) until its chunk starts
+  tile_store_bf16(cur_tile, rb, tid);
   // this wave's copies of chunk ch have landed; after the barrier every
   // wave's have, and every wave is done with chunk ch - 1
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (ch + 1 < n_chunks) {
-    if (kBf16) {
-      tile_load_bf16(reinterpret_cast<uint4(&)[kBf16Items]>(rb), static_cast<const uint16_t*>(g), n_tokens, d_model,
-                     (ch + 1) * kChunk, c_strip, tid);
-    } else {
-      tile_dma(nxt_tile, static_cast<const float*>(g), neg_zero, n_tokens, d_model, (ch + 1) * kChunk, c_strip, wave,
-               lane);
-    }
+    tile_load_bf16(rb, g, n_tokens, d_model, (ch + 1) * kChunk, c_strip, tid);
     levels_dma(nxt_lv, lvt, t_pad, bin0, n_bins, (ch + 1) * kChunk, wave, lane);
   }
   if (bin_ok) {
@@ -216,7 +193,7 @@ __device__ __forceinline__ void scatter_chunk(char* cur_tile, char* cur_lv, char
   }
 }
 
-// Workgroup (bin group, strip): 8 bins (one wave each) and 256 columns (4
+// bf16 gradients.  Workgroup (bin group, strip): 8 bins (one wave each) and 256 columns (4
 // per lane), walking every chunk of the batch in order.  Per chunk each wave
 // takes the 64 tokens in order: the token's row from the LDS tile (static
 // offsets, read 8 tokens ahead) is added into the accumulator of the token's
@@ -226,12 +203,10 @@ __device__ __forceinline__ void scatter_chunk(char* cur_tile, char* cur_lv, char
 // barrier that starts chunk ch - 1 (all waves have then finished chunk ch - 2,
 // the buffer's previous contents), so it lands while chunk ch - 1 is added;
 // one barrier per chunk.
-template <bool kBf16>
 __global__ void __launch_bounds__(kBwdThreads)
-scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_levels, int d_model,
-               const uint8_t* __restrict__ lvt, int64_t t_pad, const float* __restrict__ neg_zero, int64_t n_chunks,
-               int n_groups, int n_strips, int per_xcd, float* __restrict__ out,
-               int accumulate) {
+scatter_kernel(const uint16_t* __restrict__ g, int64_t n_tokens, int n_bins, int n_levels, int d_model,
+               const uint8_t* __restrict__ lvt, int64_t t_pad, int64_t n_chunks, int n_groups, int n_strips,
+               int per_xcd, float* __restrict__ out, int accumulate) {
   __shared__ __attribute__((aligned(1024))) char tile_a[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char tile_b[kTileBytes];
   __shared__ __attribute__((aligned(16))) char lv_a[kLvBytes];
@@ -255,20 +230,15 @@ scatter_kernel(const void* __restrict__ g, int64_t n_tokens, int n_bins, int n_l
 
   f32x16_t ax = 0.0f, ay = 0.0f, az = 0.0f, aw = 0.0f;
 
-  uint4 rb[kBf16 ? kBf16Items : 1];
-  if (kBf16) {
-    tile_load_bf16(reinterpret_cast<uint4(&)[kBf16Items]>(rb), static_cast<const uint16_t*>(g), n_tokens, d_model,
-                   0, c_strip, tid);
-  } else {
-    tile_dma(tile_a, static_cast<const float*>(g), neg_zero, n_tokens, d_model, 0, c_strip, wave, lane);
-  }
+  uint4 rb[kBf16Items];
+  tile_load_bf16(rb, g, n_tokens, d_model, 0, c_strip, tid);
   levels_dma(lv_a, lvt, t_pad, bin0, n_bins, 0, wave, lane);
   for (int64_t ch = 0; ch < n_chunks; ch += 2) {
-    scatter_chunk<kBf16>(tile_a, lv_a, tile_b, lv_b, ch, g, n_tokens, n_bins, d_model, lvt, t_pad, neg_zero,
-                         n_chunks, c_strip, bin0, bin_ok, wave, lane, tid, rb, ax, ay, az, aw);
+    scatter_chunk(tile_a, lv_a, tile_b, lv_b, ch, g, n_tokens, n_bins, d_model, lvt, t_pad, n_chunks, c_strip, bin0,
+                  bin_ok, wave, lane, tid, rb, ax, ay, az, aw);
     if (ch + 1 < n_chunks) {
-      scatter_chunk<kBf16>(tile_b, lv_b, tile_a, lv_a, ch + 1, g, n_tokens, n_bins, d_model, lvt, t_pad, neg_zero,
-                           n_chunks, c_strip, bin0, bin_ok, wave, lane, tid, rb, ax, ay, az, aw);
+      scatter_chunk(tile_b, lv_b, tile_a, lv_a, ch + 1, g, n_tokens, n_bins, d_model, lvt, t_pad, n_chunks, c_strip,
+                    bin0, bin_ok, wave, lane, tid, rb, ax, ay, az, aw);
     }
   }
 
@@ -825,9 +795,9 @@ hipError_t launch_embed_backward(const uint8_t* levels, int64_t n_tokens, int n_
   const int64_t blocks = static_cast<int64_t>(per_xcd) * 8 * n_groups;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (dsum_bf16) {
-    hipLaunchKernelGGL(scatter_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kBwdThreads), 0, stream, dsum,
-                       n_tokens, n_bins, n_levels, d_model, lvt, t_pad, neg_zero, n_chunks, n_groups, n_strips,
-                       per_xcd, dtable, accumulate ? 1 : 0);
+    hipLaunchKernelGGL(scatter_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBwdThreads), 0, stream,
+                       static_cast<const uint16_t*>(dsum), n_tokens, n_bins, n_levels, d_model, lvt, t_pad, n_chunks,
+                       n_groups, n_strips, per_xcd, dtable, accumulate ? 1 : 0);
   } else {
     const int groups16 = (n_bins + kS16Bins - 1) / kS16Bins;
     const int strips16 = (d_model + kS16Cols - 1) / kS16Cols;
